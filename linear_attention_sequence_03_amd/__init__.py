@@ -1,0 +1,15 @@
+"""Gated delta rule forward pass (Gated DeltaNet / KDA) for MI355X (gfx950).
+
+The compute path is a C-ABI shared library (``libgdr.so``, declared in
+``include/gdr.h``) of hand-written HIP kernels; :mod:`.gdr` is a thin ctypes
+binding with the same entry-point names.  PyTorch is used only for device
+memory and streams.
+"""
+from .gdr import (  # noqa: F401
+    GdrError,
+    gdr_chunk_fwd,
+    gdr_chunk_fwd_workspace_size,
+    gdr_decode_step,
+    gdr_status_string,
+    load_library,
+)

@@ -1,0 +1,116 @@
+"""Seeded synthetic inputs for the gated delta rule (shared by tests and bench).
+
+This module holds no arithmetic of the method itself: it only draws random
+tensors with the distributions of the workloads and rounds them to their storage
+type.  Both the GPU path and the CPU oracle consume exactly the arrays returned
+here (the oracle after an exact widening to fp64).
+
+Distributions (the workloads' recipe):
+  q, k   ~ N(0,1), then scaled to unit L2 norm over d_k per (b,t,h)
+  v      ~ N(0,1)
+  beta   = sigmoid(N(0,1))
+  log_alpha ~ U(-0.1, -0.001)      per (b,t,h), or per (b,t,h,channel)
+  S0 / S ~ N(0, std^2)              when present
+Draw order: q, k, v, beta logits, log_alpha, then S0 / S, from
+``numpy.random.Generator(PCG64(seed))``.  q, k, v are rounded to the storage
+type (bf16 round-to-nearest-even, or fp32); the gates and states are fp32.
+The returned arrays are float32 whose values are exactly representable in the
+storage type, so a cast to bf16 on the device is exact.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    call: str            # "chunk" or "decode"
+    gate: str            # "scalar" (Gated DeltaNet) or "channel" (KDA)
+    io: str              # "f32" or "bf16": storage type of q, k, v and o
+    B: int
+    H: int
+    T: int
+    d: int               # d_k = d_v
+    chunk: int
+    s0_std: Optional[float]
+    tol: float           # normwise relative tolerance of o and of the state
+    seed: int
+
+
+# The five workloads (tokens/s of #1 is the headline number; #4 is the decode step).
+WORKLOADS = [
+    Workload("gdn_chunk_f32_B1_H2_T256_d64", "chunk", "scalar", "f32",
+             1, 2, 256, 64, 64, None, 1e-4, 1000),
+    Workload("gdn_prefill_bf16_B4_H16_T4096_d128", "chunk", "scalar", "bf16",
+             4, 16, 4096, 128, 64, None, 2e-2, 1001),
+    Workload("kda_prefill_bf16_B2_H32_T8192_d128", "chunk", "channel", "bf16",
+             2, 32, 8192, 128, 64, None, 2e-2, 1002),
+    Workload("gdn_prefill_s0_bf16_B1_H32_T32768_d128", "chunk", "scalar", "bf16",
+             1, 32, 32768, 128, 64, 0.02, 2e-2, 1003),
+    Workload("gdn_decode_f32_B256_H32_d128", "decode", "scalar", "f32",
+             256, 32, 1, 128, 0, 0.05, 1e-4, 1004),
+]
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round to the nearest bf16 (ties to even); return float32 holding it."""
+    f = np.ascontiguousarray(x, dtype=np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return (u.astype(np.uint32) << 16).view(np.float32)
+
+
+def _store(x: np.ndarray, io: str) -> np.ndarray:
+    if io == "bf16":
+        return round_bf16(x)
+    if io == "f32":
+        return np.ascontiguousarray(x, dtype=np.float32)
+    raise ValueError(io)
+
+
+def _unit_rows(rng, shape) -> np.ndarray:
+    x = rng.standard_normal(shape)
+    x /= np.linalg.norm(x, axis=-1, keepdims=True)
+    return x
+
+
+def chunk_inputs(B, T, H, dk, dv, gate="scalar", io="bf16", seed=0,
+                 s0_std=None, log_alpha_range=(-0.1, -0.001)):
+    """Inputs of one whole-sequence call, as a dict of float32 numpy arrays."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = _store(_unit_rows(rng, (B, T, H, dk)), io)
+    k = _store(_unit_rows(rng, (B, T, H, dk)), io)
+    v = _store(rng.standard_normal((B, T, H, dv)), io)
+    beta = (1.0 / (1.0 + np.exp(-rng.standard_normal((B, T, H))))).astype(np.float32)
+    la_shape = (B, T, H, dk) if gate == "channel" else (B, T, H)
+    lo, hi = log_alpha_range
+    log_alpha = rng.uniform(lo, hi, la_shape).astype(np.float32)
+    S0 = None
+    if s0_std is not None:
+        S0 = (rng.standard_normal((B, H, dv, dk)) * s0_std).astype(np.float32)
+    return dict(q=q, k=k, v=v, log_alpha=log_alpha, beta=beta, S0=S0)
+
+
+def decode_inputs(B, H, dk, dv, gate="scalar", io="f32", seed=0, s_std=0.05,
+                  log_alpha_range=(-0.1, -0.001)):
+    """Inputs of one decode step, as a dict of float32 numpy arrays."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = _store(_unit_rows(rng, (B, H, dk)), io)
+    k = _store(_unit_rows(rng, (B, H, dk)), io)
+    v = _store(rng.standard_normal((B, H, dv)), io)
+    beta = (1.0 / (1.0 + np.exp(-rng.standard_normal((B, H))))).astype(np.float32)
+    la_shape = (B, H, dk) if gate == "channel" else (B, H)
+    lo, hi = log_alpha_range
+    log_alpha = rng.uniform(lo, hi, la_shape).astype(np.float32)
+    S = (rng.standard_normal((B, H, dv, dk)) * s_std).astype(np.float32)
+    return dict(q=q, k=k, v=v, log_alpha=log_alpha, beta=beta, S=S)
+
+
+def workload_inputs(w: Workload):
+    if w.call == "chunk":
+        return chunk_inputs(w.B, w.T, w.H, w.d, w.d, w.gate, w.io, w.seed, w.s0_std)
+    return decode_inputs(w.B, w.H, w.d, w.d, w.gate, w.io, w.seed, w.s0_std)

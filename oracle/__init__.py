@@ -1,0 +1,13 @@
+"""fp64 CPU oracle of the gated delta rule forward pass (test infrastructure).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
+this package.  The product library never imports, links or calls it, and the
+two share no code.
+
+* :mod:`oracle.gdr_oracle` -- ctypes front end of ``gdr_oracle.c`` (token-by-token
+  fp64 recurrence, threads over independent (b,h) pairs).
+* :mod:`oracle.exact` -- exact rational brute force that multiplies out the
+  explicit per-token transition matrices; used to pin the fp64 oracle on tiny
+  shapes.
+"""
+from .gdr_oracle import build, chunk_fwd, decode_step, library_path, load  # noqa: F401

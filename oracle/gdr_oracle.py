@@ -1,0 +1,129 @@
+"""ctypes front end of the fp64 C oracle (test infrastructure only).
+
+The oracle computes, token by token and in fp64, the gated delta rule
+
+    S_t = S_{t-1} Diag(alpha_t) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+    o_t = S_t q_t,
+
+with ``S`` stored ``[d_v, d_k]`` per head (see ``gdr_oracle.c`` for the page
+citations).  Inputs are converted to fp64 exactly (they are fp32 arrays whose
+values already carry the storage rounding of the GPU inputs), so the comparison
+measures only the GPU path's own error.
+
+``build()`` compiles ``gdr_oracle.c`` with gcc into ``libgdr_oracle.so`` next to
+it; ``chunk_fwd`` / ``decode_step`` build on first use if the library is absent.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gdr_oracle.c")
+_LIB = os.path.join(_HERE, "libgdr_oracle.so")
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB
+
+
+def build(src=None, out=None) -> str:
+    """Compile the C oracle (always recompiles).  Returns the library path."""
+    out = out or _LIB
+    tmp = out + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-pthread", src or _SRC,
+           "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def load(path=None):
+    """Load the oracle library (the default one unless ``path`` is given)."""
+    global _lib
+    if path is None and _lib is not None:
+        return _lib
+    if path is None and not os.path.exists(_LIB):
+        build()
+    lib = ctypes.CDLL(path or _LIB)
+    d = ctypes.POINTER(ctypes.c_double)
+    i64 = ctypes.c_int64
+    lib.gdr_oracle_chunk_fwd.argtypes = [d, d, d, d, d, d, d, d,
+                                         i64, i64, i64, i64, i64,
+                                         ctypes.c_int, ctypes.c_int]
+    lib.gdr_oracle_chunk_fwd.restype = ctypes.c_int
+    lib.gdr_oracle_decode_step.argtypes = [d, d, d, d, d, d, d, d,
+                                           i64, i64, i64, i64, ctypes.c_int]
+    lib.gdr_oracle_decode_step.restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _f64(x):
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a):
+    if a is None:
+        return ctypes.POINTER(ctypes.c_double)()
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def chunk_fwd(q, k, v, log_alpha, beta, S0=None, threads=None, lib=None):
+    """Whole-sequence forward.
+
+    q, k: [B,T,H,dk]; v: [B,T,H,dv]; log_alpha: [B,T,H] (scalar gate) or
+    [B,T,H,dk] (channel gate); beta: [B,T,H]; S0: [B,H,dv,dk] or None (zeros).
+    Returns (o [B,T,H,dv], S_T [B,H,dv,dk]) as fp64 arrays.
+    """
+    q, k, v, la, be = (_f64(a) for a in (q, k, v, log_alpha, beta))
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    channel = la.ndim == 4
+    if k.shape != q.shape or v.shape[:3] != (B, T, H) or be.shape != (B, T, H):
+        raise ValueError("shape mismatch")
+    if la.shape != ((B, T, H, dk) if channel else (B, T, H)):
+        raise ValueError("log_alpha shape mismatch")
+    s0 = None if S0 is None else _f64(S0)
+    if s0 is not None and s0.shape != (B, H, dv, dk):
+        raise ValueError("S0 shape mismatch")
+    o = np.zeros((B, T, H, dv), np.float64)
+    st = np.zeros((B, H, dv, dk), np.float64)
+    n = default_threads() if threads is None else int(threads)
+    rc = (lib or load()).gdr_oracle_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(la), _ptr(be),
+                                      _ptr(s0), _ptr(o), _ptr(st),
+                                      B, T, H, dk, dv, int(channel), n)
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return o, st
+
+
+def decode_step(q, k, v, log_alpha, beta, S, lib=None):
+    """One recurrent step.  q,k: [B,H,dk]; v: [B,H,dv]; log_alpha: [B,H] or
+    [B,H,dk]; beta: [B,H]; S: [B,H,dv,dk].  Returns (o [B,H,dv], S' [B,H,dv,dk])."""
+    q, k, v, la, be, s = (_f64(a) for a in (q, k, v, log_alpha, beta, S))
+    B, H, dk = q.shape
+    dv = v.shape[2]
+    channel = la.ndim == 3
+    if la.shape != ((B, H, dk) if channel else (B, H)) or s.shape != (B, H, dv, dk):
+        raise ValueError("shape mismatch")
+    o = np.zeros((B, H, dv), np.float64)
+    s_out = s.copy()
+    rc = (lib or load()).gdr_oracle_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(la), _ptr(be),
+                                        _ptr(s_out), _ptr(s_out), _ptr(o),
+                                        B, H, dk, dv, int(channel))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return o, s_out
