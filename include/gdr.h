@@ -1,0 +1,126 @@
+/*
+ * gdr.h -- C ABI of the gated delta rule forward pass on MI355X (gfx950).
+ *
+ * The operation (per batch b and head h, tokens t = 0..T-1):
+ *
+ *   S_t = S_{t-1} Diag(alpha_t) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *   o_t = S_t q_t                                   (read-out after the update)
+ *
+ * S is d_v x d_k (row = value channel, column = key channel), alpha_t =
+ * exp(log_alpha_t) is one scalar per (t,h) for Gated DeltaNet or one value per
+ * key channel for Kimi Delta Attention (KDA).  Sources on the pages:
+ *  - "FG2-GDN" page, section 1: Gated DeltaNet's scalar decay alpha_t in (0,1),
+ *    KDA's channel-wise decay Diag(alpha_t), scalar writing rate beta_t;
+ *  - same page, section 3.6 (Chunkwise Parallel Training): the chunkwise WY /
+ *    UT-transform algorithm that gdr_chunk_fwd implements (triangular solve for
+ *    the UT factor, inter-chunk state propagation, intra-chunk causal product);
+ *  - same page, section 5 ("Linear Attention as Recurrent Memory"): the state
+ *    update / read-out family (the page's S is the transpose of the S here);
+ *  - same page, "Limitations / Inference Challenges": a fixed-size d_k x d_v
+ *    state per head that decoding carries and serving may roll back, which is
+ *    why gdr_decode_step may write its new state out of place.
+ *
+ * Conventions shared by every call
+ *  - All pointers are device pointers owned by the caller; the library never
+ *    allocates, frees or retains them.  Work is enqueued asynchronously on
+ *    `stream` (0 = the null stream); buffers must stay valid until it is done.
+ *  - All tensors are dense, row-major and contiguous, with 16-byte aligned base
+ *    addresses.
+ *  - q, k, v and o are fp32 (GDR_F32) or bf16 (GDR_BF16, raw 16-bit words);
+ *    log_alpha, beta and every state are always fp32.
+ *  - Arguments are validated on the host before anything is launched; on any
+ *    error nothing is launched and the call returns a non-zero status.  Input
+ *    values are not inspected: NaN and Inf propagate.
+ *  - Supported shapes: d_k = d_v in {64, 128}; chunk in {16, 32, 64};
+ *    B >= 1, H >= 1, T >= 0 (T = 0 copies S0 to S_T).
+ *  - The functions keep no state between calls and are reentrant.
+ */
+#ifndef GDR_H
+#define GDR_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GDR_OK = 0,
+    GDR_ERR_INVALID_ARG = 1, /* null / misaligned / overlapping pointer, bad size or enum */
+    GDR_ERR_UNSUPPORTED = 2, /* valid request outside the supported shapes      */
+    GDR_ERR_HIP = 3          /* the HIP runtime reported an error at launch     */
+} gdr_status;
+
+typedef enum { GDR_F32 = 0, GDR_BF16 = 1 } gdr_dtype;               /* q, k, v, o */
+typedef enum { GDR_GATE_SCALAR = 0, GDR_GATE_CHANNEL = 1 } gdr_gate; /* GDN / KDA  */
+
+/*
+ * Bytes of device workspace gdr_chunk_fwd needs for these sizes (written to
+ * *bytes).  The workspace holds the per-chunk WY factors (UT factor T, the
+ * masked intra-chunk product, decay-scaled keys and queries for the channel
+ * gate); it is produced and consumed inside one gdr_chunk_fwd call.
+ * Returns GDR_OK, or an error status for unsupported / invalid sizes.
+ */
+gdr_status gdr_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H,
+                                        int64_t dk, int64_t dv, int64_t chunk,
+                                        gdr_dtype io, gdr_gate gate, size_t *bytes);
+
+/*
+ * Whole-sequence (prefill) forward pass, chunkwise-parallel WY form
+ * ("FG2-GDN" page, section 3.6).
+ *
+ *   q, k       [B, T, H, dk]   io dtype
+ *   v          [B, T, H, dv]   io dtype
+ *   log_alpha  [B, T, H]       fp32, natural log of the decay (GDR_GATE_SCALAR)
+ *              [B, T, H, dk]   fp32, per key channel            (GDR_GATE_CHANNEL)
+ *   beta       [B, T, H]       fp32 writing rate
+ *   S0         [B, H, dv, dk]  fp32 initial state, or NULL for zeros
+ *   o          [B, T, H, dv]   io dtype, written (must not overlap any input)
+ *   S_T        [B, H, dv, dk]  fp32 final state, written; or NULL to skip
+ *   chunk      chunk length C; changes speed only, never the result beyond
+ *              rounding
+ *   workspace  device buffer of at least gdr_chunk_fwd_workspace_size() bytes
+ *              (NULL allowed when that size is 0); its contents on entry are
+ *              ignored and on return are unspecified; concurrent calls need
+ *              separate workspaces.
+ * The final chunk may be partial; tokens beyond T are never read or written.
+ */
+gdr_status gdr_chunk_fwd(const void *q, const void *k, const void *v,
+                         const float *log_alpha, const float *beta, const float *S0,
+                         void *o, float *S_T,
+                         int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                         int64_t chunk, gdr_dtype io, gdr_gate gate,
+                         void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * One recurrent decode step (one token per sequence), reading the fixed-size
+ * state and writing the next one ("FG2-GDN" page, section 5 and "Limitations /
+ * Inference Challenges").
+ *
+ *   q, k       [B, H, dk]       io dtype
+ *   v          [B, H, dv]       io dtype
+ *   log_alpha  [B, H] or [B, H, dk]  fp32 (scalar / channel gate)
+ *   beta       [B, H]           fp32
+ *   S_in       [B, H, dv, dk]   fp32 state before the token
+ *   S_out      [B, H, dv, dk]   fp32 state after the token; may equal S_in
+ *                               (in place) but must not partially overlap it
+ *   o          [B, H, dv]       io dtype, written
+ */
+gdr_status gdr_decode_step(const void *q, const void *k, const void *v,
+                           const float *log_alpha, const float *beta,
+                           const float *S_in, float *S_out, void *o,
+                           int64_t B, int64_t H, int64_t dk, int64_t dv,
+                           gdr_dtype io, gdr_gate gate, hipStream_t stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *gdr_status_string(gdr_status s);
+
+/* Details of the last error reported on the calling thread ("" if none). */
+const char *gdr_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GDR_H */

@@ -1,0 +1,114 @@
+// gdr_decode.hip -- one recurrent decode step of the gated delta rule.
+//
+// Per (b,h) and value row i of the fp32 state S [dv][dk]:
+//   s~ = S[i,:] * alpha            decay                 ("FG2-GDN" page, section 1)
+//   p  = s~ . k                    read the memory at k
+//   u  = beta (v_i - p)            delta-rule correction ("FG2-GDN" page, section 5,
+//                                                         "Delta Rule and Online Learning")
+//   S'[i,:] = s~ + u k             rank-1 write
+//   o_i = S'[i,:] . q              read-out after the update
+//
+// The step is a pure HBM stream over the state (read once, write once; no
+// reuse), so the kernel is built for bytes in flight: each lane owns one
+// 16-byte slice (4 key channels) of a row, a wave covers 64*16 bytes = 2 rows
+// (dk=128) or 4 rows (dk=64) per pass, and every lane issues all NPASS row
+// loads before any arithmetic.  Loads and stores are non-temporal (the state
+// is far larger than the caches and is not re-read).  The two dot products are
+// reduced across the lanes of a row with xor shuffles.  In-place (S_out ==
+// S_in) is safe: each 16-byte slice is read and written by the same lane.
+#include "gdr_device.hpp"
+#include "gdr_launch.hpp"
+
+namespace gdr {
+
+template <typename E>
+__device__ __forceinline__ float4 load4(const E* p) {
+    if constexpr (sizeof(E) == 4) {
+        return *reinterpret_cast<const float4*>(p);
+    } else {
+        const bf16x4 x = *reinterpret_cast<const bf16x4*>(p);
+        return make_float4((float)x[0], (float)x[1], (float)x[2], (float)x[3]);
+    }
+}
+
+template <typename E, bool CHANNEL, int DK>
+__global__ __launch_bounds__(256) void decode_kernel(
+    const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
+    const float* __restrict__ log_alpha, const float* __restrict__ beta,
+    const float* S_in, float* S_out, E* __restrict__ o, int64_t BH, int DV) {
+    constexpr int LPR = DK / 4;      // lanes per state row
+    constexpr int RPP = kWave / LPR; // rows per pass of one wave
+    constexpr int NPASS = 4;
+    constexpr int RPW = RPP * NPASS; // rows per wave
+    const int lane = threadIdx.x & 63;
+    const int64_t gw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int wpb = DV / RPW;        // waves per (b,h)
+    const int64_t bh = gw / wpb;
+    if (bh >= BH) return;
+    const int row0 = (int)(gw % wpb) * RPW + lane / LPR;
+    const int c0 = 4 * (lane % LPR);
+
+    const float4 kk = load4(k + bh * DK + c0);
+    const float4 qq = load4(q + bh * DK + c0);
+    float4 aa;
+    if constexpr (CHANNEL) {
+        const float4 la = *reinterpret_cast<const float4*>(log_alpha + bh * DK + c0);
+        aa = make_float4(expf(la.x), expf(la.y), expf(la.z), expf(la.w));
+    } else {
+        const float a = expf(log_alpha[bh]);
+        aa = make_float4(a, a, a, a);
+    }
+    const float b = beta[bh];
+
+    const int64_t base = bh * (int64_t)DV * DK;
+    f32x4 s[NPASS];
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p)
+        s[p] = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4*>(S_in + base + (int64_t)(row0 + p * RPP) * DK + c0));
+
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p) {
+        const int row = row0 + p * RPP;
+        f32x4 sd;
+        sd[0] = s[p][0] * aa.x; sd[1] = s[p][1] * aa.y;
+        sd[2] = s[p][2] * aa.z; sd[3] = s[p][3] * aa.w;
+        float pd = sd[0] * kk.x + sd[1] * kk.y + sd[2] * kk.z + sd[3] * kk.w;
+#pragma unroll
+        for (int m = LPR / 2; m >= 1; m >>= 1) pd += __shfl_xor(pd, m);
+        const float u = b * (to_f32(v[bh * DV + row]) - pd);
+        f32x4 sn;
+        sn[0] = sd[0] + u * kk.x; sn[1] = sd[1] + u * kk.y;
+        sn[2] = sd[2] + u * kk.z; sn[3] = sd[3] + u * kk.w;
+        __builtin_nontemporal_store(
+            sn, reinterpret_cast<f32x4*>(S_out + base + (int64_t)row * DK + c0));
+        float od = sn[0] * qq.x + sn[1] * qq.y + sn[2] * qq.z + sn[3] * qq.w;
+#pragma unroll
+        for (int m = LPR / 2; m >= 1; m >>= 1) od += __shfl_xor(od, m);
+        if (lane % LPR == 0) o[bh * DV + row] = from_f32<E>(od);
+    }
+}
+
+template <typename E, bool CHANNEL, int DK>
+static hipError_t launch_decode(const DecodeArgs& a) {
+    constexpr int RPW = (kWave / (DK / 4)) * 4;
+    const int64_t waves = a.B * a.H * (a.dv / RPW);
+    const int64_t blocks = (waves + 3) / 4;
+    hipLaunchKernelGGL((decode_kernel<E, CHANNEL, DK>), dim3((unsigned)blocks), dim3(256), 0,
+                       a.stream, (const E*)a.q, (const E*)a.k, (const E*)a.v, a.log_alpha,
+                       a.beta, a.S_in, a.S_out, (E*)a.o, a.B * a.H, (int)a.dv);
+    return hipGetLastError();
+}
+
+template <typename E, bool CHANNEL>
+static hipError_t launch_decode_dk(const DecodeArgs& a) {
+    return a.dk == 64 ? launch_decode<E, CHANNEL, 64>(a) : launch_decode<E, CHANNEL, 128>(a);
+}
+
+hipError_t decode_step_launch(const DecodeArgs& a) {
+    if (a.bf16)
+        return a.channel ? launch_decode_dk<__bf16, true>(a) : launch_decode_dk<__bf16, false>(a);
+    return a.channel ? launch_decode_dk<float, true>(a) : launch_decode_dk<float, false>(a);
+}
+
+}  // namespace gdr

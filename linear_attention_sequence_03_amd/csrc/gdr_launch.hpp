@@ -1,0 +1,39 @@
+// gdr_launch.hpp -- internal interface between the C ABI (argument checking)
+// and the kernel launchers.  Arguments reaching these functions are validated.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdr {
+
+struct DecodeArgs {
+    const void *q, *k, *v;
+    const float *log_alpha, *beta, *S_in;
+    float* S_out;
+    void* o;
+    int64_t B, H, dk, dv;
+    bool bf16, channel;
+    hipStream_t stream;
+};
+
+struct ChunkArgs {
+    const void *q, *k, *v;
+    const float *log_alpha, *beta, *S0;
+    void* o;
+    float* S_T;
+    int64_t B, T, H, dk, dv, chunk;
+    bool bf16, channel;
+    void* ws;
+    hipStream_t stream;
+};
+
+hipError_t decode_step_launch(const DecodeArgs& a);
+
+// Workspace bytes of one (b, h, chunk) block and of the whole call.
+size_t chunk_block_bytes(int64_t dk, int64_t chunk, bool bf16, bool channel);
+size_t chunk_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t chunk,
+                             bool bf16, bool channel);
+hipError_t chunk_fwd_launch(const ChunkArgs& a);
+
+}  // namespace gdr

@@ -1,0 +1,184 @@
+"""Thin ctypes binding of libgdr.so (argument marshalling only).
+
+Every computation happens in the HIP kernels behind the C ABI of
+``include/gdr.h``; this module checks tensor dtypes/devices, allocates outputs
+and the workspace with torch (device memory), passes raw pointers and the
+current HIP stream, and turns error codes into exceptions.  There is no CPU
+fallback: if the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY_PATH = os.path.join(_PKG, "libgdr.so")
+
+GDR_OK, GDR_ERR_INVALID_ARG, GDR_ERR_UNSUPPORTED, GDR_ERR_HIP = 0, 1, 2, 3
+GDR_F32, GDR_BF16 = 0, 1
+GDR_GATE_SCALAR, GDR_GATE_CHANNEL = 0, 1
+
+# Every symbol include/gdr.h declares.
+EXPORTS = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_decode_step",
+           "gdr_status_string", "gdr_last_error")
+
+_lib = None
+
+
+class GdrError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def load_library(path: Optional[str] = None):
+    """Load libgdr.so (built in-tree by ``build.py``).  Raises if it is absent."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIBRARY_PATH
+    if not os.path.exists(p):
+        raise ImportError("libgdr.so not built (%s); run "
+                          "`python -m linear_attention_sequence_03_amd.build`" % p)
+    lib = ctypes.CDLL(p)
+    vp, i64, f = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.gdr_status_string.argtypes = [f]
+    lib.gdr_status_string.restype = ctypes.c_char_p
+    lib.gdr_last_error.argtypes = []
+    lib.gdr_last_error.restype = ctypes.c_char_p
+    lib.gdr_chunk_fwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64, f, f,
+                                                 ctypes.POINTER(ctypes.c_size_t)]
+    lib.gdr_chunk_fwd_workspace_size.restype = f
+    lib.gdr_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp,
+                                  i64, i64, i64, i64, i64, i64, f, f,
+                                  vp, ctypes.c_size_t, vp]
+    lib.gdr_chunk_fwd.restype = f
+    lib.gdr_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp,
+                                    i64, i64, i64, i64, f, f, vp]
+    lib.gdr_decode_step.restype = f
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def gdr_status_string(status: int) -> str:
+    return load_library().gdr_status_string(int(status)).decode()
+
+
+def _raise(status: int):
+    lib = load_library()
+    detail = lib.gdr_last_error().decode()
+    raise GdrError(status, "%s: %s" % (lib.gdr_status_string(status).decode(), detail))
+
+
+def _io_code(dtype) -> int:
+    import torch
+    if dtype == torch.float32:
+        return GDR_F32
+    if dtype == torch.bfloat16:
+        return GDR_BF16
+    raise TypeError("q/k/v must be float32 or bfloat16, got %s" % dtype)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _need(name, t, dtype, shape, device):
+    if t.dtype != dtype:
+        raise TypeError("%s: dtype %s, expected %s" % (name, t.dtype, dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s: shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if t.device != device:
+        raise ValueError("%s: on %s, expected %s" % (name, t.device, device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _stream(device, stream):
+    import torch
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def gdr_chunk_fwd_workspace_size(B, T, H, dk, dv, chunk, io, gate) -> int:
+    out = ctypes.c_size_t(0)
+    st = load_library().gdr_chunk_fwd_workspace_size(B, T, H, dk, dv, chunk, io, gate,
+                                                     ctypes.byref(out))
+    if st != GDR_OK:
+        _raise(st)
+    return int(out.value)
+
+
+def gdr_chunk_fwd(q, k, v, log_alpha, beta, S0=None, chunk: int = 64, o=None, S_T=None,
+                  workspace=None, want_state: bool = True, stream=None) -> Tuple:
+    """Whole-sequence forward.  q,k: [B,T,H,dk]; v: [B,T,H,dv] (fp32 or bf16);
+    log_alpha: [B,T,H] (scalar gate) or [B,T,H,dk] (channel gate), fp32;
+    beta: [B,T,H] fp32; S0: [B,H,dv,dk] fp32 or None.
+    Returns (o [B,T,H,dv] in the io dtype, S_T [B,H,dv,dk] fp32 or None)."""
+    import torch
+    dev = q.device
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    io = _io_code(q.dtype)
+    gate = GDR_GATE_CHANNEL if log_alpha.dim() == 4 else GDR_GATE_SCALAR
+    _need("q", q, q.dtype, (B, T, H, dk), dev)
+    _need("k", k, q.dtype, (B, T, H, dk), dev)
+    _need("v", v, q.dtype, (B, T, H, dv), dev)
+    _need("log_alpha", log_alpha, torch.float32,
+          (B, T, H, dk) if gate == GDR_GATE_CHANNEL else (B, T, H), dev)
+    _need("beta", beta, torch.float32, (B, T, H), dev)
+    if S0 is not None:
+        _need("S0", S0, torch.float32, (B, H, dv, dk), dev)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
+    _need("o", o, q.dtype, (B, T, H, dv), dev)
+    if S_T is None and want_state:
+        S_T = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+    if S_T is not None:
+        _need("S_T", S_T, torch.float32, (B, H, dv, dk), dev)
+    nbytes = gdr_chunk_fwd_workspace_size(B, T, H, dk, dv, chunk, io, gate)
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load_library().gdr_chunk_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0), _ptr(o), _ptr(S_T),
+        B, T, H, dk, dv, chunk, io, gate, _ptr(workspace), wbytes, _stream(dev, stream))
+    if st != GDR_OK:
+        _raise(st)
+    return o, S_T
+
+
+def gdr_decode_step(q, k, v, log_alpha, beta, S, S_out=None, o=None, inplace: bool = False,
+                    stream=None) -> Tuple:
+    """One decode step.  q,k: [B,H,dk]; v: [B,H,dv]; log_alpha: [B,H] or [B,H,dk];
+    beta: [B,H]; S: [B,H,dv,dk] fp32.  ``inplace=True`` writes the new state into
+    S.  Returns (o [B,H,dv], S_out)."""
+    import torch
+    dev = q.device
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    io = _io_code(q.dtype)
+    gate = GDR_GATE_CHANNEL if log_alpha.dim() == 3 else GDR_GATE_SCALAR
+    _need("q", q, q.dtype, (B, H, dk), dev)
+    _need("k", k, q.dtype, (B, H, dk), dev)
+    _need("v", v, q.dtype, (B, H, dv), dev)
+    _need("log_alpha", log_alpha, torch.float32,
+          (B, H, dk) if gate == GDR_GATE_CHANNEL else (B, H), dev)
+    _need("beta", beta, torch.float32, (B, H), dev)
+    _need("S", S, torch.float32, (B, H, dv, dk), dev)
+    if inplace:
+        S_out = S
+    elif S_out is None:
+        S_out = torch.empty_like(S)
+    _need("S_out", S_out, torch.float32, (B, H, dv, dk), dev)
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=q.dtype, device=dev)
+    _need("o", o, q.dtype, (B, H, dv), dev)
+    st = load_library().gdr_decode_step(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S), _ptr(S_out), _ptr(o),
+        B, H, dk, dv, io, gate, _stream(dev, stream))
+    if st != GDR_OK:
+        _raise(st)
+    return o, S_out
