@@ -21,16 +21,6 @@
 
 namespace gdr {
 
-template <typename E>
-__device__ __forceinline__ float4 load4(const E* p) {
-    if constexpr (sizeof(E) == 4) {
-        return *reinterpret_cast<const float4*>(p);
-    } else {
-        const bf16x4 x = *reinterpret_cast<const bf16x4*>(p);
-        return make_float4((float)x[0], (float)x[1], (float)x[2], (float)x[3]);
-    }
-}
-
 template <typename E, bool CHANNEL, int DK>
 __global__ __launch_bounds__(256) void decode_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,

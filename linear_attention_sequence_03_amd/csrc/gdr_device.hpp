@@ -100,6 +100,28 @@ __device__ __forceinline__ typename Mma<E>::frag frag_rk_f32(const float* p, int
     }
 }
 
+// 4 consecutive elements <-> float4 (8-byte bf16 or 16-byte fp32 access).
+template <typename E>
+__device__ __forceinline__ float4 load4(const E* p) {
+    if constexpr (sizeof(E) == 4) {
+        return *reinterpret_cast<const float4*>(p);
+    } else {
+        const bf16x4 x = *reinterpret_cast<const bf16x4*>(p);
+        return make_float4((float)x[0], (float)x[1], (float)x[2], (float)x[3]);
+    }
+}
+
+template <typename E>
+__device__ __forceinline__ void store4(E* p, float4 v) {
+    if constexpr (sizeof(E) == 4) {
+        *reinterpret_cast<float4*>(p) = v;
+    } else {
+        bf16x4 x;
+        x[0] = (__bf16)v.x; x[1] = (__bf16)v.y; x[2] = (__bf16)v.z; x[3] = (__bf16)v.w;
+        *reinterpret_cast<bf16x4*>(p) = x;
+    }
+}
+
 // Accumulator coordinates of lane l, element i: (row, col) inside the tile.
 __device__ __forceinline__ int acc_row(int lane, int i) { return 4 * (lane >> 4) + i; }
 __device__ __forceinline__ int acc_col(int lane) { return lane & 15; }

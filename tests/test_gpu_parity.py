@@ -212,7 +212,9 @@ def test_full_forgetting(io):
     q, k, v, be = (inp[n].astype(np.float64) for n in ("q", "k", "v", "beta"))
     want = (be * np.einsum("bthc,bthc->bth", k, q))[..., None] * v
     assert np.isfinite(host(o)).all()
-    assert rel_err(host(o), want) <= (1e-5 if io == "f32" else 4e-3)
+    # bf16: T, D and P are rounded to bf16 as matrix-core operands and o on
+    # output, four roundings of 2^-9 each; the stated bf16 tolerance applies.
+    assert rel_err(host(o), want) <= (1e-5 if io == "f32" else TOL["bf16"])
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
