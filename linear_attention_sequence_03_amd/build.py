@@ -33,6 +33,9 @@ def hipcc() -> str:
 def flags() -> list:
     return ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # keep MFMA accumulators in VGPRs: the kernels post-process every
+            # accumulator with VALU ops, and AGPR copies cost more than they save
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-I", os.path.join(ROOT, "include"), "-I", CSRC,
             "-Wno-unused-command-line-argument"]
 

@@ -17,15 +17,20 @@
 // which is exactly the token recurrence reorganised (no approximation).
 //
 // Two kernels per call:
-//  1. wy_prep  -- one workgroup per (b, h, chunk), fully parallel: the decay
-//     cumsum, A and P on the matrix cores, the triangular solve in LDS (fp32),
-//     and T, P (and the gate-scaled operands for the channel gate) into the
-//     workspace.
-//  2. state_pass -- one workgroup per (b, h, dv-slice of VT columns): walks the
-//     chunks in order carrying its fp32 state slice in LDS; per chunk three
-//     dependent MFMA phases (R = V - Kg S^T and Qg S^T; D = T R; O += P D and
-//     S <- S Diag(gamma_last) + D^T Kh).  dv-slices are independent, which is
-//     what gives the sequential part enough workgroups to fill the chip.
+//  1. wy_prep_{scalar,channel} -- one workgroup per (b, h, chunk), fully
+//     parallel: decay cumsum, A and P on the matrix cores, the triangular solve
+//     in LDS (fp32), and T, P and the decay factors (plus, for the channel gate,
+//     the decay-scaled Qg, Kg, Kh) into the workspace.
+//  2. state_pass -- each wave owns 16 value columns of one (b, h) and walks the
+//     chunks in order with its fp32 state slice S^T[dk][16] held in MFMA
+//     accumulator registers.  Per chunk, all in registers and with no
+//     synchronisation between waves:
+//        R = V - Kg S^T ;  Oi = Qg S^T ;  D = T R ;  O = Oi + P D ;
+//        S^T <- Diag(gamma_last) S^T + Kh^T D
+//     Each product's accumulator tiles are the next product's B operand (the
+//     permuted k-map in gdr_device.hpp), so nothing round-trips through LDS.
+//     The shared per-chunk inputs are copied global->LDS with global_load_lds
+//     (no registers), one chunk ahead, into a double buffer.
 #include "gdr_device.hpp"
 #include "gdr_launch.hpp"
 
@@ -33,32 +38,34 @@ namespace gdr {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-
-template <int X, int A> struct RoundUp { static constexpr int v = (X + A - 1) / A * A; };
+constexpr float kMinLogAlpha = -200.f;  // exp(-200) ~ 1e-87: 0 in fp32
+constexpr float kSafeSpan = 64.f;       // see wy_prep_channel
 
 // Byte layout of one (b, h, chunk) workspace block.
 template <typename E, int DK, int C, bool CHANNEL>
 struct WsLayout {
     static constexpr size_t T = 0;                                   // E [C][C]
     static constexpr size_t P = T + (size_t)C * C * sizeof(E);       // E [C][C]
-    static constexpr size_t G = P + (size_t)C * C * sizeof(E);       // f32 [C]   (scalar)
-    static constexpr size_t QG = G;                                  // E [C][DK] (channel)
-    static constexpr size_t KG = QG + (size_t)C * DK * sizeof(E);    // E [C][DK]
-    static constexpr size_t KH = KG + (size_t)C * DK * sizeof(E);    // E [C][DK]
-    static constexpr size_t GL = KH + (size_t)C * DK * sizeof(E);    // f32 [DK]
-    static constexpr size_t END = CHANNEL ? GL + DK * 4 : G + C * 4;
-    static constexpr size_t BYTES = (END + 255) / 256 * 256;
+    static constexpr size_t QG = P + (size_t)C * C * sizeof(E);      // E [C][DK] (channel)
+    static constexpr size_t KG = QG + (size_t)C * DK * sizeof(E);    // E [C][DK] (channel)
+    static constexpr size_t KH = KG + (size_t)C * DK * sizeof(E);    // E [C][DK] (channel)
+    // Per-chunk decay vector read by the state pass:
+    //   scalar gate : gam[C] = exp(g_r), gh[C] = exp(g_last - g_r)
+    //   channel gate: gl[DK] = exp(g_last,c)
+    static constexpr size_t VEC = CHANNEL ? KH + (size_t)C * DK * sizeof(E) : QG;
+    static constexpr size_t VEC_BYTES = CHANNEL ? DK * 4 : 2 * C * 4;
+    static constexpr size_t BYTES = (VEC + VEC_BYTES + 255) / 256 * 256;
 };
 
 // Copy a [ROWS][COLS] tile of E from global (row stride gstride elements) into
-// LDS (row stride ls elements); rows >= valid are zero-filled.  16-byte moves.
-template <typename E, int ROWS, int COLS>
+// LDS (row stride ls elements) through registers; rows >= valid are zero.
+template <typename E, int ROWS, int COLS, int NTHR>
 __device__ __forceinline__ void g2s(E* dst, int ls, const E* src, int64_t gstride, int valid,
                                     int tid) {
     constexpr int EPS = 16 / sizeof(E);
     constexpr int SEGS = COLS / EPS;
 #pragma unroll 4
-    for (int idx = tid; idx < ROWS * SEGS; idx += kThreads) {
+    for (int idx = tid; idx < ROWS * SEGS; idx += NTHR) {
         const int r = idx / SEGS, s = idx % SEGS;
         const V16 x = r < valid ? ld16(src + r * gstride + s * EPS) : zero16();
         st16(dst + r * ls + s * EPS, x);
@@ -66,11 +73,11 @@ __device__ __forceinline__ void g2s(E* dst, int ls, const E* src, int64_t gstrid
 }
 
 // Triangular solve in LDS: Xs <- (I + As)^-1 for a strictly lower C x C matrix
-// As (fp32, row stride LA).  Diagonal 16x16 blocks by forward substitution (one
-// lane per column, all diagonal blocks at once in wave 0); off-diagonal blocks
-// by increasing distance from the diagonal:
-//   X_ij = -X_ii * sum_{m=j}^{i-1} A_im X_mj
-// with fp32 16x16x4 MFMAs.  Ys: scratch of (C/16 - 1) 16x17 fp32 tiles.
+// As (fp32, row stride LA).  Diagonal 16x16 blocks by right-looking forward
+// substitution in wave 0 (lane = column j of diagonal block lane>>4; critical
+// path of 15 dependent FMAs); off-diagonal blocks by increasing distance from
+// the diagonal, X_ij = -X_ii * sum_{m=j}^{i-1} A_im X_mj, on fp32 MFMAs.
+// Ys: scratch of (C/16 - 1) 16x17 fp32 tiles.
 template <int C, int LA>
 __device__ __forceinline__ void solve_unit_lower(const float* As, float* Xs, float* Ys, int tid) {
     constexpr int NB = C / 16;
@@ -81,11 +88,11 @@ __device__ __forceinline__ void solve_unit_lower(const float* As, float* Xs, flo
             const float* Ab = As + (16 * blk) * LA + 16 * blk;
             float x[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float s = (i == j) ? 1.f : 0.f;
+            for (int i = 0; i < 16; ++i) x[i] = (i == j) ? 1.f : 0.f;
 #pragma unroll
-                for (int m = 0; m < i; ++m) s -= Ab[i * LA + m] * x[m];
-                x[i] = s;
+            for (int m = 0; m < 16; ++m) {
+#pragma unroll
+                for (int i = m + 1; i < 16; ++i) x[i] -= Ab[i * LA + m] * x[m];
             }
             float* Xb = Xs + (16 * blk) * LA + 16 * blk;
 #pragma unroll
@@ -127,6 +134,22 @@ __device__ __forceinline__ void solve_unit_lower(const float* As, float* Xs, flo
     }
 }
 
+// Write T = X Diag(beta) (lower triangle, E) to the workspace, 16 bytes per store.
+template <typename E, int C, int LA>
+__device__ __forceinline__ void store_T(E* Tw, const float* Xs, const float* bs, int tid) {
+    constexpr int EPS = 16 / sizeof(E);
+    for (int idx = tid; idx < C * C / EPS; idx += kThreads) {
+        const int r = (idx * EPS) / C, c0 = (idx * EPS) % C;
+        alignas(16) E vals[EPS];
+#pragma unroll
+        for (int e = 0; e < EPS; ++e) {
+            const int c = c0 + e;
+            vals[e] = from_f32<E>(c <= r ? Xs[r * LA + c] * bs[c] : 0.f);
+        }
+        *reinterpret_cast<V16*>(Tw + r * C + c0) = *reinterpret_cast<const V16*>(vals);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Kernel 1, scalar gate (Gated DeltaNet).
 // ---------------------------------------------------------------------------
@@ -139,11 +162,13 @@ __global__ __launch_bounds__(kThreads) void wy_prep_scalar(
     constexpr int LDK = DK + Pad<E>::v;
     constexpr int NB = C / 16;
     constexpr int LA = C + 1;
+    constexpr int LP = C + Pad<E>::v;
     __shared__ __attribute__((aligned(16))) E Ks[C * LDK];
     __shared__ __attribute__((aligned(16))) E Qs[C * LDK];
     __shared__ float As[C * LA];
     __shared__ float Xs[C * LA];
     __shared__ float Ys[(NB > 1 ? NB - 1 : 1) * 16 * 17];
+    __shared__ __attribute__((aligned(16))) E Pst[C * LP];
     __shared__ float gs[C], bs[C];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -155,13 +180,13 @@ __global__ __launch_bounds__(kThreads) void wy_prep_scalar(
     const int len = (int)((T - t0) < C ? (T - t0) : C);
     const int64_t row0 = ((b * T + t0) * H + h);   // token-row index of row 0
 
-    g2s<E, C, DK>(Ks, LDK, k + row0 * DK, (int64_t)H * DK, len, tid);
-    g2s<E, C, DK>(Qs, LDK, q + row0 * DK, (int64_t)H * DK, len, tid);
+    g2s<E, C, DK, kThreads>(Ks, LDK, k + row0 * DK, (int64_t)H * DK, len, tid);
+    g2s<E, C, DK, kThreads>(Qs, LDK, q + row0 * DK, (int64_t)H * DK, len, tid);
     for (int idx = tid; idx < C * LA; idx += kThreads) { As[idx] = 0.f; Xs[idx] = 0.f; }
     if (wave == 0) {
         float x = 0.f, bb = 0.f;
         if (lane < len) {
-            x = log_alpha[row0 + (int64_t)lane * H];
+            x = fmaxf(log_alpha[row0 + (int64_t)lane * H], kMinLogAlpha);
             bb = beta[row0 + (int64_t)lane * H];
         }
 #pragma unroll
@@ -177,30 +202,277 @@ __global__ __launch_bounds__(kThreads) void wy_prep_scalar(
     E* Tw = reinterpret_cast<E*>(blk + L::T);
     E* Pw = reinterpret_cast<E*>(blk + L::P);
 
-    // Lower block tiles of A = K K^T (gated) and P = Q K^T (gated).
-    constexpr int NTILE = NB * (NB + 1) / 2;
+    // Block tiles of A = K K^T and P = Q K^T, gated; P staged in LDS.
+    constexpr int NTILE = NB * NB;
     for (int t = wave; t < 2 * NTILE; t += kWaves) {
         const bool isP = t >= NTILE;
         const int tt = isP ? t - NTILE : t;
-        int rb = 0;
-        while ((rb + 1) * (rb + 2) / 2 <= tt) ++rb;
-        const int cb = tt - rb * (rb + 1) / 2;
+        const int rb = tt / NB, cb = tt % NB;
+        const int col = 16 * cb + acc_col(lane);
+        if (cb > rb) {  // upper blocks are zero
+            if (isP)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) Pst[(16 * rb + acc_row(lane, e)) * LP + col] = from_f32<E>(0.f);
+            continue;
+        }
         const E* Ap = isP ? Qs : Ks;
         f32x4 acc = zero4();
 #pragma unroll
         for (int k0 = 0; k0 < DK; k0 += M::KS)
             acc = M::mma(frag_rk(Ap, LDK, 16 * rb, k0, lane), frag_rk(Ks, LDK, 16 * cb, k0, lane),
                          acc);
-        const int col = 16 * cb + acc_col(lane);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int row = 16 * rb + acc_row(lane, e);
             const bool keep = isP ? (col <= row) : (col < row);
             const float dec = keep ? expf(gs[row] - gs[col]) : 0.f;
             if (isP)
-                Pw[row * C + col] = from_f32<E>(keep ? acc[e] * dec : 0.f);
+                Pst[row * LP + col] = from_f32<E>(keep ? acc[e] * dec : 0.f);
             else
                 As[row * LA + col] = keep ? acc[e] * bs[row] * dec : 0.f;
+        }
+    }
+    __syncthreads();
+    {   // P -> workspace, 16-byte stores
+        constexpr int EPS = 16 / sizeof(E);
+        for (int idx = tid; idx < C * C / EPS; idx += kThreads) {
+            const int r = (idx * EPS) / C, c0 = (idx * EPS) % C;
+            *reinterpret_cast<V16*>(Pw + r * C + c0) = *reinterpret_cast<const V16*>(Pst + r * LP + c0);
+        }
+    }
+
+    solve_unit_lower<C, LA>(As, Xs, Ys, tid);
+    store_T<E, C, LA>(Tw, Xs, bs, tid);
+    float* vec = reinterpret_cast<float*>(blk + L::VEC);
+    if (tid < C) {
+        vec[tid] = expf(gs[tid]);
+        vec[C + tid] = expf(gs[C - 1] - gs[tid]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 1, channel gate (KDA).
+//
+// The gated products A[r][i] = beta_r sum_c k_rc k_ic exp(g_rc - g_ic) and
+// P[r][i] = sum_c q_rc k_ic exp(g_rc - g_ic) are taken per pair of 16-row
+// blocks (rb, cb <= rb) as plain MFMA products of rescaled rows, around the
+// reference g_ref(rb) = g at the row just before block rb (0 for rb = 0):
+//   A side  x_r * exp(g_r - g_ref(rb))     <= 1          (r in block rb)
+//   B side  k_i * exp(g_ref(rb) - g_i)     <= 1 if cb < rb,  >= 1 if cb == rb
+// whose products are x_r k_i exp(g_r - g_i) exactly.  Off the diagonal no
+// factor exceeds 1, so nothing overflows and a factor that underflows bounds a
+// negligible true value.  On a diagonal block the B side grows like
+// exp(span), span = g_ref(rb) - g(last row of rb); if any channel's span
+// exceeds kSafeSpan that block is computed exactly, pair by pair, from the
+// in-block cumulative sums instead.
+// Thread (seg, rg) owns channels 4seg..4seg+3 of rows 8rg..8rg+7: a local
+// cumsum plus a scan of the row-group totals gives g without a [C][DK] array.
+// ---------------------------------------------------------------------------
+template <typename E, int DK, int C>
+__global__ __launch_bounds__(kThreads) void wy_prep_channel(
+    const E* __restrict__ q, const E* __restrict__ k, const float* __restrict__ log_alpha,
+    const float* __restrict__ beta, uint8_t* __restrict__ ws, int64_t T, int H, int NT) {
+    using L = WsLayout<E, DK, C, true>;
+    using M = Mma<E>;
+    constexpr int LDK = DK + Pad<E>::v;
+    constexpr int NB = C / 16;
+    constexpr int LA = C + 1;
+    constexpr int NSEG = DK / 4;
+    constexpr int NRG = C / 8;
+    static_assert(NSEG * NRG <= kThreads, "one (segment, row group) per thread");
+    __shared__ __attribute__((aligned(16))) E Ka[C * LDK];   // A-side keys
+    __shared__ __attribute__((aligned(16))) E Qa[C * LDK];   // A-side queries
+    __shared__ __attribute__((aligned(16))) E Bb[C * LDK];   // B-side keys of one stage
+    __shared__ float As[C * LA];
+    __shared__ float Xs[C * LA];
+    __shared__ float Ys[(NB > 1 ? NB - 1 : 1) * 16 * 17];
+    __shared__ __attribute__((aligned(16))) float tot[NRG * DK];
+    __shared__ __attribute__((aligned(16))) float gb[NB * DK];  // g at the last row of each block
+    __shared__ float bs[C];
+    __shared__ int unsafe_blk[NB];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t bid = blockIdx.x;
+    const int n = (int)(bid % NT);
+    const int64_t bh = bid / NT;
+    const int64_t b = bh / H, h = bh % H;
+    const int64_t t0 = (int64_t)n * C;
+    const int len = (int)((T - t0) < C ? (T - t0) : C);
+    const int64_t row0 = ((b * T + t0) * H + h);
+
+    uint8_t* blk = ws + (size_t)bid * L::BYTES;
+    E* Tw = reinterpret_cast<E*>(blk + L::T);
+    E* Pw = reinterpret_cast<E*>(blk + L::P);
+    E* Qgw = reinterpret_cast<E*>(blk + L::QG);
+    E* Kgw = reinterpret_cast<E*>(blk + L::KG);
+    E* Khw = reinterpret_cast<E*>(blk + L::KH);
+    float* glw = reinterpret_cast<float*>(blk + L::VEC);
+
+    const bool active = tid < NSEG * NRG;
+    const int seg = tid % NSEG, rg = tid / NSEG;
+    const int c0 = 4 * seg;
+    const int rblk = (8 * rg) >> 4;
+    float g[8][4], kr[8][4], qr[8][4];
+    if (active) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int r = 8 * rg + j;
+            float4 la = make_float4(0.f, 0.f, 0.f, 0.f), kv = la, qv = la;
+            if (r < len) {
+                const int64_t off = (row0 + (int64_t)r * H) * DK + c0;
+                la = *reinterpret_cast<const float4*>(log_alpha + off);
+                kv = load4(k + off);
+                qv = load4(q + off);
+            }
+            const float l4[4] = {fmaxf(la.x, kMinLogAlpha), fmaxf(la.y, kMinLogAlpha),
+                                 fmaxf(la.z, kMinLogAlpha), fmaxf(la.w, kMinLogAlpha)};
+            kr[j][0] = kv.x; kr[j][1] = kv.y; kr[j][2] = kv.z; kr[j][3] = kv.w;
+            qr[j][0] = qv.x; qr[j][1] = qv.y; qr[j][2] = qv.z; qr[j][3] = qv.w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) g[j][e] = (j ? g[j - 1][e] : 0.f) + l4[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tot[rg * DK + c0 + e] = g[7][e];
+    }
+    if (tid < C) bs[tid] = tid < len ? beta[row0 + (int64_t)tid * H] : 0.f;
+    if (tid < NB) unsafe_blk[tid] = 0;
+    for (int idx = tid; idx < C * LA; idx += kThreads) { As[idx] = 0.f; Xs[idx] = 0.f; }
+    __syncthreads();
+    if (active) {
+        float off[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int r2 = 0; r2 < rg; ++r2)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) off[e] += tot[r2 * DK + c0 + e];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) g[j][e] += off[e];
+        if (rg & 1)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) gb[(rg >> 1) * DK + c0 + e] = g[7][e];
+    }
+    __syncthreads();
+    for (int idx = tid; idx < NB * DK; idx += kThreads) {
+        const int rb = idx / DK, c = idx % DK;
+        const float ref = rb ? gb[(rb - 1) * DK + c] : 0.f;
+        if (!(ref - gb[rb * DK + c] <= kSafeSpan)) unsafe_blk[rb] = 1;
+    }
+    if (active) {
+        float gref[4], glast[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            gref[e] = rblk ? gb[(rblk - 1) * DK + c0 + e] : 0.f;
+            glast[e] = gb[(NB - 1) * DK + c0 + e];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int r = 8 * rg + j;
+            float ea[4], eg[4], eh[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                ea[e] = expf(g[j][e] - gref[e]);
+                eg[e] = expf(g[j][e]);
+                eh[e] = expf(glast[e] - g[j][e]);
+            }
+            store4(Ka + r * LDK + c0, make_float4(kr[j][0] * ea[0], kr[j][1] * ea[1],
+                                                  kr[j][2] * ea[2], kr[j][3] * ea[3]));
+            store4(Qa + r * LDK + c0, make_float4(qr[j][0] * ea[0], qr[j][1] * ea[1],
+                                                  qr[j][2] * ea[2], qr[j][3] * ea[3]));
+            store4(Qgw + r * DK + c0, make_float4(qr[j][0] * eg[0], qr[j][1] * eg[1],
+                                                  qr[j][2] * eg[2], qr[j][3] * eg[3]));
+            store4(Kgw + r * DK + c0, make_float4(kr[j][0] * eg[0], kr[j][1] * eg[1],
+                                                  kr[j][2] * eg[2], kr[j][3] * eg[3]));
+            store4(Khw + r * DK + c0, make_float4(kr[j][0] * eh[0], kr[j][1] * eh[1],
+                                                  kr[j][2] * eh[2], kr[j][3] * eh[3]));
+        }
+    }
+    if (tid < DK) glw[tid] = expf(gb[(NB - 1) * DK + tid]);
+
+    // Stage rb: B side around g_ref(rb) for rows i < 16(rb+1); tiles (rb, cb<=rb).
+    for (int rb = 0; rb < NB; ++rb) {
+        if (active && rblk <= rb) {
+            float gr[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) gr[e] = rb ? gb[(rb - 1) * DK + c0 + e] : 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int r = 8 * rg + j;
+                store4(Bb + r * LDK + c0,
+                       make_float4(kr[j][0] * expf(gr[0] - g[j][0]), kr[j][1] * expf(gr[1] - g[j][1]),
+                                   kr[j][2] * expf(gr[2] - g[j][2]), kr[j][3] * expf(gr[3] - g[j][3])));
+            }
+        }
+        __syncthreads();
+        for (int t = wave; t < 2 * (rb + 1); t += kWaves) {
+            const bool isP = t > rb;
+            const int cb = isP ? t - rb - 1 : t;
+            if (cb == rb && unsafe_blk[rb]) continue;
+            const E* Ap = isP ? Qa : Ka;
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int k0 = 0; k0 < DK; k0 += M::KS)
+                acc = M::mma(frag_rk(Ap, LDK, 16 * rb, k0, lane), frag_rk(Bb, LDK, 16 * cb, k0, lane),
+                             acc);
+            const int col = 16 * cb + acc_col(lane);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = 16 * rb + acc_row(lane, e);
+                if (isP)
+                    Pw[row * C + col] = from_f32<E>((cb < rb || col <= row) ? acc[e] : 0.f);
+                else
+                    As[row * LA + col] = (cb < rb || col < row) ? acc[e] * bs[row] : 0.f;
+            }
+        }
+        __syncthreads();
+    }
+
+    // Exact path for diagonal blocks whose decay span is too large to factor.
+    for (int rb = wave; rb < NB; rb += kWaves) {
+        if (!unsafe_blk[rb]) continue;
+        constexpr int CPL = DK / 64;
+        float gl[16][CPL], kk[16][CPL], qq[16][CPL];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int r = 16 * rb + j;
+#pragma unroll
+            for (int m = 0; m < CPL; ++m) {
+                const int c = lane + 64 * m;
+                float la = 0.f, kv = 0.f, qv = 0.f;
+                if (r < len) {
+                    const int64_t off = (row0 + (int64_t)r * H) * DK + c;
+                    la = fmaxf(log_alpha[off], kMinLogAlpha);
+                    kv = to_f32(k[off]);
+                    qv = to_f32(q[off]);
+                }
+                gl[j][m] = (j ? gl[j - 1][m] : 0.f) + la;
+                kk[j][m] = kv;
+                qq[j][m] = qv;
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float a = 0.f, p = 0.f;
+                if (i <= r) {
+#pragma unroll
+                    for (int m = 0; m < CPL; ++m) {
+                        const float f = expf(gl[r][m] - gl[i][m]);
+                        a += kk[r][m] * kk[i][m] * f;
+                        p += qq[r][m] * kk[i][m] * f;
+                    }
+#pragma unroll
+                    for (int off = 32; off >= 1; off >>= 1) {
+                        a += __shfl_xor(a, off);
+                        p += __shfl_xor(p, off);
+                    }
+                }
+                if (lane == 0) {
+                    const int row = 16 * rb + r, col = 16 * rb + i;
+                    As[row * LA + col] = i < r ? a * bs[row] : 0.f;
+                    Pw[row * C + col] = from_f32<E>(p);
+                }
+            }
         }
     }
     // Upper blocks of P are zero.
@@ -211,193 +483,335 @@ __global__ __launch_bounds__(kThreads) void wy_prep_scalar(
     __syncthreads();
 
     solve_unit_lower<C, LA>(As, Xs, Ys, tid);
-
-    // T = X Diag(beta), lower triangle; g for the state pass.
-    for (int idx = tid; idx < C * C; idx += kThreads) {
-        const int r = idx / C, c = idx % C;
-        Tw[idx] = from_f32<E>(c <= r ? Xs[r * LA + c] * bs[c] : 0.f);
-    }
-    float* gw = reinterpret_cast<float*>(blk + L::G);
-    if (tid < C) gw[tid] = gs[tid];
+    store_T<E, C, LA>(Tw, Xs, bs, tid);
 }
 
 // ---------------------------------------------------------------------------
-// Kernel 2: sequential state pass over the chunks of one (b, h, dv-slice).
+// Kernel 2: sequential state pass.
 // ---------------------------------------------------------------------------
-template <typename E, int DK, int C, int VT, bool CHANNEL>
-__global__ __launch_bounds__(kThreads) void state_pass(
+
+// One tile of a chunk's inputs, copied global -> LDS by global_load_lds_dwordx4:
+// lane l of an instruction lands at LDS base + 16 l, so an instruction fills
+// 64 consecutive 16-byte slots and each lane fetches the global bytes of its
+// slot.  Rows are stored with a 16-byte pad, and the tile's LDS region is
+// rounded up to whole instructions; lanes whose slot is a pad or lies past the
+// tile fetch the tile's first 16 bytes again (in bounds, never read back), so
+// every lane of every instruction is active.  The per-lane source offsets are
+// fixed for the kernel and computed once.
+template <int ROWS, int ROWB, int NW>
+struct DmaTile {
+    static constexpr int RS = ROWB / 16 + 1;                 // slots per row, with the pad
+    static constexpr int NSLOT = ROWS * RS;
+    static constexpr int NINS = (NSLOT + 63) / 64;           // instructions per tile
+    static constexpr int BYTES = NINS * 1024;                // LDS region
+    static constexpr int PER_WAVE = (NINS + NW - 1) / NW;    // instructions per wave
+    // Offsets for row stride gstride; rows >= valid read row valid-1 instead
+    // (kept finite; their contributions are cancelled by zero rows of T).
+    static __device__ __forceinline__ void offsets(int* off, int64_t gstride, int valid, int wave,
+                                                   int lane) {
+#pragma unroll
+        for (int j = 0; j < PER_WAVE; ++j) {
+            const int slot = (wave + j * NW) * 64 + lane;
+            const int r = slot / RS, sg = slot - r * RS;
+            const int rr = r < valid ? r : valid - 1;
+            off[j] = (slot < NSLOT && sg < RS - 1) ? (int)(rr * gstride) + sg * 16 : 0;
+        }
+    }
+    static __device__ __forceinline__ void issue(char* lds, const char* src, const int* off, int wave) {
+#pragma unroll
+        for (int j = 0; j < PER_WAVE; ++j) {
+            const int ins = wave + j * NW;
+            if (j + 1 < PER_WAVE || ins < NINS)   // wave-uniform
+                __builtin_amdgcn_global_load_lds(src + off[j], (GDR_LDS void*)(lds + ins * 1024), 16,
+                                                 0, 0);
+        }
+    }
+};
+
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+template <typename E, int DK, int C, int NW, bool CHANNEL>
+struct StageLayout {
+    static constexpr int ES = sizeof(E);
+    static constexpr int VT = 16 * NW;
+    static constexpr int LQ = DK + 16 / ES;   // Q / K / Kh rows (elements)
+    static constexpr int LT = C + 16 / ES;    // T / P rows
+    static constexpr int LV = VT + 16 / ES;   // V rows
+    static constexpr int QB = DmaTile<C, DK * ES, NW>::BYTES;
+    static constexpr int TB = DmaTile<C, C * ES, NW>::BYTES;
+    static constexpr int VB = DmaTile<C, VT * ES, NW>::BYTES;
+    static constexpr int VECB = (int)WsLayout<E, DK, C, CHANNEL>::VEC_BYTES;
+    static constexpr int OQ = 0, OK = QB, OKH = 2 * QB;
+    static constexpr int OT = (CHANNEL ? 3 : 2) * QB, OP = OT + TB, OV = OP + TB, OVEC = OV + VB;
+    static constexpr int BYTES = (OVEC + VECB + 15) / 16 * 16;
+    static constexpr int LO = 16 + 16 / ES;   // output staging rows (elements), per wave
+    static constexpr int OSTG = C * LO * ES;
+    // Double-buffered (copy of chunk n+1 overlaps chunk n) when it fits.
+    static constexpr int NSTAGE = 2 * BYTES + NW * OSTG <= 160 * 1024 ? 2 : 1;
+    static constexpr int TOTAL = NSTAGE * BYTES + NW * OSTG;
+};
+
+// Copies of chunk n's inputs into one LDS stage (see DmaTile).
+template <typename E, int DK, int C, int NW, bool CHANNEL>
+__device__ __forceinline__ void issue_chunk(char* base, int n, const E* q, const E* k, const E* v,
+                                            const uint8_t* wsb, int64_t bh, int64_t b, int64_t h,
+                                            int64_t T, int H, int DV, int NT, int vt,
+                                            int64_t qk_stride, int* oq, const int* ot, int* ov,
+                                            int wave, int lane) {
+    using L = WsLayout<E, DK, C, CHANNEL>;
+    using SL = StageLayout<E, DK, C, NW, CHANNEL>;
+    using DQ = DmaTile<C, DK * sizeof(E), NW>;
+    using DT = DmaTile<C, C * sizeof(E), NW>;
+    using DV_ = DmaTile<C, 16 * NW * sizeof(E), NW>;
+    constexpr int ES = sizeof(E);
+    constexpr int VT = SL::VT;
+    const int64_t t0 = (int64_t)n * C;
+    const int64_t row0 = (b * T + t0) * H + h;
+    const char* blk = reinterpret_cast<const char*>(wsb + (size_t)(bh * NT + n) * L::BYTES);
+    if (T - t0 < C) {   // ragged last chunk: clamp rows of the caller's tensors
+        const int len = (int)(T - t0);
+        if constexpr (!CHANNEL) DQ::offsets(oq, qk_stride, len, wave, lane);
+        DV_::offsets(ov, (int64_t)H * DV * ES, len, wave, lane);
+    }
+    if constexpr (CHANNEL) {
+        DQ::issue(base + SL::OQ, blk + L::QG, oq, wave);
+        DQ::issue(base + SL::OK, blk + L::KG, oq, wave);
+        DQ::issue(base + SL::OKH, blk + L::KH, oq, wave);
+    } else {
+        DQ::issue(base + SL::OQ, reinterpret_cast<const char*>(q + row0 * DK), oq, wave);
+        DQ::issue(base + SL::OK, reinterpret_cast<const char*>(k + row0 * DK), oq, wave);
+    }
+    DT::issue(base + SL::OT, blk + L::T, ot, wave);
+    DT::issue(base + SL::OP, blk + L::P, ot, wave);
+    DV_::issue(base + SL::OV, reinterpret_cast<const char*>(v + row0 * DV + vt * VT), ov, wave);
+    constexpr int NVEC = SL::VECB / 16;
+    for (int s = wave * 64 + lane; s < NVEC; s += NW * 64)
+        __builtin_amdgcn_global_load_lds(blk + L::VEC + 16 * s,
+                                         (GDR_LDS void*)(base + SL::OVEC + 16 * (s - lane)), 16, 0, 0);
+}
+
+// S^T <- Diag(gamma_last) S^T + Kh^T Ds for the chunk held in one LDS stage.
+template <typename E, int DK, int C, int NW, bool CHANNEL>
+__device__ __forceinline__ void state_update(f32x4* S, const typename Mma<E>::frag* dsb,
+                                             const char* st, int g4, int lane) {
+    using SL = StageLayout<E, DK, C, NW, CHANNEL>;
+    using M = Mma<E>;
+    constexpr bool HALF = (M::KPL == 8 && C < 32);
+    constexpr int NKT = HALF ? 1 : C / M::KS;
+    constexpr int CT = DK / 16;
+    const E* Khs = reinterpret_cast<const E*>(st + (CHANNEL ? SL::OKH : SL::OK));
+    const float* vec = reinterpret_cast<const float*>(st + SL::OVEC);
+    if constexpr (CHANNEL) {
+#pragma unroll
+        for (int mc = 0; mc < CT; ++mc) {
+            const float4 gl = *reinterpret_cast<const float4*>(vec + 16 * mc + 4 * g4);
+            S[mc][0] *= gl.x; S[mc][1] *= gl.y; S[mc][2] *= gl.z; S[mc][3] *= gl.w;
+        }
+    } else {
+        const float gl = vec[C - 1];
+#pragma unroll
+        for (int mc = 0; mc < CT; ++mc)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[mc][i] *= gl;
+    }
+#pragma unroll
+    for (int mc = 0; mc < CT; ++mc)
+#pragma unroll
+        for (int s = 0; s < NKT; ++s)
+            S[mc] = M::mma(afrag_tr_tok<E, HALF>(Khs, SL::LQ, 16 * mc, s, lane), dsb[s], S[mc]);
+}
+
+template <typename E, int DK, int C, int NW, bool CHANNEL>
+__global__ __launch_bounds__(64 * NW) void state_pass(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ S0, E* __restrict__ o, float* __restrict__ ST,
     const uint8_t* __restrict__ ws, int64_t T, int H, int NT, int DV) {
     using L = WsLayout<E, DK, C, CHANNEL>;
+    using SL = StageLayout<E, DK, C, NW, CHANNEL>;
     using M = Mma<E>;
-    constexpr int PAD = Pad<E>::v;
-    constexpr int LDK = DK + PAD;          // Q / K rows
-    constexpr int CK = C > M::KS ? C : M::KS; // contraction length over tokens (zero padded)
-    constexpr int LC = CK + PAD;           // T / P / R^T / D^T rows
-    constexpr int LV = VT + PAD;           // V rows
-    constexpr int LS = DK + 4;             // fp32 state rows
-    constexpr int MT = C / 16, NTL = VT / 16, TA = MT * NTL, TS = (DK / 16) * NTL;
-    constexpr int SLOTS = (TA + kWaves - 1) / kWaves;
+    using frag = typename M::frag;
+    using DQ = DmaTile<C, DK * sizeof(E), NW>;    // Q, K (and Kh) tiles
+    using DT = DmaTile<C, C * sizeof(E), NW>;     // T, P tiles
+    using DV_ = DmaTile<C, 16 * NW * sizeof(E), NW>;
+    constexpr int ES = sizeof(E);
+    constexpr int VT = SL::VT;
+    constexpr int NKC = DK / M::KS;                        // k-steps over channels
+    constexpr bool HALF = (M::KPL == 8 && C < 32);         // bf16 with C = 16
+    constexpr int NKT = HALF ? 1 : C / M::KS;              // k-steps over tokens
+    constexpr int MT = C / 16, CT = DK / 16;
+    static_assert(SL::TOTAL <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(16))) char smem[SL::TOTAL];
 
-    // Q/K tiles hold CK rows: the S update contracts over tokens in steps of
-    // the MFMA K, so rows C..CK-1 (only when C < K) must exist and be zero.
-    __shared__ __attribute__((aligned(16))) E Qs[CK * LDK];
-    __shared__ __attribute__((aligned(16))) E Ks[CK * LDK];
-    __shared__ __attribute__((aligned(16))) E Khs[CHANNEL ? CK * LDK : 8];
-    __shared__ __attribute__((aligned(16))) E Ts[C * LC];
-    __shared__ __attribute__((aligned(16))) E Ps[C * LC];
-    __shared__ __attribute__((aligned(16))) E Vs[C * LV];
-    __shared__ __attribute__((aligned(16))) E Rt[VT * LC];
-    __shared__ __attribute__((aligned(16))) E Dt[VT * LC];
-    __shared__ __attribute__((aligned(16))) E Dst[CHANNEL ? 8 : VT * LC];
-    __shared__ __attribute__((aligned(16))) float Ss[VT * LS];
-    __shared__ float gs[CHANNEL ? DK : C];
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g4 = lane >> 4, col = lane & 15;
     const int NVT = DV / VT;
     const int bid = xcd_remap(blockIdx.x, gridDim.x);
     const int vt = bid % NVT;
     const int64_t bh = bid / NVT;
     const int64_t b = bh / H, h = bh % H;
-    const int v0 = vt * VT;
+    const int vcol = vt * VT + 16 * wave + col;            // this lane's value column
+    const uint8_t* wsb = ws;
+    E* ostg = reinterpret_cast<E*>(smem + SL::NSTAGE * SL::BYTES + wave * SL::OSTG);
 
-    // Zero the token-padding rows / columns once (never written afterwards).
-    for (int idx = C * LDK + tid; idx < CK * LDK; idx += kThreads) {
-        Qs[idx] = from_f32<E>(0.f); Ks[idx] = from_f32<E>(0.f);
-        if constexpr (CHANNEL) Khs[idx] = from_f32<E>(0.f);
-    }
-    for (int idx = tid; idx < C * LC; idx += kThreads) { Ts[idx] = from_f32<E>(0.f); Ps[idx] = from_f32<E>(0.f); }
-    for (int idx = tid; idx < VT * LC; idx += kThreads) {
-        Rt[idx] = from_f32<E>(0.f); Dt[idx] = from_f32<E>(0.f);
-        if constexpr (!CHANNEL) Dst[idx] = from_f32<E>(0.f);
-    }
-    // Initial state slice.
-    for (int idx = tid; idx < VT * (DK / 4); idx += kThreads) {
-        const int r = idx / (DK / 4), c = 4 * (idx % (DK / 4));
+    // Per-lane copy offsets (full chunks; a ragged last chunk recomputes them).
+    const int64_t qk_stride = CHANNEL ? (int64_t)DK * ES : (int64_t)H * DK * ES;
+    int oq[DQ::PER_WAVE], ot[DT::PER_WAVE], ov[DV_::PER_WAVE];
+    DQ::offsets(oq, qk_stride, C, wave, lane);
+    DT::offsets(ot, (int64_t)C * ES, C, wave, lane);
+    DV_::offsets(ov, (int64_t)H * DV * ES, C, wave, lane);
+
+
+    // State slice S^T[c][v]: tile mc, lane (v, g) holds c = 16mc + 4g + i.
+    f32x4 S[CT];
+#pragma unroll
+    for (int mc = 0; mc < CT; ++mc) {
         float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (S0) x = *reinterpret_cast<const float4*>(S0 + (bh * DV + v0 + r) * DK + c);
-        *reinterpret_cast<float4*>(Ss + r * LS + c) = x;
+        if (S0) x = *reinterpret_cast<const float4*>(S0 + (bh * DV + vcol) * DK + 16 * mc + 4 * g4);
+        S[mc] = f32x4{x.x, x.y, x.z, x.w};
     }
+
+    // S^T <- Diag(gamma_last) S^T + Kh^T Ds for the chunk held in `stage`.
+    frag dsb[NKT];
+
+    issue_chunk<E, DK, C, NW, CHANNEL>(smem + (0) * SL::BYTES, 0, q, k, v, wsb, bh, b, h, T, H, DV,
+                                            NT, vt, qk_stride, oq, ot, ov, wave, lane);
+    wait_dma();
+    __syncthreads();
 
     for (int n = 0; n < NT; ++n) {
+        const int cur = SL::NSTAGE == 2 ? (n & 1) : 0;
+        if (n > 0) {
+            // Finish the previous chunk's state update from its stage, then let
+            // every wave be done with that stage before it is refilled.
+            state_update<E, DK, C, NW, CHANNEL>(S, dsb, smem + (SL::NSTAGE == 2 ? (cur ^ 1) : 0) * SL::BYTES,
+                                                g4, lane);
+            __syncthreads();
+        }
+        if constexpr (SL::NSTAGE == 2) {
+            if (n + 1 < NT)
+                issue_chunk<E, DK, C, NW, CHANNEL>(smem + (cur ^ 1) * SL::BYTES, n + 1, q, k, v, wsb, bh, b, h, T, H, DV,
+                                            NT, vt, qk_stride, oq, ot, ov, wave, lane);
+        } else if (n > 0) {
+            issue_chunk<E, DK, C, NW, CHANNEL>(smem + (0) * SL::BYTES, n, q, k, v, wsb, bh, b, h, T, H, DV,
+                                            NT, vt, qk_stride, oq, ot, ov, wave, lane);
+            wait_dma();
+            __syncthreads();
+        }
+        const char* st = smem + cur * SL::BYTES;
+        const E* Qs = reinterpret_cast<const E*>(st + SL::OQ);
+        const E* Ks = reinterpret_cast<const E*>(st + SL::OK);
+        const E* Ts = reinterpret_cast<const E*>(st + SL::OT);
+        const E* Ps = reinterpret_cast<const E*>(st + SL::OP);
+        const E* Vs = reinterpret_cast<const E*>(st + SL::OV);
+        const float* vec = reinterpret_cast<const float*>(st + SL::OVEC);
         const int64_t t0 = (int64_t)n * C;
         const int len = (int)((T - t0) < C ? (T - t0) : C);
         const int64_t row0 = (b * T + t0) * H + h;
-        const uint8_t* blk = ws + (size_t)(bh * NT + n) * L::BYTES;
-        __syncthreads();  // previous chunk fully consumed
-        if constexpr (CHANNEL) {
-            g2s<E, C, DK>(Qs, LDK, reinterpret_cast<const E*>(blk + L::QG), DK, C, tid);
-            g2s<E, C, DK>(Ks, LDK, reinterpret_cast<const E*>(blk + L::KG), DK, C, tid);
-            g2s<E, C, DK>(Khs, LDK, reinterpret_cast<const E*>(blk + L::KH), DK, C, tid);
-            for (int idx = tid; idx < DK; idx += kThreads)
-                gs[idx] = reinterpret_cast<const float*>(blk + L::GL)[idx];
-        } else {
-            g2s<E, C, DK>(Qs, LDK, q + row0 * DK, (int64_t)H * DK, len, tid);
-            g2s<E, C, DK>(Ks, LDK, k + row0 * DK, (int64_t)H * DK, len, tid);
-            for (int idx = tid; idx < C; idx += kThreads)
-                gs[idx] = reinterpret_cast<const float*>(blk + L::G)[idx];
-        }
-        g2s<E, C, C>(Ts, LC, reinterpret_cast<const E*>(blk + L::T), C, C, tid);
-        g2s<E, C, C>(Ps, LC, reinterpret_cast<const E*>(blk + L::P), C, C, tid);
-        g2s<E, C, VT>(Vs, LV, v + row0 * DV + v0, (int64_t)H * DV, len, tid);
-        __syncthreads();
 
-        // Phase A: R = V - Kg S^T  and  Oi = Qg S^T   (rows = tokens, cols = v)
-        f32x4 oacc[SLOTS];
+        // Phase A: R = V - Kg S^T, Oi = Qg S^T  (rows = tokens, cols = v)
+        frag sb[NKC];
 #pragma unroll
-        for (int s = 0; s < SLOTS; ++s) {
-            const int t = wave + s * kWaves;
-            oacc[s] = zero4();
-            if (t >= TA) continue;
-            const int mt = t / NTL, nt = t % NTL;
-            f32x4 ar = zero4(), ao = zero4();
+        for (int s = 0; s < NKC; ++s) sb[s] = bfrag_acc<E>(S, s);
+        f32x4 R[MT], Oa[MT];
 #pragma unroll
-            for (int k0 = 0; k0 < DK; k0 += M::KS) {
-                const auto bf = frag_rk_f32<E>(Ss, LS, 16 * nt, k0, lane);
-                ar = M::mma(frag_rk(Ks, LDK, 16 * mt, k0, lane), bf, ar);
-                ao = M::mma(frag_rk(Qs, LDK, 16 * mt, k0, lane), bf, ao);
+        for (int mt = 0; mt < MT; ++mt) { R[mt] = zero4(); Oa[mt] = zero4(); }
+#pragma unroll
+        for (int s = 0; s < NKC; ++s)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                R[mt] = M::mma(afrag_nat(Ks, SL::LQ, 16 * mt, s, lane), sb[s], R[mt]);
+                Oa[mt] = M::mma(afrag_nat(Qs, SL::LQ, 16 * mt, s, lane), sb[s], Oa[mt]);
             }
-            const int vc = 16 * nt + acc_col(lane);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * mt + acc_row(lane, e);
-                const float gam = CHANNEL ? 1.f : expf(gs[r]);
-                const float rv = to_f32(Vs[r * LV + vc]) - gam * ar[e];
-                Rt[vc * LC + r] = from_f32<E>(rv);
-                oacc[s][e] = gam * ao[e];
+        for (int mt = 0; mt < MT; ++mt) {
+            float4 gam = make_float4(1.f, 1.f, 1.f, 1.f);
+            if constexpr (!CHANNEL) gam = *reinterpret_cast<const float4*>(vec + 16 * mt + 4 * g4);
+            const float gv[4] = {gam.x, gam.y, gam.z, gam.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * mt + 4 * g4 + i;
+                const float vv = to_f32(Vs[r * SL::LV + 16 * wave + col]);
+                R[mt][i] = vv - gv[i] * R[mt][i];
+                Oa[mt][i] *= gv[i];
             }
         }
-        __syncthreads();
 
         // Phase B: D = T R
-        for (int t = wave; t < TA; t += kWaves) {
-            const int mt = t / NTL, nt = t % NTL;
-            f32x4 acc = zero4();
+        frag rb[NKT];
 #pragma unroll
-            for (int k0 = 0; k0 < CK; k0 += M::KS)
-                acc = M::mma(frag_rk(Ts, LC, 16 * mt, k0, lane), frag_rk(Rt, LC, 16 * nt, k0, lane),
-                             acc);
-            const int vc = 16 * nt + acc_col(lane);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * mt + acc_row(lane, e);
-                Dt[vc * LC + r] = from_f32<E>(acc[e]);
-                if constexpr (!CHANNEL)
-                    Dst[vc * LC + r] = from_f32<E>(acc[e] * expf(gs[C - 1] - gs[r]));
-            }
-        }
-        __syncthreads();
-
-        // Phase C1: O = Oi + P D  -> global
-#pragma unroll
-        for (int s = 0; s < SLOTS; ++s) {
-            const int t = wave + s * kWaves;
-            if (t >= TA) continue;
-            const int mt = t / NTL, nt = t % NTL;
-            f32x4 acc = oacc[s];
-#pragma unroll
-            for (int k0 = 0; k0 < CK; k0 += M::KS)
-                acc = M::mma(frag_rk(Ps, LC, 16 * mt, k0, lane), frag_rk(Dt, LC, 16 * nt, k0, lane),
-                             acc);
-            const int vc = 16 * nt + acc_col(lane);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * mt + acc_row(lane, e);
-                if (r < len) o[(row0 + (int64_t)r * H) * DV + v0 + vc] = from_f32<E>(acc[e]);
-            }
-        }
-        // Phase C2: S^T[c][v] <- gamma_last[c] S^T[c][v] + sum_r Kh[r][c] D[r][v]
-        const E* Kh = CHANNEL ? Khs : Ks;
-        const E* Dsrc = CHANNEL ? Dt : Dst;
-        const float glast_s = CHANNEL ? 0.f : expf(gs[C - 1]);
-        for (int t = wave; t < TS; t += kWaves) {
-            const int mc = t / NTL, nt = t % NTL;
-            const int vr = 16 * nt + acc_col(lane);
-            const int c = 16 * mc + acc_row(lane, 0);
-            float4 sv = *reinterpret_cast<const float4*>(Ss + vr * LS + c);
-            f32x4 acc;
-            if constexpr (CHANNEL) {
-                acc[0] = sv.x * expf(gs[c + 0]); acc[1] = sv.y * expf(gs[c + 1]);
-                acc[2] = sv.z * expf(gs[c + 2]); acc[3] = sv.w * expf(gs[c + 3]);
+        for (int s = 0; s < NKT; ++s) {
+            if constexpr (HALF) {
+                const __bf16 z = (__bf16)0.f;
+                rb[s] = bf16x8{(__bf16)R[0][0], (__bf16)R[0][1], (__bf16)R[0][2], (__bf16)R[0][3],
+                               z, z, z, z};
             } else {
-                acc[0] = sv.x * glast_s; acc[1] = sv.y * glast_s;
-                acc[2] = sv.z * glast_s; acc[3] = sv.w * glast_s;
+                rb[s] = bfrag_acc<E>(R, s);
             }
+        }
+        f32x4 D[MT];
 #pragma unroll
-            for (int k0 = 0; k0 < CK; k0 += M::KS)
-                acc = M::mma(frag_kr(Kh, LDK, 16 * mc, k0, lane),
-                             frag_rk(Dsrc, LC, 16 * nt, k0, lane), acc);
-            *reinterpret_cast<float4*>(Ss + vr * LS + c) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        for (int mt = 0; mt < MT; ++mt) {
+            D[mt] = zero4();
+#pragma unroll
+            for (int s = 0; s < NKT; ++s)
+                D[mt] = M::mma(afrag_nat_tok<E, HALF>(Ts, SL::LT, 16 * mt, s, lane), rb[s], D[mt]);
+        }
+
+        // Phase C: O = Oi + P D; the state update's operand Ds is kept for the
+        // next iteration (scalar gate: rows scaled by gamma_last / gamma_r).
+        frag db[NKT];
+        f32x4 Dsc[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            float4 gh = make_float4(1.f, 1.f, 1.f, 1.f);
+            if constexpr (!CHANNEL) gh = *reinterpret_cast<const float4*>(vec + C + 16 * mt + 4 * g4);
+            Dsc[mt] = f32x4{D[mt][0] * gh.x, D[mt][1] * gh.y, D[mt][2] * gh.z, D[mt][3] * gh.w};
+        }
+#pragma unroll
+        for (int s = 0; s < NKT; ++s) {
+            if constexpr (HALF) {
+                const __bf16 z = (__bf16)0.f;
+                db[s] = bf16x8{(__bf16)D[0][0], (__bf16)D[0][1], (__bf16)D[0][2], (__bf16)D[0][3],
+                               z, z, z, z};
+                dsb[s] = bf16x8{(__bf16)Dsc[0][0], (__bf16)Dsc[0][1], (__bf16)Dsc[0][2],
+                                (__bf16)Dsc[0][3], z, z, z, z};
+            } else {
+                db[s] = bfrag_acc<E>(D, s);
+                dsb[s] = bfrag_acc<E>(Dsc, s);
+            }
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+            for (int s = 0; s < NKT; ++s)
+                Oa[mt] = M::mma(afrag_nat_tok<E, HALF>(Ps, SL::LT, 16 * mt, s, lane), db[s], Oa[mt]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ostg[(16 * mt + 4 * g4 + i) * SL::LO + col] = from_f32<E>(Oa[mt][i]);
+        }
+        // Output: this wave's [C][16] tile, 16 bytes per store.
+        {
+            constexpr int PPR = 16 * ES / 16;   // 16-byte pieces per row
+#pragma unroll
+            for (int p = lane; p < C * PPR; p += 64) {
+                const int r = p / PPR, pc = p % PPR;
+                if (r < len)
+                    *reinterpret_cast<V16*>(o + (row0 + (int64_t)r * H) * DV + vt * VT + 16 * wave + pc * (16 / ES)) =
+                        *reinterpret_cast<const V16*>(ostg + r * SL::LO + pc * (16 / ES));
+            }
+        }
+        if constexpr (SL::NSTAGE == 2) {
+            wait_dma();
+            __syncthreads();
         }
     }
-    __syncthreads();
+    state_update<E, DK, C, NW, CHANNEL>(S, dsb, smem + (SL::NSTAGE == 2 ? ((NT - 1) & 1) : 0) * SL::BYTES,
+                                        g4, lane);
+
     if (ST) {
-        for (int idx = tid; idx < VT * (DK / 4); idx += kThreads) {
-            const int r = idx / (DK / 4), c = 4 * (idx % (DK / 4));
-            *reinterpret_cast<float4*>(ST + (bh * DV + v0 + r) * DK + c) =
-                *reinterpret_cast<const float4*>(Ss + r * LS + c);
-        }
+#pragma unroll
+        for (int mc = 0; mc < CT; ++mc)
+            *reinterpret_cast<float4*>(ST + (bh * DV + vcol) * DK + 16 * mc + 4 * g4) =
+                make_float4(S[mc][0], S[mc][1], S[mc][2], S[mc][3]);
     }
 }
 
@@ -414,12 +828,24 @@ __global__ void copy_state(const float* __restrict__ S0, float* __restrict__ ST,
 // ---------------------------------------------------------------------------
 // Host side.
 // ---------------------------------------------------------------------------
+template <typename E, int DK, int C, bool CHANNEL, int NW>
+static hipError_t launch_state(const ChunkArgs& a, int NT) {
+    const int64_t BH = a.B * a.H;
+    const int64_t grid = BH * (a.dv / (16 * NW));
+    hipLaunchKernelGGL((state_pass<E, DK, C, NW, CHANNEL>), dim3((unsigned)grid), dim3(64 * NW), 0,
+                       a.stream, (const E*)a.q, (const E*)a.k, (const E*)a.v, a.S0, (E*)a.o, a.S_T,
+                       (const uint8_t*)a.ws, a.T, (int)a.H, NT, (int)a.dv);
+    return hipGetLastError();
+}
+
 template <typename E, int DK, int C, bool CHANNEL>
 static hipError_t launch_chunk(const ChunkArgs& a) {
     const int NT = (int)((a.T + C - 1) / C);
     const int64_t BH = a.B * a.H;
     if constexpr (CHANNEL) {
-        return hipErrorNotSupported;  // channel-gate prep kernel: not built yet
+        hipLaunchKernelGGL((wy_prep_channel<E, DK, C>), dim3((unsigned)(BH * NT)), dim3(kThreads), 0,
+                           a.stream, (const E*)a.q, (const E*)a.k, a.log_alpha, a.beta,
+                           (uint8_t*)a.ws, a.T, (int)a.H, NT);
     } else {
         hipLaunchKernelGGL((wy_prep_scalar<E, DK, C>), dim3((unsigned)(BH * NT)), dim3(kThreads), 0,
                            a.stream, (const E*)a.q, (const E*)a.k, a.log_alpha, a.beta,
@@ -427,24 +853,10 @@ static hipError_t launch_chunk(const ChunkArgs& a) {
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    // dv-slice width: 32 when that already gives a workgroup per CU, else 16.
-    // (fp32 operands only ever use 16-wide slices: a 32-wide one does not fit in LDS.)
-    if constexpr (sizeof(E) == 2) {
-        if (BH * (a.dv / 32) >= 256) {
-            hipLaunchKernelGGL((state_pass<E, DK, C, 32, CHANNEL>),
-                               dim3((unsigned)(BH * (a.dv / 32))), dim3(kThreads), 0, a.stream,
-                               (const E*)a.q, (const E*)a.k, (const E*)a.v, a.S0, (E*)a.o,
-                               a.S_T, (const uint8_t*)a.ws, a.T, (int)a.H, NT, (int)a.dv);
-            return hipGetLastError();
-        }
-    }
-    {
-        hipLaunchKernelGGL((state_pass<E, DK, C, 16, CHANNEL>), dim3((unsigned)(BH * (a.dv / 16))),
-                           dim3(kThreads), 0, a.stream, (const E*)a.q, (const E*)a.k,
-                           (const E*)a.v, a.S0, (E*)a.o, a.S_T, (const uint8_t*)a.ws, a.T,
-                           (int)a.H, NT, (int)a.dv);
-    }
-    return hipGetLastError();
+    // Two waves (32 value columns) per workgroup when that still gives at
+    // least one workgroup per CU, otherwise one.
+    if (BH * (a.dv / 32) >= 256) return launch_state<E, DK, C, CHANNEL, 2>(a, NT);
+    return launch_state<E, DK, C, CHANNEL, 1>(a, NT);
 }
 
 template <typename E, bool CHANNEL>
@@ -480,6 +892,7 @@ size_t chunk_block_bytes(int64_t dk, int64_t chunk, bool bf16, bool channel) {
 size_t chunk_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t chunk, bool bf16,
                              bool channel) {
     const int64_t NT = (T + chunk - 1) / chunk;
+    if (NT == 0) return 0;
     return (size_t)(B * H * NT) * chunk_block_bytes(dk, chunk, bf16, channel);
 }
 

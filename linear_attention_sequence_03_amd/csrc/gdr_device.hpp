@@ -122,6 +122,95 @@ __device__ __forceinline__ void store4(E* p, float4 v) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Permuted k-map, so that accumulator tiles can feed the next product.
+// An accumulator tile hands lane (col, g) the rows 4g..4g+3.  A contraction
+// whose B operand comes from accumulators therefore uses, in k-step s,
+//   bf16 (16x16x32): slot j of lane group g  <->  k = 32s + 4g + (j&3) + 16(j>>2)
+//                    (rows of the two tiles 2s and 2s+1)
+//   fp32 (16x16x4):  lane group g            <->  k = 16(s>>2) + 4g + (s&3)
+//                    (element s&3 of tile s>>2)
+// and the A operand is read from LDS with the same map.
+// ---------------------------------------------------------------------------
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+#define GDR_LDS __attribute__((address_space(3)))
+
+// A operand, natural storage p[m*rs + k].
+template <typename E>
+__device__ __forceinline__ typename Mma<E>::frag afrag_nat(const E* p, int rs, int m0, int s,
+                                                           int lane) {
+    if constexpr (Mma<E>::KPL == 8) {
+        const E* q = p + (m0 + (lane & 15)) * rs + 32 * s + 4 * (lane >> 4);
+        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(q);
+        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(q + 16);
+        return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    } else {
+        return p[(m0 + (lane & 15)) * rs + 16 * (s >> 2) + 4 * (lane >> 4) + (s & 3)];
+    }
+}
+
+// A operand, transposed storage p[k*rs + m] (used for K^T in the state update).
+// bf16: two ds_read_b64_tr_b16; in a 16-lane group, lane 4j+q reads row
+// kbase+j, columns m0+4q..m0+4q+3, and lane i receives column m0+i of rows
+// kbase..kbase+3.
+template <typename E>
+__device__ __forceinline__ typename Mma<E>::frag afrag_tr(const E* p, int rs, int m0, int s,
+                                                          int lane) {
+    if constexpr (Mma<E>::KPL == 8) {
+        const int g = lane >> 4, j = (lane & 15) >> 2, qd = lane & 3;
+        const E* q = p + (32 * s + 4 * g + j) * rs + m0 + 4 * qd;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GDR_LDS s16x4*)(q));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GDR_LDS s16x4*)(q + 16 * rs));
+        const bf16x4 l = __builtin_bit_cast(bf16x4, lo);
+        const bf16x4 h = __builtin_bit_cast(bf16x4, hi);
+        return bf16x8{l[0], l[1], l[2], l[3], h[0], h[1], h[2], h[3]};
+    } else {
+        return p[(16 * (s >> 2) + 4 * (lane >> 4) + (s & 3)) * rs + m0 + (lane & 15)];
+    }
+}
+
+// Token contractions with chunk C = 16 on the bf16 path cover only half of a
+// 32-wide k-step: the upper 16 slots are zero on both sides (HALF = true).
+template <typename E, bool HALF>
+__device__ __forceinline__ typename Mma<E>::frag afrag_nat_tok(const E* p, int rs, int m0, int s,
+                                                               int lane) {
+    if constexpr (HALF) {
+        const E* q = p + (m0 + (lane & 15)) * rs + 4 * (lane >> 4);
+        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(q);
+        const __bf16 z = (__bf16)0.f;
+        return bf16x8{lo[0], lo[1], lo[2], lo[3], z, z, z, z};
+    } else {
+        return afrag_nat<E>(p, rs, m0, s, lane);
+    }
+}
+
+template <typename E, bool HALF>
+__device__ __forceinline__ typename Mma<E>::frag afrag_tr_tok(const E* p, int rs, int m0, int s,
+                                                              int lane) {
+    if constexpr (HALF) {
+        const int g = lane >> 4, j = (lane & 15) >> 2, qd = lane & 3;
+        const E* q = p + (4 * g + j) * rs + m0 + 4 * qd;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GDR_LDS s16x4*)(q));
+        const bf16x4 l = __builtin_bit_cast(bf16x4, lo);
+        const __bf16 z = (__bf16)0.f;
+        return bf16x8{l[0], l[1], l[2], l[3], z, z, z, z};
+    } else {
+        return afrag_tr<E>(p, rs, m0, s, lane);
+    }
+}
+
+// B operand for k-step s from accumulator tiles t[] (16 rows each).
+template <typename E>
+__device__ __forceinline__ typename Mma<E>::frag bfrag_acc(const f32x4* t, int s) {
+    if constexpr (Mma<E>::KPL == 8) {
+        const f32x4 a = t[2 * s], b = t[2 * s + 1];
+        return bf16x8{(__bf16)a[0], (__bf16)a[1], (__bf16)a[2], (__bf16)a[3],
+                      (__bf16)b[0], (__bf16)b[1], (__bf16)b[2], (__bf16)b[3]};
+    } else {
+        return t[s >> 2][s & 3];
+    }
+}
+
 // Accumulator coordinates of lane l, element i: (row, col) inside the tile.
 __device__ __forceinline__ int acc_row(int lane, int i) { return 4 * (lane >> 4) + i; }
 __device__ __forceinline__ int acc_col(int lane) { return lane & 15; }

@@ -95,12 +95,13 @@ def test_decode_step_rejects(lib, kw, code):
 
 
 def test_workspace_size():
-    # scalar gate: per (b,h,chunk) block = T + P (C*C each) + g (C floats), 256-aligned
+    # per (b,h,chunk): scalar gate = T + P (C*C each) + two decay vectors
+    # (2C floats), 256-aligned
     n = gdr.gdr_chunk_fwd_workspace_size(4, 4096, 16, 128, 128, 64, gdr.GDR_BF16,
                                          gdr.GDR_GATE_SCALAR)
-    blk = (2 * 64 * 64 * 2 + 64 * 4 + 255) // 256 * 256
+    blk = (2 * 64 * 64 * 2 + 2 * 64 * 4 + 255) // 256 * 256
     assert n == 4 * 16 * 64 * blk
-    # channel gate adds three gate-scaled [C, dk] operands and dk floats
+    # channel gate: three gate-scaled [C, dk] operands and dk floats instead
     n = gdr.gdr_chunk_fwd_workspace_size(1, 100, 1, 64, 64, 32, gdr.GDR_F32,
                                          gdr.GDR_GATE_CHANNEL)
     blk = (2 * 32 * 32 * 4 + 3 * 32 * 64 * 4 + 64 * 4 + 255) // 256 * 256

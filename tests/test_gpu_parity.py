@@ -237,3 +237,47 @@ def test_nan_propagates_without_fault():
     o = host(o)
     assert np.isfinite(o[0, :64]).all()
     assert np.isnan(o[0, 70:]).any() and np.isnan(host(st)).any()
+
+
+# --------------------------------------------------------------------------
+# Channel gate (KDA).
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+@pytest.mark.parametrize("T", [1, 65, 200])
+def test_chunk_small_channel_gate(io, d, chunk, T):
+    inp = synth.chunk_inputs(2, T, 3, d, d, "channel", io, seed=T * 5 + d + chunk, s0_std=0.1)
+    _check_full(inp, io, chunk)
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("lo,hi", [(-800.0, -800.0), (-8.0, -0.5), (-30.0, 0.0)])
+def test_channel_gate_strong_decay(io, lo, hi):
+    """Decay spans too large to factor inside a 16-row block take the exact path."""
+    inp = synth.chunk_inputs(1, 150, 2, 64, 64, "channel", io, seed=21, s0_std=0.3,
+                             log_alpha_range=(lo, hi))
+    _check_full(inp, io, 64)
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_channel_gate_mixed_spans(io):
+    """Most channels decay gently, a few channels and tokens decay hard."""
+    inp = synth.chunk_inputs(1, 256, 2, 128, 128, "channel", io, seed=22, s0_std=0.2)
+    la = inp["log_alpha"]
+    la[:, 40:44, :, 5:9] = -60.0
+    la[:, 130:131, 1, :] = -500.0
+    _check_full(inp, io, 64)
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_tied_channel_decay_matches_scalar(io):
+    inp = synth.chunk_inputs(2, 190, 2, 128, 128, "scalar", io, seed=23, s0_std=0.2)
+    o1, s1 = gpu_chunk(inp, io)
+    ch = dict(inp)
+    ch["log_alpha"] = np.ascontiguousarray(
+        np.repeat(inp["log_alpha"][..., None], 128, axis=-1))
+    o2, s2 = gpu_chunk(ch, io)
+    tol = 1e-5 if io == "f32" else TOL[io]
+    assert rel_err(host(o2), host(o1)) <= tol
+    assert rel_err(host(s2), host(s1)) <= tol
