@@ -537,9 +537,10 @@ struct StageLayout {
     static constexpr int LQ = DK + 16 / ES;   // Q / K / Kh rows (elements)
     static constexpr int LT = C + 16 / ES;    // T / P rows
     static constexpr int LV = VT + 16 / ES;   // V rows
-    static constexpr int QB = DmaTile<C, DK * ES, NW>::BYTES;
-    static constexpr int TB = DmaTile<C, C * ES, NW>::BYTES;
-    static constexpr int VB = DmaTile<C, VT * ES, NW>::BYTES;
+    static constexpr int NL = 2;              // loader waves per workgroup
+    static constexpr int QB = DmaTile<C, DK * ES, NL>::BYTES;
+    static constexpr int TB = DmaTile<C, C * ES, NL>::BYTES;
+    static constexpr int VB = DmaTile<C, VT * ES, NL>::BYTES;
     static constexpr int VECB = (int)WsLayout<E, DK, C, CHANNEL>::VEC_BYTES;
     static constexpr int OQ = 0, OK = QB, OKH = 2 * QB;
     static constexpr int OT = (CHANNEL ? 3 : 2) * QB, OP = OT + TB, OV = OP + TB, OVEC = OV + VB;
@@ -551,8 +552,10 @@ struct StageLayout {
     static constexpr int TOTAL = NSTAGE * BYTES + NW * OSTG;
 };
 
-// Copies of chunk n's inputs into one LDS stage (see DmaTile).
-template <typename E, int DK, int C, int NW, bool CHANNEL>
+// Copies of chunk n's inputs into one LDS stage (see DmaTile).  PARTS selects
+// the keys/queries (bit 0) and the T, P, V and decay-vector tiles (bit 1), so
+// a chunk's copies can be spread over the previous chunk's computation.
+template <typename E, int DK, int C, int NW, bool CHANNEL, int PARTS>
 __device__ __forceinline__ void issue_chunk(char* base, int n, const E* q, const E* k, const E* v,
                                             const uint8_t* wsb, int64_t bh, int64_t b, int64_t h,
                                             int64_t T, int H, int DV, int NT, int vt,
@@ -560,9 +563,9 @@ __device__ __forceinline__ void issue_chunk(char* base, int n, const E* q, const
                                             int wave, int lane) {
     using L = WsLayout<E, DK, C, CHANNEL>;
     using SL = StageLayout<E, DK, C, NW, CHANNEL>;
-    using DQ = DmaTile<C, DK * sizeof(E), NW>;
-    using DT = DmaTile<C, C * sizeof(E), NW>;
-    using DV_ = DmaTile<C, 16 * NW * sizeof(E), NW>;
+    using DQ = DmaTile<C, DK * sizeof(E), SL::NL>;
+    using DT = DmaTile<C, C * sizeof(E), SL::NL>;
+    using DV_ = DmaTile<C, 16 * NW * sizeof(E), SL::NL>;
     constexpr int ES = sizeof(E);
     constexpr int VT = SL::VT;
     const int64_t t0 = (int64_t)n * C;
@@ -570,10 +573,11 @@ __device__ __forceinline__ void issue_chunk(char* base, int n, const E* q, const
     const char* blk = reinterpret_cast<const char*>(wsb + (size_t)(bh * NT + n) * L::BYTES);
     if (T - t0 < C) {   // ragged last chunk: clamp rows of the caller's tensors
         const int len = (int)(T - t0);
-        if constexpr (!CHANNEL) DQ::offsets(oq, qk_stride, len, wave, lane);
-        DV_::offsets(ov, (int64_t)H * DV * ES, len, wave, lane);
+        if constexpr (!CHANNEL && (PARTS & 1)) DQ::offsets(oq, qk_stride, len, wave, lane);
+        if constexpr ((PARTS & 2) != 0) DV_::offsets(ov, (int64_t)H * DV * ES, len, wave, lane);
     }
-    if constexpr (CHANNEL) {
+    if constexpr ((PARTS & 1) == 0) {
+    } else if constexpr (CHANNEL) {
         DQ::issue(base + SL::OQ, blk + L::QG, oq, wave);
         DQ::issue(base + SL::OK, blk + L::KG, oq, wave);
         DQ::issue(base + SL::OKH, blk + L::KH, oq, wave);
@@ -581,13 +585,30 @@ __device__ __forceinline__ void issue_chunk(char* base, int n, const E* q, const
         DQ::issue(base + SL::OQ, reinterpret_cast<const char*>(q + row0 * DK), oq, wave);
         DQ::issue(base + SL::OK, reinterpret_cast<const char*>(k + row0 * DK), oq, wave);
     }
-    DT::issue(base + SL::OT, blk + L::T, ot, wave);
-    DT::issue(base + SL::OP, blk + L::P, ot, wave);
-    DV_::issue(base + SL::OV, reinterpret_cast<const char*>(v + row0 * DV + vt * VT), ov, wave);
-    constexpr int NVEC = SL::VECB / 16;
-    for (int s = wave * 64 + lane; s < NVEC; s += NW * 64)
-        __builtin_amdgcn_global_load_lds(blk + L::VEC + 16 * s,
-                                         (GDR_LDS void*)(base + SL::OVEC + 16 * (s - lane)), 16, 0, 0);
+    if constexpr ((PARTS & 2) != 0) {
+        DT::issue(base + SL::OT, blk + L::T, ot, wave);
+        DT::issue(base + SL::OP, blk + L::P, ot, wave);
+        DV_::issue(base + SL::OV, reinterpret_cast<const char*>(v + row0 * DV + vt * VT), ov, wave);
+        constexpr int NVEC = SL::VECB / 16;
+        for (int s = wave * 64 + lane; s < NVEC; s += SL::NL * 64)
+            __builtin_amdgcn_global_load_lds(blk + L::VEC + 16 * s,
+                                             (GDR_LDS void*)(base + SL::OVEC + 16 * (s - lane)), 16, 0, 0);
+    }
+}
+
+// One wave's staged [C][16] output tile -> o, 16 bytes per store (rows < len).
+template <typename E, int C, int LO>
+__device__ __forceinline__ void store_out(E* o, const E* ostg, int64_t row0, int H, int DV, int c0,
+                                          int len, int lane) {
+    constexpr int ES = sizeof(E);
+    constexpr int PPR = 16 * ES / 16;   // 16-byte pieces per row
+#pragma unroll
+    for (int p = lane; p < C * PPR; p += 64) {
+        const int r = p / PPR, pc = p % PPR;
+        if (r < len)
+            *reinterpret_cast<V16*>(o + (row0 + (int64_t)r * H) * DV + c0 + pc * (16 / ES)) =
+                *reinterpret_cast<const V16*>(ostg + r * LO + pc * (16 / ES));
+    }
 }
 
 // S^T <- Diag(gamma_last) S^T + Kh^T Ds for the chunk held in one LDS stage.
@@ -614,25 +635,30 @@ __device__ __forceinline__ void state_update(f32x4* S, const typename Mma<E>::fr
 #pragma unroll
             for (int i = 0; i < 4; ++i) S[mc][i] *= gl;
     }
+    // All transposed key fragments first, so their LDS latencies overlap.
+    typename M::frag kf[CT][NKT];
 #pragma unroll
     for (int mc = 0; mc < CT; ++mc)
 #pragma unroll
-        for (int s = 0; s < NKT; ++s)
-            S[mc] = M::mma(afrag_tr_tok<E, HALF>(Khs, SL::LQ, 16 * mc, s, lane), dsb[s], S[mc]);
+        for (int s = 0; s < NKT; ++s) kf[mc][s] = afrag_tr_tok<E, HALF>(Khs, SL::LQ, 16 * mc, s, lane);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < NKT; ++s)
+#pragma unroll
+        for (int mc = 0; mc < CT; ++mc) S[mc] = M::mma(kf[mc][s], dsb[s], S[mc]);
 }
 
 template <typename E, int DK, int C, int NW, bool CHANNEL>
-__global__ __launch_bounds__(64 * NW) void state_pass(
+__global__ __launch_bounds__(64 * (NW + 2)) __attribute__((amdgpu_waves_per_eu(1, 1))) void state_pass(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ S0, E* __restrict__ o, float* __restrict__ ST,
     const uint8_t* __restrict__ ws, int64_t T, int H, int NT, int DV) {
-    using L = WsLayout<E, DK, C, CHANNEL>;
     using SL = StageLayout<E, DK, C, NW, CHANNEL>;
     using M = Mma<E>;
     using frag = typename M::frag;
-    using DQ = DmaTile<C, DK * sizeof(E), NW>;    // Q, K (and Kh) tiles
-    using DT = DmaTile<C, C * sizeof(E), NW>;     // T, P tiles
-    using DV_ = DmaTile<C, 16 * NW * sizeof(E), NW>;
+    using DQ = DmaTile<C, DK * sizeof(E), SL::NL>;    // Q, K (and Kh) tiles
+    using DT = DmaTile<C, C * sizeof(E), SL::NL>;     // T, P tiles
+    using DV_ = DmaTile<C, 16 * NW * sizeof(E), SL::NL>;
     constexpr int ES = sizeof(E);
     constexpr int VT = SL::VT;
     constexpr int NKC = DK / M::KS;                        // k-steps over channels
@@ -649,17 +675,45 @@ __global__ __launch_bounds__(64 * NW) void state_pass(
     const int vt = bid % NVT;
     const int64_t bh = bid / NVT;
     const int64_t b = bh / H, h = bh % H;
-    const int vcol = vt * VT + 16 * wave + col;            // this lane's value column
     const uint8_t* wsb = ws;
+
+    // Waves NW and NW+1 only copy the chunk inputs global -> LDS (their copy
+    // instructions may stall issue for a long time; the compute waves never
+    // issue any).  Both roles pass the same barriers in the same order:
+    //   prologue: B0;  chunk n: [n>0: B1] [1 stage, n>0: Bready] [2 stages: B2]
+    if (wave >= NW) {
+        const int lw = wave - NW;
+        const int64_t qk_stride = CHANNEL ? (int64_t)DK * ES : (int64_t)H * DK * ES;
+        int oq[DQ::PER_WAVE], ot[DT::PER_WAVE], ov[DV_::PER_WAVE];
+        DQ::offsets(oq, qk_stride, C, lw, lane);
+        DT::offsets(ot, (int64_t)C * ES, C, lw, lane);
+        DV_::offsets(ov, (int64_t)H * DV * ES, C, lw, lane);
+        issue_chunk<E, DK, C, NW, CHANNEL, 3>(smem, 0, q, k, v, wsb, bh, b, h, T, H, DV, NT, vt,
+                                              qk_stride, oq, ot, ov, lw, lane);
+        wait_dma();
+        __syncthreads();                                                   // B0
+        for (int n = 0; n < NT; ++n) {
+            if (n > 0) __syncthreads();                                    // B1
+            if constexpr (SL::NSTAGE == 2) {
+                if (n + 1 < NT) {
+                    issue_chunk<E, DK, C, NW, CHANNEL, 3>(smem + ((n + 1) & 1) * SL::BYTES, n + 1, q, k, v,
+                                                          wsb, bh, b, h, T, H, DV, NT, vt, qk_stride, oq,
+                                                          ot, ov, lw, lane);
+                    wait_dma();
+                }
+                __syncthreads();                                           // B2
+            } else if (n > 0) {
+                issue_chunk<E, DK, C, NW, CHANNEL, 3>(smem, n, q, k, v, wsb, bh, b, h, T, H, DV, NT, vt,
+                                                      qk_stride, oq, ot, ov, lw, lane);
+                wait_dma();
+                __syncthreads();                                           // Bready
+            }
+        }
+        return;
+    }
+
+    const int vcol = vt * VT + 16 * wave + col;            // this lane's value column
     E* ostg = reinterpret_cast<E*>(smem + SL::NSTAGE * SL::BYTES + wave * SL::OSTG);
-
-    // Per-lane copy offsets (full chunks; a ragged last chunk recomputes them).
-    const int64_t qk_stride = CHANNEL ? (int64_t)DK * ES : (int64_t)H * DK * ES;
-    int oq[DQ::PER_WAVE], ot[DT::PER_WAVE], ov[DV_::PER_WAVE];
-    DQ::offsets(oq, qk_stride, C, wave, lane);
-    DT::offsets(ot, (int64_t)C * ES, C, wave, lane);
-    DV_::offsets(ov, (int64_t)H * DV * ES, C, wave, lane);
-
 
     // State slice S^T[c][v]: tile mc, lane (v, g) holds c = 16mc + 4g + i.
     f32x4 S[CT];
@@ -669,33 +723,21 @@ __global__ __launch_bounds__(64 * NW) void state_pass(
         if (S0) x = *reinterpret_cast<const float4*>(S0 + (bh * DV + vcol) * DK + 16 * mc + 4 * g4);
         S[mc] = f32x4{x.x, x.y, x.z, x.w};
     }
-
-    // S^T <- Diag(gamma_last) S^T + Kh^T Ds for the chunk held in `stage`.
-    frag dsb[NKT];
-
-    issue_chunk<E, DK, C, NW, CHANNEL>(smem + (0) * SL::BYTES, 0, q, k, v, wsb, bh, b, h, T, H, DV,
-                                            NT, vt, qk_stride, oq, ot, ov, wave, lane);
-    wait_dma();
-    __syncthreads();
+    frag dsb[NKT];   // the state update's D operand, carried to the next chunk
+    __syncthreads();                                                       // B0
 
     for (int n = 0; n < NT; ++n) {
         const int cur = SL::NSTAGE == 2 ? (n & 1) : 0;
+        const int64_t t0 = (int64_t)n * C;
+        const int64_t row0 = (b * T + t0) * H + h;
         if (n > 0) {
-            // Finish the previous chunk's state update from its stage, then let
-            // every wave be done with that stage before it is refilled.
+            // The previous chunk's state update, from its stage; then every
+            // wave is done with that stage and the loaders may refill it.
             state_update<E, DK, C, NW, CHANNEL>(S, dsb, smem + (SL::NSTAGE == 2 ? (cur ^ 1) : 0) * SL::BYTES,
                                                 g4, lane);
-            __syncthreads();
-        }
-        if constexpr (SL::NSTAGE == 2) {
-            if (n + 1 < NT)
-                issue_chunk<E, DK, C, NW, CHANNEL>(smem + (cur ^ 1) * SL::BYTES, n + 1, q, k, v, wsb, bh, b, h, T, H, DV,
-                                            NT, vt, qk_stride, oq, ot, ov, wave, lane);
-        } else if (n > 0) {
-            issue_chunk<E, DK, C, NW, CHANNEL>(smem + (0) * SL::BYTES, n, q, k, v, wsb, bh, b, h, T, H, DV,
-                                            NT, vt, qk_stride, oq, ot, ov, wave, lane);
-            wait_dma();
-            __syncthreads();
+            __syncthreads();                                               // B1
+            store_out<E, C, SL::LO>(o, ostg, row0 - (int64_t)C * H, H, DV, vt * VT + 16 * wave, C, lane);
+            if constexpr (SL::NSTAGE == 1) __syncthreads();                // Bready
         }
         const char* st = smem + cur * SL::BYTES;
         const E* Qs = reinterpret_cast<const E*>(st + SL::OQ);
@@ -704,9 +746,6 @@ __global__ __launch_bounds__(64 * NW) void state_pass(
         const E* Ps = reinterpret_cast<const E*>(st + SL::OP);
         const E* Vs = reinterpret_cast<const E*>(st + SL::OV);
         const float* vec = reinterpret_cast<const float*>(st + SL::OVEC);
-        const int64_t t0 = (int64_t)n * C;
-        const int len = (int)((T - t0) < C ? (T - t0) : C);
-        const int64_t row0 = (b * T + t0) * H + h;
 
         // Phase A: R = V - Kg S^T, Oi = Qg S^T  (rows = tokens, cols = v)
         frag sb[NKC];
@@ -715,13 +754,29 @@ __global__ __launch_bounds__(64 * NW) void state_pass(
         f32x4 R[MT], Oa[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) { R[mt] = zero4(); Oa[mt] = zero4(); }
+        // Fragments are loaded a whole k-step pair ahead of their MFMAs (LDS
+        // returns in order, so each MFMA waits only for its own operands).
+        constexpr int KH2 = NKC >= 2 ? 2 : 1;
 #pragma unroll
-        for (int s = 0; s < NKC; ++s)
+        for (int s0 = 0; s0 < NKC; s0 += KH2) {
+            frag kf[KH2][MT], qf[KH2][MT];
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                R[mt] = M::mma(afrag_nat(Ks, SL::LQ, 16 * mt, s, lane), sb[s], R[mt]);
-                Oa[mt] = M::mma(afrag_nat(Qs, SL::LQ, 16 * mt, s, lane), sb[s], Oa[mt]);
-            }
+            for (int s = 0; s < KH2; ++s)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    kf[s][mt] = afrag_nat(Ks, SL::LQ, 16 * mt, s0 + s, lane);
+                    qf[s][mt] = afrag_nat(Qs, SL::LQ, 16 * mt, s0 + s, lane);
+                }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int s = 0; s < KH2; ++s)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    R[mt] = M::mma(kf[s][mt], sb[s0 + s], R[mt]);
+                    Oa[mt] = M::mma(qf[s][mt], sb[s0 + s], Oa[mt]);
+                }
+            __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             float4 gam = make_float4(1.f, 1.f, 1.f, 1.f);
@@ -749,12 +804,19 @@ __global__ __launch_bounds__(64 * NW) void state_pass(
             }
         }
         f32x4 D[MT];
+        {
+            frag tf[MT][NKT];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            D[mt] = zero4();
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int s = 0; s < NKT; ++s) tf[mt][s] = afrag_nat_tok<E, HALF>(Ts, SL::LT, 16 * mt, s, lane);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) D[mt] = zero4();
 #pragma unroll
             for (int s = 0; s < NKT; ++s)
-                D[mt] = M::mma(afrag_nat_tok<E, HALF>(Ts, SL::LT, 16 * mt, s, lane), rb[s], D[mt]);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) D[mt] = M::mma(tf[mt][s], rb[s], D[mt]);
         }
 
         // Phase C: O = Oi + P D; the state update's operand Ds is kept for the
@@ -780,33 +842,31 @@ __global__ __launch_bounds__(64 * NW) void state_pass(
                 dsb[s] = bfrag_acc<E>(Dsc, s);
             }
         }
+        {
+            frag pf[MT][NKT];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int s = 0; s < NKT; ++s) pf[mt][s] = afrag_nat_tok<E, HALF>(Ps, SL::LT, 16 * mt, s, lane);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int s = 0; s < NKT; ++s)
-                Oa[mt] = M::mma(afrag_nat_tok<E, HALF>(Ps, SL::LT, 16 * mt, s, lane), db[s], Oa[mt]);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) Oa[mt] = M::mma(pf[mt][s], db[s], Oa[mt]);
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) ostg[(16 * mt + 4 * g4 + i) * SL::LO + col] = from_f32<E>(Oa[mt][i]);
-        }
-        // Output: this wave's [C][16] tile, 16 bytes per store.
-        {
-            constexpr int PPR = 16 * ES / 16;   // 16-byte pieces per row
-#pragma unroll
-            for (int p = lane; p < C * PPR; p += 64) {
-                const int r = p / PPR, pc = p % PPR;
-                if (r < len)
-                    *reinterpret_cast<V16*>(o + (row0 + (int64_t)r * H) * DV + vt * VT + 16 * wave + pc * (16 / ES)) =
-                        *reinterpret_cast<const V16*>(ostg + r * SL::LO + pc * (16 / ES));
-            }
-        }
-        if constexpr (SL::NSTAGE == 2) {
-            wait_dma();
-            __syncthreads();
-        }
+        if constexpr (SL::NSTAGE == 2) __syncthreads();                    // B2
     }
     state_update<E, DK, C, NW, CHANNEL>(S, dsb, smem + (SL::NSTAGE == 2 ? ((NT - 1) & 1) : 0) * SL::BYTES,
                                         g4, lane);
-
+    {
+        const int64_t t0 = (int64_t)(NT - 1) * C;
+        store_out<E, C, SL::LO>(o, ostg, (b * T + t0) * H + h, H, DV, vt * VT + 16 * wave,
+                                (int)(T - t0), lane);
+    }
     if (ST) {
 #pragma unroll
         for (int mc = 0; mc < CT; ++mc)
@@ -832,7 +892,7 @@ template <typename E, int DK, int C, bool CHANNEL, int NW>
 static hipError_t launch_state(const ChunkArgs& a, int NT) {
     const int64_t BH = a.B * a.H;
     const int64_t grid = BH * (a.dv / (16 * NW));
-    hipLaunchKernelGGL((state_pass<E, DK, C, NW, CHANNEL>), dim3((unsigned)grid), dim3(64 * NW), 0,
+    hipLaunchKernelGGL((state_pass<E, DK, C, NW, CHANNEL>), dim3((unsigned)grid), dim3(64 * (NW + 2)), 0,
                        a.stream, (const E*)a.q, (const E*)a.k, (const E*)a.v, a.S0, (E*)a.o, a.S_T,
                        (const uint8_t*)a.ws, a.T, (int)a.H, NT, (int)a.dv);
     return hipGetLastError();
