@@ -134,6 +134,122 @@ __device__ __forceinline__ void solve_unit_lower(const float* As, float* Xs, flo
     }
 }
 
+// Lower 16x16 block tiles of a C x C matrix, stored tile by tile (fp32, rows
+// padded to 17): tile (i, j), j <= i, starts at tl(i, j) * kTS.
+constexpr int kTS = 16 * 17;
+__device__ __forceinline__ int tl(int i, int j) { return i * (i + 1) / 2 + j; }
+__device__ __forceinline__ int ablk(int row, int col) {
+    return tl(row >> 4, col >> 4) * kTS + (row & 15) * 17 + (col & 15);
+}
+
+// exp(x) through the hardware base-2 exponential (x <= 0 here; underflows to 0).
+__device__ __forceinline__ float fast_exp(float x) {
+    return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+}
+
+// Copy two [ROWS][COLS] tiles (same row strides) global -> LDS through
+// registers, all loads issued before any LDS store (one memory round trip).
+template <typename E, int ROWS, int COLS, int NTHR>
+__device__ __forceinline__ void g2s_pair(E* d0, E* d1, int ls, const E* s0, const E* s1,
+                                         int64_t gstride, int valid, int tid) {
+    constexpr int EPS = 16 / sizeof(E);
+    constexpr int SEGS = COLS / EPS;
+    constexpr int PER = (ROWS * SEGS + NTHR - 1) / NTHR;
+    V16 a[PER], b[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int idx = tid + i * NTHR;
+        const int r = idx / SEGS, sg = idx % SEGS;
+        const bool ok = idx < ROWS * SEGS && r < valid;
+        a[i] = ok ? ld16(s0 + r * gstride + sg * EPS) : zero16();
+        b[i] = ok ? ld16(s1 + r * gstride + sg * EPS) : zero16();
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int idx = tid + i * NTHR;
+        const int r = idx / SEGS, sg = idx % SEGS;
+        if (idx < ROWS * SEGS) {
+            st16(d0 + r * ls + sg * EPS, a[i]);
+            st16(d1 + r * ls + sg * EPS, b[i]);
+        }
+    }
+}
+
+// T = (I + A)^-1 Diag(beta) from the lower block tiles of A (Ablk; strictly
+// lower inside the diagonal tiles), written to the workspace.  Wave 0 inverts
+// the diagonal 16x16 blocks by right-looking forward substitution (one lane
+// per column of every diagonal block; 15 dependent FMAs deep) into Xd; then
+// wave j builds column block j of X = (I + A)^-1 alone, in registers:
+//   X_ij = -X_ii * sum_{m=j}^{i-1} A_im X_mj      (i = j+1 .. NB-1)
+// on fp32 16x16x4 MFMAs, each new tile feeding the next product as its B
+// operand, and stores T_ij = X_ij Diag(beta_j) straight from the accumulators.
+template <typename E, int C>
+__device__ __forceinline__ void solve_store_T(const float* Ablk, float* Xd, const float* bs, E* Tw,
+                                              int tid) {
+    constexpr int NB = C / 16;
+    using MF = Mma<float>;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int g4 = lane >> 4, col = lane & 15;
+    if (wave == 0) {
+        const int blk = lane >> 4, j = lane & 15;
+        if (blk < NB) {
+            const float* Ab = Ablk + tl(blk, blk) * kTS;
+            float x[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) x[i] = (i == j) ? 1.f : 0.f;
+#pragma unroll
+            for (int m = 0; m < 16; ++m) {
+#pragma unroll
+                for (int i = m + 1; i < 16; ++i) x[i] -= Ab[i * 17 + m] * x[m];
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) Xd[blk * kTS + i * 17 + j] = x[i];
+        }
+    }
+    __syncthreads();
+    const int j = wave;
+    if (j >= NB) return;
+    const float bcol = bs[16 * j + col];
+    // diagonal tile and the zero tiles above it
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int r = 4 * g4 + e;
+        Tw[(16 * j + r) * C + 16 * j + col] = from_f32<E>(Xd[j * kTS + r * 17 + col] * bcol);
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        if (i < j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Tw[(16 * i + 4 * g4 + e) * C + 16 * j + col] = from_f32<E>(0.f);
+    }
+    f32x4 X[NB];
+#pragma unroll
+    for (int i = 1; i < NB; ++i) {
+        X[i] = zero4();
+        if (i <= j) continue;
+        f32x4 Y = zero4();
+#pragma unroll
+        for (int m = 0; m < i; ++m) {
+            if (m < j) continue;
+            const float* Aim = Ablk + tl(i, m) * kTS;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const float a = Aim[col * 17 + 4 * g4 + s];
+                const float b = (m == j) ? Xd[j * kTS + (4 * g4 + s) * 17 + col] : X[m][s];
+                Y = MF::mma(a, b, Y);
+            }
+        }
+        f32x4 Z = zero4();
+#pragma unroll
+        for (int s = 0; s < 4; ++s) Z = MF::mma(Xd[i * kTS + col * 17 + 4 * g4 + s], Y[s], Z);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            X[i][e] = -Z[e];
+            Tw[(16 * i + 4 * g4 + e) * C + 16 * j + col] = from_f32<E>(-Z[e] * bcol);
+        }
+    }
+}
+
 // Write T = X Diag(beta) (lower triangle, E) to the workspace, 16 bytes per store.
 template <typename E, int C, int LA>
 __device__ __forceinline__ void store_T(E* Tw, const float* Xs, const float* bs, int tid) {
@@ -151,7 +267,9 @@ __device__ __forceinline__ void store_T(E* Tw, const float* Xs, const float* bs,
 }
 
 // ---------------------------------------------------------------------------
-// Kernel 1, scalar gate (Gated DeltaNet).
+// Kernel 1, scalar gate (Gated DeltaNet).  Tiles: wave w takes the A tiles
+// (w even) or P tiles (w odd) of row blocks {p, NB-1-p}, p = w/2, which gives
+// every wave 5 tiles at C = 64.
 // ---------------------------------------------------------------------------
 template <typename E, int DK, int C>
 __global__ __launch_bounds__(kThreads) void wy_prep_scalar(
@@ -161,17 +279,14 @@ __global__ __launch_bounds__(kThreads) void wy_prep_scalar(
     using M = Mma<E>;
     constexpr int LDK = DK + Pad<E>::v;
     constexpr int NB = C / 16;
-    constexpr int LA = C + 1;
-    constexpr int LP = C + Pad<E>::v;
     __shared__ __attribute__((aligned(16))) E Ks[C * LDK];
     __shared__ __attribute__((aligned(16))) E Qs[C * LDK];
-    __shared__ float As[C * LA];
-    __shared__ float Xs[C * LA];
-    __shared__ float Ys[(NB > 1 ? NB - 1 : 1) * 16 * 17];
-    __shared__ __attribute__((aligned(16))) E Pst[C * LP];
+    __shared__ float Ablk[NB * (NB + 1) / 2 * kTS];
+    __shared__ float Xd[NB * kTS];
     __shared__ float gs[C], bs[C];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g4 = lane >> 4, col = lane & 15;
     const int64_t bid = blockIdx.x;
     const int n = (int)(bid % NT);
     const int64_t bh = bid / NT;
@@ -180,9 +295,7 @@ __global__ __launch_bounds__(kThreads) void wy_prep_scalar(
     const int len = (int)((T - t0) < C ? (T - t0) : C);
     const int64_t row0 = ((b * T + t0) * H + h);   // token-row index of row 0
 
-    g2s<E, C, DK, kThreads>(Ks, LDK, k + row0 * DK, (int64_t)H * DK, len, tid);
-    g2s<E, C, DK, kThreads>(Qs, LDK, q + row0 * DK, (int64_t)H * DK, len, tid);
-    for (int idx = tid; idx < C * LA; idx += kThreads) { As[idx] = 0.f; Xs[idx] = 0.f; }
+    g2s_pair<E, C, DK, kThreads>(Ks, Qs, LDK, k + row0 * DK, q + row0 * DK, (int64_t)H * DK, len, tid);
     if (wave == 0) {
         float x = 0.f, bb = 0.f;
         if (lane < len) {
@@ -202,47 +315,48 @@ __global__ __launch_bounds__(kThreads) void wy_prep_scalar(
     E* Tw = reinterpret_cast<E*>(blk + L::T);
     E* Pw = reinterpret_cast<E*>(blk + L::P);
 
-    // Block tiles of A = K K^T and P = Q K^T, gated; P staged in LDS.
-    constexpr int NTILE = NB * NB;
-    for (int t = wave; t < 2 * NTILE; t += kWaves) {
-        const bool isP = t >= NTILE;
-        const int tt = isP ? t - NTILE : t;
-        const int rb = tt / NB, cb = tt % NB;
-        const int col = 16 * cb + acc_col(lane);
-        if (cb > rb) {  // upper blocks are zero
-            if (isP)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) Pst[(16 * rb + acc_row(lane, e)) * LP + col] = from_f32<E>(0.f);
-            continue;
-        }
+    // Tiles of A = K K^T (gated, beta-scaled, strictly lower) into Ablk and of
+    // P = Q K^T (gated, lower incl. diagonal) straight to the workspace.
+    const int pr = wave >> 1;
+    const bool isP = wave & 1;
+    if (pr < (NB + 1) / 2) {
         const E* Ap = isP ? Qs : Ks;
-        f32x4 acc = zero4();
 #pragma unroll
-        for (int k0 = 0; k0 < DK; k0 += M::KS)
-            acc = M::mma(frag_rk(Ap, LDK, 16 * rb, k0, lane), frag_rk(Ks, LDK, 16 * cb, k0, lane),
-                         acc);
+        for (int sel = 0; sel < 2; ++sel) {
+            const int rb = sel == 0 ? pr : NB - 1 - pr;
+            if (sel == 1 && rb == pr) break;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int row = 16 * rb + acc_row(lane, e);
-            const bool keep = isP ? (col <= row) : (col < row);
-            const float dec = keep ? expf(gs[row] - gs[col]) : 0.f;
-            if (isP)
-                Pst[row * LP + col] = from_f32<E>(keep ? acc[e] * dec : 0.f);
-            else
-                As[row * LA + col] = keep ? acc[e] * bs[row] * dec : 0.f;
+            for (int cb = 0; cb < NB; ++cb) {
+                if (cb > rb) {
+                    if (isP)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            Pw[(16 * rb + 4 * g4 + e) * C + 16 * cb + col] = from_f32<E>(0.f);
+                    continue;
+                }
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int k0 = 0; k0 < DK; k0 += M::KS)
+                    acc = M::mma(frag_rk(Ap, LDK, 16 * rb, k0, lane), frag_rk(Ks, LDK, 16 * cb, k0, lane),
+                                 acc);
+                const int c = 16 * cb + col;
+                const float gc = gs[c];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * rb + 4 * g4 + e;
+                    const bool keep = isP ? (c <= r) : (c < r);
+                    const float dec = keep ? fast_exp(gs[r] - gc) : 0.f;
+                    if (isP)
+                        Pw[r * C + c] = from_f32<E>(acc[e] * dec);
+                    else
+                        Ablk[ablk(r, c)] = acc[e] * bs[r] * dec;
+                }
+            }
         }
     }
     __syncthreads();
-    {   // P -> workspace, 16-byte stores
-        constexpr int EPS = 16 / sizeof(E);
-        for (int idx = tid; idx < C * C / EPS; idx += kThreads) {
-            const int r = (idx * EPS) / C, c0 = (idx * EPS) % C;
-            *reinterpret_cast<V16*>(Pw + r * C + c0) = *reinterpret_cast<const V16*>(Pst + r * LP + c0);
-        }
-    }
 
-    solve_unit_lower<C, LA>(As, Xs, Ys, tid);
-    store_T<E, C, LA>(Tw, Xs, bs, tid);
+    solve_store_T<E, C>(Ablk, Xd, bs, Tw, tid);
     float* vec = reinterpret_cast<float*>(blk + L::VEC);
     if (tid < C) {
         vec[tid] = expf(gs[tid]);
