@@ -7,15 +7,28 @@ call over the whole batch.  The same line also carries the decode step
 (gdr_decode_step, B=256, H=32, d=128, fp32 state) as achieved HBM GB/s.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+    python bench.py --traffic        # HBM bytes per call from rocprofv3 counters
 
 Prints ONE JSON line.  Only one GPU is used; --gpus above 1 exits.
+
+`roofline.traffic` is the HBM bytes one prefill call moves, from two
+rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE) over the call's kernels,
+each scaled by what the same counter reads for a plain 256 MiB device copy
+(libgdr_calib.so: 16-byte loads and stores).
+`--traffic` measures it and writes a summary; the default run reports it only
+when that summary was taken from the current kernel sources (hash match).
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
+import subprocess
 import sys
+import tempfile
 import time
 
 import numpy as np
@@ -46,12 +59,83 @@ def decode_algorithmic(B, H, d, io_bytes=4):
     return bh * (2 * d * d * 4 + 4 * d * io_bytes + 8)
 
 
-def cpu_baseline(inp, threads):
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gdr_chunk_fwd_gdn_B4_H16_T4096_d128.traffic.txt")
+COPY_BYTES = 256 << 20
+PREFILL_KERNELS = ("wy_prep", "state_pass")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "linear_attention_sequence_03_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def cpu_baseline(inp, threads, min_seconds=10.0, max_reps=40):
+    """The oracle over the whole workload, repeated until ~min_seconds."""
     import oracle
-    t = time.perf_counter()
-    oracle.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], None,
-                     threads=threads)
-    return time.perf_counter() - t
+    reps, t0 = 0, time.perf_counter()
+    while reps < max_reps:
+        oracle.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], None,
+                         threads=threads)
+        reps += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
+    return reps, time.perf_counter() - t0
+
+
+def traffic_probe():
+    """Program run under rocprofv3 --pmc: 3 prefill calls, then 3 plain copies."""
+    import torch
+    from linear_attention_sequence_03_amd import gdr_chunk_fwd, synth
+    w = synth.WORKLOADS[1]
+    inp = synth.workload_inputs(w)
+    dev = torch.device("cuda:0")
+    t = {n: torch.from_numpy(inp[n]).to(dev) for n in ("q", "k", "v", "log_alpha", "beta")}
+    for n in ("q", "k", "v"):
+        t[n] = t[n].to(torch.bfloat16)
+    for _ in range(3):
+        gdr_chunk_fwd(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], None, chunk=w.chunk)
+    import ctypes
+    calib = ctypes.CDLL(os.path.join(ROOT, "linear_attention_sequence_03_amd", "libgdr_calib.so"))
+    calib.gdr_calib_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                     ctypes.c_void_p]
+    src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    for _ in range(3):
+        assert calib.gdr_calib_copy(src.data_ptr(), dst.data_ptr(), COPY_BYTES, stream) == 0
+    torch.cuda.synchronize()
+
+
+def measure_traffic(outdir):
+    """Two rocprofv3 --pmc passes over traffic_probe(); returns bytes per call."""
+    res = {}
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        d = tempfile.mkdtemp(prefix="pmc_", dir=outdir)
+        cmd = ["rocprofv3", "--pmc", ctr, "--output-format", "csv", "-d", d, "-o", "run", "--",
+               sys.executable, os.path.abspath(__file__), "--traffic-probe"]
+        subprocess.run(cmd, check=True, stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL,
+                       timeout=240)
+        rows = []
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            rows += list(csv.DictReader(open(f)))
+        per = {}
+        for r in rows:
+            name = r["Kernel_Name"]
+            key = next((k for k in PREFILL_KERNELS if k in name), None)
+            if key is None and "gdr_calib_copy_kernel" in name:
+                key = "copy"
+            if key:
+                per.setdefault(key, []).append(float(r["Counter_Value"]))
+        kib_copy = sum(per["copy"]) / len(per["copy"])
+        factor = (COPY_BYTES / 1024.0) / kib_copy
+        kib_call = sum(sum(per[k]) / len(per[k]) for k in PREFILL_KERNELS if k in per)
+        res[ctr] = dict(kib_per_call=kib_call, copy_kib=kib_copy, factor=factor,
+                        bytes_per_call=kib_call * factor * 1024.0)
+    return res
 
 
 def main():
@@ -61,7 +145,32 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-steps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic", action="store_true",
+                    help="measure HBM bytes per call with rocprofv3 and write a summary")
+    ap.add_argument("--traffic-probe", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out"))
     args = ap.parse_args()
+    if args.traffic_probe:
+        traffic_probe()
+        return
+    if args.traffic:
+        os.makedirs(args.out, exist_ok=True)
+        res = measure_traffic(args.out)
+        total = res["FETCH_SIZE"]["bytes_per_call"] + res["WRITE_SIZE"]["bytes_per_call"]
+        path = os.path.join(args.out, os.path.basename(TRAFFIC_FILE))
+        with open(path, "w") as fh:
+            fh.write("# HBM traffic of one gdr_chunk_fwd call (B=4,T=4096,H=16,d=128,chunk=64, bf16)\n")
+            fh.write("# command: python bench.py --traffic   (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)\n")
+            fh.write("# kernels: %s; calibration: plain %d MiB device copy\n"
+                     % (", ".join(PREFILL_KERNELS), COPY_BYTES >> 20))
+            fh.write("source_hash=%s\n" % kernel_source_hash())
+            for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+                r = res[ctr]
+                fh.write("%s_kib_per_call=%.1f\n%s_copy_kib=%.1f\n%s_factor=%.4f\n"
+                         % (ctr, r["kib_per_call"], ctr, r["copy_kib"], ctr, r["factor"]))
+            fh.write("traffic_bytes_per_call=%.0f\n" % total)
+        print(json.dumps({"traffic_bytes_per_call": total, "summary": path, **res}))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only (this path has no multi-GPU part); "
               "run with --gpus 1", file=sys.stderr)
@@ -127,6 +236,12 @@ def main():
 
     nbytes, flops = prefill_algorithmic(B, T, H, d, C)
     launch_ms = float(np.mean(warm))
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        kv = dict(l.strip().split("=", 1) for l in open(TRAFFIC_FILE)
+                  if "=" in l and not l.startswith("#"))
+        if kv.get("source_hash") == kernel_source_hash():
+            traffic = float(kv["traffic_bytes_per_call"])
     achieved = nbytes / (launch_ms * 1e-3) / 1e9
     tflops = flops / (launch_ms * 1e-3) / 1e12
 
@@ -170,7 +285,7 @@ def main():
                    "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "gdr_chunk_fwd (wy_prep + state_pass)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": nbytes,
                      "launch_ms_mean": launch_ms,
                      "launch_ms_cold_cache_mean": float(np.mean(cold))},
@@ -184,11 +299,12 @@ def main():
     if not args.no_cpu_baseline:
         import oracle.gdr_oracle as og
         threads = min(16, og.default_threads())
-        secs = cpu_baseline(inp, threads)
-        out["cpu_baseline"] = {"value": B * T / secs, "unit": "tokens/s", "cores": threads,
+        reps, secs = cpu_baseline(inp, threads)
+        out["cpu_baseline"] = {"value": reps * B * T / secs, "unit": "tokens/s", "cores": threads,
                                "kind": "oracle",
                                "sample": "the whole prefill workload (B=4,T=4096,H=16,d=128) "
-                                         "in the fp64 token-by-token oracle, %.1f s" % secs}
+                                         "through the fp64 token-by-token oracle, %d times, "
+                                         "%.1f s" % (reps, secs)}
     print(json.dumps(out))
 
 
