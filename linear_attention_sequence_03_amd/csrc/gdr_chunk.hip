@@ -1066,7 +1066,7 @@ size_t chunk_block_bytes(int64_t dk, int64_t chunk, bool bf16, bool channel) {
 size_t chunk_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t chunk, bool bf16,
                              bool channel) {
     const int64_t NT = (T + chunk - 1) / chunk;
-    if (NT == 0) return 0;
+    if (NT == 0 || fused_chunk_supported(dk, chunk, bf16, channel)) return 0;
     return (size_t)(B * H * NT) * chunk_block_bytes(dk, chunk, bf16, channel);
 }
 
@@ -1078,6 +1078,7 @@ hipError_t chunk_fwd_launch(const ChunkArgs& a) {
                            a.S0, a.S_T, n4);
         return hipGetLastError();
     }
+    if (fused_chunk_supported(a.dk, a.chunk, a.bf16, a.channel)) return fused_chunk_launch(a);
     if (a.bf16)
         return a.channel ? dispatch_shape<__bf16, true>(a) : dispatch_shape<__bf16, false>(a);
     return a.channel ? dispatch_shape<float, true>(a) : dispatch_shape<float, false>(a);

@@ -36,4 +36,8 @@ size_t chunk_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_
                              bool bf16, bool channel);
 hipError_t chunk_fwd_launch(const ChunkArgs& a);
 
+// Single-kernel path (bf16, scalar gate, 64-token chunks): needs no workspace.
+bool fused_chunk_supported(int64_t dk, int64_t chunk, bool bf16, bool channel);
+hipError_t fused_chunk_launch(const ChunkArgs& a);
+
 }  // namespace gdr

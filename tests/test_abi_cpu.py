@@ -95,12 +95,16 @@ def test_decode_step_rejects(lib, kw, code):
 
 
 def test_workspace_size():
-    # per (b,h,chunk): scalar gate = T + P (C*C each) + two decay vectors
-    # (2C floats), 256-aligned
-    n = gdr.gdr_chunk_fwd_workspace_size(4, 4096, 16, 128, 128, 64, gdr.GDR_BF16,
+    # bf16 scalar gate with 64-token chunks runs as one kernel: no workspace
+    for d in (64, 128):
+        assert gdr.gdr_chunk_fwd_workspace_size(4, 4096, 16, d, d, 64, gdr.GDR_BF16,
+                                                gdr.GDR_GATE_SCALAR) == 0
+    # two-kernel path, per (b,h,chunk): scalar gate = T + P (C*C each) + two
+    # decay vectors (2C floats), 256-aligned
+    n = gdr.gdr_chunk_fwd_workspace_size(4, 4096, 16, 128, 128, 32, gdr.GDR_BF16,
                                          gdr.GDR_GATE_SCALAR)
-    blk = (2 * 64 * 64 * 2 + 2 * 64 * 4 + 255) // 256 * 256
-    assert n == 4 * 16 * 64 * blk
+    blk = (2 * 32 * 32 * 2 + 2 * 32 * 4 + 255) // 256 * 256
+    assert n == 4 * 16 * 128 * blk
     # channel gate: three gate-scaled [C, dk] operands and dk floats instead
     n = gdr.gdr_chunk_fwd_workspace_size(1, 100, 1, 64, 64, 32, gdr.GDR_F32,
                                          gdr.GDR_GATE_CHANNEL)
