@@ -16,7 +16,8 @@
 //   prep P   (1 wave)    window w: chunk w+1  decay vectors, off-diagonal blocks
 //                                             of A (handed to prep T through an
 //                                             LDS flag), P
-//   loaders  (2 waves)   window w: chunk w+2  global -> LDS copies
+//   loaders  (2 waves)   window w: chunk w+2  global -> LDS copies; loader 0
+//                                             then builds the chunk's gate table
 // A chunk's inputs therefore live in a 3-deep ring of LDS stages and its T / P
 // tiles in a 2-deep ring; T and P never leave the chip, and every global byte
 // is read once per workgroup.
@@ -45,10 +46,6 @@ constexpr float kFMinLogAlpha = -200.f;   // e^-200 is 0 in fp32
 
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ float fexp(float x) {
-    return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
-}
-
 __device__ __forceinline__ f32x4 mma16(f16x4 a, f16x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
@@ -76,18 +73,26 @@ struct FLayout {
     static constexpr int VT = 16 * NW;
     static constexpr int QB = FC * DK * 2;
     static constexpr int VB = FC * VT * 2;
-    static constexpr int S_Q = 0, S_K = QB, S_V = 2 * QB, S_LA = S_V + VB, S_BE = S_LA + FC * 4;
-    static constexpr int STAGE = S_BE + FC * 4;
+    static constexpr int S_Q = 0, S_K = QB, S_V = 2 * QB;
+    static constexpr int STAGE = S_V + VB;
     static constexpr int NSTAGE = 3;
-    static constexpr int T_T = 0, T_P = FC * FC * 2, T_VEC = 2 * FC * FC * 2;   // VEC: gamma, gamma_last/gamma
-    static constexpr int TPB = T_VEC + 2 * FC * 4;
+    static constexpr int T_T = 0, T_P = FC * FC * 2;
+    static constexpr int TPB = 2 * FC * FC * 2;
     static constexpr int TP0 = NSTAGE * STAGE;
     static constexpr int XA = TP0 + 2 * TPB;              // diagonal blocks of A (transposed), then
                                                           // blockdiag of their 8x8 inverses; fp32, tile
                                                           // stride 272, rows of 16
-    static constexpr int GT = XA + FNB * 272 * 4;         // gate table of the T wave: g, beta, eb, fb (4 x 64 floats)
-    static constexpr int GP = GT + 4 * FC * 4;            // gate table of the P wave
-    static constexpr int AO = GP + 4 * FC * 4;            // off-diagonal blocks of A (P wave -> T wave), fp16 per lane
+    // Gate tables, a 3-deep ring (chunk n in slot n % 3), 64 floats per field:
+    static constexpr int G_G2 = 0;        // g_r * log2(e), g the in-chunk cumulative log decay
+    static constexpr int G_BE = 1;        // beta_r
+    static constexpr int G_EB = 2;        // e^{g_r - g_end(blk(r) - 1)}  (decay since the previous block's end)
+    static constexpr int G_FB = 3;        // e^{g_end(blk(r)) - g_r}       (decay until the own block's end)
+    static constexpr int G_GM = 4;        // gamma_r = e^{g_r}
+    static constexpr int G_GH = 5;        // e^{g_last - g_r}
+    static constexpr int G_CX = 6;        // e^{g_end(rb-1) - g_end(cb)} for (cb, rb) = (0,2), (0,3), (1,3)
+    static constexpr int GSLOT = 6 * FC * 4 + 64;
+    static constexpr int GT0 = XA + FNB * 272 * 4;
+    static constexpr int AO = GT0 + 3 * GSLOT;            // off-diagonal blocks of A (P wave -> T wave), fp16 per lane
     static constexpr int FLAG = AO + 6 * 64 * 8;          // chunk index + 1 whose blocks are in AO
     static constexpr int TOTAL = FLAG + 16;
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
@@ -180,37 +185,52 @@ struct FragOffsets {
     }
 };
 
-// Loader wave lw (0 or 1): copies of chunk inputs into one stage.  Rows at or
+// Loader wave lw (0 or 1): copies of chunk inputs into one stage, half of the
+// 1 KB copy instructions each.  The per-lane source offsets (bytes from the
+// chunk's first row) are fixed for full chunks and computed once; rows at or
 // past len repeat row len-1 (finite; the prep masks them out).
 template <int DK, int NW>
+struct LoadOffsets {
+    static constexpr int NIQ = FLayout<DK, NW>::QB / 1024 / 2;   // Q (and K) instructions per loader
+    static constexpr int NIV = FLayout<DK, NW>::VB / 1024 / 2;   // V instructions per loader
+    int qk[NIQ];
+    int v[NIV];
+    __device__ __forceinline__ void set(int len, int H, int DV, int vt, int lw, int lane) {
+        constexpr int VT = 16 * NW, RP = DK / 8, RPV = VT / 8;
+#pragma unroll
+        for (int j = 0; j < NIQ; ++j) {
+            const int slot = 64 * (2 * j + lw) + lane;
+            const int r = slot / RP, pp = slot % RP;
+            qk[j] = (r < len ? r : len - 1) * (H * DK * 2) + 16 * (pp ^ swz_qk<DK>(r));
+        }
+#pragma unroll
+        for (int j = 0; j < NIV; ++j) {
+            const int slot = 64 * (2 * j + lw) + lane;
+            const int r = slot / RPV, pp = slot % RPV;
+            v[j] = (r < len ? r : len - 1) * (H * DV * 2) + vt * VT * 2 + 16 * (pp ^ swz_v<VT>(r));
+        }
+    }
+};
+
+template <int DK, int NW>
 __device__ __forceinline__ void load_chunk(char* stg, const __bf16* q, const __bf16* k, const __bf16* v,
-                                           const float* la, const float* be, int64_t row0, int len,
-                                           int H, int DV, int vt, int lw, int lane) {
+                                           int64_t row0, int DV, const LoadOffsets<DK, NW>& lo, int lw) {
     using L = FLayout<DK, NW>;
-    constexpr int RP = DK / 8, NI = L::QB / 1024;
-    const int64_t qks = (int64_t)H * DK * 2;
+    using LO = LoadOffsets<DK, NW>;
     const char* qb = reinterpret_cast<const char*>(q + row0 * DK);
     const char* kb = reinterpret_cast<const char*>(k + row0 * DK);
+    const char* vb = reinterpret_cast<const char*>(v + row0 * DV);
 #pragma unroll
-    for (int ins = lw; ins < NI; ins += 2) {
-        const int slot = 64 * ins + lane;
-        const int r = slot / RP, pp = slot % RP;
-        const int64_t off = (int64_t)(r < len ? r : len - 1) * qks + 16 * (pp ^ swz_qk<DK>(r));
-        __builtin_amdgcn_global_load_lds(qb + off, (GDR_LDS void*)(stg + L::S_Q + 1024 * ins), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(kb + off, (GDR_LDS void*)(stg + L::S_K + 1024 * ins), 16, 0, 0);
+    for (int j = 0; j < LO::NIQ; ++j) {
+        const int ins = 2 * j + lw;
+        __builtin_amdgcn_global_load_lds(qb + (uint32_t)lo.qk[j], (GDR_LDS void*)(stg + L::S_Q + 1024 * ins), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(kb + (uint32_t)lo.qk[j], (GDR_LDS void*)(stg + L::S_K + 1024 * ins), 16, 0, 0);
     }
-    constexpr int VT = L::VT, RPV = VT / 8, NIV = L::VB / 1024;
-    const int64_t vs = (int64_t)H * DV * 2;
-    const char* vb = reinterpret_cast<const char*>(v + row0 * DV + vt * VT);
 #pragma unroll
-    for (int ins = lw; ins < NIV; ins += 2) {
-        const int slot = 64 * ins + lane;
-        const int r = slot / RPV, pp = slot % RPV;
-        const int64_t off = (int64_t)(r < len ? r : len - 1) * vs + 16 * (pp ^ swz_v<VT>(r));
-        __builtin_amdgcn_global_load_lds(vb + off, (GDR_LDS void*)(stg + L::S_V + 1024 * ins), 16, 0, 0);
+    for (int j = 0; j < LO::NIV; ++j) {
+        const int ins = 2 * j + lw;
+        __builtin_amdgcn_global_load_lds(vb + (uint32_t)lo.v[j], (GDR_LDS void*)(stg + L::S_V + 1024 * ins), 16, 0, 0);
     }
-    const float* gsrc = (lw == 0 ? la : be) + row0 + (int64_t)(lane < len ? lane : len - 1) * H;
-    __builtin_amdgcn_global_load_lds(gsrc, (GDR_LDS void*)(stg + (lw == 0 ? L::S_LA : L::S_BE)), 4, 0, 0);
 }
 
 // DPP move of x (row_shr, row_bcast); lanes without a source get 0.
@@ -237,42 +257,41 @@ __device__ __forceinline__ float lane_value(float x, int l) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
 }
 
-// Per-chunk gate table (lane = token row r, rows >= len have log alpha = 0 and
-// beta = 0):  tab[r] = g_r,  tab[64+r] = beta_r,
-//             tab[128+r] = e^{g_r - g_end(blk(r)-1)}  (decay since the previous block's end)
-//             tab[192+r] = e^{g_end(blk(r)) - g_r}    (decay until the own block's end)
-// so that for r in block rb > cb >= blk(i):
-//   e^{g_r - g_i} = tab[128+r] * e^{g_end(rb-1) - g_end(cb)} * tab[192+i],
+// The gate table of one chunk (layout in FLayout), built by loader 0 from the
+// chunk's gate values (lane r holds log alpha and beta of token r).  Lane = token row r; rows >= len get
+// log alpha = 0 and beta = 0.  With the block-boundary factors, for r in block
+// rb > cb >= blk(i):
+//   e^{g_r - g_i} = EB[r] * CX(cb, rb) * FB[i],
 // a product of factors <= 1 (no overflow; an underflow bounds a negligible value).
-struct GateEnds { float g, e0, e1, e2, e3; };
-
 template <int DK, int NW>
-__device__ __forceinline__ GateEnds gate_table(const char* st, int len, int lane, float* tab) {
+__device__ __forceinline__ void gate_table(float la, float bb, int len, int lane, float* tab) {
     using L = FLayout<DK, NW>;
-    const float* LA = reinterpret_cast<const float*>(st + L::S_LA);
-    const float* BE = reinterpret_cast<const float*>(st + L::S_BE);
-    const float la = lane < len ? fmaxf(LA[lane], kFMinLogAlpha) : 0.f;
-    const float bb = lane < len ? BE[lane] : 0.f;
-    GateEnds G;
-    G.g = wave_scan(la);
-    G.e0 = lane_value(G.g, 15);
-    G.e1 = lane_value(G.g, 31);
-    G.e2 = lane_value(G.g, 47);
-    G.e3 = lane_value(G.g, 63);
+    la = lane < len ? fmaxf(la, kFMinLogAlpha) : 0.f;
+    bb = lane < len ? bb : 0.f;
+    const float g2 = wave_scan(la * 1.4426950408889634f);
+    const float e0 = lane_value(g2, 15), e1 = lane_value(g2, 31), e2 = lane_value(g2, 47),
+                e3 = lane_value(g2, 63);
     const int blk = lane >> 4;
-    const float gprev = blk == 0 ? 0.f : (blk == 1 ? G.e0 : (blk == 2 ? G.e1 : G.e2));
-    const float gend = blk == 0 ? G.e0 : (blk == 1 ? G.e1 : (blk == 2 ? G.e2 : G.e3));
-    tab[lane] = G.g;
-    tab[FC + lane] = bb;
-    tab[2 * FC + lane] = fexp(G.g - gprev);
-    tab[3 * FC + lane] = fexp(gend - G.g);
-    return G;
+    const float gprev = blk == 0 ? 0.f : (blk == 1 ? e0 : (blk == 2 ? e1 : e2));
+    const float gend = blk == 0 ? e0 : (blk == 1 ? e1 : (blk == 2 ? e2 : e3));
+    tab[L::G_G2 * FC + lane] = g2;
+    tab[L::G_BE * FC + lane] = bb;
+    tab[L::G_EB * FC + lane] = __builtin_amdgcn_exp2f(g2 - gprev);
+    tab[L::G_FB * FC + lane] = __builtin_amdgcn_exp2f(gend - g2);
+    tab[L::G_GM * FC + lane] = __builtin_amdgcn_exp2f(g2);
+    tab[L::G_GH * FC + lane] = __builtin_amdgcn_exp2f(e3 - g2);
+    if (lane < 3) {
+        const float d = lane == 0 ? e1 - e0 : (lane == 1 ? e2 - e0 : e2 - e1);
+        tab[L::G_CX * FC + lane] = __builtin_amdgcn_exp2f(d);
+    }
 }
 
-// e^{g_end(rb-1) - g_end(cb)} for cb < rb (1 when the blocks are adjacent).
-__device__ __forceinline__ float cross_decay(const GateEnds& G, int cb, int rb) {
-    const float e[4] = {G.e0, G.e1, G.e2, G.e3};
-    return rb == cb + 1 ? 1.f : fexp(e[rb - 1] - e[cb]);
+// CX(cb, rb) (1 when the blocks are adjacent), from the table.
+template <int DK, int NW>
+__device__ __forceinline__ float cross_decay(const float* tab, int cb, int rb) {
+    using L = FLayout<DK, NW>;
+    if (rb == cb + 1) return 1.f;
+    return tab[L::G_CX * FC + (cb == 0 ? rb - 2 : 2)];
 }
 
 // Prep T: T = (I + A)^-1 Diag(beta) for one chunk, in one wave.
@@ -286,17 +305,17 @@ __device__ __forceinline__ float cross_decay(const GateEnds& G, int cb, int rb) 
 //    16x16x16 MFMAs, in both operand layouts.
 //  - Off-diagonal blocks of X = (I + A)^-1 by the block recurrence
 //        X_ij = -X_ii sum_{m=j}^{i-1} A_im X_mj
-//    on fp16 16x16x16 MFMAs with fp32 accumulation, row block by row block.
+//    (carried out for T = X Diag(beta) directly) on fp16 16x16x16 MFMAs with
+//    fp32 accumulation, row block by row block.
 //  Entries of A and X are bounded by small constants here (unit-norm keys,
 //  beta <= 1, decays <= 1), well inside fp16's range; T is rounded to bf16 after.
 template <int DK, int NW>
-__device__ __forceinline__ void prep_t(char* smem, const char* st, char* tp, int n, int len, int lane) {
+__device__ __forceinline__ void prep_t(char* smem, const char* st, const float* tab, char* tp, int n,
+                                       int lane) {
     using L = FLayout<DK, NW>;
     constexpr int NKC = DK / 32;
-    float* tab = reinterpret_cast<float*>(smem + L::GT);
     float* xa = reinterpret_cast<float*>(smem + L::XA);
     const int col = lane & 15, g4 = lane >> 4;
-    const GateEnds G = gate_table<DK, NW>(st, len, lane, tab);
 
     bf16x8 kf[FNB][NKC];
 #pragma unroll
@@ -312,19 +331,18 @@ __device__ __forceinline__ void prep_t(char* smem, const char* st, char* tp, int
 #pragma unroll
         for (int b = 0; b < FNB; ++b) Gd[b] = Mma<__bf16>::mma(kf[b][s], kf[b][s], Gd[b]);
     // A_bb in B layout (row 4g4 + e, column col), also stored transposed:
-    // xa[b][m][i] = A_bb[i][m].
+    // xa[b][m][i] = A_bb[i][m].  Entries on or above the diagonal are not
+    // masked: nothing reads them (the substitution uses rows i > m only, and N
+    // lies strictly below).
     f32x4 Ab[FNB];
 #pragma unroll
     for (int b = 0; b < FNB; ++b) {
-        const float4 gr = *reinterpret_cast<const float4*>(tab + 16 * b + 4 * g4);
-        const float4 br = *reinterpret_cast<const float4*>(tab + FC + 16 * b + 4 * g4);
-        const float gc = tab[16 * b + col];
+        const float4 gr = *reinterpret_cast<const float4*>(tab + L::G_G2 * FC + 16 * b + 4 * g4);
+        const float4 br = *reinterpret_cast<const float4*>(tab + L::G_BE * FC + 16 * b + 4 * g4);
+        const float gc = tab[L::G_G2 * FC + 16 * b + col];
         const float grv[4] = {gr.x, gr.y, gr.z, gr.w}, brv[4] = {br.x, br.y, br.z, br.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float a = Gd[b][e] * brv[e] * fexp(grv[e] - gc);
-            Ab[b][e] = col < 4 * g4 + e ? a : 0.f;
-        }
+        for (int e = 0; e < 4; ++e) Ab[b][e] = Gd[b][e] * brv[e] * __builtin_amdgcn_exp2f(grv[e] - gc);
         *reinterpret_cast<float4*>(xa + b * 272 + col * 16 + 4 * g4) =
             make_float4(Ab[b][0], Ab[b][1], Ab[b][2], Ab[b][3]);
     }
@@ -404,17 +422,17 @@ __device__ __forceinline__ void prep_t(char* smem, const char* st, char* tp, int
 #pragma unroll
             for (int cb = 0; cb < rb; ++cb) Ao[rb][cb] = ao[(rb * (rb - 1) / 2 + cb) * 64 + lane];
     }
-    // Row wavefront: for row block i, every column block j < i at once (the
-    // X_mj it needs, m < i, are done), so independent chains interleave.
+    // T = X Diag(beta) satisfies the same recurrence, T_ij = -X_ii sum A_im T_mj,
+    // from T_jj = X_jj Diag(beta_j).  Row wavefront: for row block i, every
+    // column block j < i at once (the T_mj it needs, m < i, are done), so
+    // independent chains interleave.
     char* Tt = tp + L::T_T;
-    float bC[FNB];
-#pragma unroll
-    for (int b = 0; b < FNB; ++b) bC[b] = tab[FC + 16 * b + col];
-    f16x4 xm[FNB][FNB];   // B layout of X_mj, fp16
+    f16x4 xm[FNB][FNB];   // B layout of T_mj, fp16
 #pragma unroll
     for (int j = 0; j < FNB; ++j) {
-        tp_store(Tt, j, j, lane, Xb[j] * bC[j]);
-        xm[j][j] = to_f16(Xb[j]);
+        const f32x4 t = Xb[j] * tab[L::G_BE * FC + 16 * j + col];
+        tp_store(Tt, j, j, lane, t);
+        xm[j][j] = to_f16(t);
     }
 #pragma unroll
     for (int i = 1; i < FNB; ++i) {
@@ -429,22 +447,19 @@ __device__ __forceinline__ void prep_t(char* smem, const char* st, char* tp, int
         for (int j = 0; j < i; ++j) {
             const f32x4 z = -mma16(Xa[i], to_f16(y[j]), zero4());
             xm[i][j] = to_f16(z);
-            tp_store(Tt, i, j, lane, z * bC[j]);
+            tp_store(Tt, i, j, lane, z);
         }
     }
 }
 
-// Prep P: gamma vectors and P = (Q K^T) masked and decayed, stored transposed.
+// Prep P: the off-diagonal blocks of A (for the T wave) and P = (Q K^T)
+// masked and decayed, stored transposed.
 template <int DK, int NW>
-__device__ __forceinline__ void prep_p(char* smem, const char* st, char* tp, int n, int len, int lane) {
+__device__ __forceinline__ void prep_p(char* smem, const char* st, const float* tab, char* tp, int n,
+                                       int lane) {
     using L = FLayout<DK, NW>;
     constexpr int NKC = DK / 32;
-    float* tab = reinterpret_cast<float*>(smem + L::GP);
     const int col = lane & 15, g4 = lane >> 4;
-    const GateEnds G = gate_table<DK, NW>(st, len, lane, tab);
-    float* vec = reinterpret_cast<float*>(tp + L::T_VEC);
-    vec[lane] = fexp(G.g);
-    vec[FC + lane] = fexp(G.e3 - G.g);
 
     bf16x8 kf[FNB][NKC], qf[FNB][NKC];
 #pragma unroll
@@ -475,11 +490,11 @@ __device__ __forceinline__ void prep_p(char* smem, const char* st, char* tp, int
         f16x4* ao = reinterpret_cast<f16x4*>(smem + L::AO);
 #pragma unroll
         for (int rb = 1; rb < FNB; ++rb) {
-            const float f0 = tab[FC + 16 * rb + col] * tab[2 * FC + 16 * rb + col];
+            const float f0 = tab[L::G_BE * FC + 16 * rb + col] * tab[L::G_EB * FC + 16 * rb + col];
 #pragma unroll
             for (int cb = 0; cb < rb; ++cb) {
-                const float4 fr = *reinterpret_cast<const float4*>(tab + 3 * FC + 16 * cb + 4 * g4);
-                const float f = f0 * cross_decay(G, cb, rb);
+                const float4 fr = *reinterpret_cast<const float4*>(tab + L::G_FB * FC + 16 * cb + 4 * g4);
+                const float f = f0 * cross_decay<DK, NW>(tab, cb, rb);
                 f32x4 acc = go[rb * (rb - 1) / 2 + cb];
                 acc[0] *= f * fr.x;
                 acc[1] *= f * fr.y;
@@ -507,18 +522,19 @@ __device__ __forceinline__ void prep_p(char* smem, const char* st, char* tp, int
     char* Pt = tp + L::T_P;
 #pragma unroll
     for (int rb = 0; rb < FNB; ++rb) {
-        const float4 gr = *reinterpret_cast<const float4*>(tab + 16 * rb + 4 * g4);
-        const float4 er = *reinterpret_cast<const float4*>(tab + 2 * FC + 16 * rb + 4 * g4);
+        const float4 gr = *reinterpret_cast<const float4*>(tab + L::G_G2 * FC + 16 * rb + 4 * g4);
+        const float4 er = *reinterpret_cast<const float4*>(tab + L::G_EB * FC + 16 * rb + 4 * g4);
         const float grv[4] = {gr.x, gr.y, gr.z, gr.w}, erv[4] = {er.x, er.y, er.z, er.w};
 #pragma unroll
         for (int cb = 0; cb <= rb; ++cb) {
             f32x4 acc = pa[rb * (rb + 1) / 2 + cb];
             if (cb == rb) {
-                const float gc = tab[16 * cb + col];
+                const float gc = tab[L::G_G2 * FC + 16 * cb + col];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[e] = col <= 4 * g4 + e ? acc[e] * fexp(grv[e] - gc) : 0.f;
+                for (int e = 0; e < 4; ++e)
+                    acc[e] = col <= 4 * g4 + e ? acc[e] * __builtin_amdgcn_exp2f(grv[e] - gc) : 0.f;
             } else {
-                const float f = cross_decay(G, cb, rb) * tab[3 * FC + 16 * cb + col];
+                const float f = cross_decay<DK, NW>(tab, cb, rb) * tab[L::G_FB * FC + 16 * cb + col];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) acc[e] *= erv[e] * f;
             }
@@ -549,6 +565,7 @@ __global__ __launch_bounds__(64 * (NW + 4)) void fused_chunk(
     const int64_t b = bh / H, h = bh % H;
 #define GDR_STAGE(n) (smem + ((n) % 3) * L::STAGE)
 #define GDR_TPBUF(n) (smem + L::TP0 + ((n) & 1) * L::TPB)
+#define GDR_GTAB(n) (reinterpret_cast<float*>(smem + L::GT0 + ((n) % 3) * L::GSLOT))
 #define GDR_LEN(n) ((int)((T - (int64_t)(n) * FC) < FC ? (T - (int64_t)(n) * FC) : FC))
 #define GDR_ROW0(n) ((b * T + (int64_t)(n) * FC) * H + h)
 
@@ -557,6 +574,7 @@ __global__ __launch_bounds__(64 * (NW + 4)) void fused_chunk(
         const int vcol0 = vt * VT + 16 * wave;
         const int vcol = vcol0 + col;
         const FragOffsets<DK, VT> fo(lane, wave);
+        const int olane = (col * H * DV + vcol0 + 4 * g4) * 2;   // byte offset of the lane's output piece
         f32x4 S[CT];
 #pragma unroll
         for (int mc = 0; mc < CT; ++mc) {
@@ -582,7 +600,7 @@ __global__ __launch_bounds__(64 * (NW + 4)) void fused_chunk(
                 const char* st = GDR_STAGE(n);
                 const char* tp = GDR_TPBUF(n);
                 const int len = GDR_LEN(n);
-                const float* vec = reinterpret_cast<const float*>(tp + L::T_VEC);
+                const float* tab = GDR_GTAB(n);
 
                 // The window's work in phases; each phase first issues the LDS
                 // reads of a later phase, so their latency is covered by MFMAs
@@ -603,7 +621,7 @@ __global__ __launch_bounds__(64 * (NW + 4)) void fused_chunk(
 #pragma unroll
                 for (int mt = 0; mt < FNB; ++mt) {
                     vv[mt] = fo.vf(st + L::S_V, mt);
-                    gm[mt] = *reinterpret_cast<const float4*>(vec + 16 * mt + 4 * g4);
+                    gm[mt] = *reinterpret_cast<const float4*>(tab + L::G_GM * FC + 16 * mt + 4 * g4);
                 }
                 // Phase 1: R = K S^T (rows = tokens) from the prefetched K fragments.
                 M::frag sb[NKC];
@@ -652,10 +670,10 @@ __global__ __launch_bounds__(64 * (NW + 4)) void fused_chunk(
                 for (int mt = 0; mt < FNB; ++mt) {
 #pragma unroll
                     for (int s = 0; s < NKT; ++s) pf[mt][s] = fo.tpf(tp + L::T_P, mt, s);
-                    gh[mt] = *reinterpret_cast<const float4*>(vec + FC + 16 * mt + 4 * g4);
-                    gc[mt] = vec[16 * mt + col];
+                    gh[mt] = *reinterpret_cast<const float4*>(tab + L::G_GH * FC + 16 * mt + 4 * g4);
+                    gc[mt] = tab[L::G_GM * FC + 16 * mt + col];
                 }
-                const float gl = vec[FC - 1];
+                const float gl = tab[L::G_GM * FC + FC - 1];
                 __builtin_amdgcn_sched_barrier(0);
                 // Phase 3: S^T <- gamma_last S^T + K^T (Diag(gamma_last / gamma) D).
                 M::frag db[NKT], dsb[NKT];
@@ -709,14 +727,21 @@ __global__ __launch_bounds__(64 * (NW + 4)) void fused_chunk(
                         for (int s = 0; s < NKP; ++s)
                             kn[mt][s] = fo.qkf(GDR_STAGE(n + 1) + L::S_K, mt, s);
                 }
-                // Output rows: lane (col, g4) of tile mt holds o[16mt + col][vcol0 + 4g4 + e].
-                const int64_t row0 = GDR_ROW0(n);
+                // Output rows: lane (col, g4) of tile mt holds o[16mt + col][vcol0 + 4g4 + e]
+                // (wave-uniform row base, per-lane 32-bit offset).
+                char* ob = reinterpret_cast<char*>(o) + GDR_ROW0(n) * DV * 2;
+                const int64_t tstride = (int64_t)16 * H * DV * 2;
+                if (len == FC) {
 #pragma unroll
-                for (int mt = 0; mt < FNB; ++mt) {
-                    const int r = 16 * mt + col;
-                    if (r < len) {
+                    for (int mt = 0; mt < FNB; ++mt) {
                         const bf16x4 y = {(__bf16)Oa[mt][0], (__bf16)Oa[mt][1], (__bf16)Oa[mt][2], (__bf16)Oa[mt][3]};
-                        *reinterpret_cast<bf16x4*>(o + (row0 + (int64_t)r * H) * DV + vcol0 + 4 * g4) = y;
+                        *reinterpret_cast<bf16x4*>(ob + mt * tstride + olane) = y;
+                    }
+                } else {
+#pragma unroll
+                    for (int mt = 0; mt < FNB; ++mt) {
+                        const bf16x4 y = {(__bf16)Oa[mt][0], (__bf16)Oa[mt][1], (__bf16)Oa[mt][2], (__bf16)Oa[mt][3]};
+                        if (16 * mt + col < len) *reinterpret_cast<bf16x4*>(ob + mt * tstride + olane) = y;
                     }
                 }
             }
@@ -743,7 +768,7 @@ __global__ __launch_bounds__(64 * (NW + 4)) void fused_chunk(
                 }
         for (int w = -2; w < NT; ++w) {
             const int n = w + 1;
-            if (n >= 0 && n < NT) prep_t<DK, NW>(smem, GDR_STAGE(n), GDR_TPBUF(n), n, GDR_LEN(n), lane);
+            if (n >= 0 && n < NT) prep_t<DK, NW>(smem, GDR_STAGE(n), GDR_GTAB(n), GDR_TPBUF(n), n, lane);
             __syncthreads();
         }
     } else if (wave == NW + 1) {
@@ -751,18 +776,37 @@ __global__ __launch_bounds__(64 * (NW + 4)) void fused_chunk(
         if (lane == 0) *reinterpret_cast<int*>(smem + L::FLAG) = 0;
         for (int w = -2; w < NT; ++w) {
             const int n = w + 1;
-            if (n >= 0 && n < NT) prep_p<DK, NW>(smem, GDR_STAGE(n), GDR_TPBUF(n), n, GDR_LEN(n), lane);
+            if (n >= 0 && n < NT) prep_p<DK, NW>(smem, GDR_STAGE(n), GDR_GTAB(n), GDR_TPBUF(n), n, lane);
             __syncthreads();
         }
     } else {
         // ---------------- loaders ----------------
+        // Window w copies chunk c = w + 2 into its stage; loader 0 then builds
+        // chunk c's gate table from gate values gathered one window earlier
+        // (so nothing waits inside the window), and both gather chunk c + 1's.
         const int lw = wave - NW - 2;
+        LoadOffsets<DK, NW> lo;
+        lo.set(FC, H, DV, vt, lw, lane);
+        float la, bb;
+        {
+            const int64_t go = GDR_ROW0(0) + (int64_t)(lane < GDR_LEN(0) ? lane : GDR_LEN(0) - 1) * H;
+            la = log_alpha[go];
+            bb = beta[go];
+        }
         for (int w = -2; w < NT; ++w) {
             const int n = w + 2;
             if (n < NT) {
-                load_chunk<DK, NW>(GDR_STAGE(n), q, k, v, log_alpha, beta, GDR_ROW0(n), GDR_LEN(n), H, DV,
-                                   vt, lw, lane);
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                const int len = GDR_LEN(n);
+                if (len < FC) lo.set(len, H, DV, vt, lw, lane);   // ragged last chunk
+                load_chunk<DK, NW>(GDR_STAGE(n), q, k, v, GDR_ROW0(n), DV, lo, lw);
+                if (lw == 0) gate_table<DK, NW>(la, bb, len, lane, GDR_GTAB(n));
+                if (n + 1 < NT) {
+                    const int len1 = GDR_LEN(n + 1);
+                    const int64_t go = GDR_ROW0(n + 1) + (int64_t)(lane < len1 ? lane : len1 - 1) * H;
+                    la = log_alpha[go];
+                    bb = beta[go];
+                }
+                __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): copies and gathers landed
             }
             __syncthreads();
         }
@@ -771,6 +815,7 @@ __global__ __launch_bounds__(64 * (NW + 4)) void fused_chunk(
 #undef GDR_TPBUF
 #undef GDR_LEN
 #undef GDR_ROW0
+#undef GDR_GTAB
 }
 
 template <int DK, int NW>
