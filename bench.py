@@ -61,7 +61,7 @@ def decode_algorithmic(B, H, d, io_bytes=4):
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gdr_chunk_fwd_gdn_B4_H16_T4096_d128.traffic.txt")
 COPY_BYTES = 256 << 20
-PREFILL_KERNELS = ("wy_prep", "state_pass")
+PREFILL_KERNELS = ("fused_chunk", "wy_prep", "state_pass")
 
 
 def kernel_source_hash():
@@ -133,6 +133,7 @@ def measure_traffic(outdir):
         kib_copy = sum(per["copy"]) / len(per["copy"])
         factor = (COPY_BYTES / 1024.0) / kib_copy
         kib_call = sum(sum(per[k]) / len(per[k]) for k in PREFILL_KERNELS if k in per)
+        res.setdefault("kernels", sorted(k for k in PREFILL_KERNELS if k in per))
         res[ctr] = dict(kib_per_call=kib_call, copy_kib=kib_copy, factor=factor,
                         bytes_per_call=kib_call * factor * 1024.0)
     return res
@@ -162,7 +163,7 @@ def main():
             fh.write("# HBM traffic of one gdr_chunk_fwd call (B=4,T=4096,H=16,d=128,chunk=64, bf16)\n")
             fh.write("# command: python bench.py --traffic   (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)\n")
             fh.write("# kernels: %s; calibration: plain %d MiB device copy\n"
-                     % (", ".join(PREFILL_KERNELS), COPY_BYTES >> 20))
+                     % (", ".join(res.get("kernels", PREFILL_KERNELS)), COPY_BYTES >> 20))
             fh.write("source_hash=%s\n" % kernel_source_hash())
             for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
                 r = res[ctr]
@@ -283,7 +284,7 @@ def main():
         "config": {"workload": w.name, "call": "gdr_chunk_fwd", "gate": "scalar",
                    "B": B, "T": T, "H": H, "d_k": d, "d_v": d, "chunk": C,
                    "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "gdr_chunk_fwd (wy_prep + state_pass)",
+        "roofline": {"bound": "hbm", "kernel": "gdr_chunk_fwd (single kernel: fused_chunk<128, 2>)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": nbytes,
