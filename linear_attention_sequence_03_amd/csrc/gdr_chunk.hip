@@ -601,6 +601,416 @@ __global__ __launch_bounds__(kThreads) void wy_prep_channel(
 }
 
 // ---------------------------------------------------------------------------
+// Kernel 1, channel gate (KDA), bf16 io.  One wave per 16-token block b of the
+// chunk (C/16 waves); the block's q, k and log alpha stay in registers in MFMA
+// operand layout: lane (x, kg) = (lane % 16, lane / 16) holds token row
+// 16b + x, channels 32s + 8kg + (0..7) of channel step s.
+//  - g (per channel, in-chunk cumulative, log2 units): a scan over the 16 lanes
+//    of a DPP row (row_shr 1, 2, 4, 8) plus the totals of the earlier blocks,
+//    exchanged through LDS.
+//  - Gram tiles (b, cb <= b) of A = Diag(beta) (K.Gamma)(K/Gamma)^T and of
+//    P = (Q.Gamma)(K/Gamma)^T on the matrix cores, around reference points that
+//    keep the factors in range:
+//      cb < b: ref = g at the last row of block cb; A side x_r 2^{g_r - ref} <= 1,
+//              B side k_i 2^{ref - g_i} <= 1 (built once by wave cb, in LDS);
+//      cb = b: ref = g at the last row of block b - 1 (0 for b = 0); the B side
+//              k_i 2^{ref - g_i} >= 1 grows with the block's decay span, and if
+//              some channel's span exceeds kSafeSpan nats the block is summed
+//              exactly, pair by pair.
+//    The tiles come out transposed ("row layout": lane (x, kg) holds row x,
+//    columns 4kg..4kg+3), which is the A operand of the fp32 MFMA below.
+//  - T = (I + A)^-1 Diag(beta): each wave inverts its diagonal block by forward
+//    substitution in fp32, then row block by row block
+//        T_bj = -X_bb sum_{m=j}^{b-1} A_bm T_mj
+//    on fp32 16x16x4 MFMAs, the tiles of earlier rows coming through LDS.
+//  - Outputs in the workspace layout the state pass reads: T and P (row-major,
+//    zero above the diagonal blocks), Qg = Q.Gamma, Kg = K.Gamma,
+//    Kh = K.(gamma_C / Gamma) and gl = gamma_C.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_shr(float x) {
+    // lanes without a source in their row of 16 get 0
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf,
+                                                                  0xf, false));
+}
+
+// LDS of one workgroup of wy_prep_channel_bf16.
+template <int DK, int C>
+struct ChanPrepSmem {
+    static constexpr int NB = C / 16, NKS = DK / 32;
+    static constexpr int NPUB = NB > 1 ? NB - 1 : 1;
+    static constexpr int NTP = NB > 1 ? NB * (NB - 1) / 2 : 1;
+    static constexpr int SR = C + 8;                     // staging row stride (bf16)
+    alignas(16) float tot[NB][DK];                       // block totals of g
+    alignas(16) bf16x8 bpub[NPUB][NKS][64];              // B sides of blocks < NB-1
+    alignas(16) float xa[NB][16 * 16];                   // A_bb^T for the substitution
+    alignas(16) float xx[NB][16 * 17];                   // X_bb = (I + A_bb)^-1
+    alignas(16) f32x4 tpub[NTP][64];                     // T tiles of rows < NB-1
+    alignas(16) __bf16 stg[NB][16 * SR];                 // row-block staging of P, T
+    alignas(16) float bsh[C];
+};
+
+// The work of wave BW (16-row block BW).  The block index is a compile-time
+// constant, so no matrix instruction sits under a wave-dependent condition.
+template <int DK, int C, int BW>
+__device__ __forceinline__ void chan_prep_wave(ChanPrepSmem<DK, C>& sm, const __bf16* __restrict__ q,
+                                               const __bf16* __restrict__ k,
+                                               const float* __restrict__ log_alpha,
+                                               const float* __restrict__ beta, uint8_t* __restrict__ ws,
+                                               int64_t T, int H, int NT) {
+    using L = WsLayout<__bf16, DK, C, true>;
+    using M = Mma<__bf16>;
+    using MF = Mma<float>;
+    constexpr int NB = C / 16;
+    constexpr int NKS = DK / 32;
+    constexpr float kLog2e = 1.4426950408889634f;
+    constexpr float kSafeSpan2 = kSafeSpan * kLog2e;
+    constexpr int NPUB = NB > 1 ? NB - 1 : 1;
+    constexpr int NTP = NB > 1 ? NB * (NB - 1) / 2 : 1;
+    constexpr int SR = C + 8;                 // staging row stride (bf16), 16-byte aligned rows
+    constexpr int NPC = 2 * C;                // 16-byte pieces of a 16-row block of a C x C tile
+    auto& tot = sm.tot;
+    auto& bpub = sm.bpub;
+    auto& xa = sm.xa;
+    auto& xx = sm.xx;
+    auto& tpub = sm.tpub;
+    auto& stg = sm.stg;
+    auto& bsh = sm.bsh;
+    constexpr int b = BW;   // this wave's 16-row block
+    const int lane = threadIdx.x & 63;
+    const int x = lane & 15, kg = lane >> 4;
+    const int64_t bid = blockIdx.x;
+    const int n = (int)(bid % NT);
+    const int64_t bh = bid / NT;
+    const int64_t bi = bh / H, h = bh % H;
+    const int64_t t0 = (int64_t)n * C;
+    const int len = (int)((T - t0) < C ? (T - t0) : C);
+    const int64_t row0 = (bi * T + t0) * H + h;
+    uint8_t* blk = ws + (size_t)bid * L::BYTES;
+
+    const int r = 16 * b + x;
+    const bool valid = r < len;   // rows past len read row len-1 and are zeroed
+    const int64_t grow = row0 + (int64_t)(valid ? r : len - 1) * H;
+    const float be = valid ? beta[grow] : 0.f;
+    if (kg == 0) bsh[r] = be;
+
+    // Loads of channel step s: k or q (bf16x8), log alpha (in log2 units).
+    auto ld_qk = [&](const __bf16* p, int s) {
+        const bf16x8 t = *reinterpret_cast<const bf16x8*>(p + grow * DK + 32 * s + 8 * kg);
+        return valid ? t : bf16x8{};
+    };
+    auto ld_la = [&](int s, float* la) {
+        const float* p = log_alpha + grow * DK + 32 * s + 8 * kg;
+        const float4 l0 = *reinterpret_cast<const float4*>(p);
+        const float4 l1 = *reinterpret_cast<const float4*>(p + 4);
+        const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) la[j] = valid ? fmaxf(lv[j], kMinLogAlpha) * kLog2e : 0.f;
+    };
+    // In-block inclusive scan over the 16 rows (one DPP row per channel group).
+    auto scan = [&](float* v) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            float u = v[j];
+            u += dpp_shr<0x111>(u);
+            u += dpp_shr<0x112>(u);
+            u += dpp_shr<0x114>(u);
+            u += dpp_shr<0x118>(u);
+            v[j] = u;
+        }
+    };
+    auto ld_tot = [&](int cb, int s, float* tv) {
+        const float* tp = &tot[cb][32 * s + 8 * kg];
+        const float4 a0 = *reinterpret_cast<const float4*>(tp);
+        const float4 a1 = *reinterpret_cast<const float4*>(tp + 4);
+        tv[0] = a0.x; tv[1] = a0.y; tv[2] = a0.z; tv[3] = a0.w;
+        tv[4] = a1.x; tv[5] = a1.y; tv[6] = a1.z; tv[7] = a1.w;
+    };
+
+    f32x4 ga[NB], gp[NB];
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) ga[cb] = gp[cb] = zero4();
+    bool unsafe_lane = false;
+    // ---- per channel step s: g, the scaled operands, this block's B side,
+    //      then the Gram tiles (b, cb <= b) ----
+#pragma unroll 1
+    for (int s = 0; s < NKS; ++s) {
+        float gs[8];
+        ld_la(s, gs);
+        const bf16x8 kv = ld_qk(k, s), qv = ld_qk(q, s);
+        scan(gs);
+        if (x == 15) {
+            float* tp = &tot[b][32 * s + 8 * kg];
+            *reinterpret_cast<float4*>(tp) = make_float4(gs[0], gs[1], gs[2], gs[3]);
+            *reinterpret_cast<float4*>(tp + 4) = make_float4(gs[4], gs[5], gs[6], gs[7]);
+        }
+        __syncthreads();
+        float off[8], end[8], last[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) off[j] = end[j] = last[j] = 0.f;
+#pragma unroll
+        for (int cb = 0; cb < NB; ++cb) {
+            float tv[8];
+            ld_tot(cb, s, tv);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (cb < b) off[j] += tv[j];
+                if (cb <= b) end[j] += tv[j];
+                last[j] += tv[j];
+                if (cb == b && !(-tv[j] <= kSafeSpan2)) unsafe_lane = true;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) gs[j] += off[j];
+        const size_t eo = ((size_t)r * DK + 32 * s + 8 * kg) * sizeof(__bf16);
+        {
+            bf16x8 qg, kgv;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float eg = __builtin_amdgcn_exp2f(gs[j]);
+                qg[j] = (__bf16)((float)qv[j] * eg);
+                kgv[j] = (__bf16)((float)kv[j] * eg);
+            }
+            *reinterpret_cast<bf16x8*>(blk + L::QG + eo) = qg;
+            *reinterpret_cast<bf16x8*>(blk + L::KG + eo) = kgv;
+        }
+        {
+            bf16x8 kh;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) kh[j] = (__bf16)((float)kv[j] * __builtin_amdgcn_exp2f(last[j] - gs[j]));
+            *reinterpret_cast<bf16x8*>(blk + L::KH + eo) = kh;
+        }
+        if (b < NB - 1) {
+            bf16x8 kb;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) kb[j] = (__bf16)((float)kv[j] * __builtin_amdgcn_exp2f(end[j] - gs[j]));
+            bpub[b < NPUB ? b : 0][s][lane] = kb;
+        }
+        if (b == 0 && x == 0) {
+            float* glw = reinterpret_cast<float*>(blk + L::VEC) + 32 * s + 8 * kg;
+            *reinterpret_cast<float4*>(glw) =
+                make_float4(__builtin_amdgcn_exp2f(last[0]), __builtin_amdgcn_exp2f(last[1]),
+                            __builtin_amdgcn_exp2f(last[2]), __builtin_amdgcn_exp2f(last[3]));
+            *reinterpret_cast<float4*>(glw + 4) =
+                make_float4(__builtin_amdgcn_exp2f(last[4]), __builtin_amdgcn_exp2f(last[5]),
+                            __builtin_amdgcn_exp2f(last[6]), __builtin_amdgcn_exp2f(last[7]));
+        }
+        __syncthreads();
+
+        // A sides around the end of block cb (cb < b) against wave cb's B sides;
+        // the last one (cb = b - 1) is also the diagonal's A side.
+        bf16x8 ka, qa;
+        float ref[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ref[j] = 0.f;
+#pragma unroll
+        for (int cb = 0; cb < NB - 1; ++cb) {
+            if (cb < b) {
+                float tv[8];
+                ld_tot(cb, s, tv);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    ref[j] += tv[j];
+                    const float e = __builtin_amdgcn_exp2f(gs[j] - ref[j]);
+                    ka[j] = (__bf16)((float)kv[j] * e);
+                    qa[j] = (__bf16)((float)qv[j] * e);
+                }
+                const bf16x8 bs = bpub[cb][s][lane];
+                ga[cb] = M::mma(bs, ka, ga[cb]);
+                gp[cb] = M::mma(bs, qa, gp[cb]);
+            }
+        }
+        if (b == 0) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float e = __builtin_amdgcn_exp2f(gs[j]);
+                ka[j] = (__bf16)((float)kv[j] * e);
+                qa[j] = (__bf16)((float)qv[j] * e);
+            }
+        }
+        bf16x8 kd;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) kd[j] = (__bf16)((float)kv[j] * __builtin_amdgcn_exp2f(ref[j] - gs[j]));
+#pragma unroll
+        for (int cb = 0; cb < NB; ++cb)
+            if (cb == b) {
+                ga[cb] = M::mma(kd, ka, ga[cb]);
+                gp[cb] = M::mma(kd, qa, gp[cb]);
+            }
+    }
+    if (__ballot(unsafe_lane) != 0) {   // wave-uniform
+        // Exact diagonal block: sum_c x_rc k_ic 2^{g_rc - g_ic} (i <= r), row i
+        // of the block fetched from lane (i, kg); g (the in-block part suffices:
+        // the offsets cancel), q and k rebuilt per step.  Rare, so kept small.
+        f32x4 ea = zero4(), ep = zero4();
+#pragma unroll 1
+        for (int y = 0; y < 16; ++y) {
+            float a = 0.f, p = 0.f;
+#pragma unroll 1
+            for (int s = 0; s < NKS; ++s) {
+                float gs[8];
+                ld_la(s, gs);
+                const bf16x8 kv = ld_qk(k, s), qv = ld_qk(q, s);
+                scan(gs);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float kf = (float)kv[j];
+                    const float ky = __shfl(kf, y + 16 * kg);
+                    const float gy = __shfl(gs[j], y + 16 * kg);
+                    const float f = y <= x ? __builtin_amdgcn_exp2f(gs[j] - gy) : 0.f;
+                    a += kf * ky * f;
+                    p += (float)qv[j] * ky * f;
+                }
+            }
+            a += __shfl_xor(a, 16);
+            a += __shfl_xor(a, 32);
+            p += __shfl_xor(p, 16);
+            p += __shfl_xor(p, 32);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (y == 4 * kg + e) {
+                    ea[e] = a;
+                    ep[e] = p;
+                }
+        }
+#pragma unroll
+        for (int cb = 0; cb < NB; ++cb)
+            if (cb == b) {
+                ga[cb] = ea;
+                gp[cb] = ep;
+            }
+    }
+    // beta and the masks: A strictly lower, P lower including the diagonal
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int y = 4 * kg + e;
+            ga[cb][e] = (cb < b || (cb == b && y < x)) ? ga[cb][e] * be : 0.f;
+            gp[cb][e] = (cb < b || (cb == b && y <= x)) ? gp[cb][e] : 0.f;
+        }
+
+    // ---- P: row block b through the staging tile to the workspace ----
+    __bf16* sb = stg[b];
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) {
+        const bf16x4 v = {(__bf16)gp[cb][0], (__bf16)gp[cb][1], (__bf16)gp[cb][2], (__bf16)gp[cb][3]};
+        *reinterpret_cast<bf16x4*>(sb + x * SR + 16 * cb + 4 * kg) = v;
+    }
+    __builtin_amdgcn_wave_barrier();
+    uint8_t* Pw = blk + L::P + (size_t)(16 * b) * C * sizeof(__bf16);
+#pragma unroll
+    for (int i = 0; i < (NPC + 63) / 64; ++i) {
+        const int p = lane + 64 * i;
+        if (p < NPC) {
+            const int rr = p / (C / 8), pc = p % (C / 8);
+            *reinterpret_cast<V16*>(Pw + (size_t)p * 16) = *reinterpret_cast<const V16*>(sb + rr * SR + 8 * pc);
+        }
+    }
+
+    // ---- X_bb = (I + A_bb)^-1: lane j (mod 16) builds column j ----
+    float* xab = xa[b];
+    float* xxb = xx[b];
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb)
+        if (cb == b)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) xab[(4 * kg + e) * 16 + x] = ga[cb][e];   // xab[m][i] = A[i][m]
+    __builtin_amdgcn_wave_barrier();
+    {
+        const int jc = x;
+        float xv[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xv[i] = i == jc ? 1.f : 0.f;
+#pragma unroll
+        for (int m = 0; m < 15; ++m) {
+            float am[16];
+#pragma unroll
+            for (int qd = (m + 1) / 4; qd < 4; ++qd) {
+                const float4 t = *reinterpret_cast<const float4*>(xab + m * 16 + 4 * qd);
+                am[4 * qd] = t.x; am[4 * qd + 1] = t.y; am[4 * qd + 2] = t.z; am[4 * qd + 3] = t.w;
+            }
+#pragma unroll
+            for (int i = m + 1; i < 16; ++i) xv[i] -= am[i] * xv[m];
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xxb[i * 17 + jc] = xv[i];
+    }
+    __builtin_amdgcn_wave_barrier();
+    f32x4 xr, tt[NB];   // X_bb in row layout; T row block b (tiles j <= b), accumulator layout
+    {
+        f32x4 xn;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            xr[e] = xxb[x * 17 + 4 * kg + e];
+            xn[e] = xxb[(4 * kg + e) * 17 + x];
+        }
+        const float bc = bsh[16 * b + x];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) tt[j] = (j == b) ? xn * bc : zero4();
+    }
+    if (b < NB - 1) {
+#pragma unroll
+        for (int j = 0; j < NB - 1; ++j)
+            if (j == b) tpub[(j * (j + 1) / 2 + j) < NTP ? j * (j + 1) / 2 + j : 0][lane] = tt[j];
+    }
+    // ---- row wavefront: step t builds T_tj, j < t, on wave t ----
+#pragma unroll
+    for (int t = 1; t < NB; ++t) {
+        __syncthreads();
+        if (b == t) {
+#pragma unroll
+            for (int j = 0; j < t; ++j) {
+                f32x4 y = zero4();
+#pragma unroll
+                for (int m = j; m < t; ++m) {
+                    const f32x4 tm = tpub[m * (m + 1) / 2 + j][lane];
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) y = MF::mma(ga[m][s], tm[s], y);
+                }
+                f32x4 zt = zero4();
+#pragma unroll
+                for (int s = 0; s < 4; ++s) zt = MF::mma(xr[s], y[s], zt);
+                tt[j] = -zt;
+                if (t < NB - 1) tpub[t * (t + 1) / 2 + j][lane] = tt[j];
+            }
+        }
+    }
+
+    // ---- T: row block b through the staging tile to the workspace ----
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sb[(4 * kg + e) * SR + 16 * j + x] = (__bf16)tt[j][e];
+    __builtin_amdgcn_wave_barrier();
+    uint8_t* Tw = blk + L::T + (size_t)(16 * b) * C * sizeof(__bf16);
+#pragma unroll
+    for (int i = 0; i < (NPC + 63) / 64; ++i) {
+        const int p = lane + 64 * i;
+        if (p < NPC) {
+            const int rr = p / (C / 8), pc = p % (C / 8);
+            *reinterpret_cast<V16*>(Tw + (size_t)p * 16) = *reinterpret_cast<const V16*>(sb + rr * SR + 8 * pc);
+        }
+    }
+}
+
+template <int DK, int C>
+__global__ __launch_bounds__(64 * (C / 16), 4) void wy_prep_channel_bf16(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const float* __restrict__ log_alpha,
+    const float* __restrict__ beta, uint8_t* __restrict__ ws, int64_t T, int H, int NT) {
+    __shared__ ChanPrepSmem<DK, C> sm;
+    const int w = threadIdx.x >> 6;
+    constexpr int NB = C / 16;
+    if (w == 0) chan_prep_wave<DK, C, 0>(sm, q, k, log_alpha, beta, ws, T, H, NT);
+    if constexpr (NB > 1)
+        if (w == 1) chan_prep_wave<DK, C, (NB > 1 ? 1 : 0)>(sm, q, k, log_alpha, beta, ws, T, H, NT);
+    if constexpr (NB > 2) {
+        if (w == 2) chan_prep_wave<DK, C, (NB > 2 ? 2 : 0)>(sm, q, k, log_alpha, beta, ws, T, H, NT);
+        if (w == 3) chan_prep_wave<DK, C, (NB > 3 ? 3 : 0)>(sm, q, k, log_alpha, beta, ws, T, H, NT);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Kernel 2: sequential state pass.
 // ---------------------------------------------------------------------------
 
@@ -1016,7 +1426,11 @@ template <typename E, int DK, int C, bool CHANNEL>
 static hipError_t launch_chunk(const ChunkArgs& a) {
     const int NT = (int)((a.T + C - 1) / C);
     const int64_t BH = a.B * a.H;
-    if constexpr (CHANNEL) {
+    if constexpr (CHANNEL && sizeof(E) == 2) {
+        hipLaunchKernelGGL((wy_prep_channel_bf16<DK, C>), dim3((unsigned)(BH * NT)), dim3(64 * (C / 16)), 0,
+                           a.stream, (const __bf16*)a.q, (const __bf16*)a.k, a.log_alpha, a.beta,
+                           (uint8_t*)a.ws, a.T, (int)a.H, NT);
+    } else if constexpr (CHANNEL) {
         hipLaunchKernelGGL((wy_prep_channel<E, DK, C>), dim3((unsigned)(BH * NT)), dim3(kThreads), 0,
                            a.stream, (const E*)a.q, (const E*)a.k, a.log_alpha, a.beta,
                            (uint8_t*)a.ws, a.T, (int)a.H, NT);

@@ -163,6 +163,23 @@ def test_chunk_size_invariance_f32():
         assert rel_err(host(st), host(outs[0][1])) <= 1e-5
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_chunk_size_invariance_bf16(d):
+    """bf16, scalar gate: chunk 64 runs the single fused kernel, chunks 16 and 32
+    the two-kernel path with its fp32 solve; all three must agree (and match the
+    oracle) to the bf16 tolerance."""
+    inp = synth.chunk_inputs(2, 333, 3, d, d, "scalar", "bf16", seed=31 + d, s0_std=0.2)
+    outs = [gpu_chunk(inp, "bf16", chunk=c) for c in (16, 32, 64)]
+    o_ref, st_ref = oracle.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"],
+                                     inp["beta"], inp["S0"])
+    for o, st in outs:
+        assert rel_err(host(o), o_ref) <= TOL["bf16"]
+        assert rel_err(host(st), st_ref) <= TOL["bf16"]
+    for o, st in outs[:2]:
+        assert rel_err(host(outs[2][0]), host(o)) <= TOL["bf16"]
+        assert rel_err(host(outs[2][1]), host(st)) <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_split_resume(io):
     inp = synth.chunk_inputs(2, 333, 2, 64, 64, "scalar", io, seed=12, s0_std=0.2)
