@@ -7,6 +7,8 @@ call over the whole batch.  The same line also carries the decode step
 (gdr_decode_step, B=256, H=32, d=128, fp32 state) as achieved HBM GB/s.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+    python bench.py --workload 2     # the same line for another prefill workload
+                                     # (2: KDA B=2,H=32,T=8192; 3: GDN B=1,H=32,T=32768 with S0)
     python bench.py --traffic        # HBM bytes per call from rocprofv3 counters
 
 Prints ONE JSON line.  Only one GPU is used; --gpus above 1 exits.
@@ -41,12 +43,13 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 
 
-def prefill_algorithmic(B, T, H, d, C, io_bytes=2, s0=False):
-    """Bytes: q,k,v read and o written once (io dtype), log_alpha and beta (fp32)
-    read once, S_T written (and S0 read) once.  FLOPs: 6d^2 + 3Cd + C^2 per
-    head-token (the FG2-GDN page's per-head kernel accounting, section 3.6)."""
+def prefill_algorithmic(B, T, H, d, C, io_bytes=2, s0=False, channel=False):
+    """Bytes: q,k,v read and o written once (io dtype), log_alpha (fp32, one per
+    head-token, or d_k of them for the channel gate) and beta (fp32) read once,
+    S_T written (and S0 read) once.  FLOPs: 6d^2 + 3Cd + C^2 per head-token (the
+    FG2-GDN page's per-head kernel accounting, section 3.6)."""
     ht = B * T * H
-    per_ht = 4 * d * io_bytes + 4 + 4
+    per_ht = 4 * d * io_bytes + (4 * d if channel else 4) + 4
     state = B * H * d * d * 4
     nbytes = ht * per_ht + state * (2 if s0 else 1)
     flops = ht * (6 * d * d + 3 * C * d + C * C)
@@ -62,6 +65,11 @@ def decode_algorithmic(B, H, d, io_bytes=4):
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gdr_chunk_fwd_gdn_B4_H16_T4096_d128.traffic.txt")
 COPY_BYTES = 256 << 20
 PREFILL_KERNELS = ("fused_chunk", "wy_prep", "state_pass")
+ROOFLINE_KERNEL = {
+    1: "gdr_chunk_fwd (single kernel: fused_chunk<128, 2>)",
+    2: "gdr_chunk_fwd (wy_prep_channel_bf16<128, 64> + state_pass<bf16, 128, 64, 2, channel>)",
+    3: "gdr_chunk_fwd (single kernel: fused_chunk<128, 1>)",
+}
 
 
 def kernel_source_hash():
@@ -72,12 +80,12 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def cpu_baseline(inp, threads, min_seconds=10.0, max_reps=40):
+def cpu_baseline(inp, threads, min_seconds=10.0, max_reps=40, S0=None):
     """The oracle over the whole workload, repeated until ~min_seconds."""
     import oracle
     reps, t0 = 0, time.perf_counter()
     while reps < max_reps:
-        oracle.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], None,
+        oracle.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], S0,
                          threads=threads)
         reps += 1
         if time.perf_counter() - t0 >= min_seconds:
@@ -145,6 +153,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-steps", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=1, choices=(1, 2, 3),
+                    help="prefill workload to time (1 is the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", action="store_true",
                     help="measure HBM bytes per call with rocprofv3 and write a summary")
@@ -179,14 +189,16 @@ def main():
 
     import torch
     from linear_attention_sequence_03_amd import gdr_chunk_fwd, gdr_decode_step, synth
-    from linear_attention_sequence_03_amd.gdr import (GDR_BF16, GDR_GATE_SCALAR,
+    from linear_attention_sequence_03_amd.gdr import (GDR_BF16, GDR_GATE_CHANNEL, GDR_GATE_SCALAR,
                                                       gdr_chunk_fwd_workspace_size)
 
     assert torch.cuda.is_available(), "no GPU visible"
     devn = torch.device("cuda:0")
-    w = synth.WORKLOADS[1]
+    w = synth.WORKLOADS[args.workload]
     inp = synth.workload_inputs(w)
     B, T, H, d, C = w.B, w.T, w.H, w.d, w.chunk
+    channel = inp["log_alpha"].ndim == 4
+    S0 = torch.from_numpy(inp["S0"]).to(devn) if inp.get("S0") is not None else None
     bf = torch.bfloat16
     q = torch.from_numpy(inp["q"]).to(devn).to(bf)
     k = torch.from_numpy(inp["k"]).to(devn).to(bf)
@@ -195,11 +207,12 @@ def main():
     be = torch.from_numpy(inp["beta"]).to(devn)
     o = torch.empty((B, T, H, d), dtype=bf, device=devn)
     st = torch.empty((B, H, d, d), dtype=torch.float32, device=devn)
-    ws = torch.empty(gdr_chunk_fwd_workspace_size(B, T, H, d, d, C, GDR_BF16, GDR_GATE_SCALAR),
+    ws = torch.empty(gdr_chunk_fwd_workspace_size(B, T, H, d, d, C, GDR_BF16,
+                                                  GDR_GATE_CHANNEL if channel else GDR_GATE_SCALAR),
                      dtype=torch.uint8, device=devn)
 
     def step():
-        gdr_chunk_fwd(q, k, v, la, be, None, chunk=C, o=o, S_T=st, workspace=ws)
+        gdr_chunk_fwd(q, k, v, la, be, S0, chunk=C, o=o, S_T=st, workspace=ws)
 
     for _ in range(args.warmup):
         step()
@@ -235,10 +248,10 @@ def main():
     warm = [a.elapsed_time(b) for a, b in ev2]
     del flush
 
-    nbytes, flops = prefill_algorithmic(B, T, H, d, C)
+    nbytes, flops = prefill_algorithmic(B, T, H, d, C, s0=S0 is not None, channel=channel)
     launch_ms = float(np.mean(warm))
     traffic = None
-    if os.path.exists(TRAFFIC_FILE):
+    if args.workload == 1 and os.path.exists(TRAFFIC_FILE):
         kv = dict(l.strip().split("=", 1) for l in open(TRAFFIC_FILE)
                   if "=" in l and not l.startswith("#"))
         if kv.get("source_hash") == kernel_source_hash():
@@ -280,11 +293,12 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded; q,k unit-norm N(0,1), v N(0,1), beta sigmoid(N(0,1)), "
-                "log_alpha U(-0.1,-0.001))",
-        "config": {"workload": w.name, "call": "gdr_chunk_fwd", "gate": "scalar",
+                "log_alpha U(-0.1,-0.001)%s)" % (", S0 N(0,0.02^2)" if S0 is not None else ""),
+        "config": {"workload": w.name, "call": "gdr_chunk_fwd",
+                   "gate": "channel" if channel else "scalar",
                    "B": B, "T": T, "H": H, "d_k": d, "d_v": d, "chunk": C,
                    "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "gdr_chunk_fwd (single kernel: fused_chunk<128, 2>)",
+        "roofline": {"bound": "hbm", "kernel": ROOFLINE_KERNEL[args.workload],
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": nbytes,
@@ -300,12 +314,12 @@ def main():
     if not args.no_cpu_baseline:
         import oracle.gdr_oracle as og
         threads = min(16, og.default_threads())
-        reps, secs = cpu_baseline(inp, threads)
+        reps, secs = cpu_baseline(inp, threads, S0=inp.get("S0"))
         out["cpu_baseline"] = {"value": reps * B * T / secs, "unit": "tokens/s", "cores": threads,
                                "kind": "oracle",
-                               "sample": "the whole prefill workload (B=4,T=4096,H=16,d=128) "
+                               "sample": "the whole prefill workload (B=%d,T=%d,H=%d,d=%d) "
                                          "through the fp64 token-by-token oracle, %d times, "
-                                         "%.1f s" % (reps, secs)}
+                                         "%.1f s" % (B, T, H, d, reps, secs)}
     print(json.dumps(out))
 
 
