@@ -74,3 +74,30 @@ def run(q, k, v, alpha, beta, S0=None):
         outs.append([sum((S[i][c] * Fraction(q[t][c]) for c in range(dk)), Fraction(0))
                      for i in range(dv)])
     return outs, S
+
+
+def run_fg2(q, k, v, alpha, sk, sv, S0=None):
+    """Channel-wise write rates (FG2), whole sequence for ONE head, exactly.
+
+    ``sk`` (T lists of d_k) and ``sv`` (T lists of d_v) are the square roots of
+    the write rates beta^k and beta^v, given as rationals so that the scaled key
+    k~ = sk * k and value v~ = sv * v stay rational.  Per token the explicit
+    transition Diag(alpha_t) (I - k~ k~^T) multiplies the state and the write
+    v~ k~^T is added ("FG2-GDN" page, sections 3.2 and 3.6: the tied
+    diagonal-plus-rank-1 transition on the scaled keys).
+    """
+    T = len(q)
+    dk = len(k[0])
+    dv = len(v[0])
+    S = _zeros(dv, dk) if S0 is None else [[Fraction(x) for x in row] for row in S0]
+    outs = []
+    for t in range(T):
+        kt = [Fraction(sk[t][c]) * Fraction(k[t][c]) for c in range(dk)]
+        vt = [Fraction(sv[t][i]) * Fraction(v[t][i]) for i in range(dv)]
+        S = _matmul(S, transition([Fraction(a) for a in alpha[t]], Fraction(1), kt))
+        for i in range(dv):
+            for c in range(dk):
+                S[i][c] += vt[i] * kt[c]
+        outs.append([sum((S[i][c] * Fraction(q[t][c]) for c in range(dk)), Fraction(0))
+                     for i in range(dv)])
+    return outs, S

@@ -47,6 +47,23 @@
  * Threads split the independent (b,h) pairs; each pair is computed by exactly
  * one thread with the sequential loop above, so the result does not depend on
  * the thread count.
+ *
+ * Channel-wise write rate (FG2-GDN and FG2-GDN+, "FG2-GDN" page, sections 3.2,
+ * 3.4-3.6 and 6): the scalar beta_t becomes a vector beta^k_t in R^{d_k} that
+ * enters through the scaled key k~_t = sqrt(beta^k_t) (elementwise) * k_t, and
+ * the value is scaled the same way, v~_t = sqrt(beta^v_t) * v_t, with
+ * beta^v = beta^k for FG2-GDN (d_k = d_v) and a separate beta^v in R^{d_v} for
+ * FG2-GDN+.  The update keeps the tied, symmetric form with unit rate on the
+ * scaled vectors:
+ *
+ *   S_t = S_{t-1} Diag(alpha_t) (I - k~_t k~_t^T) + v~_t k~_t^T,   o_t = S_t q_t
+ *
+ * The page prints neither equation; this is the reading that keeps its stated
+ * properties: a tied diagonal-plus-rank-1 transition, elementwise square roots
+ * and scalings only, the same chunkwise algorithm with the scaled keys, and
+ * exactly KDA (Gated DeltaNet for a scalar decay) when beta^k = beta^v is the
+ * same number in every channel (k~ k~^T = beta k k^T, v~ k~^T = beta v k^T).
+ * Queries are not scaled.
  */
 #include <math.h>
 #include <pthread.h>
@@ -158,5 +175,115 @@ int gdr_oracle_decode_step(const double *q, const double *k, const double *v,
              channel_gate != 0, beta[u], o + u * dv, a, dk, dv);
     }
     free(a);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Channel-wise write rate (FG2): the delta rule with unit rate on the scaled  */
+/* key sqrt(beta^k) k and the scaled value sqrt(beta^v) v (see the header).    */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+    const double *q, *k, *v, *log_alpha, *beta_k, *beta_v, *S0;
+    double *o, *S_T;
+    int64_t B, T, H, dk, dv;
+    int channel_gate;
+    int64_t next_unit;
+    pthread_mutex_t mu;
+} job_fg2_t;
+
+/* The scaled key and value of one token. */
+static void scale_kv(const double *k, const double *v, const double *bk, const double *bv,
+                     double *ks, double *vs, int64_t dk, int64_t dv)
+{
+    for (int64_t c = 0; c < dk; ++c) ks[c] = sqrt(bk[c]) * k[c];
+    for (int64_t i = 0; i < dv; ++i) vs[i] = sqrt(bv[i]) * v[i];
+}
+
+static void *worker_fg2(void *arg)
+{
+    job_fg2_t *J = (job_fg2_t *)arg;
+    const int64_t dk = J->dk, dv = J->dv, T = J->T, H = J->H;
+    double *S = (double *)malloc(sizeof(double) * dv * dk);
+    double *a = (double *)malloc(sizeof(double) * dk);
+    double *ks = (double *)malloc(sizeof(double) * dk);
+    double *vs = (double *)malloc(sizeof(double) * dv);
+    for (;;) {
+        pthread_mutex_lock(&J->mu);
+        int64_t u = J->next_unit++;
+        pthread_mutex_unlock(&J->mu);
+        if (u >= J->B * J->H) break;
+        const int64_t b = u / H, h = u % H;
+        if (J->S0)
+            memcpy(S, J->S0 + u * dv * dk, sizeof(double) * dv * dk);
+        else
+            memset(S, 0, sizeof(double) * dv * dk);
+        for (int64_t t = 0; t < T; ++t) {
+            const int64_t bth = (b * T + t) * H + h;
+            const double *la = J->log_alpha + (J->channel_gate ? bth * dk : bth);
+            const double *bk = J->beta_k + bth * dk;
+            const double *bv = J->beta_v ? J->beta_v + bth * dv : bk;
+            scale_kv(J->k + bth * dk, J->v + bth * dv, bk, bv, ks, vs, dk, dv);
+            step(S, J->q + bth * dk, ks, vs, la, J->channel_gate, 1.0, J->o + bth * dv, a, dk, dv);
+        }
+        if (J->S_T) memcpy(J->S_T + u * dv * dk, S, sizeof(double) * dv * dk);
+    }
+    free(S);
+    free(a);
+    free(ks);
+    free(vs);
+    return NULL;
+}
+
+/* Full sequence with channel-wise write rates.  beta_k: [B,T,H,dk];
+ * beta_v: [B,T,H,dv] or NULL (then beta^v = beta^k, which needs dk == dv).
+ * Returns 0 on success, -1 on bad arguments. */
+int gdr_oracle_fg2_chunk_fwd(const double *q, const double *k, const double *v,
+                             const double *log_alpha, const double *beta_k, const double *beta_v,
+                             const double *S0, double *o, double *S_T,
+                             int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                             int channel_gate, int nthreads)
+{
+    if (!q || !k || !v || !log_alpha || !beta_k || !o) return -1;
+    if (B < 1 || T < 0 || H < 1 || dk < 1 || dv < 1) return -1;
+    if (!beta_v && dk != dv) return -1;
+    job_fg2_t J = {q, k, v, log_alpha, beta_k, beta_v, S0, o, S_T, B, T, H, dk, dv,
+                   channel_gate != 0, 0};
+    pthread_mutex_init(&J.mu, NULL);
+    int64_t units = B * H;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > units) nthreads = (int)units;
+    pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    for (int i = 0; i < nthreads; ++i) pthread_create(&th[i], NULL, worker_fg2, &J);
+    for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+    free(th);
+    pthread_mutex_destroy(&J.mu);
+    return 0;
+}
+
+/* One decode step with channel-wise write rates; S_out may equal S_in. */
+int gdr_oracle_fg2_decode_step(const double *q, const double *k, const double *v,
+                               const double *log_alpha, const double *beta_k,
+                               const double *beta_v, const double *S_in, double *S_out,
+                               double *o, int64_t B, int64_t H, int64_t dk, int64_t dv,
+                               int channel_gate)
+{
+    if (!q || !k || !v || !log_alpha || !beta_k || !S_in || !S_out || !o) return -1;
+    if (B < 1 || H < 1 || dk < 1 || dv < 1) return -1;
+    if (!beta_v && dk != dv) return -1;
+    double *a = (double *)malloc(sizeof(double) * dk);
+    double *ks = (double *)malloc(sizeof(double) * dk);
+    double *vs = (double *)malloc(sizeof(double) * dv);
+    for (int64_t u = 0; u < B * H; ++u) {
+        if (S_out != S_in)
+            memcpy(S_out + u * dv * dk, S_in + u * dv * dk, sizeof(double) * dv * dk);
+        const double *la = log_alpha + (channel_gate ? u * dk : u);
+        const double *bk = beta_k + u * dk;
+        scale_kv(k + u * dk, v + u * dv, bk, beta_v ? beta_v + u * dv : bk, ks, vs, dk, dv);
+        step(S_out + u * dv * dk, q + u * dk, ks, vs, la, channel_gate != 0, 1.0, o + u * dv, a,
+             dk, dv);
+    }
+    free(a);
+    free(ks);
+    free(vs);
     return 0;
 }

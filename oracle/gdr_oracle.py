@@ -59,6 +59,13 @@ def load(path=None):
     lib.gdr_oracle_decode_step.argtypes = [d, d, d, d, d, d, d, d,
                                            i64, i64, i64, i64, ctypes.c_int]
     lib.gdr_oracle_decode_step.restype = ctypes.c_int
+    lib.gdr_oracle_fg2_chunk_fwd.argtypes = [d, d, d, d, d, d, d, d, d,
+                                             i64, i64, i64, i64, i64,
+                                             ctypes.c_int, ctypes.c_int]
+    lib.gdr_oracle_fg2_chunk_fwd.restype = ctypes.c_int
+    lib.gdr_oracle_fg2_decode_step.argtypes = [d, d, d, d, d, d, d, d, d,
+                                               i64, i64, i64, i64, ctypes.c_int]
+    lib.gdr_oracle_fg2_decode_step.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -124,6 +131,55 @@ def decode_step(q, k, v, log_alpha, beta, S, lib=None):
     rc = (lib or load()).gdr_oracle_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(la), _ptr(be),
                                         _ptr(s_out), _ptr(s_out), _ptr(o),
                                         B, H, dk, dv, int(channel))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return o, s_out
+
+
+def fg2_chunk_fwd(q, k, v, log_alpha, beta_k, beta_v=None, S0=None, threads=None, lib=None):
+    """Whole-sequence forward with channel-wise write rates (FG2-GDN / FG2-GDN+).
+
+    q, k: [B,T,H,dk]; v: [B,T,H,dv]; log_alpha: [B,T,H] or [B,T,H,dk];
+    beta_k: [B,T,H,dk]; beta_v: [B,T,H,dv] or None (= beta_k, needs dk == dv);
+    S0: [B,H,dv,dk] or None.  Returns (o, S_T) as fp64 arrays.
+    """
+    q, k, v, la, bk = (_f64(a) for a in (q, k, v, log_alpha, beta_k))
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    channel = la.ndim == 4
+    if k.shape != q.shape or v.shape[:3] != (B, T, H) or bk.shape != (B, T, H, dk):
+        raise ValueError("shape mismatch")
+    if la.shape != ((B, T, H, dk) if channel else (B, T, H)):
+        raise ValueError("log_alpha shape mismatch")
+    bv = None if beta_v is None else _f64(beta_v)
+    if bv is not None and bv.shape != (B, T, H, dv):
+        raise ValueError("beta_v shape mismatch")
+    s0 = None if S0 is None else _f64(S0)
+    o = np.zeros((B, T, H, dv), np.float64)
+    st = np.zeros((B, H, dv, dk), np.float64)
+    n = default_threads() if threads is None else int(threads)
+    rc = (lib or load()).gdr_oracle_fg2_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(la), _ptr(bk),
+                                                  _ptr(bv), _ptr(s0), _ptr(o), _ptr(st),
+                                                  B, T, H, dk, dv, int(channel), n)
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return o, st
+
+
+def fg2_decode_step(q, k, v, log_alpha, beta_k, beta_v, S, lib=None):
+    """One recurrent step with channel-wise write rates.  q,k: [B,H,dk]; v: [B,H,dv];
+    log_alpha: [B,H] or [B,H,dk]; beta_k: [B,H,dk]; beta_v: [B,H,dv] or None;
+    S: [B,H,dv,dk].  Returns (o [B,H,dv], S')."""
+    q, k, v, la, bk, s = (_f64(a) for a in (q, k, v, log_alpha, beta_k, S))
+    B, H, dk = q.shape
+    dv = v.shape[2]
+    channel = la.ndim == 3
+    bv = None if beta_v is None else _f64(beta_v)
+    o = np.zeros((B, H, dv), np.float64)
+    s_out = s.copy()
+    rc = (lib or load()).gdr_oracle_fg2_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(la), _ptr(bk),
+                                                    _ptr(bv), _ptr(s_out), _ptr(s_out), _ptr(o),
+                                                    B, H, dk, dv, int(channel))
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
     return o, s_out
