@@ -114,6 +114,46 @@ gdr_status gdr_decode_step(const void *q, const void *k, const void *v,
                            int64_t B, int64_t H, int64_t dk, int64_t dv,
                            gdr_dtype io, gdr_gate gate, hipStream_t stream);
 
+/*
+ * Channel-wise write rates: FG2-GDN and FG2-GDN+ ("FG2-GDN" page, sections 3.2,
+ * 3.4-3.6).  The scalar beta_t becomes a vector beta^k_t in R^{d_k} that enters
+ * through the scaled key k~ = sqrt(beta^k) * k (elementwise); the value is
+ * scaled the same way, v~ = sqrt(beta^v) * v, with beta^v = beta^k for FG2-GDN
+ * and a separate d_v-vector for FG2-GDN+.  The update is the tied delta rule
+ * with unit rate on the scaled vectors,
+ *
+ *   S_t = S_{t-1} Diag(alpha_t) (I - k~_t k~_t^T) + v~_t k~_t^T,   o_t = S_t q_t,
+ *
+ * which is KDA (Gated DeltaNet with a scalar decay) when every channel has the
+ * same rate.  The page prints neither equation; this is the reading that keeps
+ * its stated properties (tied diagonal-plus-rank-1 transition, elementwise
+ * square roots and scalings, the chunkwise algorithm unchanged).
+ *
+ *   beta_k     [B, T, H, dk]   fp32 key-side rates     ([B, H, dk] for decode)
+ *   beta_v     [B, T, H, dv]   fp32 value-side rates, or NULL for beta_k
+ *                              ([B, H, dv] for decode)
+ * Everything else is as in gdr_chunk_fwd / gdr_decode_step (log_alpha may be
+ * scalar or channel-wise, selected by `gate`).  The prefill workspace also
+ * holds the scaled k and v of the whole call, so it is larger than
+ * gdr_chunk_fwd's; its size comes from gdr_fg2_chunk_fwd_workspace_size.
+ */
+gdr_status gdr_fg2_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H,
+                                            int64_t dk, int64_t dv, int64_t chunk,
+                                            gdr_dtype io, gdr_gate gate, size_t *bytes);
+
+gdr_status gdr_fg2_chunk_fwd(const void *q, const void *k, const void *v,
+                             const float *log_alpha, const float *beta_k, const float *beta_v,
+                             const float *S0, void *o, float *S_T,
+                             int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                             int64_t chunk, gdr_dtype io, gdr_gate gate,
+                             void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+gdr_status gdr_fg2_decode_step(const void *q, const void *k, const void *v,
+                               const float *log_alpha, const float *beta_k, const float *beta_v,
+                               const float *S_in, float *S_out, void *o,
+                               int64_t B, int64_t H, int64_t dk, int64_t dv,
+                               gdr_dtype io, gdr_gate gate, hipStream_t stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char *gdr_status_string(gdr_status s);
 

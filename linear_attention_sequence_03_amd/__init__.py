@@ -1,4 +1,5 @@
-"""Gated delta rule forward pass (Gated DeltaNet / KDA) for MI355X (gfx950).
+"""Gated delta rule forward pass (Gated DeltaNet / KDA / channel-wise write
+rates as in FG2-GDN) for MI355X (gfx950).
 
 The compute path is a C-ABI shared library (``libgdr.so``, declared in
 ``include/gdr.h``) of hand-written HIP kernels; :mod:`.gdr` is a thin ctypes
@@ -10,6 +11,9 @@ from .gdr import (  # noqa: F401
     gdr_chunk_fwd,
     gdr_chunk_fwd_workspace_size,
     gdr_decode_step,
+    gdr_fg2_chunk_fwd,
+    gdr_fg2_chunk_fwd_workspace_size,
+    gdr_fg2_decode_step,
     gdr_status_string,
     load_library,
 )

@@ -179,4 +179,84 @@ gdr_status gdr_decode_step(const void* q, const void* k, const void* v, const fl
     return GDR_OK;
 }
 
+gdr_status gdr_fg2_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t dk,
+                                            int64_t dv, int64_t chunk, gdr_dtype io, gdr_gate gate,
+                                            size_t* bytes) {
+    gdr_status s = gdr_chunk_fwd_workspace_size(B, T, H, dk, dv, chunk, io, gate, bytes);
+    if (s != GDR_OK) return s;
+    if (mul({B, T, H, dk + dv}) < 0) return fail(GDR_ERR_UNSUPPORTED, "tensor sizes overflow");
+    *bytes = gdr::fg2_workspace_bytes(B, T, H, dk, dv, chunk, io == GDR_BF16, gate == GDR_GATE_CHANNEL);
+    return GDR_OK;
+}
+
+gdr_status gdr_fg2_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
+                             const float* beta_k, const float* beta_v, const float* S0, void* o,
+                             float* S_T, int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                             int64_t chunk, gdr_dtype io, gdr_gate gate, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+    size_t need = 0;
+    gdr_status s = gdr_fg2_chunk_fwd_workspace_size(B, T, H, dk, dv, chunk, io, gate, &need);
+    if (s != GDR_OK) return s;
+    const int64_t ntok = mul({B, T, H});
+    if (ntok < 0 || mul({ntok, dk}) < 0 || mul({B, H, dv, dk}) < 0)
+        return fail(GDR_ERR_UNSUPPORTED, "tensor sizes overflow");
+    if (mul({B, H, dv / 16}) > INT32_MAX) return fail(GDR_ERR_UNSUPPORTED, "B*H too large");
+    if (T > 0 && (!q || !k || !v || !log_alpha || !beta_k || !o))
+        return fail(GDR_ERR_INVALID_ARG, "q, k, v, log_alpha, beta_k and o must be non-NULL");
+    if (need > 0 && !workspace) return fail(GDR_ERR_INVALID_ARG, "workspace is NULL");
+    if (workspace_bytes < need)
+        return fail(GDR_ERR_INVALID_ARG, "workspace too small (%zu < %zu bytes)", workspace_bytes, need);
+    const size_t es = io == GDR_BF16 ? 2 : 4;
+    const int64_t la_elems = gate == GDR_GATE_CHANNEL ? ntok * dk : ntok;
+    const Range rs[] = {
+        rng("q", q, ntok * dk, es),          rng("k", k, ntok * dk, es),
+        rng("v", v, ntok * dv, es),          rng("log_alpha", log_alpha, la_elems, 4),
+        rng("beta_k", beta_k, ntok * dk, 4), rng("beta_v", beta_v, ntok * dv, 4),
+        rng("S0", S0, B * H * dv * dk, 4),   rng("o", o, ntok * dv, es),
+        rng("S_T", S_T, B * H * dv * dk, 4), rng("workspace", workspace, (int64_t)need, 1),
+    };
+    s = check_ptrs(rs, 10, 7);
+    if (s != GDR_OK) return s;
+    gdr::ChunkArgs a{q, k, v, log_alpha, nullptr, S0, o, S_T, B, T, H, dk, dv, chunk,
+                     io == GDR_BF16, gate == GDR_GATE_CHANNEL, workspace, stream};
+    const hipError_t err = gdr::fg2_chunk_fwd_launch(a, beta_k, beta_v);
+    if (err != hipSuccess) return fail(GDR_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(err));
+    return GDR_OK;
+}
+
+gdr_status gdr_fg2_decode_step(const void* q, const void* k, const void* v, const float* log_alpha,
+                               const float* beta_k, const float* beta_v, const float* S_in,
+                               float* S_out, void* o, int64_t B, int64_t H, int64_t dk, int64_t dv,
+                               gdr_dtype io, gdr_gate gate, hipStream_t stream) {
+    g_last_error[0] = 0;
+    gdr_status s = check_common(B, H, dk, dv, io, gate);
+    if (s != GDR_OK) return s;
+    const int64_t nst = mul({B, H, dv, dk});
+    if (nst < 0 || mul({B, H, dv}) > ((int64_t)INT32_MAX) * 4)
+        return fail(GDR_ERR_UNSUPPORTED, "state too large");
+    if (!q || !k || !v || !log_alpha || !beta_k || !S_in || !S_out || !o)
+        return fail(GDR_ERR_INVALID_ARG, "all pointers except beta_v must be non-NULL");
+    const size_t es = io == GDR_BF16 ? 2 : 4;
+    const int64_t bh = B * H;
+    const Range in_state = rng("S_in", S_in, nst, 4);
+    const Range out_state = rng("S_out", S_out, nst, 4);
+    if (S_in != S_out && overlap(in_state, out_state))
+        return fail(GDR_ERR_INVALID_ARG, "S_out partially overlaps S_in");
+    const Range rs[] = {
+        rng("q", q, bh * dk, es), rng("k", k, bh * dk, es), rng("v", v, bh * dv, es),
+        rng("log_alpha", log_alpha, gate == GDR_GATE_CHANNEL ? bh * dk : bh, 4),
+        rng("beta_k", beta_k, bh * dk, 4), rng("beta_v", beta_v, bh * dv, 4),
+        S_in == S_out ? Range{"S_in", 0, 0} : in_state,
+        out_state, rng("o", o, bh * dv, es),
+    };
+    if (!aligned16(S_in)) return fail(GDR_ERR_INVALID_ARG, "S_in is not 16-byte aligned");
+    s = check_ptrs(rs, 9, 7);
+    if (s != GDR_OK) return s;
+    gdr::DecodeArgs a{q, k, v, log_alpha, nullptr, S_in, S_out, o, B, H, dk, dv,
+                      io == GDR_BF16, gate == GDR_GATE_CHANNEL, stream, beta_k, beta_v};
+    const hipError_t err = gdr::decode_step_launch(a);
+    if (err != hipSuccess) return fail(GDR_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(err));
+    return GDR_OK;
+}
+
 }  // extern "C"

@@ -16,15 +16,20 @@
 // is far larger than the caches and is not re-read).  The two dot products are
 // reduced across the lanes of a row with xor shuffles.  In-place (S_out ==
 // S_in) is safe: each 16-byte slice is read and written by the same lane.
+//
+// With channel-wise write rates (FG2, "FG2-GDN" page, sections 3.2 and 3.4)
+// the same step runs with unit rate on the scaled key sqrt(beta^k) * k and the
+// scaled value sqrt(beta^v) * v (beta^v = beta^k unless given).
 #include "gdr_device.hpp"
 #include "gdr_launch.hpp"
 
 namespace gdr {
 
-template <typename E, bool CHANNEL, int DK>
+template <typename E, bool CHANNEL, int DK, bool FG2>
 __global__ __launch_bounds__(256) void decode_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta,
+    const float* __restrict__ beta_k, const float* __restrict__ beta_v,
     const float* S_in, float* S_out, E* __restrict__ o, int64_t BH, int DV) {
     constexpr int LPR = DK / 4;      // lanes per state row
     constexpr int RPP = kWave / LPR; // rows per pass of one wave
@@ -38,7 +43,11 @@ __global__ __launch_bounds__(256) void decode_kernel(
     const int row0 = (int)(gw % wpb) * RPW + lane / LPR;
     const int c0 = 4 * (lane % LPR);
 
-    const float4 kk = load4(k + bh * DK + c0);
+    float4 kk = load4(k + bh * DK + c0);
+    if constexpr (FG2) {
+        const float4 r = *reinterpret_cast<const float4*>(beta_k + bh * DK + c0);
+        kk = make_float4(sqrtf(r.x) * kk.x, sqrtf(r.y) * kk.y, sqrtf(r.z) * kk.z, sqrtf(r.w) * kk.w);
+    }
     const float4 qq = load4(q + bh * DK + c0);
     float4 aa;
     if constexpr (CHANNEL) {
@@ -48,7 +57,8 @@ __global__ __launch_bounds__(256) void decode_kernel(
         const float a = expf(log_alpha[bh]);
         aa = make_float4(a, a, a, a);
     }
-    const float b = beta[bh];
+    const float b = FG2 ? 1.f : beta[bh];
+    const float* vrate = FG2 ? (beta_v ? beta_v : beta_k) : nullptr;
 
     const int64_t base = bh * (int64_t)DV * DK;
     f32x4 s[NPASS];
@@ -66,7 +76,9 @@ __global__ __launch_bounds__(256) void decode_kernel(
         float pd = sd[0] * kk.x + sd[1] * kk.y + sd[2] * kk.z + sd[3] * kk.w;
 #pragma unroll
         for (int m = LPR / 2; m >= 1; m >>= 1) pd += __shfl_xor(pd, m);
-        const float u = b * (to_f32(v[bh * DV + row]) - pd);
+        float vi = to_f32(v[bh * DV + row]);
+        if constexpr (FG2) vi *= sqrtf(vrate[bh * DV + row]);
+        const float u = b * (vi - pd);
         f32x4 sn;
         sn[0] = sd[0] + u * kk.x; sn[1] = sd[1] + u * kk.y;
         sn[2] = sd[2] + u * kk.z; sn[3] = sd[3] + u * kk.w;
@@ -84,9 +96,16 @@ static hipError_t launch_decode(const DecodeArgs& a) {
     constexpr int RPW = (kWave / (DK / 4)) * 4;
     const int64_t waves = a.B * a.H * (a.dv / RPW);
     const int64_t blocks = (waves + 3) / 4;
-    hipLaunchKernelGGL((decode_kernel<E, CHANNEL, DK>), dim3((unsigned)blocks), dim3(256), 0,
-                       a.stream, (const E*)a.q, (const E*)a.k, (const E*)a.v, a.log_alpha,
-                       a.beta, a.S_in, a.S_out, (E*)a.o, a.B * a.H, (int)a.dv);
+    if (a.beta_k)
+        hipLaunchKernelGGL((decode_kernel<E, CHANNEL, DK, true>), dim3((unsigned)blocks), dim3(256), 0,
+                           a.stream, (const E*)a.q, (const E*)a.k, (const E*)a.v, a.log_alpha,
+                           a.beta, a.beta_k, a.beta_v, a.S_in, a.S_out, (E*)a.o, a.B * a.H,
+                           (int)a.dv);
+    else
+        hipLaunchKernelGGL((decode_kernel<E, CHANNEL, DK, false>), dim3((unsigned)blocks), dim3(256),
+                           0, a.stream, (const E*)a.q, (const E*)a.k, (const E*)a.v, a.log_alpha,
+                           a.beta, a.beta_k, a.beta_v, a.S_in, a.S_out, (E*)a.o, a.B * a.H,
+                           (int)a.dv);
     return hipGetLastError();
 }
 

@@ -15,6 +15,9 @@ struct DecodeArgs {
     int64_t B, H, dk, dv;
     bool bf16, channel;
     hipStream_t stream;
+    // Channel-wise write rates (beta unused then): beta_k [B,H,dk], beta_v
+    // [B,H,dv] or NULL for beta_k.  NULL beta_k selects the scalar rate.
+    const float *beta_k = nullptr, *beta_v = nullptr;
 };
 
 struct ChunkArgs {
@@ -39,5 +42,11 @@ hipError_t chunk_fwd_launch(const ChunkArgs& a);
 // Single-kernel path (bf16, scalar gate, 64-token chunks): needs no workspace.
 bool fused_chunk_supported(int64_t dk, int64_t chunk, bool bf16, bool channel);
 hipError_t fused_chunk_launch(const ChunkArgs& a);
+
+// Channel-wise write rates: a prologue scales k and v into the workspace, then
+// the chunk path above runs with unit rate.
+size_t fg2_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, int64_t chunk,
+                           bool bf16, bool channel);
+hipError_t fg2_chunk_fwd_launch(const ChunkArgs& a, const float* beta_k, const float* beta_v);
 
 }  // namespace gdr

@@ -21,6 +21,7 @@ GDR_GATE_SCALAR, GDR_GATE_CHANNEL = 0, 1
 
 # Every symbol include/gdr.h declares.
 EXPORTS = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_decode_step",
+           "gdr_fg2_chunk_fwd_workspace_size", "gdr_fg2_chunk_fwd", "gdr_fg2_decode_step",
            "gdr_status_string", "gdr_last_error")
 
 _lib = None
@@ -57,6 +58,16 @@ def load_library(path: Optional[str] = None):
     lib.gdr_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp,
                                     i64, i64, i64, i64, f, f, vp]
     lib.gdr_decode_step.restype = f
+    lib.gdr_fg2_chunk_fwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64, f, f,
+                                                     ctypes.POINTER(ctypes.c_size_t)]
+    lib.gdr_fg2_chunk_fwd_workspace_size.restype = f
+    lib.gdr_fg2_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                      i64, i64, i64, i64, i64, i64, f, f,
+                                      vp, ctypes.c_size_t, vp]
+    lib.gdr_fg2_chunk_fwd.restype = f
+    lib.gdr_fg2_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                        i64, i64, i64, i64, f, f, vp]
+    lib.gdr_fg2_decode_step.restype = f
     if path is None:
         _lib = lib
     return lib
@@ -179,6 +190,90 @@ def gdr_decode_step(q, k, v, log_alpha, beta, S, S_out=None, o=None, inplace: bo
     st = load_library().gdr_decode_step(
         _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S), _ptr(S_out), _ptr(o),
         B, H, dk, dv, io, gate, _stream(dev, stream))
+    if st != GDR_OK:
+        _raise(st)
+    return o, S_out
+
+
+def gdr_fg2_chunk_fwd_workspace_size(B, T, H, dk, dv, chunk, io, gate) -> int:
+    out = ctypes.c_size_t(0)
+    st = load_library().gdr_fg2_chunk_fwd_workspace_size(B, T, H, dk, dv, chunk, io, gate,
+                                                         ctypes.byref(out))
+    if st != GDR_OK:
+        _raise(st)
+    return int(out.value)
+
+
+def gdr_fg2_chunk_fwd(q, k, v, log_alpha, beta_k, beta_v=None, S0=None, chunk: int = 64, o=None,
+                      S_T=None, workspace=None, want_state: bool = True, stream=None) -> Tuple:
+    """Whole-sequence forward with channel-wise write rates (FG2-GDN; FG2-GDN+
+    when ``beta_v`` is given).  beta_k: [B,T,H,dk] fp32; beta_v: [B,T,H,dv] fp32 or
+    None (= beta_k).  Other arguments as in :func:`gdr_chunk_fwd`."""
+    import torch
+    dev = q.device
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    io = _io_code(q.dtype)
+    gate = GDR_GATE_CHANNEL if log_alpha.dim() == 4 else GDR_GATE_SCALAR
+    _need("q", q, q.dtype, (B, T, H, dk), dev)
+    _need("k", k, q.dtype, (B, T, H, dk), dev)
+    _need("v", v, q.dtype, (B, T, H, dv), dev)
+    _need("log_alpha", log_alpha, torch.float32,
+          (B, T, H, dk) if gate == GDR_GATE_CHANNEL else (B, T, H), dev)
+    _need("beta_k", beta_k, torch.float32, (B, T, H, dk), dev)
+    if beta_v is not None:
+        _need("beta_v", beta_v, torch.float32, (B, T, H, dv), dev)
+    if S0 is not None:
+        _need("S0", S0, torch.float32, (B, H, dv, dk), dev)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
+    _need("o", o, q.dtype, (B, T, H, dv), dev)
+    if S_T is None and want_state:
+        S_T = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+    if S_T is not None:
+        _need("S_T", S_T, torch.float32, (B, H, dv, dk), dev)
+    nbytes = gdr_fg2_chunk_fwd_workspace_size(B, T, H, dk, dv, chunk, io, gate)
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load_library().gdr_fg2_chunk_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta_k), _ptr(beta_v), _ptr(S0), _ptr(o),
+        _ptr(S_T), B, T, H, dk, dv, chunk, io, gate, _ptr(workspace), wbytes, _stream(dev, stream))
+    if st != GDR_OK:
+        _raise(st)
+    return o, S_T
+
+
+def gdr_fg2_decode_step(q, k, v, log_alpha, beta_k, beta_v, S, S_out=None, o=None,
+                        inplace: bool = False, stream=None) -> Tuple:
+    """One decode step with channel-wise write rates.  beta_k: [B,H,dk]; beta_v:
+    [B,H,dv] or None (= beta_k).  Other arguments as in :func:`gdr_decode_step`."""
+    import torch
+    dev = q.device
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    io = _io_code(q.dtype)
+    gate = GDR_GATE_CHANNEL if log_alpha.dim() == 3 else GDR_GATE_SCALAR
+    _need("q", q, q.dtype, (B, H, dk), dev)
+    _need("k", k, q.dtype, (B, H, dk), dev)
+    _need("v", v, q.dtype, (B, H, dv), dev)
+    _need("log_alpha", log_alpha, torch.float32,
+          (B, H, dk) if gate == GDR_GATE_CHANNEL else (B, H), dev)
+    _need("beta_k", beta_k, torch.float32, (B, H, dk), dev)
+    if beta_v is not None:
+        _need("beta_v", beta_v, torch.float32, (B, H, dv), dev)
+    _need("S", S, torch.float32, (B, H, dv, dk), dev)
+    if inplace:
+        S_out = S
+    elif S_out is None:
+        S_out = torch.empty_like(S)
+    _need("S_out", S_out, torch.float32, (B, H, dv, dk), dev)
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=q.dtype, device=dev)
+    _need("o", o, q.dtype, (B, H, dv), dev)
+    st = load_library().gdr_fg2_decode_step(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta_k), _ptr(beta_v), _ptr(S),
+        _ptr(S_out), _ptr(o), B, H, dk, dv, io, gate, _stream(dev, stream))
     if st != GDR_OK:
         _raise(st)
     return o, S_out

@@ -114,3 +114,16 @@ def workload_inputs(w: Workload):
     if w.call == "chunk":
         return chunk_inputs(w.B, w.T, w.H, w.d, w.d, w.gate, w.io, w.seed, w.s0_std)
     return decode_inputs(w.B, w.H, w.d, w.d, w.gate, w.io, w.seed, w.s0_std)
+
+
+def write_rates(shape_k, dv=None, seed=0):
+    """Channel-wise write rates for the FG2 calls: beta^k = sigmoid(N(0,1)) of
+    shape ``shape_k`` (leading dims + [dk]) and, when ``dv`` is given, a separate
+    beta^v = sigmoid(N(0,1)) with last dim dv.  Drawn from their own seeded
+    stream, so the other inputs of a workload do not change."""
+    rng = np.random.Generator(np.random.PCG64(seed + 5000))
+    bk = (1.0 / (1.0 + np.exp(-rng.standard_normal(shape_k)))).astype(np.float32)
+    bv = None
+    if dv is not None:
+        bv = (1.0 / (1.0 + np.exp(-rng.standard_normal(tuple(shape_k[:-1]) + (dv,))))).astype(np.float32)
+    return bk, bv

@@ -123,3 +123,53 @@ def test_binding_type_checks_before_calling():
         gdr.gdr_chunk_fwd(q.double(), q, q, torch.zeros(1, 4, 1), torch.zeros(1, 4, 1))
     with pytest.raises(ValueError):
         gdr.gdr_chunk_fwd(q, q, q, torch.zeros(1, 4, 2), torch.zeros(1, 4, 1))
+
+
+# ----- channel-wise write rates (FG2) ----------------------------------------
+def _fg2_chunk(lib, q=0, k=1, v=2, la=3, bk=4, bv=None, s0=None, o=6, st=7, ws=8, B=1, T=128, H=2,
+               dk=64, dv=64, chunk=64, io=0, gate=1, wsbytes=1 << 23):
+    p = lambda i: None if i is None else (_addr(i) if isinstance(i, int) else i)  # noqa: E731
+    return lib.gdr_fg2_chunk_fwd(p(q), p(k), p(v), p(la), p(bk), p(bv), p(s0), p(o), p(st),
+                                 B, T, H, dk, dv, chunk, io, gate, p(ws), wsbytes, None)
+
+
+def _fg2_decode(lib, q=0, k=1, v=2, la=3, bk=4, bv=None, si=5, so=6, o=7, B=2, H=2, dk=64, dv=64,
+                io=0, gate=1):
+    p = lambda i: None if i is None else (_addr(i) if isinstance(i, int) else i)  # noqa: E731
+    return lib.gdr_fg2_decode_step(p(q), p(k), p(v), p(la), p(bk), p(bv), p(si), p(so), p(o),
+                                   B, H, dk, dv, io, gate, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(bk=None), 1), (dict(q=None), 1), (dict(ws=None), 1), (dict(wsbytes=1024), 1),
+    (dict(dk=64, dv=128), 2), (dict(chunk=8), 2), (dict(gate=3), 1),
+    (dict(bk=ctypes.c_void_p(BASE + 4 * MB + 4)), 1),     # misaligned
+    (dict(o=ctypes.c_void_p(BASE + 4 * MB + 4096)), 1),   # o inside beta_k
+    (dict(bv=ctypes.c_void_p(BASE + 6 * MB)), 1),         # beta_v is o
+])
+def test_fg2_chunk_fwd_rejects(lib, kw, code):
+    assert _fg2_chunk(lib, **kw) == code
+    assert lib.gdr_last_error()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(bk=None), 1), (dict(so=None), 1), (dict(dk=128, dv=64), 2),
+    (dict(o=ctypes.c_void_p(BASE + 4 * MB)), 1),          # o is beta_k
+    (dict(bv=ctypes.c_void_p(BASE + 9 * MB + 8)), 1),     # misaligned beta_v
+])
+def test_fg2_decode_step_rejects(lib, kw, code):
+    assert _fg2_decode(lib, **kw) == code
+
+
+def test_fg2_workspace_size():
+    """The FG2 workspace is the chunk path's plus the scaled k and v of the
+    whole call and one unit rate per token, each 256-byte aligned."""
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    for io, es in ((gdr.GDR_F32, 4), (gdr.GDR_BF16, 2)):
+        for gate in (gdr.GDR_GATE_SCALAR, gdr.GDR_GATE_CHANNEL):
+            B, T, H, d, C = 2, 100, 3, 64, 32
+            inner = gdr.gdr_chunk_fwd_workspace_size(B, T, H, d, d, C, io, gate)
+            ntok = B * T * H
+            want = al(inner) + 2 * al(ntok * d * es) + al(ntok * 4)
+            assert gdr.gdr_fg2_chunk_fwd_workspace_size(B, T, H, d, d, C, io, gate) == want
+    assert gdr.gdr_fg2_chunk_fwd_workspace_size(1, 0, 1, 64, 64, 16, 0, 1) == 0
