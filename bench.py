@@ -9,6 +9,8 @@ call over the whole batch.  The same line also carries the decode step
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
     python bench.py --workload 2     # the same line for another prefill workload
                                      # (2: KDA B=2,H=32,T=8192; 3: GDN B=1,H=32,T=32768 with S0)
+    python bench.py --workload 2 --fg2   # channel-wise write rates (FG2-GDN+) on that
+                                         # shape, with the overhead over the KDA call
     python bench.py --traffic        # HBM bytes per call from rocprofv3 counters
 
 Prints ONE JSON line.  Only one GPU is used; --gpus above 1 exits.
@@ -43,13 +45,13 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 
 
-def prefill_algorithmic(B, T, H, d, C, io_bytes=2, s0=False, channel=False):
+def prefill_algorithmic(B, T, H, d, C, io_bytes=2, s0=False, channel=False, fg2=False):
     """Bytes: q,k,v read and o written once (io dtype), log_alpha (fp32, one per
     head-token, or d_k of them for the channel gate) and beta (fp32) read once,
     S_T written (and S0 read) once.  FLOPs: 6d^2 + 3Cd + C^2 per head-token (the
     FG2-GDN page's per-head kernel accounting, section 3.6)."""
     ht = B * T * H
-    per_ht = 4 * d * io_bytes + (4 * d if channel else 4) + 4
+    per_ht = 4 * d * io_bytes + (4 * d if channel else 4) + (2 * 4 * d if fg2 else 4)
     state = B * H * d * d * 4
     nbytes = ht * per_ht + state * (2 if s0 else 1)
     flops = ht * (6 * d * d + 3 * C * d + C * C)
@@ -155,6 +157,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=20)
     ap.add_argument("--workload", type=int, default=1, choices=(1, 2, 3),
                     help="prefill workload to time (1 is the headline)")
+    ap.add_argument("--fg2", action="store_true",
+                    help="time gdr_fg2_chunk_fwd with key and value rates (FG2-GDN+) instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", action="store_true",
                     help="measure HBM bytes per call with rocprofv3 and write a summary")
@@ -188,9 +192,11 @@ def main():
         sys.exit(2)
 
     import torch
-    from linear_attention_sequence_03_amd import gdr_chunk_fwd, gdr_decode_step, synth
+    from linear_attention_sequence_03_amd import (gdr_chunk_fwd, gdr_decode_step, gdr_fg2_chunk_fwd,
+                                                  synth)
     from linear_attention_sequence_03_amd.gdr import (GDR_BF16, GDR_GATE_CHANNEL, GDR_GATE_SCALAR,
-                                                      gdr_chunk_fwd_workspace_size)
+                                                      gdr_chunk_fwd_workspace_size,
+                                                      gdr_fg2_chunk_fwd_workspace_size)
 
     assert torch.cuda.is_available(), "no GPU visible"
     devn = torch.device("cuda:0")
@@ -207,12 +213,22 @@ def main():
     be = torch.from_numpy(inp["beta"]).to(devn)
     o = torch.empty((B, T, H, d), dtype=bf, device=devn)
     st = torch.empty((B, H, d, d), dtype=torch.float32, device=devn)
-    ws = torch.empty(gdr_chunk_fwd_workspace_size(B, T, H, d, d, C, GDR_BF16,
-                                                  GDR_GATE_CHANNEL if channel else GDR_GATE_SCALAR),
+    gate = GDR_GATE_CHANNEL if channel else GDR_GATE_SCALAR
+    ws = torch.empty(gdr_chunk_fwd_workspace_size(B, T, H, d, d, C, GDR_BF16, gate),
                      dtype=torch.uint8, device=devn)
 
-    def step():
+    def plain_step():
         gdr_chunk_fwd(q, k, v, la, be, S0, chunk=C, o=o, S_T=st, workspace=ws)
+
+    step = plain_step
+    if args.fg2:
+        bk, bv = synth.write_rates((B, T, H, d), d, seed=w.seed)
+        bk, bv = torch.from_numpy(bk).to(devn), torch.from_numpy(bv).to(devn)
+        ws2 = torch.empty(gdr_fg2_chunk_fwd_workspace_size(B, T, H, d, d, C, GDR_BF16, gate),
+                          dtype=torch.uint8, device=devn)
+
+        def step():
+            gdr_fg2_chunk_fwd(q, k, v, la, bk, bv, S0, chunk=C, o=o, S_T=st, workspace=ws2)
 
     for _ in range(args.warmup):
         step()
@@ -248,7 +264,28 @@ def main():
     warm = [a.elapsed_time(b) for a, b in ev2]
     del flush
 
-    nbytes, flops = prefill_algorithmic(B, T, H, d, C, s0=S0 is not None, channel=channel)
+    nbytes, flops = prefill_algorithmic(B, T, H, d, C, s0=S0 is not None, channel=channel,
+                                        fg2=args.fg2)
+    fg2_info = None
+    if args.fg2:
+        # the same call without rates, timed the same way, for the overhead
+        for _ in range(3):
+            plain_step()
+        ev3 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for a, b in ev3:
+            a.record(stream)
+            plain_step()
+            b.record(stream)
+        torch.cuda.synchronize()
+        base_ms = float(np.mean([a.elapsed_time(b) for a, b in ev3]))
+        base_bytes, _ = prefill_algorithmic(B, T, H, d, C, s0=S0 is not None, channel=channel)
+        fg2_info = {"call": "gdr_fg2_chunk_fwd (key and value rates: FG2-GDN+)",
+                    "launch_ms_mean": float(np.mean(warm)),
+                    "base_call": "gdr_chunk_fwd (scalar rate)", "base_launch_ms_mean": base_ms,
+                    "overhead": float(np.mean(warm)) / base_ms - 1.0,
+                    "algorithmic_bytes": nbytes, "base_algorithmic_bytes": base_bytes,
+                    "bytes_overhead": nbytes / base_bytes - 1.0}
     launch_ms = float(np.mean(warm))
     traffic = None
     if args.workload == 1 and os.path.exists(TRAFFIC_FILE):
@@ -294,11 +331,14 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded; q,k unit-norm N(0,1), v N(0,1), beta sigmoid(N(0,1)), "
                 "log_alpha U(-0.1,-0.001)%s)" % (", S0 N(0,0.02^2)" if S0 is not None else ""),
-        "config": {"workload": w.name, "call": "gdr_chunk_fwd",
+        "config": {"workload": w.name + ("_fg2plus" if args.fg2 else ""),
+                   "call": "gdr_fg2_chunk_fwd" if args.fg2 else "gdr_chunk_fwd",
                    "gate": "channel" if channel else "scalar",
                    "B": B, "T": T, "H": H, "d_k": d, "d_v": d, "chunk": C,
                    "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": ROOFLINE_KERNEL[args.workload],
+        "roofline": {"bound": "hbm",
+                     "kernel": ("gdr_fg2_chunk_fwd (fg2_scale prologue + " if args.fg2 else "")
+                     + ROOFLINE_KERNEL[args.workload] + (")" if args.fg2 else ""),
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": nbytes,
@@ -311,7 +351,9 @@ def main():
                    "algorithmic_bytes": dbytes, "achieved_GBs": dgbs,
                    "peak_GBs": HBM_PEAK_GBS, "frac": dgbs / HBM_PEAK_GBS},
     }
-    if not args.no_cpu_baseline:
+    if fg2_info is not None:
+        out["fg2"] = fg2_info
+    if not args.no_cpu_baseline and not args.fg2:
         import oracle.gdr_oracle as og
         threads = min(16, og.default_threads())
         reps, secs = cpu_baseline(inp, threads, S0=inp.get("S0"))

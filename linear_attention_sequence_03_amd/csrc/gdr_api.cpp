@@ -184,7 +184,9 @@ gdr_status gdr_fg2_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int
                                             size_t* bytes) {
     gdr_status s = gdr_chunk_fwd_workspace_size(B, T, H, dk, dv, chunk, io, gate, bytes);
     if (s != GDR_OK) return s;
-    if (mul({B, T, H, dk + dv}) < 0) return fail(GDR_ERR_UNSUPPORTED, "tensor sizes overflow");
+    const int64_t groups = mul({B, T, H, (dk + dv) / 8});   // one prologue thread each
+    if (groups < 0 || groups > (int64_t)UINT32_MAX - 256)
+        return fail(GDR_ERR_UNSUPPORTED, "B*T*H too large for the rate prologue");
     *bytes = gdr::fg2_workspace_bytes(B, T, H, dk, dv, chunk, io == GDR_BF16, gate == GDR_GATE_CHANNEL);
     return GDR_OK;
 }

@@ -11,8 +11,6 @@
 // holds literally: this file scales k and v once (a prologue over the whole
 // call, into the caller's workspace) and runs the ordinary chunk path on
 // (q, k~, v~) with beta = 1.
-#include <algorithm>
-
 #include "gdr_device.hpp"
 #include "gdr_launch.hpp"
 
@@ -23,7 +21,9 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // One thread per 8 elements of a row of k (the first dk/8 groups of a token)
-// or of v (the rest); the unit rates are written by the first ntok threads.
+// or of v (the rest): one 16-byte (bf16) or 32-byte (fp32) load of the vector,
+// two 16-byte non-temporal loads of the rates (read once), one store of the
+// scaled result.  The unit rates are written by the first ntok threads.
 template <typename E>
 __global__ __launch_bounds__(256) void fg2_scale(const E* __restrict__ k, const E* __restrict__ v,
                                                  const float* __restrict__ beta_k,
@@ -32,24 +32,31 @@ __global__ __launch_bounds__(256) void fg2_scale(const E* __restrict__ k, const 
                                                  float* __restrict__ ones, int64_t ntok, int dk,
                                                  int dv) {
     const int gk = dk / 8, gt = (dk + dv) / 8;
-    const int64_t n = ntok * gt;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-         i += (int64_t)gridDim.x * blockDim.x) {
-        if (i < ntok) ones[i] = 1.f;
-        const int64_t tok = i / gt;
-        const int g = (int)(i % gt);
-        const bool isk = g < gk;
-        const int64_t off = isk ? tok * dk + 8 * g : tok * dv + 8 * (g - gk);
-        const E* src = isk ? k : v;
-        const float* rate = isk ? beta_k : (beta_v ? beta_v : beta_k);
-        E* dst = isk ? ks : vs;
-        const float4 r0 = *reinterpret_cast<const float4*>(rate + off);
-        const float4 r1 = *reinterpret_cast<const float4*>(rate + off + 4);
-        const float4 x0 = load4(src + off), x1 = load4(src + off + 4);
-        store4(dst + off, make_float4(sqrtf(r0.x) * x0.x, sqrtf(r0.y) * x0.y, sqrtf(r0.z) * x0.z,
-                                      sqrtf(r0.w) * x0.w));
-        store4(dst + off + 4, make_float4(sqrtf(r1.x) * x1.x, sqrtf(r1.y) * x1.y,
-                                          sqrtf(r1.z) * x1.z, sqrtf(r1.w) * x1.w));
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= ntok * gt) return;
+    if (i < ntok) ones[i] = 1.f;
+    const int64_t tok = i / gt;
+    const int g = (int)(i - tok * gt);
+    const bool isk = g < gk;
+    const int64_t off = isk ? tok * dk + 8 * g : tok * dv + 8 * (g - gk);
+    const float* rate = (isk ? beta_k : (beta_v ? beta_v : beta_k)) + off;
+    const f32x4 r0 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(rate));
+    const f32x4 r1 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(rate + 4));
+    const float sr[8] = {sqrtf(r0[0]), sqrtf(r0[1]), sqrtf(r0[2]), sqrtf(r0[3]),
+                         sqrtf(r1[0]), sqrtf(r1[1]), sqrtf(r1[2]), sqrtf(r1[3])};
+    const E* src = (isk ? k : v) + off;
+    E* dst = (isk ? ks : vs) + off;
+    if constexpr (sizeof(E) == 2) {
+        const bf16x8 x = *reinterpret_cast<const bf16x8*>(src);
+        bf16x8 y;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) y[j] = (__bf16)(sr[j] * (float)x[j]);
+        *reinterpret_cast<bf16x8*>(dst) = y;
+    } else {
+        const float4 x0 = *reinterpret_cast<const float4*>(src);
+        const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
+        *reinterpret_cast<float4*>(dst) = make_float4(sr[0] * x0.x, sr[1] * x0.y, sr[2] * x0.z, sr[3] * x0.w);
+        *reinterpret_cast<float4*>(dst + 4) = make_float4(sr[4] * x1.x, sr[5] * x1.y, sr[6] * x1.z, sr[7] * x1.w);
     }
 }
 
@@ -74,7 +81,7 @@ hipError_t fg2_chunk_fwd_launch(const ChunkArgs& a, const float* beta_k, const f
     char* vs = ks + align_up((size_t)ntok * a.dk * es);
     float* ones = reinterpret_cast<float*>(vs + align_up((size_t)ntok * a.dv * es));
     const int64_t work = ntok * ((a.dk + a.dv) / 8);
-    const int64_t blocks = std::min<int64_t>((work + 255) / 256, 256 * 32);
+    const int64_t blocks = (work + 255) / 256;
     if (a.bf16)
         hipLaunchKernelGGL((fg2_scale<__bf16>), dim3((unsigned)blocks), dim3(256), 0, a.stream,
                            (const __bf16*)a.k, (const __bf16*)a.v, beta_k, beta_v, (__bf16*)ks,
