@@ -115,6 +115,39 @@ gdr_status gdr_decode_step(const void *q, const void *k, const void *v,
                            gdr_dtype io, gdr_gate gate, hipStream_t stream);
 
 /*
+ * Several tokens per sequence in one pass over the state: verifying a run of
+ * draft tokens in speculative decoding, then keeping the state of the accepted
+ * prefix (the pages name both the per-token rollback of the recurrent state
+ * and its fixed d_k x d_v size as the serving problem: "FG2-GDN" page,
+ * "Limitations / Inference Challenges").  Tokens t = 0..Td-1 of each sequence
+ * are applied to S_in in order, exactly as Td calls of gdr_decode_step would:
+ *
+ *   q, k       [B, Td, H, dk]   io dtype
+ *   v          [B, Td, H, dv]   io dtype
+ *   log_alpha  [B, Td, H] or [B, Td, H, dk]   fp32 (scalar / channel gate)
+ *   beta       [B, Td, H]       fp32
+ *   S_in       [B, H, dv, dk]   fp32 state before the first token; only read
+ *                               (unless S_out == S_in)
+ *   S_out      [B, H, dv, dk]   fp32, receives the state after the first n_b
+ *                               tokens of sequence b; may equal S_in (in place),
+ *                               must not partially overlap it; NULL writes no
+ *                               state (a read-only verification pass)
+ *   accepted   [B] int32 device array of n_b, each clamped to [0, Td]; NULL
+ *              means n_b = Td for every sequence.  4-byte aligned.
+ *   o          [B, Td, H, dv]   io dtype, o_t for every token; NULL skips them
+ * 1 <= Td <= 64 (longer runs belong to gdr_chunk_fwd).  The state is read once
+ * and written at most once, so the call costs about one decode step of HBM
+ * traffic whatever Td is.  A typical round: gdr_decode_multi(S_in, S_out=NULL,
+ * o) to score the drafts, then gdr_decode_multi(S_in, S_out, accepted, o=NULL)
+ * to commit the accepted prefix.
+ */
+gdr_status gdr_decode_multi(const void *q, const void *k, const void *v,
+                            const float *log_alpha, const float *beta,
+                            const float *S_in, float *S_out, const int32_t *accepted, void *o,
+                            int64_t B, int64_t Td, int64_t H, int64_t dk, int64_t dv,
+                            gdr_dtype io, gdr_gate gate, hipStream_t stream);
+
+/*
  * Channel-wise write rates: FG2-GDN and FG2-GDN+ ("FG2-GDN" page, sections 3.2,
  * 3.4-3.6).  The scalar beta_t becomes a vector beta^k_t in R^{d_k} that enters
  * through the scaled key k~ = sqrt(beta^k) * k (elementwise); the value is

@@ -179,6 +179,50 @@ gdr_status gdr_decode_step(const void* q, const void* k, const void* v, const fl
     return GDR_OK;
 }
 
+gdr_status gdr_decode_multi(const void* q, const void* k, const void* v, const float* log_alpha,
+                            const float* beta, const float* S_in, float* S_out,
+                            const int32_t* accepted, void* o, int64_t B, int64_t Td, int64_t H,
+                            int64_t dk, int64_t dv, gdr_dtype io, gdr_gate gate, hipStream_t stream) {
+    g_last_error[0] = 0;
+    gdr_status s = check_common(B, H, dk, dv, io, gate);
+    if (s != GDR_OK) return s;
+    if (Td < 1 || Td > 64)
+        return fail(GDR_ERR_UNSUPPORTED, "Td must be in [1, 64] (Td=%lld); use gdr_chunk_fwd for longer runs",
+                    (long long)Td);
+    const int64_t nst = mul({B, H, dv, dk});
+    if (nst < 0 || mul({B, H, dv}) > ((int64_t)INT32_MAX) * 4 || mul({B, Td, H, dk}) < 0)
+        return fail(GDR_ERR_UNSUPPORTED, "tensors too large");
+    if (!q || !k || !v || !log_alpha || !beta || !S_in)
+        return fail(GDR_ERR_INVALID_ARG, "q, k, v, log_alpha, beta and S_in must be non-NULL");
+    if (!S_out && !o) return GDR_OK;   // nothing requested
+    const size_t es = io == GDR_BF16 ? 2 : 4;
+    const int64_t ntok = B * Td * H;
+    const Range in_state = rng("S_in", S_in, nst, 4);
+    const Range out_state = rng("S_out", S_out, nst, 4);
+    if (S_out && S_in != S_out && overlap(in_state, out_state))
+        return fail(GDR_ERR_INVALID_ARG, "S_out partially overlaps S_in");
+    const Range acc = rng("accepted", accepted, B, 4);
+    if (accepted && (reinterpret_cast<uintptr_t>(accepted) & 3u))
+        return fail(GDR_ERR_INVALID_ARG, "accepted is not 4-byte aligned");
+    const Range rs[] = {
+        rng("q", q, ntok * dk, es), rng("k", k, ntok * dk, es), rng("v", v, ntok * dv, es),
+        rng("log_alpha", log_alpha, gate == GDR_GATE_CHANNEL ? ntok * dk : ntok, 4),
+        rng("beta", beta, ntok, 4),
+        S_in == S_out ? Range{"S_in", 0, 0} : in_state,
+        out_state, rng("o", o, ntok * dv, es),
+    };
+    if (!aligned16(S_in)) return fail(GDR_ERR_INVALID_ARG, "S_in is not 16-byte aligned");
+    s = check_ptrs(rs, 8, 6);
+    if (s != GDR_OK) return s;
+    for (int i = 6; i < 8; ++i)
+        if (overlap(rs[i], acc)) return fail(GDR_ERR_INVALID_ARG, "%s overlaps accepted", rs[i].name);
+    gdr::DecodeMultiArgs a{q, k, v, log_alpha, beta, S_in, S_out, accepted, o, B, Td, H, dk, dv,
+                           io == GDR_BF16, gate == GDR_GATE_CHANNEL, stream};
+    const hipError_t err = gdr::decode_multi_launch(a);
+    if (err != hipSuccess) return fail(GDR_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(err));
+    return GDR_OK;
+}
+
 gdr_status gdr_fg2_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t dk,
                                             int64_t dv, int64_t chunk, gdr_dtype io, gdr_gate gate,
                                             size_t* bytes) {

@@ -91,6 +91,112 @@ __global__ __launch_bounds__(256) void decode_kernel(
     }
 }
 
+// Several tokens per sequence in one pass over the state (speculative decoding:
+// verify a run of draft tokens, then keep the state of the accepted prefix;
+// "FG2-GDN" page, "Limitations / Inference Challenges").  Same lane layout as
+// decode_kernel; the lane's NPASS row slices stay in registers while the
+// tokens t = 0..Td-1 are applied in order, o_t is written after token t (when
+// o is given), and the state after the first n tokens is stored, n =
+// accepted[b] clamped to [0, Td] (Td when accepted is NULL; nothing stored
+// when S_out is NULL).  S_out may equal S_in: a lane writes only the slice it
+// read, after it has read it.
+template <typename E, bool CHANNEL, int DK>
+__global__ __launch_bounds__(256) void decode_multi_kernel(
+    const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
+    const float* __restrict__ log_alpha, const float* __restrict__ beta, const float* S_in,
+    float* S_out, const int32_t* __restrict__ accepted, E* __restrict__ o, int64_t BH, int H,
+    int Td, int DV) {
+    constexpr int LPR = DK / 4;
+    constexpr int RPP = kWave / LPR;
+    constexpr int NPASS = 4;
+    constexpr int RPW = RPP * NPASS;
+    const int lane = threadIdx.x & 63;
+    const int64_t gw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int wpb = DV / RPW;
+    const int64_t bh = gw / wpb;
+    if (bh >= BH) return;
+    const int64_t b = bh / H, h = bh % H;
+    const int row0 = (int)(gw % wpb) * RPW + lane / LPR;
+    const int c0 = 4 * (lane % LPR);
+    int nacc = Td;
+    if (accepted) nacc = min(max(accepted[b], 0), Td);
+
+    const int64_t base = bh * (int64_t)DV * DK;
+    f32x4 s[NPASS];
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p)
+        s[p] = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4*>(S_in + base + (int64_t)(row0 + p * RPP) * DK + c0));
+    if (S_out && nacc == 0) {
+#pragma unroll
+        for (int p = 0; p < NPASS; ++p)
+            __builtin_nontemporal_store(
+                s[p], reinterpret_cast<f32x4*>(S_out + base + (int64_t)(row0 + p * RPP) * DK + c0));
+    }
+    for (int t = 0; t < Td; ++t) {
+        const int64_t bth = (b * Td + t) * H + h;   // token row of [B, Td, H, *]
+        const float4 kk = load4(k + bth * DK + c0);
+        const float4 qq = load4(q + bth * DK + c0);
+        float4 aa;
+        if constexpr (CHANNEL) {
+            const float4 la = *reinterpret_cast<const float4*>(log_alpha + bth * DK + c0);
+            aa = make_float4(expf(la.x), expf(la.y), expf(la.z), expf(la.w));
+        } else {
+            const float a = expf(log_alpha[bth]);
+            aa = make_float4(a, a, a, a);
+        }
+        const float bt = beta[bth];
+#pragma unroll
+        for (int p = 0; p < NPASS; ++p) {
+            const int row = row0 + p * RPP;
+            f32x4 sd;
+            sd[0] = s[p][0] * aa.x; sd[1] = s[p][1] * aa.y;
+            sd[2] = s[p][2] * aa.z; sd[3] = s[p][3] * aa.w;
+            float pd = sd[0] * kk.x + sd[1] * kk.y + sd[2] * kk.z + sd[3] * kk.w;
+#pragma unroll
+            for (int m = LPR / 2; m >= 1; m >>= 1) pd += __shfl_xor(pd, m);
+            const float u = bt * (to_f32(v[bth * DV + row]) - pd);
+            s[p][0] = sd[0] + u * kk.x; s[p][1] = sd[1] + u * kk.y;
+            s[p][2] = sd[2] + u * kk.z; s[p][3] = sd[3] + u * kk.w;
+            if (o) {
+                float od = s[p][0] * qq.x + s[p][1] * qq.y + s[p][2] * qq.z + s[p][3] * qq.w;
+#pragma unroll
+                for (int m = LPR / 2; m >= 1; m >>= 1) od += __shfl_xor(od, m);
+                if (lane % LPR == 0) o[bth * DV + row] = from_f32<E>(od);
+            }
+        }
+        if (S_out && t + 1 == nacc) {
+#pragma unroll
+            for (int p = 0; p < NPASS; ++p)
+                __builtin_nontemporal_store(
+                    s[p], reinterpret_cast<f32x4*>(S_out + base + (int64_t)(row0 + p * RPP) * DK + c0));
+        }
+    }
+}
+
+template <typename E, bool CHANNEL, int DK>
+static hipError_t launch_decode_multi(const DecodeMultiArgs& a) {
+    constexpr int RPW = (kWave / (DK / 4)) * 4;
+    const int64_t waves = a.B * a.H * (a.dv / RPW);
+    const int64_t blocks = (waves + 3) / 4;
+    hipLaunchKernelGGL((decode_multi_kernel<E, CHANNEL, DK>), dim3((unsigned)blocks), dim3(256), 0,
+                       a.stream, (const E*)a.q, (const E*)a.k, (const E*)a.v, a.log_alpha, a.beta,
+                       a.S_in, a.S_out, a.accepted, (E*)a.o, a.B * a.H, (int)a.H, (int)a.Td,
+                       (int)a.dv);
+    return hipGetLastError();
+}
+
+template <typename E, bool CHANNEL>
+static hipError_t launch_decode_multi_dk(const DecodeMultiArgs& a) {
+    return a.dk == 64 ? launch_decode_multi<E, CHANNEL, 64>(a) : launch_decode_multi<E, CHANNEL, 128>(a);
+}
+
+hipError_t decode_multi_launch(const DecodeMultiArgs& a) {
+    if (a.bf16)
+        return a.channel ? launch_decode_multi_dk<__bf16, true>(a) : launch_decode_multi_dk<__bf16, false>(a);
+    return a.channel ? launch_decode_multi_dk<float, true>(a) : launch_decode_multi_dk<float, false>(a);
+}
+
 template <typename E, bool CHANNEL, int DK>
 static hipError_t launch_decode(const DecodeArgs& a) {
     constexpr int RPW = (kWave / (DK / 4)) * 4;

@@ -20,6 +20,19 @@ struct DecodeArgs {
     const float *beta_k = nullptr, *beta_v = nullptr;
 };
 
+// Several tokens per sequence in one pass over the state (draft verification
+// and accepted-prefix commit).
+struct DecodeMultiArgs {
+    const void *q, *k, *v;
+    const float *log_alpha, *beta, *S_in;
+    float* S_out;               // NULL: no state written
+    const int32_t* accepted;    // [B] or NULL (= Td)
+    void* o;                    // NULL: no outputs written
+    int64_t B, Td, H, dk, dv;
+    bool bf16, channel;
+    hipStream_t stream;
+};
+
 struct ChunkArgs {
     const void *q, *k, *v;
     const float *log_alpha, *beta, *S0;
@@ -32,6 +45,7 @@ struct ChunkArgs {
 };
 
 hipError_t decode_step_launch(const DecodeArgs& a);
+hipError_t decode_multi_launch(const DecodeMultiArgs& a);
 
 // Workspace bytes of one (b, h, chunk) block and of the whole call.
 size_t chunk_block_bytes(int64_t dk, int64_t chunk, bool bf16, bool channel);

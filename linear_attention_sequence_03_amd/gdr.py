@@ -20,7 +20,7 @@ GDR_F32, GDR_BF16 = 0, 1
 GDR_GATE_SCALAR, GDR_GATE_CHANNEL = 0, 1
 
 # Every symbol include/gdr.h declares.
-EXPORTS = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_decode_step",
+EXPORTS = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_decode_step", "gdr_decode_multi",
            "gdr_fg2_chunk_fwd_workspace_size", "gdr_fg2_chunk_fwd", "gdr_fg2_decode_step",
            "gdr_status_string", "gdr_last_error")
 
@@ -58,6 +58,9 @@ def load_library(path: Optional[str] = None):
     lib.gdr_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp,
                                     i64, i64, i64, i64, f, f, vp]
     lib.gdr_decode_step.restype = f
+    lib.gdr_decode_multi.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                     i64, i64, i64, i64, i64, f, f, vp]
+    lib.gdr_decode_multi.restype = f
     lib.gdr_fg2_chunk_fwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64, f, f,
                                                      ctypes.POINTER(ctypes.c_size_t)]
     lib.gdr_fg2_chunk_fwd_workspace_size.restype = f
@@ -274,6 +277,45 @@ def gdr_fg2_decode_step(q, k, v, log_alpha, beta_k, beta_v, S, S_out=None, o=Non
     st = load_library().gdr_fg2_decode_step(
         _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta_k), _ptr(beta_v), _ptr(S),
         _ptr(S_out), _ptr(o), B, H, dk, dv, io, gate, _stream(dev, stream))
+    if st != GDR_OK:
+        _raise(st)
+    return o, S_out
+
+
+def gdr_decode_multi(q, k, v, log_alpha, beta, S, S_out=None, accepted=None, o=None,
+                     want_o: bool = True, inplace: bool = False, stream=None) -> Tuple:
+    """Td tokens per sequence in one pass over the state.  q,k: [B,Td,H,dk];
+    v: [B,Td,H,dv]; log_alpha: [B,Td,H] or [B,Td,H,dk]; beta: [B,Td,H];
+    S: [B,H,dv,dk] fp32 (read only unless ``inplace``).  ``S_out`` (or S itself
+    with ``inplace=True``) receives the state after ``accepted[b]`` tokens
+    (int32 [B] on the device; None = all Td); with neither, no state is
+    written.  Returns (o [B,Td,H,dv] or None, S_out or None)."""
+    import torch
+    dev = q.device
+    B, Td, H, dk = q.shape
+    dv = v.shape[-1]
+    io = _io_code(q.dtype)
+    gate = GDR_GATE_CHANNEL if log_alpha.dim() == 4 else GDR_GATE_SCALAR
+    _need("q", q, q.dtype, (B, Td, H, dk), dev)
+    _need("k", k, q.dtype, (B, Td, H, dk), dev)
+    _need("v", v, q.dtype, (B, Td, H, dv), dev)
+    _need("log_alpha", log_alpha, torch.float32,
+          (B, Td, H, dk) if gate == GDR_GATE_CHANNEL else (B, Td, H), dev)
+    _need("beta", beta, torch.float32, (B, Td, H), dev)
+    _need("S", S, torch.float32, (B, H, dv, dk), dev)
+    if inplace:
+        S_out = S
+    if S_out is not None:
+        _need("S_out", S_out, torch.float32, (B, H, dv, dk), dev)
+    if accepted is not None:
+        _need("accepted", accepted, torch.int32, (B,), dev)
+    if o is None and want_o:
+        o = torch.empty((B, Td, H, dv), dtype=q.dtype, device=dev)
+    if o is not None:
+        _need("o", o, q.dtype, (B, Td, H, dv), dev)
+    st = load_library().gdr_decode_multi(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S), _ptr(S_out),
+        _ptr(accepted), _ptr(o), B, Td, H, dk, dv, io, gate, _stream(dev, stream))
     if st != GDR_OK:
         _raise(st)
     return o, S_out

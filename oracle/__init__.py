@@ -12,5 +12,5 @@ two share no code.
   explicit per-token transition matrices; used to pin the fp64 oracle on tiny
   shapes.
 """
-from .gdr_oracle import (build, chunk_fwd, decode_step, fg2_chunk_fwd, fg2_decode_step,  # noqa: F401
-                         library_path, load)
+from .gdr_oracle import (build, chunk_fwd, decode_multi, decode_step, fg2_chunk_fwd,  # noqa: F401
+                         fg2_decode_step, library_path, load)

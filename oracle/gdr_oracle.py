@@ -183,3 +183,23 @@ def fg2_decode_step(q, k, v, log_alpha, beta_k, beta_v, S, lib=None):
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
     return o, s_out
+
+
+def decode_multi(q, k, v, log_alpha, beta, S, accepted=None, lib=None):
+    """Td tokens per sequence applied to the state S in order, as Td decode
+    steps would (speculative-decoding verify / commit).  q,k: [B,Td,H,dk];
+    v: [B,Td,H,dv]; log_alpha: [B,Td,H] or [B,Td,H,dk]; beta: [B,Td,H];
+    S: [B,H,dv,dk]; accepted: B integers (clamped to [0, Td]) or None (= Td).
+    Returns (o [B,Td,H,dv] from every token, S_out [B,H,dv,dk] = the state after
+    the first accepted[b] tokens of sequence b).  A composition of the
+    whole-sequence recurrence above, with no arithmetic of its own."""
+    q, k, v, la, be, s = (_f64(a) for a in (q, k, v, log_alpha, beta, S))
+    B, Td = q.shape[:2]
+    o, _ = chunk_fwd(q, k, v, la, be, s, lib=lib)
+    s_out = s.copy()
+    for b in range(B):
+        n = Td if accepted is None else int(min(max(int(accepted[b]), 0), Td))
+        sl = lambda a: a[b:b + 1, :n]  # noqa: E731
+        _, st = chunk_fwd(sl(q), sl(k), sl(v), sl(la), sl(be), s[b:b + 1], lib=lib)
+        s_out[b] = st[0]
+    return o, s_out

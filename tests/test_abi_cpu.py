@@ -173,3 +173,28 @@ def test_fg2_workspace_size():
             want = al(inner) + 2 * al(ntok * d * es) + al(ntok * 4)
             assert gdr.gdr_fg2_chunk_fwd_workspace_size(B, T, H, d, d, C, io, gate) == want
     assert gdr.gdr_fg2_chunk_fwd_workspace_size(1, 0, 1, 64, 64, 16, 0, 1) == 0
+
+
+# ----- several tokens per call ------------------------------------------------
+def _multi(lib, q=0, k=1, v=2, la=3, be=4, si=5, so=6, acc=9, o=7, B=2, Td=4, H=2, dk=64, dv=64,
+           io=0, gate=0):
+    p = lambda i: None if i is None else (_addr(i) if isinstance(i, int) else i)  # noqa: E731
+    return lib.gdr_decode_multi(p(q), p(k), p(v), p(la), p(be), p(si), p(so), p(acc), p(o),
+                                B, Td, H, dk, dv, io, gate, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(si=None), 1), (dict(Td=0), 2), (dict(Td=65), 2),
+    (dict(dk=128, dv=64), 2), (dict(gate=4), 1),
+    (dict(acc=ctypes.c_void_p(BASE + 9 * MB + 2)), 1),     # misaligned accepted
+    (dict(so=ctypes.c_void_p(BASE + 5 * MB + 4096)), 1),   # partial overlap with S_in
+    (dict(o=ctypes.c_void_p(BASE + 9 * MB)), 1),           # o is accepted
+    (dict(o=ctypes.c_void_p(BASE + 1 * MB)), 1),           # o is k
+])
+def test_decode_multi_rejects(lib, kw, code):
+    assert _multi(lib, **kw) == code
+    assert lib.gdr_last_error()
+
+
+def test_decode_multi_nothing_requested_is_ok(lib):
+    assert _multi(lib, so=None, o=None) == 0

@@ -335,3 +335,32 @@ def test_empty_sequence_returns_start_state():
     o, st = oracle.chunk_fwd(q, k, v, la, be, S0)
     assert o.shape[1] == 0
     np.testing.assert_array_equal(st, S0)
+
+
+# --------------------------------------------------------------------------
+# Several tokens per call (verify a run of drafts, keep an accepted prefix).
+# --------------------------------------------------------------------------
+def test_decode_multi_is_repeated_decode_steps():
+    q, k, v, la, be, S0 = _rand_inputs(400, B=3, T=6, channel=True)
+    accepted = [0, 4, 6]
+    o, s_out = oracle.decode_multi(q, k, v, la, be, S0, accepted)
+    for b in range(3):
+        S = S0[b:b + 1].copy()
+        for t in range(6):
+            sl = lambda a: np.ascontiguousarray(a[b:b + 1, t])  # noqa: E731
+            ot, S = oracle.decode_step(sl(q), sl(k), sl(v), sl(la), sl(be), S)
+            np.testing.assert_allclose(ot[0], o[b, t], rtol=0, atol=1e-13)
+            if t + 1 == accepted[b]:
+                np.testing.assert_allclose(S[0], s_out[b], rtol=0, atol=1e-13)
+    np.testing.assert_array_equal(s_out[0], S0[0])     # nothing accepted: state kept
+
+
+def test_decode_multi_clamps_and_defaults():
+    q, k, v, la, be, S0 = _rand_inputs(401, B=2, T=5)
+    o1, s1 = oracle.decode_multi(q, k, v, la, be, S0, [-3, 99])
+    o2, s2 = oracle.decode_multi(q, k, v, la, be, S0, None)
+    _, st = oracle.chunk_fwd(q, k, v, la, be, S0)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(s1[0], S0[0])
+    np.testing.assert_allclose(s1[1], st[1], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(s2, st, rtol=0, atol=1e-14)
