@@ -317,6 +317,42 @@ def main():
     dbytes = decode_algorithmic(wd.B, wd.H, wd.d)
     dgbs = dbytes / (dms * 1e-3) / 1e9
 
+    # Several tokens per sequence on the same resident state (speculative
+    # decoding): a read-only pass scoring Td draft tokens, then the commit of
+    # the accepted prefixes in place.
+    from linear_attention_sequence_03_amd import gdr_decode_multi
+    Td = 4
+    mi = synth.chunk_inputs(wd.B, Td, wd.H, wd.d, wd.d, "scalar", "f32", seed=wd.seed + 1)
+    mq, mk, mv, mla, mbe = (torch.from_numpy(mi[n]).to(devn)
+                            for n in ("q", "k", "v", "log_alpha", "beta"))
+    macc = torch.from_numpy(np.random.Generator(np.random.PCG64(wd.seed)).integers(
+        0, Td + 1, wd.B).astype(np.int32)).to(devn)
+    mo = torch.empty((wd.B, Td, wd.H, wd.d), dtype=torch.float32, device=devn)
+
+    def verify():
+        gdr_decode_multi(mq, mk, mv, mla, mbe, S, o=mo)
+
+    def commit():
+        gdr_decode_multi(mq, mk, mv, mla, mbe, S, accepted=macc, want_o=False, inplace=True)
+
+    mres = {}
+    for name, fn in (("verify", verify), ("commit", commit)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        mev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.decode_steps)]
+        for a, b in mev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        mres[name] = float(np.mean([a.elapsed_time(b) for a, b in mev]))
+    state_bytes = wd.B * wd.H * wd.d * wd.d * 4
+    vec_bytes = wd.B * Td * wd.H * (4 * wd.d * 4 + 8)
+    mv_bytes = state_bytes + vec_bytes                      # read the state once
+    mc_bytes = 2 * state_bytes + vec_bytes - wd.B * Td * wd.H * wd.d * 4   # no o written
+
     out = {
         "metric": METRIC,
         "value": B * T / (ms_per_step * 1e-3),
@@ -350,6 +386,13 @@ def main():
                    "tokens_per_s": wd.B / (dms * 1e-3),
                    "algorithmic_bytes": dbytes, "achieved_GBs": dgbs,
                    "peak_GBs": HBM_PEAK_GBS, "frac": dgbs / HBM_PEAK_GBS},
+        "decode_multi": {"call": "gdr_decode_multi", "draft_tokens": Td,
+                         "verify_ms": mres["verify"], "verify_bytes": mv_bytes,
+                         "verify_GBs": mv_bytes / (mres["verify"] * 1e-3) / 1e9,
+                         "commit_ms": mres["commit"], "commit_bytes": mc_bytes,
+                         "commit_GBs": mc_bytes / (mres["commit"] * 1e-3) / 1e9,
+                         "note": "verify: state read once, o for all draft tokens; commit: "
+                                 "state of the accepted prefix written in place"},
     }
     if fg2_info is not None:
         out["fg2"] = fg2_info

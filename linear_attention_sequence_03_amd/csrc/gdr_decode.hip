@@ -91,25 +91,40 @@ __global__ __launch_bounds__(256) void decode_kernel(
     }
 }
 
+// Sum over the LPR (4 or 8) consecutive lanes that share a state row, left in
+// every one of them: DPP quad permutations (xor 1, xor 2), then the half-row
+// mirror (lane i <-> 7 - i) for 8 lanes.  No LDS traffic.
+template <int LPR>
+__device__ __forceinline__ float row_sum(float x) {
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xf, 0xf, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xf, 0xf, false));
+    if constexpr (LPR == 8)
+        x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x141, 0xf, 0xf, false));
+    return x;
+}
+
 // Several tokens per sequence in one pass over the state (speculative decoding:
 // verify a run of draft tokens, then keep the state of the accepted prefix;
-// "FG2-GDN" page, "Limitations / Inference Challenges").  Same lane layout as
-// decode_kernel; the lane's NPASS row slices stay in registers while the
-// tokens t = 0..Td-1 are applied in order, o_t is written after token t (when
-// o is given), and the state after the first n tokens is stored, n =
-// accepted[b] clamped to [0, Td] (Td when accepted is NULL; nothing stored
-// when S_out is NULL).  S_out may equal S_in: a lane writes only the slice it
-// read, after it has read it.
+// "FG2-GDN" page, "Limitations / Inference Challenges").  The state rows stay
+// in registers while the tokens t = 0..Td-1 are applied in order, so the work
+// per token is arithmetic and two row reductions; the layout is chosen for
+// cheap reductions: LPR = DK/16 lanes share a row, lane c holds the 16
+// channels 4(c + LPR j) + e (j, e < 4: each of its four 16-byte accesses is
+// part of one contiguous row segment across the row's lanes), and a row sum is
+// three DPP steps.  o_t is written after token t (when o is given), and the
+// state after the first n tokens is stored, n = accepted[b] clamped to
+// [0, Td] (Td when accepted is NULL; nothing stored when S_out is NULL).
+// S_out may equal S_in: a lane writes only the slices it read, after reading.
 template <typename E, bool CHANNEL, int DK>
 __global__ __launch_bounds__(256) void decode_multi_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta, const float* S_in,
     float* S_out, const int32_t* __restrict__ accepted, E* __restrict__ o, int64_t BH, int H,
     int Td, int DV) {
-    constexpr int LPR = DK / 4;
-    constexpr int RPP = kWave / LPR;
-    constexpr int NPASS = 4;
-    constexpr int RPW = RPP * NPASS;
+    constexpr int LPR = DK / 16;     // lanes per state row
+    constexpr int RPP = kWave / LPR; // rows per pass of one wave
+    constexpr int NPASS = 2;
+    constexpr int RPW = RPP * NPASS; // rows per wave
     const int lane = threadIdx.x & 63;
     const int64_t gw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int wpb = DV / RPW;
@@ -117,66 +132,77 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(
     if (bh >= BH) return;
     const int64_t b = bh / H, h = bh % H;
     const int row0 = (int)(gw % wpb) * RPW + lane / LPR;
-    const int c0 = 4 * (lane % LPR);
+    const int cl = lane % LPR;
     int nacc = Td;
     if (accepted) nacc = min(max(accepted[b], 0), Td);
 
     const int64_t base = bh * (int64_t)DV * DK;
-    f32x4 s[NPASS];
+    auto sp = [&](int p, int j) { return base + (int64_t)(row0 + p * RPP) * DK + 4 * (cl + LPR * j); };
+    f32x4 s[NPASS][4];
 #pragma unroll
     for (int p = 0; p < NPASS; ++p)
-        s[p] = __builtin_nontemporal_load(
-            reinterpret_cast<const f32x4*>(S_in + base + (int64_t)(row0 + p * RPP) * DK + c0));
-    if (S_out && nacc == 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            s[p][j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S_in + sp(p, j)));
+    auto store_state = [&]() {
 #pragma unroll
         for (int p = 0; p < NPASS; ++p)
-            __builtin_nontemporal_store(
-                s[p], reinterpret_cast<f32x4*>(S_out + base + (int64_t)(row0 + p * RPP) * DK + c0));
-    }
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                __builtin_nontemporal_store(s[p][j], reinterpret_cast<f32x4*>(S_out + sp(p, j)));
+    };
+    if (S_out && nacc == 0) store_state();
     for (int t = 0; t < Td; ++t) {
         const int64_t bth = (b * Td + t) * H + h;   // token row of [B, Td, H, *]
-        const float4 kk = load4(k + bth * DK + c0);
-        const float4 qq = load4(q + bth * DK + c0);
-        float4 aa;
-        if constexpr (CHANNEL) {
-            const float4 la = *reinterpret_cast<const float4*>(log_alpha + bth * DK + c0);
-            aa = make_float4(expf(la.x), expf(la.y), expf(la.z), expf(la.w));
-        } else {
-            const float a = expf(log_alpha[bth]);
-            aa = make_float4(a, a, a, a);
+        float4 kk[4], qq[4], aa[4];
+        float a1 = 1.f;
+        if constexpr (!CHANNEL) a1 = expf(log_alpha[bth]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c = 4 * (cl + LPR * j);
+            kk[j] = load4(k + bth * DK + c);
+            qq[j] = load4(q + bth * DK + c);
+            if constexpr (CHANNEL) {
+                const float4 la = *reinterpret_cast<const float4*>(log_alpha + bth * DK + c);
+                aa[j] = make_float4(expf(la.x), expf(la.y), expf(la.z), expf(la.w));
+            } else {
+                aa[j] = make_float4(a1, a1, a1, a1);
+            }
         }
         const float bt = beta[bth];
 #pragma unroll
         for (int p = 0; p < NPASS; ++p) {
             const int row = row0 + p * RPP;
-            f32x4 sd;
-            sd[0] = s[p][0] * aa.x; sd[1] = s[p][1] * aa.y;
-            sd[2] = s[p][2] * aa.z; sd[3] = s[p][3] * aa.w;
-            float pd = sd[0] * kk.x + sd[1] * kk.y + sd[2] * kk.z + sd[3] * kk.w;
+            float pd = 0.f;
 #pragma unroll
-            for (int m = LPR / 2; m >= 1; m >>= 1) pd += __shfl_xor(pd, m);
+            for (int j = 0; j < 4; ++j) {
+                s[p][j][0] *= aa[j].x; s[p][j][1] *= aa[j].y;
+                s[p][j][2] *= aa[j].z; s[p][j][3] *= aa[j].w;
+                pd += s[p][j][0] * kk[j].x + s[p][j][1] * kk[j].y + s[p][j][2] * kk[j].z +
+                      s[p][j][3] * kk[j].w;
+            }
+            pd = row_sum<LPR>(pd);
             const float u = bt * (to_f32(v[bth * DV + row]) - pd);
-            s[p][0] = sd[0] + u * kk.x; s[p][1] = sd[1] + u * kk.y;
-            s[p][2] = sd[2] + u * kk.z; s[p][3] = sd[3] + u * kk.w;
-            if (o) {
-                float od = s[p][0] * qq.x + s[p][1] * qq.y + s[p][2] * qq.z + s[p][3] * qq.w;
+            float od = 0.f;
 #pragma unroll
-                for (int m = LPR / 2; m >= 1; m >>= 1) od += __shfl_xor(od, m);
-                if (lane % LPR == 0) o[bth * DV + row] = from_f32<E>(od);
+            for (int j = 0; j < 4; ++j) {
+                s[p][j][0] += u * kk[j].x; s[p][j][1] += u * kk[j].y;
+                s[p][j][2] += u * kk[j].z; s[p][j][3] += u * kk[j].w;
+                od += s[p][j][0] * qq[j].x + s[p][j][1] * qq[j].y + s[p][j][2] * qq[j].z +
+                      s[p][j][3] * qq[j].w;
+            }
+            if (o) {
+                od = row_sum<LPR>(od);
+                if (cl == 0) o[bth * DV + row] = from_f32<E>(od);
             }
         }
-        if (S_out && t + 1 == nacc) {
-#pragma unroll
-            for (int p = 0; p < NPASS; ++p)
-                __builtin_nontemporal_store(
-                    s[p], reinterpret_cast<f32x4*>(S_out + base + (int64_t)(row0 + p * RPP) * DK + c0));
-        }
+        if (S_out && t + 1 == nacc) store_state();
     }
 }
 
 template <typename E, bool CHANNEL, int DK>
 static hipError_t launch_decode_multi(const DecodeMultiArgs& a) {
-    constexpr int RPW = (kWave / (DK / 4)) * 4;
+    constexpr int RPW = (kWave / (DK / 16)) * 2;
     const int64_t waves = a.B * a.H * (a.dv / RPW);
     const int64_t blocks = (waves + 3) / 4;
     hipLaunchKernelGGL((decode_multi_kernel<E, CHANNEL, DK>), dim3((unsigned)blocks), dim3(256), 0,
