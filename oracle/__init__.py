@@ -7,10 +7,11 @@ two share no code.
 * :mod:`oracle.gdr_oracle` -- ctypes front end of ``gdr_oracle.c`` (token-by-token
   fp64 recurrence, threads over independent (b,h) pairs).
   It also holds the channel-wise write-rate variant (FG2): ``fg2_chunk_fwd`` /
-  ``fg2_decode_step``.
+  ``fg2_decode_step``, and the decoupled erase / write gates (Gated DeltaNet-2):
+  ``gdn2_chunk_fwd``.
 * :mod:`oracle.exact` -- exact rational brute force that multiplies out the
   explicit per-token transition matrices; used to pin the fp64 oracle on tiny
   shapes.
 """
 from .gdr_oracle import (build, chunk_fwd, decode_multi, decode_step, fg2_chunk_fwd,  # noqa: F401
-                         fg2_decode_step, library_path, load)
+                         fg2_decode_step, gdn2_chunk_fwd, library_path, load)

@@ -101,3 +101,30 @@ def run_fg2(q, k, v, alpha, sk, sv, S0=None):
         outs.append([sum((S[i][c] * Fraction(q[t][c]) for c in range(dk)), Fraction(0))
                      for i in range(dv)])
     return outs, S
+
+
+def run_gdn2(q, k, v, alpha, erase, write, S0=None):
+    """Decoupled erase and write gates (Gated DeltaNet-2 reading), ONE head,
+    exactly: per token the explicit transition Diag(alpha) (I - k (b*k)^T)
+    multiplies the state and the write (w*v) k^T is added.  ``erase`` is T lists
+    of d_k, ``write`` T lists of d_v."""
+    T = len(q)
+    dk = len(k[0])
+    dv = len(v[0])
+    S = _zeros(dv, dk) if S0 is None else [[Fraction(x) for x in row] for row in S0]
+    outs = []
+    for t in range(T):
+        kt = [Fraction(x) for x in k[t]]
+        et = [Fraction(erase[t][c]) * kt[c] for c in range(dk)]
+        proj = [[(Fraction(1) if i == j else Fraction(0)) - kt[i] * et[j] for j in range(dk)]
+                for i in range(dk)]
+        diag = [[Fraction(alpha[t][i]) if i == j else Fraction(0) for j in range(dk)]
+                for i in range(dk)]
+        S = _matmul(S, _matmul(diag, proj))
+        for i in range(dv):
+            u = Fraction(write[t][i]) * Fraction(v[t][i])
+            for c in range(dk):
+                S[i][c] += u * kt[c]
+        outs.append([sum((S[i][c] * Fraction(q[t][c]) for c in range(dk)), Fraction(0))
+                     for i in range(dv)])
+    return outs, S

@@ -64,6 +64,21 @@
  * exactly KDA (Gated DeltaNet for a scalar decay) when beta^k = beta^v is the
  * same number in every channel (k~ k~^T = beta k k^T, v~ k~^T = beta v k^T).
  * Queries are not scaled.
+ *
+ * Decoupled erase and write gates (Gated DeltaNet-2; "Daily Papers" pages,
+ * the Gated DeltaNet-2 abstract and citation notes): a channel-wise erase gate
+ * b_t in R^{d_k} on the key side and a channel-wise write gate w_t in R^{d_v}
+ * on the value side replace the tied scalar beta_t:
+ *
+ *   S_t = S_{t-1} Diag(alpha_t) (I - k_t (b_t * k_t)^T) + (w_t * v_t) k_t^T
+ *
+ * i.e. read the decayed memory at k, erase that read along the gated key
+ * b * k (the asymmetric "erase factor"), write the gated value along k.  The
+ * page prints no equation; this reading keeps what it states: the delta-rule
+ * fast-weight structure, erase on the key side and write on the value side,
+ * KDA (Gated DeltaNet for a scalar decay) when b_t and w_t collapse to the same
+ * scalar beta_t, and an erase factor that is beta_r gamma_r^2 kbar_r in the
+ * scalar-decay chunk form (kbar_r = k_r / gamma_r).
  */
 #include <math.h>
 #include <pthread.h>
@@ -285,5 +300,90 @@ int gdr_oracle_fg2_decode_step(const double *q, const double *k, const double *v
     free(a);
     free(ks);
     free(vs);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Decoupled erase and write gates (Gated DeltaNet-2, see the header).        */
+/* ------------------------------------------------------------------------ */
+static void step_gdn2(double *S, const double *q, const double *k, const double *v,
+                      const double *log_alpha, int channel_gate, const double *eb,
+                      const double *ww, double *o, double *a, int64_t dk, int64_t dv)
+{
+    for (int64_t c = 0; c < dk; ++c)
+        a[c] = exp(channel_gate ? log_alpha[c] : log_alpha[0]);
+    for (int64_t i = 0; i < dv; ++i) {
+        double *row = S + i * dk;
+        for (int64_t c = 0; c < dk; ++c) row[c] *= a[c];          /* decay            */
+        double r = 0.0;
+        for (int64_t c = 0; c < dk; ++c) r += row[c] * k[c];      /* read at k        */
+        for (int64_t c = 0; c < dk; ++c) row[c] -= r * eb[c] * k[c]; /* erase along b*k */
+        const double u = ww[i] * v[i];
+        for (int64_t c = 0; c < dk; ++c) row[c] += u * k[c];      /* write w*v along k */
+        double acc = 0.0;
+        for (int64_t c = 0; c < dk; ++c) acc += row[c] * q[c];
+        o[i] = acc;
+    }
+}
+
+typedef struct {
+    const double *q, *k, *v, *log_alpha, *eb, *ww, *S0;
+    double *o, *S_T;
+    int64_t B, T, H, dk, dv;
+    int channel_gate;
+    int64_t next_unit;
+    pthread_mutex_t mu;
+} job_gdn2_t;
+
+static void *worker_gdn2(void *arg)
+{
+    job_gdn2_t *J = (job_gdn2_t *)arg;
+    const int64_t dk = J->dk, dv = J->dv, T = J->T, H = J->H;
+    double *S = (double *)malloc(sizeof(double) * dv * dk);
+    double *a = (double *)malloc(sizeof(double) * dk);
+    for (;;) {
+        pthread_mutex_lock(&J->mu);
+        int64_t u = J->next_unit++;
+        pthread_mutex_unlock(&J->mu);
+        if (u >= J->B * J->H) break;
+        const int64_t b = u / H, h = u % H;
+        if (J->S0)
+            memcpy(S, J->S0 + u * dv * dk, sizeof(double) * dv * dk);
+        else
+            memset(S, 0, sizeof(double) * dv * dk);
+        for (int64_t t = 0; t < T; ++t) {
+            const int64_t bth = (b * T + t) * H + h;
+            const double *la = J->log_alpha + (J->channel_gate ? bth * dk : bth);
+            step_gdn2(S, J->q + bth * dk, J->k + bth * dk, J->v + bth * dv, la, J->channel_gate,
+                      J->eb + bth * dk, J->ww + bth * dv, J->o + bth * dv, a, dk, dv);
+        }
+        if (J->S_T) memcpy(J->S_T + u * dv * dk, S, sizeof(double) * dv * dk);
+    }
+    free(S);
+    free(a);
+    return NULL;
+}
+
+/* Full sequence with decoupled gates.  erase: [B,T,H,dk]; write: [B,T,H,dv].
+ * Returns 0 on success, -1 on bad arguments. */
+int gdr_oracle_gdn2_chunk_fwd(const double *q, const double *k, const double *v,
+                              const double *log_alpha, const double *erase, const double *write,
+                              const double *S0, double *o, double *S_T,
+                              int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                              int channel_gate, int nthreads)
+{
+    if (!q || !k || !v || !log_alpha || !erase || !write || !o) return -1;
+    if (B < 1 || T < 0 || H < 1 || dk < 1 || dv < 1) return -1;
+    job_gdn2_t J = {q, k, v, log_alpha, erase, write, S0, o, S_T, B, T, H, dk, dv,
+                    channel_gate != 0, 0};
+    pthread_mutex_init(&J.mu, NULL);
+    int64_t units = B * H;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > units) nthreads = (int)units;
+    pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    for (int i = 0; i < nthreads; ++i) pthread_create(&th[i], NULL, worker_gdn2, &J);
+    for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+    free(th);
+    pthread_mutex_destroy(&J.mu);
     return 0;
 }

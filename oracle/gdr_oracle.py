@@ -66,6 +66,10 @@ def load(path=None):
     lib.gdr_oracle_fg2_decode_step.argtypes = [d, d, d, d, d, d, d, d, d,
                                                i64, i64, i64, i64, ctypes.c_int]
     lib.gdr_oracle_fg2_decode_step.restype = ctypes.c_int
+    lib.gdr_oracle_gdn2_chunk_fwd.argtypes = [d, d, d, d, d, d, d, d, d,
+                                              i64, i64, i64, i64, i64,
+                                              ctypes.c_int, ctypes.c_int]
+    lib.gdr_oracle_gdn2_chunk_fwd.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -203,3 +207,29 @@ def decode_multi(q, k, v, log_alpha, beta, S, accepted=None, lib=None):
         _, st = chunk_fwd(sl(q), sl(k), sl(v), sl(la), sl(be), s[b:b + 1], lib=lib)
         s_out[b] = st[0]
     return o, s_out
+
+
+def gdn2_chunk_fwd(q, k, v, log_alpha, erase, write, S0=None, threads=None, lib=None):
+    """Whole-sequence forward with decoupled erase and write gates (Gated
+    DeltaNet-2 reading, see gdr_oracle.c).  q, k: [B,T,H,dk]; v: [B,T,H,dv];
+    log_alpha: [B,T,H] or [B,T,H,dk]; erase: [B,T,H,dk]; write: [B,T,H,dv];
+    S0: [B,H,dv,dk] or None.  Returns (o, S_T) as fp64 arrays."""
+    q, k, v, la, eb, ww = (_f64(a) for a in (q, k, v, log_alpha, erase, write))
+    B, T, H, dk = q.shape
+    dv = v.shape[3]
+    channel = la.ndim == 4
+    if k.shape != q.shape or v.shape[:3] != (B, T, H) or eb.shape != (B, T, H, dk) \
+            or ww.shape != (B, T, H, dv):
+        raise ValueError("shape mismatch")
+    if la.shape != ((B, T, H, dk) if channel else (B, T, H)):
+        raise ValueError("log_alpha shape mismatch")
+    s0 = None if S0 is None else _f64(S0)
+    o = np.zeros((B, T, H, dv), np.float64)
+    st = np.zeros((B, H, dv, dk), np.float64)
+    n = default_threads() if threads is None else int(threads)
+    rc = (lib or load()).gdr_oracle_gdn2_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(la), _ptr(eb),
+                                                   _ptr(ww), _ptr(s0), _ptr(o), _ptr(st),
+                                                   B, T, H, dk, dv, int(channel), n)
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return o, st
