@@ -187,6 +187,31 @@ gdr_status gdr_fg2_decode_step(const void *q, const void *k, const void *v,
                                int64_t B, int64_t H, int64_t dk, int64_t dv,
                                gdr_dtype io, gdr_gate gate, hipStream_t stream);
 
+/*
+ * Decoupled erase and write gates: Gated DeltaNet-2 ("Daily Papers" pages, the
+ * Gated DeltaNet-2 abstract and citation notes).  A channel-wise erase gate
+ * b_t in R^{d_k} (key side) and a channel-wise write gate w_t in R^{d_v} (value
+ * side) replace the tied scalar beta_t:
+ *
+ *   S_t = S_{t-1} Diag(alpha_t) (I - k_t (b_t * k_t)^T) + (w_t * v_t) k_t^T,
+ *   o_t = S_t q_t
+ *
+ * (read the decayed memory at k, erase the read along b*k, write w*v along k).
+ * The pages give no equation; this reading keeps what they state, including
+ * KDA / Gated DeltaNet when b_t and w_t collapse to the same scalar.
+ *
+ *   erase      [B, T, H, dk]   fp32 b_t
+ *   write      [B, T, H, dv]   fp32 w_t
+ * The other arguments are as in gdr_chunk_fwd (no chunk, no workspace).  This
+ * implementation is a token-sequential scan with the state in registers (one
+ * pass over the state; time linear in T per sequence).
+ */
+gdr_status gdr_gdn2_fwd(const void *q, const void *k, const void *v,
+                        const float *log_alpha, const float *erase, const float *write,
+                        const float *S0, void *o, float *S_T,
+                        int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                        gdr_dtype io, gdr_gate gate, hipStream_t stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char *gdr_status_string(gdr_status s);
 

@@ -223,6 +223,45 @@ gdr_status gdr_decode_multi(const void* q, const void* k, const void* v, const f
     return GDR_OK;
 }
 
+gdr_status gdr_gdn2_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
+                        const float* erase, const float* write, const float* S0, void* o, float* S_T,
+                        int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, gdr_dtype io,
+                        gdr_gate gate, hipStream_t stream) {
+    g_last_error[0] = 0;
+    gdr_status s = check_common(B, H, dk, dv, io, gate);
+    if (s != GDR_OK) return s;
+    if (T < 0) return fail(GDR_ERR_INVALID_ARG, "T must be >= 0 (T=%lld)", (long long)T);
+    const int64_t ntok = mul({B, T, H});
+    if (ntok < 0 || mul({ntok, dk}) < 0 || mul({B, H, dv, dk}) < 0 || mul({B, H, dv / 16}) > INT32_MAX)
+        return fail(GDR_ERR_UNSUPPORTED, "tensor sizes overflow");
+    if (T > 0 && (!q || !k || !v || !log_alpha || !erase || !write || !o))
+        return fail(GDR_ERR_INVALID_ARG, "q, k, v, log_alpha, erase, write and o must be non-NULL");
+    const size_t es = io == GDR_BF16 ? 2 : 4;
+    const Range rs[] = {
+        rng("q", q, ntok * dk, es),          rng("k", k, ntok * dk, es),
+        rng("v", v, ntok * dv, es),
+        rng("log_alpha", log_alpha, gate == GDR_GATE_CHANNEL ? ntok * dk : ntok, 4),
+        rng("erase", erase, ntok * dk, 4),   rng("write", write, ntok * dv, 4),
+        rng("S0", S0, B * H * dv * dk, 4),   rng("o", o, ntok * dv, es),
+        rng("S_T", S_T, B * H * dv * dk, 4),
+    };
+    s = check_ptrs(rs, 9, 7);
+    if (s != GDR_OK) return s;
+    if (T == 0) {   // no tokens: S_T = S0 (zeros when S0 is NULL), same as gdr_chunk_fwd
+        if (!S_T) return GDR_OK;
+        gdr::ChunkArgs c{q, k, v, log_alpha, nullptr, S0, o, S_T, B, 0, H, dk, dv, 64,
+                         io == GDR_BF16, gate == GDR_GATE_CHANNEL, nullptr, stream};
+        const hipError_t err = gdr::chunk_fwd_launch(c);
+        if (err != hipSuccess) return fail(GDR_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(err));
+        return GDR_OK;
+    }
+    gdr::Gdn2Args a{q, k, v, log_alpha, erase, write, S0, o, S_T, B, T, H, dk, dv,
+                    io == GDR_BF16, gate == GDR_GATE_CHANNEL, stream};
+    const hipError_t err = gdr::gdn2_fwd_launch(a);
+    if (err != hipSuccess) return fail(GDR_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(err));
+    return GDR_OK;
+}
+
 gdr_status gdr_fg2_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t dk,
                                             int64_t dv, int64_t chunk, gdr_dtype io, gdr_gate gate,
                                             size_t* bytes) {

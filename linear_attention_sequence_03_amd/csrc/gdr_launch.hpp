@@ -63,4 +63,16 @@ size_t fg2_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t 
                            bool bf16, bool channel);
 hipError_t fg2_chunk_fwd_launch(const ChunkArgs& a, const float* beta_k, const float* beta_v);
 
+// Decoupled erase / write gates (token-sequential scan).
+struct Gdn2Args {
+    const void *q, *k, *v;
+    const float *log_alpha, *erase, *write, *S0;
+    void* o;
+    float* S_T;
+    int64_t B, T, H, dk, dv;
+    bool bf16, channel;
+    hipStream_t stream;
+};
+hipError_t gdn2_fwd_launch(const Gdn2Args& a);
+
 }  // namespace gdr

@@ -22,6 +22,7 @@ GDR_GATE_SCALAR, GDR_GATE_CHANNEL = 0, 1
 # Every symbol include/gdr.h declares.
 EXPORTS = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_decode_step", "gdr_decode_multi",
            "gdr_fg2_chunk_fwd_workspace_size", "gdr_fg2_chunk_fwd", "gdr_fg2_decode_step",
+           "gdr_gdn2_fwd",
            "gdr_status_string", "gdr_last_error")
 
 _lib = None
@@ -58,6 +59,9 @@ def load_library(path: Optional[str] = None):
     lib.gdr_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp,
                                     i64, i64, i64, i64, f, f, vp]
     lib.gdr_decode_step.restype = f
+    lib.gdr_gdn2_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                 i64, i64, i64, i64, i64, f, f, vp]
+    lib.gdr_gdn2_fwd.restype = f
     lib.gdr_decode_multi.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                      i64, i64, i64, i64, i64, f, f, vp]
     lib.gdr_decode_multi.restype = f
@@ -319,3 +323,38 @@ def gdr_decode_multi(q, k, v, log_alpha, beta, S, S_out=None, accepted=None, o=N
     if st != GDR_OK:
         _raise(st)
     return o, S_out
+
+
+def gdr_gdn2_fwd(q, k, v, log_alpha, erase, write, S0=None, o=None, S_T=None,
+                 want_state: bool = True, stream=None) -> Tuple:
+    """Whole-sequence forward with decoupled erase / write gates (Gated
+    DeltaNet-2).  erase: [B,T,H,dk] fp32; write: [B,T,H,dv] fp32; other
+    arguments as in :func:`gdr_chunk_fwd`.  Returns (o, S_T)."""
+    import torch
+    dev = q.device
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    io = _io_code(q.dtype)
+    gate = GDR_GATE_CHANNEL if log_alpha.dim() == 4 else GDR_GATE_SCALAR
+    _need("q", q, q.dtype, (B, T, H, dk), dev)
+    _need("k", k, q.dtype, (B, T, H, dk), dev)
+    _need("v", v, q.dtype, (B, T, H, dv), dev)
+    _need("log_alpha", log_alpha, torch.float32,
+          (B, T, H, dk) if gate == GDR_GATE_CHANNEL else (B, T, H), dev)
+    _need("erase", erase, torch.float32, (B, T, H, dk), dev)
+    _need("write", write, torch.float32, (B, T, H, dv), dev)
+    if S0 is not None:
+        _need("S0", S0, torch.float32, (B, H, dv, dk), dev)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
+    _need("o", o, q.dtype, (B, T, H, dv), dev)
+    if S_T is None and want_state:
+        S_T = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+    if S_T is not None:
+        _need("S_T", S_T, torch.float32, (B, H, dv, dk), dev)
+    st = load_library().gdr_gdn2_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(erase), _ptr(write), _ptr(S0), _ptr(o),
+        _ptr(S_T), B, T, H, dk, dv, io, gate, _stream(dev, stream))
+    if st != GDR_OK:
+        _raise(st)
+    return o, S_T

@@ -127,3 +127,13 @@ def write_rates(shape_k, dv=None, seed=0):
     if dv is not None:
         bv = (1.0 / (1.0 + np.exp(-rng.standard_normal(tuple(shape_k[:-1]) + (dv,))))).astype(np.float32)
     return bk, bv
+
+
+def gdn2_gates(B, T, H, dk, dv, seed=0):
+    """Decoupled erase / write gates for the Gated DeltaNet-2 call:
+    b = sigmoid(N(0,1)) of shape [B,T,H,dk], w = sigmoid(N(0,1)) of shape
+    [B,T,H,dv], from their own seeded stream."""
+    rng = np.random.Generator(np.random.PCG64(seed + 7000))
+    b = (1.0 / (1.0 + np.exp(-rng.standard_normal((B, T, H, dk))))).astype(np.float32)
+    w = (1.0 / (1.0 + np.exp(-rng.standard_normal((B, T, H, dv))))).astype(np.float32)
+    return b, w

@@ -198,3 +198,22 @@ def test_decode_multi_rejects(lib, kw, code):
 
 def test_decode_multi_nothing_requested_is_ok(lib):
     assert _multi(lib, so=None, o=None) == 0
+
+
+# ----- decoupled erase / write gates -----------------------------------------
+def _gdn2(lib, q=0, k=1, v=2, la=3, eb=4, ww=5, s0=None, o=6, st=7, B=1, T=64, H=2, dk=64, dv=64,
+          io=0, gate=0):
+    p = lambda i: None if i is None else (_addr(i) if isinstance(i, int) else i)  # noqa: E731
+    return lib.gdr_gdn2_fwd(p(q), p(k), p(v), p(la), p(eb), p(ww), p(s0), p(o), p(st),
+                            B, T, H, dk, dv, io, gate, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(eb=None), 1), (dict(ww=None), 1), (dict(o=None), 1), (dict(T=-1), 1),
+    (dict(dk=64, dv=128), 2), (dict(io=5), 1),
+    (dict(ww=ctypes.c_void_p(BASE + 5 * MB + 8)), 1),     # misaligned
+    (dict(o=ctypes.c_void_p(BASE + 4 * MB + 1024)), 1),   # o inside erase
+])
+def test_gdn2_rejects(lib, kw, code):
+    assert _gdn2(lib, **kw) == code
+    assert lib.gdr_last_error()

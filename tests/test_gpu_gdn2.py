@@ -1,0 +1,92 @@
+"""GPU parity of gdr_gdn2_fwd (decoupled erase / write gates, Gated DeltaNet-2
+reading) against the oracle, through the C ABI.  The state stays fp32 and is
+updated token by token, so fp32 inputs are held to 1e-4 and bf16 inputs to
+2e-2 like every other call."""
+import numpy as np
+import pytest
+
+from linear_attention_sequence_03_amd import synth
+from gpu_helpers import dev, host, io_dtype, rel_err, torch_mod
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def _run(inp, io, S0=True):
+    from linear_attention_sequence_03_amd import gdr_gdn2_fwd
+    torch = torch_mod()
+    dt = io_dtype(io)
+    o, st = gdr_gdn2_fwd(dev(inp["q"], dt), dev(inp["k"], dt), dev(inp["v"], dt),
+                         dev(inp["log_alpha"]), dev(inp["erase"]), dev(inp["write"]),
+                         dev(inp["S0"]) if (S0 and inp["S0"] is not None) else None)
+    torch.cuda.synchronize()
+    return o, st
+
+
+def _inputs(B, T, H, d, gate, io, seed, s0_std=0.1):
+    inp = synth.chunk_inputs(B, T, H, d, d, gate, io, seed=seed, s0_std=s0_std)
+    inp["erase"], inp["write"] = synth.gdn2_gates(B, T, H, d, d, seed=seed)
+    return inp
+
+
+@pytest.mark.parametrize("T", [1, 37, 200])
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+@pytest.mark.parametrize("io,d", [("f32", 64), ("f32", 128), ("bf16", 128)])
+def test_gdn2_parity(io, d, gate, T):
+    inp = _inputs(2, T, 3, d, gate, io, seed=200 + T + d)
+    o, st = _run(inp, io)
+    o_ref, st_ref = oracle.gdn2_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"],
+                                          inp["erase"], inp["write"], inp["S0"])
+    eo, es = rel_err(host(o), o_ref), rel_err(host(st), st_ref)
+    print("io=%s d=%d gate=%s T=%d err_o=%.3g err_S=%.3g" % (io, d, gate, T, eo, es))
+    assert eo <= TOL[io] and es <= TOL[io], (eo, es)
+
+
+def test_gdn2_tied_gates_match_kda_call():
+    """b = w = beta (one number per token): the Gated DeltaNet-2 call equals the
+    KDA call (two different GPU paths), fp32."""
+    from linear_attention_sequence_03_amd import gdr_chunk_fwd
+    inp = _inputs(2, 150, 2, 64, "channel", "f32", seed=230)
+    inp["erase"] = np.repeat(inp["beta"][..., None], 64, axis=-1).astype(np.float32)
+    inp["write"] = np.repeat(inp["beta"][..., None], 64, axis=-1).astype(np.float32)
+    o1, s1 = _run(inp, "f32")
+    o2, s2 = gdr_chunk_fwd(dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["log_alpha"]),
+                           dev(inp["beta"]), dev(inp["S0"]), chunk=32)
+    assert rel_err(host(o1), host(o2)) <= 1e-5
+    assert rel_err(host(s1), host(s2)) <= 1e-5
+
+
+def test_gdn2_no_start_state_and_empty():
+    from linear_attention_sequence_03_amd import gdr_gdn2_fwd
+    torch = torch_mod()
+    inp = _inputs(1, 20, 2, 64, "scalar", "bf16", seed=231, s0_std=None)
+    o, st = _run(inp, "bf16", S0=False)
+    o_ref, st_ref = oracle.gdn2_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"],
+                                          inp["erase"], inp["write"], None)
+    assert rel_err(host(o), o_ref) <= TOL["bf16"]
+    assert rel_err(host(st), st_ref) <= TOL["bf16"]
+    e = _inputs(1, 0, 2, 64, "scalar", "f32", seed=232)
+    s0 = dev(e["S0"])
+    _, st0 = gdr_gdn2_fwd(dev(e["q"]), dev(e["k"]), dev(e["v"]), dev(e["log_alpha"]),
+                          dev(e["erase"]), dev(e["write"]), s0)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(st0), e["S0"])
+
+
+def test_gdn2_full_size_sampled():
+    """The KDA workload's shape (B=2, H=32, T=8192, d=128, bf16, channel decay)
+    with both gates; sampled (b,h) pairs against the oracle."""
+    w = synth.WORKLOADS[2]
+    inp = synth.workload_inputs(w)
+    inp["erase"], inp["write"] = synth.gdn2_gates(w.B, w.T, w.H, w.d, w.d, seed=w.seed)
+    o, st = _run(inp, "bf16")
+    o, st = host(o), host(st)
+    for b, h in [(0, 3), (1, 30)]:
+        sl = lambda a: None if a is None else a[b:b + 1, :, h:h + 1]  # noqa: E731
+        o_ref, st_ref = oracle.gdn2_chunk_fwd(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]),
+                                              sl(inp["log_alpha"]), sl(inp["erase"]),
+                                              sl(inp["write"]), None)
+        assert rel_err(o[b, :, h], o_ref[0, :, 0]) <= TOL["bf16"]
+        assert rel_err(st[b, h], st_ref[0, 0]) <= TOL["bf16"]
