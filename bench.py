@@ -11,6 +11,8 @@ call over the whole batch.  The same line also carries the decode step
                                      # (2: KDA B=2,H=32,T=8192; 3: GDN B=1,H=32,T=32768 with S0)
     python bench.py --workload 2 --fg2   # channel-wise write rates (FG2-GDN+) on that
                                          # shape, with the overhead over the KDA call
+    python bench.py --workload 2 --gdn2  # decoupled erase / write gates (Gated
+                                         # DeltaNet-2) on that shape
     python bench.py --traffic        # HBM bytes per call from rocprofv3 counters
 
 Prints ONE JSON line.  Only one GPU is used; --gpus above 1 exits.
@@ -48,8 +50,10 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 def prefill_algorithmic(B, T, H, d, C, io_bytes=2, s0=False, channel=False, fg2=False):
     """Bytes: q,k,v read and o written once (io dtype), log_alpha (fp32, one per
     head-token, or d_k of them for the channel gate) and beta (fp32) read once,
-    S_T written (and S0 read) once.  FLOPs: 6d^2 + 3Cd + C^2 per head-token (the
-    FG2-GDN page's per-head kernel accounting, section 3.6)."""
+    S_T written (and S0 read) once.  With ``fg2`` the scalar beta is replaced by
+    two fp32 d-vectors per head-token (FG2's key and value rates, or Gated
+    DeltaNet-2's erase and write gates).  FLOPs: 6d^2 + 3Cd + C^2 per head-token
+    (the FG2-GDN page's per-head kernel accounting, section 3.6)."""
     ht = B * T * H
     per_ht = 4 * d * io_bytes + (4 * d if channel else 4) + (2 * 4 * d if fg2 else 4)
     state = B * H * d * d * 4
@@ -159,6 +163,8 @@ def main():
                     help="prefill workload to time (1 is the headline)")
     ap.add_argument("--fg2", action="store_true",
                     help="time gdr_fg2_chunk_fwd with key and value rates (FG2-GDN+) instead")
+    ap.add_argument("--gdn2", action="store_true",
+                    help="time gdr_gdn2_fwd (decoupled erase / write gates) instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", action="store_true",
                     help="measure HBM bytes per call with rocprofv3 and write a summary")
@@ -193,7 +199,7 @@ def main():
 
     import torch
     from linear_attention_sequence_03_amd import (gdr_chunk_fwd, gdr_decode_step, gdr_fg2_chunk_fwd,
-                                                  synth)
+                                                  gdr_gdn2_fwd, synth)
     from linear_attention_sequence_03_amd.gdr import (GDR_BF16, GDR_GATE_CHANNEL, GDR_GATE_SCALAR,
                                                       gdr_chunk_fwd_workspace_size,
                                                       gdr_fg2_chunk_fwd_workspace_size)
@@ -229,6 +235,12 @@ def main():
 
         def step():
             gdr_fg2_chunk_fwd(q, k, v, la, bk, bv, S0, chunk=C, o=o, S_T=st, workspace=ws2)
+    elif args.gdn2:
+        eb, ww = synth.gdn2_gates(B, T, H, d, d, seed=w.seed)
+        eb, ww = torch.from_numpy(eb).to(devn), torch.from_numpy(ww).to(devn)
+
+        def step():
+            gdr_gdn2_fwd(q, k, v, la, eb, ww, S0, o=o, S_T=st)
 
     for _ in range(args.warmup):
         step()
@@ -265,7 +277,7 @@ def main():
     del flush
 
     nbytes, flops = prefill_algorithmic(B, T, H, d, C, s0=S0 is not None, channel=channel,
-                                        fg2=args.fg2)
+                                        fg2=args.fg2 or args.gdn2)
     fg2_info = None
     if args.fg2:
         # the same call without rates, timed the same way, for the overhead
@@ -367,14 +379,16 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded; q,k unit-norm N(0,1), v N(0,1), beta sigmoid(N(0,1)), "
                 "log_alpha U(-0.1,-0.001)%s)" % (", S0 N(0,0.02^2)" if S0 is not None else ""),
-        "config": {"workload": w.name + ("_fg2plus" if args.fg2 else ""),
-                   "call": "gdr_fg2_chunk_fwd" if args.fg2 else "gdr_chunk_fwd",
+        "config": {"workload": w.name + ("_fg2plus" if args.fg2 else "_gdn2" if args.gdn2 else ""),
+                   "call": ("gdr_fg2_chunk_fwd" if args.fg2 else "gdr_gdn2_fwd" if args.gdn2
+                            else "gdr_chunk_fwd"),
                    "gate": "channel" if channel else "scalar",
                    "B": B, "T": T, "H": H, "d_k": d, "d_v": d, "chunk": C,
                    "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm",
-                     "kernel": ("gdr_fg2_chunk_fwd (fg2_scale prologue + " if args.fg2 else "")
-                     + ROOFLINE_KERNEL[args.workload] + (")" if args.fg2 else ""),
+                     "kernel": ("gdr_gdn2_fwd (gdn2_scan, token-sequential)" if args.gdn2 else
+                                ("gdr_fg2_chunk_fwd (fg2_scale prologue + " if args.fg2 else "")
+                                + ROOFLINE_KERNEL[args.workload] + (")" if args.fg2 else "")),
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": nbytes,
@@ -396,7 +410,7 @@ def main():
     }
     if fg2_info is not None:
         out["fg2"] = fg2_info
-    if not args.no_cpu_baseline and not args.fg2:
+    if not args.no_cpu_baseline and not (args.fg2 or args.gdn2):
         import oracle.gdr_oracle as og
         threads = min(16, og.default_threads())
         reps, secs = cpu_baseline(inp, threads, S0=inp.get("S0"))
