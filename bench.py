@@ -124,6 +124,41 @@ def traffic_probe():
     torch.cuda.synchronize()
 
 
+def copy_ceiling():
+    """A plain 16-byte device copy (libgdr_calib.so) and torch's copy at a few
+    sizes: bytes read + written per second, the practical ceiling for a
+    read-modify-write stream such as the decode step."""
+    import ctypes
+    import torch
+    dev = torch.device("cuda:0")
+    calib = ctypes.CDLL(os.path.join(ROOT, "linear_attention_sequence_03_amd", "libgdr_calib.so"))
+    calib.gdr_calib_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                     ctypes.c_void_p]
+    res = {}
+    for mib in (256, 512, 1024):
+        n = mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        for name, fn in (("calib", lambda: calib.gdr_calib_copy(src.data_ptr(), dst.data_ptr(), n,
+                                                                  stream)),
+                         ("torch", lambda: dst.copy_(src))):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(10)]
+            for a, b in ev:
+                a.record()
+                fn()
+                b.record()
+            torch.cuda.synchronize()
+            t = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e-3
+            res["%s_%dMiB_TBs" % (name, mib)] = 2 * n / t / 1e12
+        del src, dst
+    print(json.dumps(res))
+
+
 def measure_traffic(outdir):
     """Two rocprofv3 --pmc passes over traffic_probe(); returns bytes per call."""
     res = {}
@@ -169,10 +204,15 @@ def main():
     ap.add_argument("--traffic", action="store_true",
                     help="measure HBM bytes per call with rocprofv3 and write a summary")
     ap.add_argument("--traffic-probe", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--copy", action="store_true",
+                    help="time a plain device copy (the practical HBM read+write ceiling)")
     ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out"))
     args = ap.parse_args()
     if args.traffic_probe:
         traffic_probe()
+        return
+    if args.copy:
+        copy_ceiling()
         return
     if args.traffic:
         os.makedirs(args.out, exist_ok=True)
