@@ -13,5 +13,6 @@ two share no code.
   explicit per-token transition matrices; used to pin the fp64 oracle on tiny
   shapes.
 """
-from .gdr_oracle import (build, chunk_fwd, decode_multi, decode_step, fg2_chunk_fwd,  # noqa: F401
-                         fg2_decode_step, gdn2_chunk_fwd, library_path, load)
+from .gdr_oracle import (build, chunk_fwd, chunk_fwd_prologue, decode_multi,  # noqa: F401
+                         decode_step, decode_step_prologue, fg2_chunk_fwd, fg2_decode_step,
+                         gdn2_chunk_fwd, library_path, load, prologue_inputs)

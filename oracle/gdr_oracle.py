@@ -233,3 +233,35 @@ def gdn2_chunk_fwd(q, k, v, log_alpha, erase, write, S0=None, threads=None, lib=
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
     return o, st
+
+
+PROLOGUE_L2NORM_QK = 1
+PROLOGUE_BETA_SIGMOID = 2
+PROLOGUE_EPS = 1e-6
+
+
+def prologue_inputs(q, k, beta, flags, eps=PROLOGUE_EPS):
+    """The gate prologue ("FG2-GDN" page, section 3.5: queries and keys are
+    L2-normalised; the write rate is the sigmoid of its projection), applied to
+    raw inputs in fp64: q / sqrt(sum q^2 + eps) and likewise k per token and
+    head (flag 1), beta = 1 / (1 + e^{-x}) (flag 2).  eps = 1e-6 is this build's
+    choice (the page gives none); it only matters for near-zero rows."""
+    q, k, be = (_f64(a) for a in (q, k, beta))
+    if flags & PROLOGUE_L2NORM_QK:
+        q = q / np.sqrt(np.sum(q * q, axis=-1, keepdims=True) + eps)
+        k = k / np.sqrt(np.sum(k * k, axis=-1, keepdims=True) + eps)
+    if flags & PROLOGUE_BETA_SIGMOID:
+        be = 1.0 / (1.0 + np.exp(-be))
+    return q, k, be
+
+
+def chunk_fwd_prologue(q, k, v, log_alpha, beta, S0=None, flags=0, threads=None, lib=None):
+    """The whole-sequence forward on raw q, k and beta logits: the prologue
+    above, then the recurrence (a composition, no arithmetic of its own)."""
+    q2, k2, be2 = prologue_inputs(q, k, beta, flags)
+    return chunk_fwd(q2, k2, v, log_alpha, be2, S0, threads=threads, lib=lib)
+
+
+def decode_step_prologue(q, k, v, log_alpha, beta, S, flags=0, lib=None):
+    q2, k2, be2 = prologue_inputs(q, k, beta, flags)
+    return decode_step(q2, k2, v, log_alpha, be2, S, lib=lib)
