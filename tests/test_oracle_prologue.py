@@ -15,8 +15,10 @@ def _rng(seed):
 
 def _raw(seed, B=2, T=19, H=2, dk=6, dv=5, channel=True):
     r = _rng(seed)
-    q = r.standard_normal((B, T, H, dk)) * r.uniform(0.2, 5.0, (B, T, H, 1))
-    k = r.standard_normal((B, T, H, dk)) * r.uniform(0.2, 5.0, (B, T, H, 1))
+    # raw rows of norm roughly 2..20, where the epsilon of the normalisation
+    # changes a row by less than 1e-7 relative
+    q = r.standard_normal((B, T, H, dk)) * r.uniform(1.0, 8.0, (B, T, H, 1))
+    k = r.standard_normal((B, T, H, dk)) * r.uniform(1.0, 8.0, (B, T, H, 1))
     v = r.standard_normal((B, T, H, dv))
     la = r.uniform(-0.5, -0.001, (B, T, H, dk) if channel else (B, T, H))
     x = r.standard_normal((B, T, H)) * 2
@@ -37,8 +39,9 @@ def test_prologue_sigmoid_matches_scipy():
     q, k, v, la, x, S0 = _raw(2)
     o1, s1 = oracle.chunk_fwd_prologue(q, k, v, la, x, S0, flags=oracle.gdr_oracle.PROLOGUE_BETA_SIGMOID)
     o2, s2 = oracle.chunk_fwd(q, k, v, la, expit(x), S0)
-    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-13)
-    np.testing.assert_allclose(s1, s2, rtol=0, atol=1e-13)
+    # raw keys are not unit-norm here, so the state grows large: compare relatively
+    np.testing.assert_allclose(o1, o2, rtol=1e-12, atol=0)
+    np.testing.assert_allclose(s1, s2, rtol=1e-12, atol=0)
 
 
 @pytest.mark.parametrize("channel", [False, True])
@@ -60,8 +63,9 @@ def test_prologue_norm_matches_hand_normalised_inputs():
     q, k, v, la, x, S0 = _raw(4)
     qn = q / np.linalg.norm(q, axis=-1, keepdims=True)
     kn = k / np.linalg.norm(k, axis=-1, keepdims=True)
-    o1, s1 = oracle.chunk_fwd_prologue(q, k, v, la, x, S0, flags=oracle.gdr_oracle.PROLOGUE_L2NORM_QK)
-    o2, s2 = oracle.chunk_fwd(qn, kn, v, la, x, S0)
+    be = expit(x)
+    o1, s1 = oracle.chunk_fwd_prologue(q, k, v, la, be, S0, flags=oracle.gdr_oracle.PROLOGUE_L2NORM_QK)
+    o2, s2 = oracle.chunk_fwd(qn, kn, v, la, be, S0)
     np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-6)
     np.testing.assert_allclose(s1, s2, rtol=0, atol=1e-6)
     q2, k2, _ = oracle.prologue_inputs(q, k, x, oracle.gdr_oracle.PROLOGUE_L2NORM_QK)
