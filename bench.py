@@ -13,6 +13,9 @@ call over the whole batch.  The same line also carries the decode step
                                          # shape, with the overhead over the KDA call
     python bench.py --workload 2 --gdn2  # decoupled erase / write gates (Gated
                                          # DeltaNet-2) on that shape
+    python bench.py --prologue           # raw q, k and beta logits: the gate prologue
+                                         # fused into the kernels, against torch
+                                         # normalising first
     python bench.py --traffic        # HBM bytes per call from rocprofv3 counters
 
 Prints ONE JSON line.  Only one GPU is used; --gpus above 1 exits.
@@ -200,6 +203,8 @@ def main():
                     help="time gdr_fg2_chunk_fwd with key and value rates (FG2-GDN+) instead")
     ap.add_argument("--gdn2", action="store_true",
                     help="time gdr_gdn2_fwd (decoupled erase / write gates) instead")
+    ap.add_argument("--prologue", action="store_true",
+                    help="raw q, k and beta logits: time the fused gate prologue instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", action="store_true",
                     help="measure HBM bytes per call with rocprofv3 and write a summary")
@@ -275,6 +280,23 @@ def main():
 
         def step():
             gdr_fg2_chunk_fwd(q, k, v, la, bk, bv, S0, chunk=C, o=o, S_T=st, workspace=ws2)
+    elif args.prologue:
+        from linear_attention_sequence_03_amd.gdr import (GDR_PROLOGUE_BETA_SIGMOID,
+                                                          GDR_PROLOGUE_L2NORM_QK)
+        rin = synth.raw_prologue_inputs(inp, "bf16", seed=w.seed)
+        rq = torch.from_numpy(rin["q"]).to(devn).to(bf)
+        rk = torch.from_numpy(rin["k"]).to(devn).to(bf)
+        rbe = torch.from_numpy(rin["beta"]).to(devn)
+        flags = GDR_PROLOGUE_L2NORM_QK | GDR_PROLOGUE_BETA_SIGMOID
+
+        def step():
+            gdr_chunk_fwd(rq, rk, v, la, rbe, S0, chunk=C, o=o, S_T=st, workspace=ws, prologue=flags)
+
+        def torch_then_plain():
+            # the same result with the prologue done by torch before the call
+            qn = (rq.float() * torch.rsqrt((rq.float() ** 2).sum(-1, keepdim=True) + 1e-6)).to(bf)
+            kn = (rk.float() * torch.rsqrt((rk.float() ** 2).sum(-1, keepdim=True) + 1e-6)).to(bf)
+            gdr_chunk_fwd(qn, kn, v, la, torch.sigmoid(rbe), S0, chunk=C, o=o, S_T=st, workspace=ws)
     elif args.gdn2:
         eb, ww = synth.gdn2_gates(B, T, H, d, d, seed=w.seed)
         eb, ww = torch.from_numpy(eb).to(devn), torch.from_numpy(ww).to(devn)
@@ -319,6 +341,23 @@ def main():
     nbytes, flops = prefill_algorithmic(B, T, H, d, C, s0=S0 is not None, channel=channel,
                                         fg2=args.fg2 or args.gdn2)
     fg2_info = None
+    pro_info = None
+    if args.prologue:
+        for _ in range(3):
+            torch_then_plain()
+        ev4 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for a, b in ev4:
+            a.record(stream)
+            torch_then_plain()
+            b.record(stream)
+        torch.cuda.synchronize()
+        tms = float(np.mean([a.elapsed_time(b) for a, b in ev4]))
+        pro_info = {"call": "gdr_chunk_fwd_prologue (L2 norm of q, k + sigmoid of beta, fused)",
+                    "launch_ms_mean": float(np.mean(warm)),
+                    "unfused_call": "torch normalisation + sigmoid, then gdr_chunk_fwd",
+                    "unfused_ms_mean": tms,
+                    "speedup": tms / float(np.mean(warm))}
     if args.fg2:
         # the same call without rates, timed the same way, for the overhead
         for _ in range(3):
@@ -419,7 +458,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded; q,k unit-norm N(0,1), v N(0,1), beta sigmoid(N(0,1)), "
                 "log_alpha U(-0.1,-0.001)%s)" % (", S0 N(0,0.02^2)" if S0 is not None else ""),
-        "config": {"workload": w.name + ("_fg2plus" if args.fg2 else "_gdn2" if args.gdn2 else ""),
+        "config": {"workload": w.name + ("_fg2plus" if args.fg2 else "_gdn2" if args.gdn2
+                                         else "_raw_prologue" if args.prologue else ""),
                    "call": ("gdr_fg2_chunk_fwd" if args.fg2 else "gdr_gdn2_fwd" if args.gdn2
                             else "gdr_chunk_fwd"),
                    "gate": "channel" if channel else "scalar",
@@ -450,7 +490,9 @@ def main():
     }
     if fg2_info is not None:
         out["fg2"] = fg2_info
-    if not args.no_cpu_baseline and not (args.fg2 or args.gdn2):
+    if pro_info is not None:
+        out["prologue"] = pro_info
+    if not args.no_cpu_baseline and not (args.fg2 or args.gdn2 or args.prologue):
         import oracle.gdr_oracle as og
         threads = min(16, og.default_threads())
         reps, secs = cpu_baseline(inp, threads, S0=inp.get("S0"))

@@ -115,6 +115,38 @@ gdr_status gdr_decode_step(const void *q, const void *k, const void *v,
                            gdr_dtype io, gdr_gate gate, hipStream_t stream);
 
 /*
+ * The gate prologue, fused into the kernels' loads ("FG2-GDN" page, section
+ * 3.5: queries and keys are L2-normalised, and the write rate is the sigmoid of
+ * its projection).  `flags` is a bitwise OR of:
+ *   GDR_PROLOGUE_L2NORM_QK     q and k are normalised per token and head,
+ *                              x / sqrt(sum x^2 + 1e-6), inside the kernel
+ *   GDR_PROLOGUE_BETA_SIGMOID  beta holds logits; the kernel uses 1 / (1 + e^-beta)
+ * The decay is taken as log_alpha, as in the other calls (the page names a
+ * gated-decay transform without its formula).  Arguments are otherwise those of
+ * gdr_chunk_fwd / gdr_decode_step, with q, k and beta holding the raw values.
+ * The prefill prologue is fused into the bf16 paths: chunk 64 with the scalar
+ * gate (the single-kernel path) and every chunk size with the channel gate;
+ * other requests return GDR_ERR_UNSUPPORTED.  The decode step takes it for
+ * every dtype and gate.  flags = 0 is exactly gdr_chunk_fwd / gdr_decode_step.
+ */
+enum { GDR_PROLOGUE_L2NORM_QK = 1, GDR_PROLOGUE_BETA_SIGMOID = 2 };
+
+gdr_status gdr_chunk_fwd_prologue(const void *q, const void *k, const void *v,
+                                  const float *log_alpha, const float *beta, const float *S0,
+                                  void *o, float *S_T,
+                                  int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                  int64_t chunk, gdr_dtype io, gdr_gate gate,
+                                  void *workspace, size_t workspace_bytes, unsigned flags,
+                                  hipStream_t stream);
+
+gdr_status gdr_decode_step_prologue(const void *q, const void *k, const void *v,
+                                    const float *log_alpha, const float *beta,
+                                    const float *S_in, float *S_out, void *o,
+                                    int64_t B, int64_t H, int64_t dk, int64_t dv,
+                                    gdr_dtype io, gdr_gate gate, unsigned flags,
+                                    hipStream_t stream);
+
+/*
  * Several tokens per sequence in one pass over the state: verifying a run of
  * draft tokens in speculative decoding, then keeping the state of the accepted
  * prefix (the pages name both the per-token rollback of the recurrent state

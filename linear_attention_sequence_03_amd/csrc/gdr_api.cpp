@@ -107,11 +107,15 @@ gdr_status gdr_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t
     return GDR_OK;
 }
 
-gdr_status gdr_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
-                         const float* beta, const float* S0, void* o, float* S_T, int64_t B,
-                         int64_t T, int64_t H, int64_t dk, int64_t dv, int64_t chunk, gdr_dtype io,
-                         gdr_gate gate, void* workspace, size_t workspace_bytes,
-                         hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+gdr_status chunk_fwd_impl(const void* q, const void* k, const void* v, const float* log_alpha,
+                                 const float* beta, const float* S0, void* o, float* S_T, int64_t B,
+                                 int64_t T, int64_t H, int64_t dk, int64_t dv, int64_t chunk,
+                                 gdr_dtype io, gdr_gate gate, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream, unsigned prologue) {
     size_t need = 0;
     gdr_status s = gdr_chunk_fwd_workspace_size(B, T, H, dk, dv, chunk, io, gate, &need);
     if (s != GDR_OK) return s;
@@ -135,8 +139,12 @@ gdr_status gdr_chunk_fwd(const void* q, const void* k, const void* v, const floa
     };
     s = check_ptrs(rs, 9, 6);
     if (s != GDR_OK) return s;
+    if (prologue && !gdr::prologue_supported(chunk, io == GDR_BF16, gate == GDR_GATE_CHANNEL))
+        return fail(GDR_ERR_UNSUPPORTED,
+                    "the gate prologue is fused into the bf16 calls with chunk 64 (scalar gate) or the "
+                    "channel gate only");
     gdr::ChunkArgs a{q, k, v, log_alpha, beta, S0, o, S_T, B, T, H, dk, dv, chunk,
-                     io == GDR_BF16, gate == GDR_GATE_CHANNEL, workspace, stream};
+                     io == GDR_BF16, gate == GDR_GATE_CHANNEL, workspace, stream, prologue};
     const hipError_t err = gdr::chunk_fwd_launch(a);
     if (err == hipErrorNotSupported)
         return fail(GDR_ERR_UNSUPPORTED, "this gate/dtype combination is not available");
@@ -144,10 +152,48 @@ gdr_status gdr_chunk_fwd(const void* q, const void* k, const void* v, const floa
     return GDR_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+gdr_status gdr_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
+                         const float* beta, const float* S0, void* o, float* S_T, int64_t B,
+                         int64_t T, int64_t H, int64_t dk, int64_t dv, int64_t chunk, gdr_dtype io,
+                         gdr_gate gate, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+    return chunk_fwd_impl(q, k, v, log_alpha, beta, S0, o, S_T, B, T, H, dk, dv, chunk, io, gate,
+                          workspace, workspace_bytes, stream, 0);
+}
+
+gdr_status gdr_chunk_fwd_prologue(const void* q, const void* k, const void* v,
+                                  const float* log_alpha, const float* beta, const float* S0,
+                                  void* o, float* S_T, int64_t B, int64_t T, int64_t H, int64_t dk,
+                                  int64_t dv, int64_t chunk, gdr_dtype io, gdr_gate gate,
+                                  void* workspace, size_t workspace_bytes, unsigned flags,
+                                  hipStream_t stream) {
+    g_last_error[0] = 0;
+    if (flags & ~3u) return fail(GDR_ERR_INVALID_ARG, "unknown prologue flags 0x%x", flags);
+    return chunk_fwd_impl(q, k, v, log_alpha, beta, S0, o, S_T, B, T, H, dk, dv, chunk, io, gate,
+                          workspace, workspace_bytes, stream, flags);
+}
+
+gdr_status gdr_decode_step_prologue(const void* q, const void* k, const void* v,
+                                    const float* log_alpha, const float* beta, const float* S_in,
+                                    float* S_out, void* o, int64_t B, int64_t H, int64_t dk, int64_t dv,
+                                    gdr_dtype io, gdr_gate gate, unsigned flags, hipStream_t stream);
+
 gdr_status gdr_decode_step(const void* q, const void* k, const void* v, const float* log_alpha,
                            const float* beta, const float* S_in, float* S_out, void* o, int64_t B,
                            int64_t H, int64_t dk, int64_t dv, gdr_dtype io, gdr_gate gate,
                            hipStream_t stream) {
+    return gdr_decode_step_prologue(q, k, v, log_alpha, beta, S_in, S_out, o, B, H, dk, dv, io, gate,
+                                    0, stream);
+}
+
+gdr_status gdr_decode_step_prologue(const void* q, const void* k, const void* v,
+                                    const float* log_alpha, const float* beta, const float* S_in,
+                                    float* S_out, void* o, int64_t B, int64_t H, int64_t dk, int64_t dv,
+                                    gdr_dtype io, gdr_gate gate, unsigned flags, hipStream_t stream) {
     g_last_error[0] = 0;
     gdr_status s = check_common(B, H, dk, dv, io, gate);
     if (s != GDR_OK) return s;
@@ -172,8 +218,9 @@ gdr_status gdr_decode_step(const void* q, const void* k, const void* v, const fl
     if (!aligned16(S_in)) return fail(GDR_ERR_INVALID_ARG, "S_in is not 16-byte aligned");
     s = check_ptrs(rs, 8, 6);
     if (s != GDR_OK) return s;
+    if (flags & ~3u) return fail(GDR_ERR_INVALID_ARG, "unknown prologue flags 0x%x", flags);
     gdr::DecodeArgs a{q, k, v, log_alpha, beta, S_in, S_out, o, B, H, dk, dv,
-                      io == GDR_BF16, gate == GDR_GATE_CHANNEL, stream};
+                      io == GDR_BF16, gate == GDR_GATE_CHANNEL, stream, nullptr, nullptr, flags};
     const hipError_t err = gdr::decode_step_launch(a);
     if (err != hipSuccess) return fail(GDR_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(err));
     return GDR_OK;

@@ -652,12 +652,12 @@ struct ChanPrepSmem {
 
 // The work of wave BW (16-row block BW).  The block index is a compile-time
 // constant, so no matrix instruction sits under a wave-dependent condition.
-template <int DK, int C, int BW>
+template <int DK, int C, int BW, bool NORM>
 __device__ __forceinline__ void chan_prep_wave(ChanPrepSmem<DK, C>& sm, const __bf16* __restrict__ q,
                                                const __bf16* __restrict__ k,
                                                const float* __restrict__ log_alpha,
                                                const float* __restrict__ beta, uint8_t* __restrict__ ws,
-                                               int64_t T, int H, int NT) {
+                                               int64_t T, int H, int NT, bool sigb) {
     using L = WsLayout<__bf16, DK, C, true>;
     using M = Mma<__bf16>;
     using MF = Mma<float>;
@@ -691,13 +691,47 @@ __device__ __forceinline__ void chan_prep_wave(ChanPrepSmem<DK, C>& sm, const __
     const int r = 16 * b + x;
     const bool valid = r < len;   // rows past len read row len-1 and are zeroed
     const int64_t grow = row0 + (int64_t)(valid ? r : len - 1) * H;
-    const float be = valid ? beta[grow] : 0.f;
+    float be = beta[grow];
+    if (sigb) be = 1.f / (1.f + __expf(-be));   // beta from its logit (prologue)
+    be = valid ? be : 0.f;
     if (kg == 0) bsh[r] = be;
 
-    // Loads of channel step s: k or q (bf16x8), log alpha (in log2 units).
+    // Prologue: inverse L2 norms of this lane's q and k rows (the row's
+    // channels are spread over the lanes x, x+16, x+32, x+48 and the steps s).
+    float nk = 1.f, nq = 1.f;
+    if constexpr (NORM) {
+        float sk = 0.f, sq = 0.f;
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) {
+            const bf16x8 tk = *reinterpret_cast<const bf16x8*>(k + grow * DK + 32 * s + 8 * kg);
+            const bf16x8 tq = *reinterpret_cast<const bf16x8*>(q + grow * DK + 32 * s + 8 * kg);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                sk += (float)tk[j] * (float)tk[j];
+                sq += (float)tq[j] * (float)tq[j];
+            }
+        }
+        sk += __shfl_xor(sk, 16);
+        sk += __shfl_xor(sk, 32);
+        sq += __shfl_xor(sq, 16);
+        sq += __shfl_xor(sq, 32);
+        nk = 1.f / sqrtf(sk + 1e-6f);
+        nq = 1.f / sqrtf(sq + 1e-6f);
+    }
+
+    // Loads of channel step s: k or q (bf16x8, normalised by the prologue),
+    // log alpha (in log2 units).
     auto ld_qk = [&](const __bf16* p, int s) {
         const bf16x8 t = *reinterpret_cast<const bf16x8*>(p + grow * DK + 32 * s + 8 * kg);
-        return valid ? t : bf16x8{};
+        if constexpr (NORM) {
+            const float sc = p == k ? nk : nq;
+            bf16x8 u;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) u[j] = (__bf16)((float)t[j] * sc);
+            return valid ? u : bf16x8{};
+        } else {
+            return valid ? t : bf16x8{};
+        }
     };
     auto ld_la = [&](int s, float* la) {
         const float* p = log_alpha + grow * DK + 32 * s + 8 * kg;
@@ -994,19 +1028,20 @@ __device__ __forceinline__ void chan_prep_wave(ChanPrepSmem<DK, C>& sm, const __
     }
 }
 
-template <int DK, int C>
+template <int DK, int C, bool NORM>
 __global__ __launch_bounds__(64 * (C / 16), 4) void wy_prep_channel_bf16(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const float* __restrict__ log_alpha,
-    const float* __restrict__ beta, uint8_t* __restrict__ ws, int64_t T, int H, int NT) {
+    const float* __restrict__ beta, uint8_t* __restrict__ ws, int64_t T, int H, int NT, int sigb) {
     __shared__ ChanPrepSmem<DK, C> sm;
     const int w = threadIdx.x >> 6;
     constexpr int NB = C / 16;
-    if (w == 0) chan_prep_wave<DK, C, 0>(sm, q, k, log_alpha, beta, ws, T, H, NT);
+    const bool sg = sigb != 0;
+    if (w == 0) chan_prep_wave<DK, C, 0, NORM>(sm, q, k, log_alpha, beta, ws, T, H, NT, sg);
     if constexpr (NB > 1)
-        if (w == 1) chan_prep_wave<DK, C, (NB > 1 ? 1 : 0)>(sm, q, k, log_alpha, beta, ws, T, H, NT);
+        if (w == 1) chan_prep_wave<DK, C, (NB > 1 ? 1 : 0), NORM>(sm, q, k, log_alpha, beta, ws, T, H, NT, sg);
     if constexpr (NB > 2) {
-        if (w == 2) chan_prep_wave<DK, C, (NB > 2 ? 2 : 0)>(sm, q, k, log_alpha, beta, ws, T, H, NT);
-        if (w == 3) chan_prep_wave<DK, C, (NB > 3 ? 3 : 0)>(sm, q, k, log_alpha, beta, ws, T, H, NT);
+        if (w == 2) chan_prep_wave<DK, C, (NB > 2 ? 2 : 0), NORM>(sm, q, k, log_alpha, beta, ws, T, H, NT, sg);
+        if (w == 3) chan_prep_wave<DK, C, (NB > 3 ? 3 : 0), NORM>(sm, q, k, log_alpha, beta, ws, T, H, NT, sg);
     }
 }
 
@@ -1427,9 +1462,15 @@ static hipError_t launch_chunk(const ChunkArgs& a) {
     const int NT = (int)((a.T + C - 1) / C);
     const int64_t BH = a.B * a.H;
     if constexpr (CHANNEL && sizeof(E) == 2) {
-        hipLaunchKernelGGL((wy_prep_channel_bf16<DK, C>), dim3((unsigned)(BH * NT)), dim3(64 * (C / 16)), 0,
-                           a.stream, (const __bf16*)a.q, (const __bf16*)a.k, a.log_alpha, a.beta,
-                           (uint8_t*)a.ws, a.T, (int)a.H, NT);
+        const int sigb = (a.prologue & kPrologueBetaSigmoid) ? 1 : 0;
+        if (a.prologue & kPrologueL2NormQK)
+            hipLaunchKernelGGL((wy_prep_channel_bf16<DK, C, true>), dim3((unsigned)(BH * NT)), dim3(64 * (C / 16)),
+                               0, a.stream, (const __bf16*)a.q, (const __bf16*)a.k, a.log_alpha, a.beta,
+                               (uint8_t*)a.ws, a.T, (int)a.H, NT, sigb);
+        else
+            hipLaunchKernelGGL((wy_prep_channel_bf16<DK, C, false>), dim3((unsigned)(BH * NT)), dim3(64 * (C / 16)),
+                               0, a.stream, (const __bf16*)a.q, (const __bf16*)a.k, a.log_alpha, a.beta,
+                               (uint8_t*)a.ws, a.T, (int)a.H, NT, sigb);
     } else if constexpr (CHANNEL) {
         hipLaunchKernelGGL((wy_prep_channel<E, DK, C>), dim3((unsigned)(BH * NT)), dim3(kThreads), 0,
                            a.stream, (const E*)a.q, (const E*)a.k, a.log_alpha, a.beta,
@@ -1484,7 +1525,14 @@ size_t chunk_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_
     return (size_t)(B * H * NT) * chunk_block_bytes(dk, chunk, bf16, channel);
 }
 
+bool prologue_supported(int64_t chunk, bool bf16, bool channel) {
+    // fused into the loads of the single-kernel path and of the bf16
+    // channel-gate prep (the state pass reads only the prep's outputs then)
+    return bf16 && (channel || chunk == 64);
+}
+
 hipError_t chunk_fwd_launch(const ChunkArgs& a) {
+    if (a.prologue && a.T > 0 && !prologue_supported(a.chunk, a.bf16, a.channel)) return hipErrorNotSupported;
     if (a.T == 0) {
         if (!a.S_T) return hipSuccess;
         const int64_t n4 = a.B * a.H * a.dv * a.dk / 4;

@@ -17,6 +17,10 @@
 // reduced across the lanes of a row with xor shuffles.  In-place (S_out ==
 // S_in) is safe: each 16-byte slice is read and written by the same lane.
 //
+// The gate prologue ("FG2-GDN" page, section 3.5: unit-norm q and k, beta as
+// the sigmoid of its logit) runs in the kernel when asked for: each row's
+// lanes sum the squares of their key and query channels.
+//
 // With channel-wise write rates (FG2, "FG2-GDN" page, sections 3.2 and 3.4)
 // the same step runs with unit rate on the scaled key sqrt(beta^k) * k and the
 // scaled value sqrt(beta^v) * v (beta^v = beta^k unless given).
@@ -30,7 +34,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta,
     const float* __restrict__ beta_k, const float* __restrict__ beta_v,
-    const float* S_in, float* S_out, E* __restrict__ o, int64_t BH, int DV) {
+    const float* S_in, float* S_out, E* __restrict__ o, int64_t BH, int DV, int prologue) {
     constexpr int LPR = DK / 4;      // lanes per state row
     constexpr int RPP = kWave / LPR; // rows per pass of one wave
     constexpr int NPASS = 4;
@@ -48,7 +52,19 @@ __global__ __launch_bounds__(256) void decode_kernel(
         const float4 r = *reinterpret_cast<const float4*>(beta_k + bh * DK + c0);
         kk = make_float4(sqrtf(r.x) * kk.x, sqrtf(r.y) * kk.y, sqrtf(r.z) * kk.z, sqrtf(r.w) * kk.w);
     }
-    const float4 qq = load4(q + bh * DK + c0);
+    float4 qq = load4(q + bh * DK + c0);
+    if (prologue & kPrologueL2NormQK) {   // unit-norm q and k: sums over the row's lanes
+        float sk = kk.x * kk.x + kk.y * kk.y + kk.z * kk.z + kk.w * kk.w;
+        float sq = qq.x * qq.x + qq.y * qq.y + qq.z * qq.z + qq.w * qq.w;
+#pragma unroll
+        for (int m = LPR / 2; m >= 1; m >>= 1) {
+            sk += __shfl_xor(sk, m);
+            sq += __shfl_xor(sq, m);
+        }
+        const float nk = 1.f / sqrtf(sk + 1e-6f), nq = 1.f / sqrtf(sq + 1e-6f);
+        kk = make_float4(kk.x * nk, kk.y * nk, kk.z * nk, kk.w * nk);
+        qq = make_float4(qq.x * nq, qq.y * nq, qq.z * nq, qq.w * nq);
+    }
     float4 aa;
     if constexpr (CHANNEL) {
         const float4 la = *reinterpret_cast<const float4*>(log_alpha + bh * DK + c0);
@@ -57,7 +73,8 @@ __global__ __launch_bounds__(256) void decode_kernel(
         const float a = expf(log_alpha[bh]);
         aa = make_float4(a, a, a, a);
     }
-    const float b = FG2 ? 1.f : beta[bh];
+    float b = FG2 ? 1.f : beta[bh];
+    if (!FG2 && (prologue & kPrologueBetaSigmoid)) b = 1.f / (1.f + __expf(-b));
     const float* vrate = FG2 ? (beta_v ? beta_v : beta_k) : nullptr;
 
     const int64_t base = bh * (int64_t)DV * DK;
@@ -232,12 +249,12 @@ static hipError_t launch_decode(const DecodeArgs& a) {
         hipLaunchKernelGGL((decode_kernel<E, CHANNEL, DK, true>), dim3((unsigned)blocks), dim3(256), 0,
                            a.stream, (const E*)a.q, (const E*)a.k, (const E*)a.v, a.log_alpha,
                            a.beta, a.beta_k, a.beta_v, a.S_in, a.S_out, (E*)a.o, a.B * a.H,
-                           (int)a.dv);
+                           (int)a.dv, 0);
     else
         hipLaunchKernelGGL((decode_kernel<E, CHANNEL, DK, false>), dim3((unsigned)blocks), dim3(256),
                            0, a.stream, (const E*)a.q, (const E*)a.k, (const E*)a.v, a.log_alpha,
                            a.beta, a.beta_k, a.beta_v, a.S_in, a.S_out, (E*)a.o, a.B * a.H,
-                           (int)a.dv);
+                           (int)a.dv, (int)a.prologue);
     return hipGetLastError();
 }
 

@@ -90,7 +90,12 @@ struct FLayout {
     static constexpr int G_GM = 4;        // gamma_r = e^{g_r}
     static constexpr int G_GH = 5;        // e^{g_last - g_r}
     static constexpr int G_CX = 6;        // e^{g_end(rb-1) - g_end(cb)} for (cb, rb) = (0,2), (0,3), (1,3)
-    static constexpr int GSLOT = 6 * FC * 4 + 64;
+    // With the q/k normalisation of the prologue (written by prep P for the
+    // compute waves; n_k, n_q the inverse row norms):
+    static constexpr int G_GMK = 7;       // gamma_r n_k(r)
+    static constexpr int G_GQ = 8;        // gamma_r n_q(r)
+    static constexpr int G_GHK = 9;       // e^{g_last - g_r} n_k(r)
+    static constexpr int GSLOT = 10 * FC * 4;
     static constexpr int GT0 = XA + FNB * 272 * 4;
     static constexpr int AO = GT0 + 3 * GSLOT;            // off-diagonal blocks of A (P wave -> T wave), fp16 per lane
     static constexpr int FLAG = AO + 6 * 64 * 8;          // chunk index + 1 whose blocks are in AO
@@ -264,9 +269,10 @@ __device__ __forceinline__ float lane_value(float x, int l) {
 //   e^{g_r - g_i} = EB[r] * CX(cb, rb) * FB[i],
 // a product of factors <= 1 (no overflow; an underflow bounds a negligible value).
 template <int DK, int NW>
-__device__ __forceinline__ void gate_table(float la, float bb, int len, int lane, float* tab) {
+__device__ __forceinline__ void gate_table(float la, float bb, int len, int lane, float* tab, bool sigb) {
     using L = FLayout<DK, NW>;
     la = lane < len ? fmaxf(la, kFMinLogAlpha) : 0.f;
+    if (sigb) bb = 1.f / (1.f + __expf(-bb));   // beta from its logit (prologue)
     bb = lane < len ? bb : 0.f;
     const float g2 = wave_scan(la * 1.4426950408889634f);
     const float e0 = lane_value(g2, 15), e1 = lane_value(g2, 31), e2 = lane_value(g2, 47),
@@ -294,6 +300,39 @@ __device__ __forceinline__ float cross_decay(const float* tab, int cb, int rb) {
     return tab[L::G_CX * FC + (cb == 0 ? rb - 2 : 2)];
 }
 
+// Inverse L2 norms of the 16 rows of one block from its diagonal Gram tile
+// G = X X^T (accumulator layout: lane (col, g4) holds G[4g4 + e][col]).  The
+// diagonal sits on the lanes with g4 = col / 4, element col % 4; every lane
+// takes the candidate of its own element col % 4 and two register broadcasts
+// (no memory round trip) hand each lane the values it needs:
+//   c  = n(col)              (the column form),
+//   r  = n(4g4 + e), e < 4   (the row form: a permute to quad lane col % 4,
+//                             then a broadcast of each quad lane).
+constexpr float kNormEps = 1e-6f;
+struct InvNorms {
+    float c;
+    float r[4];
+};
+__device__ __forceinline__ float bcast_quad(float x, int e) {
+    const int v = __builtin_bit_cast(int, x);
+    const int y = e == 0 ? __builtin_amdgcn_mov_dpp(v, 0x00, 0xf, 0xf, false)
+                : e == 1 ? __builtin_amdgcn_mov_dpp(v, 0x55, 0xf, 0xf, false)
+                : e == 2 ? __builtin_amdgcn_mov_dpp(v, 0xAA, 0xf, 0xf, false)
+                         : __builtin_amdgcn_mov_dpp(v, 0xFF, 0xf, 0xf, false);
+    return __builtin_bit_cast(float, y);
+}
+__device__ __forceinline__ InvNorms inv_norms(const f32x4& G, int lane) {
+    const int col = lane & 15, g4 = lane >> 4, e = col & 3;
+    const float d = e == 0 ? G[0] : e == 1 ? G[1] : e == 2 ? G[2] : G[3];
+    const int nd = __builtin_bit_cast(int, __builtin_amdgcn_rsqf(d + kNormEps));
+    InvNorms n;
+    n.c = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * (col + 16 * (col >> 2)), nd));
+    const float t = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * (20 * g4 + e), nd));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) n.r[i] = bcast_quad(t, i);
+    return n;
+}
+
 // Prep T: T = (I + A)^-1 Diag(beta) for one chunk, in one wave.
 //  - The diagonal Gram tiles K_b K_b^T on the matrix cores; the off-diagonal
 //    blocks of A come from the P wave (A-operand layout) through LDS.
@@ -309,7 +348,7 @@ __device__ __forceinline__ float cross_decay(const float* tab, int cb, int rb) {
 //    fp32 accumulation, row block by row block.
 //  Entries of A and X are bounded by small constants here (unit-norm keys,
 //  beta <= 1, decays <= 1), well inside fp16's range; T is rounded to bf16 after.
-template <int DK, int NW>
+template <int DK, int NW, bool NORM>
 __device__ __forceinline__ void prep_t(char* smem, const char* st, const float* tab, char* tp, int n,
                                        int lane) {
     using L = FLayout<DK, NW>;
@@ -343,6 +382,11 @@ __device__ __forceinline__ void prep_t(char* smem, const char* st, const float* 
         const float grv[4] = {gr.x, gr.y, gr.z, gr.w}, brv[4] = {br.x, br.y, br.z, br.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) Ab[b][e] = Gd[b][e] * brv[e] * __builtin_amdgcn_exp2f(grv[e] - gc);
+        if constexpr (NORM) {   // prologue: A from the normalised keys
+            const InvNorms nk = inv_norms(Gd[b], lane);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Ab[b][e] *= nk.r[e] * nk.c;
+        }
         *reinterpret_cast<float4*>(xa + b * 272 + col * 16 + 4 * g4) =
             make_float4(Ab[b][0], Ab[b][1], Ab[b][2], Ab[b][3]);
     }
@@ -454,8 +498,8 @@ __device__ __forceinline__ void prep_t(char* smem, const char* st, const float* 
 
 // Prep P: the off-diagonal blocks of A (for the T wave) and P = (Q K^T)
 // masked and decayed, stored transposed.
-template <int DK, int NW>
-__device__ __forceinline__ void prep_p(char* smem, const char* st, const float* tab, char* tp, int n,
+template <int DK, int NW, bool NORM>
+__device__ __forceinline__ void prep_p(char* smem, const char* st, float* tab, char* tp, int n,
                                        int lane) {
     using L = FLayout<DK, NW>;
     constexpr int NKC = DK / 32;
@@ -469,6 +513,33 @@ __device__ __forceinline__ void prep_p(char* smem, const char* st, const float* 
             kf[rb][s] = qk_frag<DK>(st + L::S_K, rb, s, lane);
             qf[rb][s] = qk_frag<DK>(st + L::S_Q, rb, s, lane);
         }
+    InvNorms nk[FNB], nq[FNB];   // prologue: inverse row norms of k and q
+    if constexpr (NORM) {
+        // |k_r|^2 and |q_r|^2 from the diagonal Gram blocks, on the matrix cores
+        f32x4 gk[FNB], gq[FNB];
+#pragma unroll
+        for (int b = 0; b < FNB; ++b) gk[b] = gq[b] = zero4();
+#pragma unroll
+        for (int s = 0; s < NKC; ++s)
+#pragma unroll
+            for (int b = 0; b < FNB; ++b) {
+                gk[b] = Mma<__bf16>::mma(kf[b][s], kf[b][s], gk[b]);
+                gq[b] = Mma<__bf16>::mma(qf[b][s], qf[b][s], gq[b]);
+            }
+#pragma unroll
+        for (int b = 0; b < FNB; ++b) {
+            nk[b] = inv_norms(gk[b], lane);
+            nq[b] = inv_norms(gq[b], lane);
+        }
+        // per-token factors of the compute waves, lane = token row (this
+        // chunk's slot; the compute waves read it in the next window)
+        const float nk1 = g4 == 0 ? nk[0].c : g4 == 1 ? nk[1].c : g4 == 2 ? nk[2].c : nk[3].c;
+        const float nq1 = g4 == 0 ? nq[0].c : g4 == 1 ? nq[1].c : g4 == 2 ? nq[2].c : nq[3].c;
+        const float gm = tab[L::G_GM * FC + lane];
+        tab[L::G_GMK * FC + lane] = gm * nk1;
+        tab[L::G_GQ * FC + lane] = gm * nq1;
+        tab[L::G_GHK * FC + lane] = tab[L::G_GH * FC + lane] * nk1;
+    }
     // Off-diagonal blocks of A for the T wave, first: lane (col, g4) of block
     // (rb, cb) holds A[16rb + col][16cb + 4g4 + e], computed as K_cb K_rb^T
     // (the transpose of the needed block of the symmetric Gram matrix), with
@@ -500,6 +571,10 @@ __device__ __forceinline__ void prep_p(char* smem, const char* st, const float* 
                 acc[1] *= f * fr.y;
                 acc[2] *= f * fr.z;
                 acc[3] *= f * fr.w;
+                if constexpr (NORM) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[e] *= nk[rb].c * nk[cb].r[e];
+                }
                 ao[(rb * (rb - 1) / 2 + cb) * 64 + lane] = to_f16(acc);
             }
         }
@@ -538,16 +613,20 @@ __device__ __forceinline__ void prep_p(char* smem, const char* st, const float* 
 #pragma unroll
                 for (int e = 0; e < 4; ++e) acc[e] *= erv[e] * f;
             }
+            if constexpr (NORM) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] *= nq[rb].r[e] * nk[cb].c;
+            }
             tp_store(Pt, rb, cb, lane, acc);
         }
     }
 }
 
-template <int DK, int NW>
+template <int DK, int NW, bool NORM>
 __global__ __launch_bounds__(64 * (NW + 4)) void fused_chunk(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta, const float* __restrict__ S0,
-    __bf16* __restrict__ o, float* __restrict__ ST, int64_t T, int H, int NT, int DV) {
+    __bf16* __restrict__ o, float* __restrict__ ST, int64_t T, int H, int NT, int DV, int sigb) {
     using L = FLayout<DK, NW>;
     using M = Mma<__bf16>;
     constexpr int VT = L::VT;
@@ -621,7 +700,7 @@ __global__ __launch_bounds__(64 * (NW + 4)) void fused_chunk(
 #pragma unroll
                 for (int mt = 0; mt < FNB; ++mt) {
                     vv[mt] = fo.vf(st + L::S_V, mt);
-                    gm[mt] = *reinterpret_cast<const float4*>(tab + L::G_GM * FC + 16 * mt + 4 * g4);
+                    gm[mt] = *reinterpret_cast<const float4*>(tab + (NORM ? L::G_GMK : L::G_GM) * FC + 16 * mt + 4 * g4);
                 }
                 // Phase 1: R = K S^T (rows = tokens) from the prefetched K fragments.
                 M::frag sb[NKC];
@@ -670,8 +749,8 @@ __global__ __launch_bounds__(64 * (NW + 4)) void fused_chunk(
                 for (int mt = 0; mt < FNB; ++mt) {
 #pragma unroll
                     for (int s = 0; s < NKT; ++s) pf[mt][s] = fo.tpf(tp + L::T_P, mt, s);
-                    gh[mt] = *reinterpret_cast<const float4*>(tab + L::G_GH * FC + 16 * mt + 4 * g4);
-                    gc[mt] = tab[L::G_GM * FC + 16 * mt + col];
+                    gh[mt] = *reinterpret_cast<const float4*>(tab + (NORM ? L::G_GHK : L::G_GH) * FC + 16 * mt + 4 * g4);
+                    gc[mt] = tab[(NORM ? L::G_GQ : L::G_GM) * FC + 16 * mt + col];
                 }
                 const float gl = tab[L::G_GM * FC + FC - 1];
                 __builtin_amdgcn_sched_barrier(0);
@@ -768,7 +847,7 @@ __global__ __launch_bounds__(64 * (NW + 4)) void fused_chunk(
                 }
         for (int w = -2; w < NT; ++w) {
             const int n = w + 1;
-            if (n >= 0 && n < NT) prep_t<DK, NW>(smem, GDR_STAGE(n), GDR_GTAB(n), GDR_TPBUF(n), n, lane);
+            if (n >= 0 && n < NT) prep_t<DK, NW, NORM>(smem, GDR_STAGE(n), GDR_GTAB(n), GDR_TPBUF(n), n, lane);
             __syncthreads();
         }
     } else if (wave == NW + 1) {
@@ -776,7 +855,7 @@ __global__ __launch_bounds__(64 * (NW + 4)) void fused_chunk(
         if (lane == 0) *reinterpret_cast<int*>(smem + L::FLAG) = 0;
         for (int w = -2; w < NT; ++w) {
             const int n = w + 1;
-            if (n >= 0 && n < NT) prep_p<DK, NW>(smem, GDR_STAGE(n), GDR_GTAB(n), GDR_TPBUF(n), n, lane);
+            if (n >= 0 && n < NT) prep_p<DK, NW, NORM>(smem, GDR_STAGE(n), GDR_GTAB(n), GDR_TPBUF(n), n, lane);
             __syncthreads();
         }
     } else {
@@ -799,7 +878,7 @@ __global__ __launch_bounds__(64 * (NW + 4)) void fused_chunk(
                 const int len = GDR_LEN(n);
                 if (len < FC) lo.set(len, H, DV, vt, lw, lane);   // ragged last chunk
                 load_chunk<DK, NW>(GDR_STAGE(n), q, k, v, GDR_ROW0(n), DV, lo, lw);
-                if (lw == 0) gate_table<DK, NW>(la, bb, len, lane, GDR_GTAB(n));
+                if (lw == 0) gate_table<DK, NW>(la, bb, len, lane, GDR_GTAB(n), sigb != 0);
                 if (n + 1 < NT) {
                     const int len1 = GDR_LEN(n + 1);
                     const int64_t go = GDR_ROW0(n + 1) + (int64_t)(lane < len1 ? lane : len1 - 1) * H;
@@ -818,14 +897,24 @@ __global__ __launch_bounds__(64 * (NW + 4)) void fused_chunk(
 #undef GDR_GTAB
 }
 
-template <int DK, int NW>
+template <int DK, int NW, bool NORM>
 hipError_t launch_fused(const ChunkArgs& a) {
     const int NT = (int)((a.T + FC - 1) / FC);
     const int64_t grid = a.B * a.H * (a.dv / (16 * NW));
-    hipLaunchKernelGGL((fused_chunk<DK, NW>), dim3((unsigned)grid), dim3(64 * (NW + 4)), 0, a.stream,
+    hipLaunchKernelGGL((fused_chunk<DK, NW, NORM>), dim3((unsigned)grid), dim3(64 * (NW + 4)), 0, a.stream,
                        (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, a.log_alpha, a.beta,
-                       a.S0, (__bf16*)a.o, a.S_T, a.T, (int)a.H, NT, (int)a.dv);
+                       a.S0, (__bf16*)a.o, a.S_T, a.T, (int)a.H, NT, (int)a.dv,
+                       (a.prologue & kPrologueBetaSigmoid) ? 1 : 0);
     return hipGetLastError();
+}
+
+template <bool NORM>
+hipError_t launch_fused_n(const ChunkArgs& a) {
+    // Two compute waves (32 value columns) per workgroup when that still
+    // gives at least one workgroup per CU, otherwise one.
+    const bool two = a.B * a.H * (a.dv / 32) >= 256;
+    if (a.dk == 64) return two ? launch_fused<64, 2, NORM>(a) : launch_fused<64, 1, NORM>(a);
+    return two ? launch_fused<128, 2, NORM>(a) : launch_fused<128, 1, NORM>(a);
 }
 
 }  // namespace
@@ -835,11 +924,7 @@ bool fused_chunk_supported(int64_t dk, int64_t chunk, bool bf16, bool channel) {
 }
 
 hipError_t fused_chunk_launch(const ChunkArgs& a) {
-    // Two compute waves (32 value columns) per workgroup when that still
-    // gives at least one workgroup per CU, otherwise one.
-    const bool two = a.B * a.H * (a.dv / 32) >= 256;
-    if (a.dk == 64) return two ? launch_fused<64, 2>(a) : launch_fused<64, 1>(a);
-    return two ? launch_fused<128, 2>(a) : launch_fused<128, 1>(a);
+    return (a.prologue & kPrologueL2NormQK) ? launch_fused_n<true>(a) : launch_fused_n<false>(a);
 }
 
 }  // namespace gdr

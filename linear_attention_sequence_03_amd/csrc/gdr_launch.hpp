@@ -18,6 +18,7 @@ struct DecodeArgs {
     // Channel-wise write rates (beta unused then): beta_k [B,H,dk], beta_v
     // [B,H,dv] or NULL for beta_k.  NULL beta_k selects the scalar rate.
     const float *beta_k = nullptr, *beta_v = nullptr;
+    unsigned prologue = 0;   // gate prologue flags (scalar-rate step only)
 };
 
 // Several tokens per sequence in one pass over the state (draft verification
@@ -33,6 +34,9 @@ struct DecodeMultiArgs {
     hipStream_t stream;
 };
 
+// Gate prologue flags (in-kernel L2 normalisation of q and k, beta from logits).
+constexpr unsigned kPrologueL2NormQK = 1u, kPrologueBetaSigmoid = 2u;
+
 struct ChunkArgs {
     const void *q, *k, *v;
     const float *log_alpha, *beta, *S0;
@@ -42,6 +46,7 @@ struct ChunkArgs {
     bool bf16, channel;
     void* ws;
     hipStream_t stream;
+    unsigned prologue = 0;   // kPrologue* flags; only the bf16 paths with a fused prologue accept them
 };
 
 hipError_t decode_step_launch(const DecodeArgs& a);
@@ -52,6 +57,8 @@ size_t chunk_block_bytes(int64_t dk, int64_t chunk, bool bf16, bool channel);
 size_t chunk_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t chunk,
                              bool bf16, bool channel);
 hipError_t chunk_fwd_launch(const ChunkArgs& a);
+// Which chunk calls take the gate prologue (fused into their loads).
+bool prologue_supported(int64_t chunk, bool bf16, bool channel);
 
 // Single-kernel path (bf16, scalar gate, 64-token chunks): needs no workspace.
 bool fused_chunk_supported(int64_t dk, int64_t chunk, bool bf16, bool channel);

@@ -18,9 +18,11 @@ LIBRARY_PATH = os.path.join(_PKG, "libgdr.so")
 GDR_OK, GDR_ERR_INVALID_ARG, GDR_ERR_UNSUPPORTED, GDR_ERR_HIP = 0, 1, 2, 3
 GDR_F32, GDR_BF16 = 0, 1
 GDR_GATE_SCALAR, GDR_GATE_CHANNEL = 0, 1
+GDR_PROLOGUE_L2NORM_QK, GDR_PROLOGUE_BETA_SIGMOID = 1, 2
 
 # Every symbol include/gdr.h declares.
 EXPORTS = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_decode_step", "gdr_decode_multi",
+           "gdr_chunk_fwd_prologue", "gdr_decode_step_prologue",
            "gdr_fg2_chunk_fwd_workspace_size", "gdr_fg2_chunk_fwd", "gdr_fg2_decode_step",
            "gdr_gdn2_fwd",
            "gdr_status_string", "gdr_last_error")
@@ -59,6 +61,13 @@ def load_library(path: Optional[str] = None):
     lib.gdr_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp,
                                     i64, i64, i64, i64, f, f, vp]
     lib.gdr_decode_step.restype = f
+    lib.gdr_chunk_fwd_prologue.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp,
+                                           i64, i64, i64, i64, i64, i64, f, f,
+                                           vp, ctypes.c_size_t, ctypes.c_uint, vp]
+    lib.gdr_chunk_fwd_prologue.restype = f
+    lib.gdr_decode_step_prologue.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp,
+                                             i64, i64, i64, i64, f, f, ctypes.c_uint, vp]
+    lib.gdr_decode_step_prologue.restype = f
     lib.gdr_gdn2_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                  i64, i64, i64, i64, i64, f, f, vp]
     lib.gdr_gdn2_fwd.restype = f
@@ -130,11 +139,13 @@ def gdr_chunk_fwd_workspace_size(B, T, H, dk, dv, chunk, io, gate) -> int:
 
 
 def gdr_chunk_fwd(q, k, v, log_alpha, beta, S0=None, chunk: int = 64, o=None, S_T=None,
-                  workspace=None, want_state: bool = True, stream=None) -> Tuple:
+                  workspace=None, want_state: bool = True, stream=None, prologue: int = 0) -> Tuple:
     """Whole-sequence forward.  q,k: [B,T,H,dk]; v: [B,T,H,dv] (fp32 or bf16);
     log_alpha: [B,T,H] (scalar gate) or [B,T,H,dk] (channel gate), fp32;
     beta: [B,T,H] fp32; S0: [B,H,dv,dk] fp32 or None.
-    Returns (o [B,T,H,dv] in the io dtype, S_T [B,H,dv,dk] fp32 or None)."""
+    Returns (o [B,T,H,dv] in the io dtype, S_T [B,H,dv,dk] fp32 or None).
+    ``prologue`` (GDR_PROLOGUE_* flags) normalises q, k and / or maps beta
+    logits through a sigmoid inside the kernels."""
     import torch
     dev = q.device
     B, T, H, dk = q.shape
@@ -160,16 +171,22 @@ def gdr_chunk_fwd(q, k, v, log_alpha, beta, S0=None, chunk: int = 64, o=None, S_
     if workspace is None and nbytes > 0:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = load_library().gdr_chunk_fwd(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0), _ptr(o), _ptr(S_T),
-        B, T, H, dk, dv, chunk, io, gate, _ptr(workspace), wbytes, _stream(dev, stream))
+    if prologue:
+        st = load_library().gdr_chunk_fwd_prologue(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0), _ptr(o), _ptr(S_T),
+            B, T, H, dk, dv, chunk, io, gate, _ptr(workspace), wbytes, int(prologue),
+            _stream(dev, stream))
+    else:
+        st = load_library().gdr_chunk_fwd(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0), _ptr(o), _ptr(S_T),
+            B, T, H, dk, dv, chunk, io, gate, _ptr(workspace), wbytes, _stream(dev, stream))
     if st != GDR_OK:
         _raise(st)
     return o, S_T
 
 
 def gdr_decode_step(q, k, v, log_alpha, beta, S, S_out=None, o=None, inplace: bool = False,
-                    stream=None) -> Tuple:
+                    stream=None, prologue: int = 0) -> Tuple:
     """One decode step.  q,k: [B,H,dk]; v: [B,H,dv]; log_alpha: [B,H] or [B,H,dk];
     beta: [B,H]; S: [B,H,dv,dk] fp32.  ``inplace=True`` writes the new state into
     S.  Returns (o [B,H,dv], S_out)."""
@@ -194,9 +211,14 @@ def gdr_decode_step(q, k, v, log_alpha, beta, S, S_out=None, o=None, inplace: bo
     if o is None:
         o = torch.empty((B, H, dv), dtype=q.dtype, device=dev)
     _need("o", o, q.dtype, (B, H, dv), dev)
-    st = load_library().gdr_decode_step(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S), _ptr(S_out), _ptr(o),
-        B, H, dk, dv, io, gate, _stream(dev, stream))
+    if prologue:
+        st = load_library().gdr_decode_step_prologue(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S), _ptr(S_out), _ptr(o),
+            B, H, dk, dv, io, gate, int(prologue), _stream(dev, stream))
+    else:
+        st = load_library().gdr_decode_step(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S), _ptr(S_out), _ptr(o),
+            B, H, dk, dv, io, gate, _stream(dev, stream))
     if st != GDR_OK:
         _raise(st)
     return o, S_out

@@ -137,3 +137,16 @@ def gdn2_gates(B, T, H, dk, dv, seed=0):
     b = (1.0 / (1.0 + np.exp(-rng.standard_normal((B, T, H, dk))))).astype(np.float32)
     w = (1.0 / (1.0 + np.exp(-rng.standard_normal((B, T, H, dv))))).astype(np.float32)
     return b, w
+
+
+def raw_prologue_inputs(inp, io="bf16", seed=0):
+    """Raw inputs for the gate prologue from a workload's inputs: q and k rows
+    scaled by factors U(1, 8) per token and head (then stored in the io type),
+    beta replaced by logits N(0, 1.5^2).  Own seeded stream."""
+    rng = np.random.Generator(np.random.PCG64(seed + 9000))
+    out = dict(inp)
+    for n in ("q", "k"):
+        x = inp[n].astype(np.float64)
+        out[n] = _store(x * rng.uniform(1.0, 8.0, x.shape[:-1] + (1,)), io)
+    out["beta"] = (rng.standard_normal(inp["beta"].shape) * 1.5).astype(np.float32)
+    return out

@@ -94,6 +94,32 @@ def test_decode_step_rejects(lib, kw, code):
     assert _decode(lib, **kw) == code
 
 
+def _chunk_pro(lib, flags, q=0, k=1, v=2, la=3, be=4, o=6, st=7, ws=8, B=1, T=128, H=2, dk=64,
+               dv=64, chunk=64, io=1, gate=0, wsbytes=1 << 22):
+    p = lambda i: None if i is None else (_addr(i) if isinstance(i, int) else i)  # noqa: E731
+    return lib.gdr_chunk_fwd_prologue(p(q), p(k), p(v), p(la), p(be), None, p(o), p(st),
+                                      B, T, H, dk, dv, chunk, io, gate, p(ws), wsbytes, flags, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(flags=4), 1), (dict(flags=1 << 31), 1),              # unknown flags
+    (dict(flags=1, io=0), 2),                                   # fp32 io: not fused
+    (dict(flags=3, chunk=32), 2), (dict(flags=2, chunk=16), 2),  # scalar gate, chunk != 64
+    (dict(flags=1, q=None), 1),                                 # the plain checks still run
+])
+def test_chunk_fwd_prologue_rejects(lib, kw, code):
+    assert _chunk_pro(lib, **kw) == code
+    assert lib.gdr_last_error()
+
+
+def test_decode_step_prologue_rejects(lib):
+    p = _addr
+    args = [p(0), p(1), p(2), p(3), p(4), p(5), p(6), p(7), 2, 2, 64, 64, 0, 0]
+    assert lib.gdr_decode_step_prologue(*args, 8, None) == 1        # unknown flag
+    args[0] = None
+    assert lib.gdr_decode_step_prologue(*args, 1, None) == 1        # plain checks still run
+
+
 def test_workspace_size():
     # bf16 scalar gate with 64-token chunks runs as one kernel: no workspace
     for d in (64, 128):
