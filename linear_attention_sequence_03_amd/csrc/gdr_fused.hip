@@ -79,9 +79,9 @@ struct FLayout {
     static constexpr int T_T = 0, T_P = FC * FC * 2;
     static constexpr int TPB = 2 * FC * FC * 2;
     static constexpr int TP0 = NSTAGE * STAGE;
-    static constexpr int XA = TP0 + 2 * TPB;              // diagonal blocks of A (transposed), then
-                                                          // blockdiag of their 8x8 inverses; fp32, tile
-                                                          // stride 272, rows of 16
+    static constexpr int XA = TP0 + 2 * TPB;              // solve wave's scratch: diagonal blocks of A
+                                                          // (transposed), then blockdiag of their 8x8
+                                                          // inverses; fp32, tile stride 272, rows of 16
     // Gate tables, a 3-deep ring (chunk n in slot n % 3), 64 floats per field:
     static constexpr int G_G2 = 0;        // g_r * log2(e), g the in-chunk cumulative log decay
     static constexpr int G_BE = 1;        // beta_r
@@ -90,16 +90,20 @@ struct FLayout {
     static constexpr int G_GM = 4;        // gamma_r = e^{g_r}
     static constexpr int G_GH = 5;        // e^{g_last - g_r}
     static constexpr int G_CX = 6;        // e^{g_end(rb-1) - g_end(cb)} for (cb, rb) = (0,2), (0,3), (1,3)
-    // With the q/k normalisation of the prologue (written by prep P for the
-    // compute waves; n_k, n_q the inverse row norms):
+    // With the q/k normalisation of the prologue (written by the P wave for
+    // the compute waves; n_k, n_q the inverse row norms):
     static constexpr int G_GMK = 7;       // gamma_r n_k(r)
     static constexpr int G_GQ = 8;        // gamma_r n_q(r)
     static constexpr int G_GHK = 9;       // e^{g_last - g_r} n_k(r)
     static constexpr int GSLOT = 10 * FC * 4;
     static constexpr int GT0 = XA + FNB * 272 * 4;
-    static constexpr int AO = GT0 + 3 * GSLOT;            // off-diagonal blocks of A (P wave -> T wave), fp16 per lane
-    static constexpr int FLAG = AO + 6 * 64 * 8;          // chunk index + 1 whose blocks are in AO
-    static constexpr int TOTAL = FLAG + 16;
+    // Solve wave -> recurrence wave, a 2-deep ring (chunk c in slot c % 2): the
+    // inverted diagonal blocks X_bb (fp16, A-operand layout, 64 lanes x 4 per
+    // block), then the inverse key norms n_k (prologue).
+    static constexpr int XH = GT0 + 3 * GSLOT;
+    static constexpr int XHB = FNB * 64 * 8 + FC * 4;
+    static constexpr int TG = XH + 2 * XHB;               // solve wave's own g (log2 units) and beta rows
+    static constexpr int TOTAL = TG + 2 * FC * 4;
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
 
@@ -333,34 +337,73 @@ __device__ __forceinline__ InvNorms inv_norms(const f32x4& G, int lane) {
     return n;
 }
 
-// Prep T: T = (I + A)^-1 Diag(beta) for one chunk, in one wave.
-//  - The diagonal Gram tiles K_b K_b^T on the matrix cores; the off-diagonal
-//    blocks of A come from the P wave (A-operand layout) through LDS.
-//  - Diagonal blocks: with A_bb = [[A11, 0], [A21, A22]] (8x8 blocks),
+// Within one wave, LDS written by some lanes and read by others: the fences
+// keep the compiler from moving the reads above the writes (the hardware keeps
+// one wave's LDS accesses in order).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// T = (I + A)^-1 Diag(beta) is built by two waves, so that neither waits on
+// the other inside a window:
+//  - the solve wave inverts the diagonal blocks of chunk c one window before
+//    the recurrence wave needs them, from K fragments and gate values it reads
+//    from global memory itself (prefetched one window earlier still; the LDS
+//    stage of chunk c is being filled in the same window);
+//  - the recurrence wave forms the off-diagonal blocks of A from the chunk's
+//    LDS stage and runs the block recurrence.
+//
+// The solve wave's inputs of one chunk, from global memory: K fragments in the
+// row-wise operand layout (rows 16rb + lane%16, channels 32s + 8(lane/16) ..
+// +7) and the gate values of token row = lane; rows at or past len repeat row
+// len - 1, as in the LDS stages.
+template <int DK>
+__device__ __forceinline__ void solve_loads(const __bf16* k, const float* log_alpha, const float* beta,
+                                            int64_t row0, int len, int H, int lane,
+                                            bf16x8 (&kf)[FNB][DK / 32], float& la, float& bb) {
+#pragma unroll
+    for (int rb = 0; rb < FNB; ++rb) {
+        const int r = 16 * rb + (lane & 15);
+        const __bf16* p = k + (row0 + (int64_t)(r < len ? r : len - 1) * H) * DK + 8 * (lane >> 4);
+#pragma unroll
+        for (int s = 0; s < DK / 32; ++s) kf[rb][s] = *reinterpret_cast<const bf16x8*>(p + 32 * s);
+    }
+    const int64_t go = row0 + (int64_t)(lane < len ? lane : len - 1) * H;
+    la = log_alpha[go];
+    bb = beta[go];
+}
+
+// Solve: X_bb = (I + A_bb)^-1 of the four diagonal 16x16 blocks.
+//  - The diagonal Gram tiles K_b K_b^T on the matrix cores.
+//  - With A_bb = [[A11, 0], [A21, A22]] (8x8 blocks),
 //    D = blockdiag((I + A11)^-1, (I + A22)^-1) and N = [[0, 0], [A21, 0]],
 //        X_bb = (I + A_bb)^-1 = D - D N D.
 //    The 8x8 inverses come from forward substitution in fp32 (lane = column j
 //    of half h of block b; at most 7 dependent steps), the correction from fp16
-//    16x16x16 MFMAs, in both operand layouts.
-//  - Off-diagonal blocks of X = (I + A)^-1 by the block recurrence
-//        X_ij = -X_ii sum_{m=j}^{i-1} A_im X_mj
-//    (carried out for T = X Diag(beta) directly) on fp16 16x16x16 MFMAs with
-//    fp32 accumulation, row block by row block.
+//    16x16x16 MFMAs.
 //  Entries of A and X are bounded by small constants here (unit-norm keys,
 //  beta <= 1, decays <= 1), well inside fp16's range; T is rounded to bf16 after.
+//  Output: X_bb in A-operand layout (fp16) and, with the prologue, n_k, into
+//  the chunk's hand-off slot xh.
 template <int DK, int NW, bool NORM>
-__device__ __forceinline__ void prep_t(char* smem, const char* st, const float* tab, char* tp, int n,
-                                       int lane) {
+__device__ __forceinline__ void solve_diag(char* smem, const bf16x8 (&kf)[FNB][DK / 32], float la, float bb,
+                                           int len, bool sigb, char* xh, int lane) {
     using L = FLayout<DK, NW>;
     constexpr int NKC = DK / 32;
     float* xa = reinterpret_cast<float*>(smem + L::XA);
+    float* tg = reinterpret_cast<float*>(smem + L::TG);
     const int col = lane & 15, g4 = lane >> 4;
 
-    bf16x8 kf[FNB][NKC];
-#pragma unroll
-    for (int rb = 0; rb < FNB; ++rb)
-#pragma unroll
-        for (int s = 0; s < NKC; ++s) kf[rb][s] = qk_frag<DK>(st + L::S_K, rb, s, lane);
+    // The chunk's g (log2 units) and beta rows, as the gate table has them.
+    {
+        la = lane < len ? fmaxf(la, kFMinLogAlpha) : 0.f;
+        if (sigb) bb = 1.f / (1.f + __expf(-bb));
+        bb = lane < len ? bb : 0.f;
+        tg[lane] = wave_scan(la * 1.4426950408889634f);
+        tg[FC + lane] = bb;
+    }
     // Gram tiles of the diagonal blocks (symmetric): element (4g4 + e, col).
     f32x4 Gd[FNB];
 #pragma unroll
@@ -369,6 +412,8 @@ __device__ __forceinline__ void prep_t(char* smem, const char* st, const float* 
     for (int s = 0; s < NKC; ++s)
 #pragma unroll
         for (int b = 0; b < FNB; ++b) Gd[b] = Mma<__bf16>::mma(kf[b][s], kf[b][s], Gd[b]);
+    wave_lds_sync();
+    float nkl = 0.f;   // prologue: n_k of row = lane
     // A_bb in B layout (row 4g4 + e, column col), also stored transposed:
     // xa[b][m][i] = A_bb[i][m].  Entries on or above the diagonal are not
     // masked: nothing reads them (the substitution uses rows i > m only, and N
@@ -376,9 +421,9 @@ __device__ __forceinline__ void prep_t(char* smem, const char* st, const float* 
     f32x4 Ab[FNB];
 #pragma unroll
     for (int b = 0; b < FNB; ++b) {
-        const float4 gr = *reinterpret_cast<const float4*>(tab + L::G_G2 * FC + 16 * b + 4 * g4);
-        const float4 br = *reinterpret_cast<const float4*>(tab + L::G_BE * FC + 16 * b + 4 * g4);
-        const float gc = tab[L::G_G2 * FC + 16 * b + col];
+        const float4 gr = *reinterpret_cast<const float4*>(tg + 16 * b + 4 * g4);
+        const float4 br = *reinterpret_cast<const float4*>(tg + FC + 16 * b + 4 * g4);
+        const float gc = tg[16 * b + col];
         const float grv[4] = {gr.x, gr.y, gr.z, gr.w}, brv[4] = {br.x, br.y, br.z, br.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) Ab[b][e] = Gd[b][e] * brv[e] * __builtin_amdgcn_exp2f(grv[e] - gc);
@@ -386,10 +431,12 @@ __device__ __forceinline__ void prep_t(char* smem, const char* st, const float* 
             const InvNorms nk = inv_norms(Gd[b], lane);
 #pragma unroll
             for (int e = 0; e < 4; ++e) Ab[b][e] *= nk.r[e] * nk.c;
+            nkl = g4 == b ? nk.c : nkl;
         }
         *reinterpret_cast<float4*>(xa + b * 272 + col * 16 + 4 * g4) =
             make_float4(Ab[b][0], Ab[b][1], Ab[b][2], Ab[b][3]);
     }
+    wave_lds_sync();
     // 8x8 forward substitution: lane (blk, h, j) builds column j of (I + A_hh)^-1.
     {
         const int blk = lane >> 4, h = (lane >> 3) & 1, j = lane & 7;
@@ -415,6 +462,7 @@ __device__ __forceinline__ void prep_t(char* smem, const char* st, const float* 
 #pragma unroll
         for (int i = 0; i < 8; ++i) Ab8[i * 16 + j] = x[i];
     }
+    wave_lds_sync();
     // Operands of X_bb = D - D N D for all four blocks (loads first, selects after).
     const bool same = (g4 >> 1) == (col >> 3);   // rows 4g4.. and column col in one 8x8 half
     f32x4 DbB[FNB], DbA[FNB], NA[FNB], NB[FNB];
@@ -436,7 +484,6 @@ __device__ __forceinline__ void prep_t(char* smem, const char* st, const float* 
         }
         DbA[b] = same ? f32x4{t.x, t.y, t.z, t.w} : zero4();
     }
-    f32x4 Xb[FNB];   // X_bb, B layout: (4g4 + e, col)
     f16x4 Xa[FNB];   // X_bb, A layout: (col, 4g4 + e)
     {
         f16x4 dB[FNB], dA[FNB];
@@ -449,23 +496,79 @@ __device__ __forceinline__ void prep_t(char* smem, const char* st, const float* 
             ntdt[b] = mma16(to_f16(NB[b]), dA[b], zero4());     // B layout of N^T D^T
         }
 #pragma unroll
-        for (int b = 0; b < FNB; ++b) {
-            Xb[b] = DbB[b] - mma16(dA[b], to_f16(nd[b]), zero4());            // D - (D N D), B layout
-            Xa[b] = to_f16(DbA[b] - mma16(dB[b], to_f16(ntdt[b]), zero4()));  // the same, A layout
-        }
+        for (int b = 0; b < FNB; ++b)
+            Xa[b] = to_f16(DbA[b] - mma16(dB[b], to_f16(ntdt[b]), zero4()));  // D - (D N D), A layout
     }
-    // Off-diagonal blocks of A, from the P wave (A-operand layout).
-    while (__hip_atomic_load(reinterpret_cast<int*>(smem + L::FLAG), __ATOMIC_ACQUIRE,
-                             __HIP_MEMORY_SCOPE_WORKGROUP) != n + 1)
-        __builtin_amdgcn_s_sleep(1);
-    f16x4 Ao[FNB][FNB];
-    {
-        const f16x4* ao = reinterpret_cast<const f16x4*>(smem + L::AO);
+    f16x4* xo = reinterpret_cast<f16x4*>(xh);
+#pragma unroll
+    for (int b = 0; b < FNB; ++b) xo[b * 64 + lane] = Xa[b];
+    if constexpr (NORM) reinterpret_cast<float*>(xh + FNB * 64 * 8)[lane] = nkl;
+}
+
+// Recurrence: the off-diagonal blocks of A (K_cb K_rb^T, scaled) in A-operand
+// layout, then the off-diagonal blocks of X = (I + A)^-1 by
+//     X_ij = -X_ii sum_{m=j}^{i-1} A_im X_mj
+// (carried out for T = X Diag(beta) directly) on fp16 16x16x16 MFMAs with fp32
+// accumulation, row block by row block.  The decay of A[r][i] = beta_r
+// e^{g_r - g_i} G[r][i] is split at the block boundaries (see gate_table).
+template <int DK, int NW, bool NORM>
+__device__ __forceinline__ void recur_off(const char* st, const float* tab, const char* xh, char* tp,
+                                          int lane) {
+    using L = FLayout<DK, NW>;
+    constexpr int NKC = DK / 32;
+    const int col = lane & 15, g4 = lane >> 4;
+
+    bf16x8 kf[FNB][NKC];
+#pragma unroll
+    for (int rb = 0; rb < FNB; ++rb)
+#pragma unroll
+        for (int s = 0; s < NKC; ++s) kf[rb][s] = qk_frag<DK>(st + L::S_K, rb, s, lane);
+    const f16x4* xi = reinterpret_cast<const f16x4*>(xh);
+    f16x4 Xa[FNB];   // X_bb, A layout: (col, 4g4 + e)
+#pragma unroll
+    for (int b = 0; b < FNB; ++b) Xa[b] = xi[b * 64 + lane];
+    const float* nkv = reinterpret_cast<const float*>(xh + FNB * 64 * 8);
+    // lane (col, g4) of block (rb, cb) holds A[16rb + col][16cb + 4g4 + e]
+    constexpr int NOFF = FNB * (FNB - 1) / 2;
+    f32x4 go[NOFF];
+#pragma unroll
+    for (int t = 0; t < NOFF; ++t) go[t] = zero4();
+#pragma unroll
+    for (int s = 0; s < NKC; ++s) {
+        int t = 0;
 #pragma unroll
         for (int rb = 1; rb < FNB; ++rb)
 #pragma unroll
-            for (int cb = 0; cb < rb; ++cb) Ao[rb][cb] = ao[(rb * (rb - 1) / 2 + cb) * 64 + lane];
+            for (int cb = 0; cb < rb; ++cb, ++t) go[t] = Mma<__bf16>::mma(kf[cb][s], kf[rb][s], go[t]);
     }
+    f16x4 Ao[FNB][FNB];
+#pragma unroll
+    for (int rb = 1; rb < FNB; ++rb) {
+        const float f0 = tab[L::G_BE * FC + 16 * rb + col] * tab[L::G_EB * FC + 16 * rb + col];
+#pragma unroll
+        for (int cb = 0; cb < rb; ++cb) {
+            const float4 fr = *reinterpret_cast<const float4*>(tab + L::G_FB * FC + 16 * cb + 4 * g4);
+            const float f = f0 * cross_decay<DK, NW>(tab, cb, rb);
+            f32x4 acc = go[rb * (rb - 1) / 2 + cb];
+            acc[0] *= f * fr.x;
+            acc[1] *= f * fr.y;
+            acc[2] *= f * fr.z;
+            acc[3] *= f * fr.w;
+            if constexpr (NORM) {
+                const float nr = nkv[16 * rb + col];
+                const float4 nc = *reinterpret_cast<const float4*>(nkv + 16 * cb + 4 * g4);
+                acc[0] *= nr * nc.x; acc[1] *= nr * nc.y; acc[2] *= nr * nc.z; acc[3] *= nr * nc.w;
+            }
+            Ao[rb][cb] = to_f16(acc);
+        }
+    }
+    // X_bb in B layout (4g4 + e, col) from the A layout: X_bb = X_bb I.
+    f16x4 eye;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) eye[j] = col == 4 * g4 + j ? (_Float16)1.f : (_Float16)0.f;
+    f32x4 Xb[FNB];
+#pragma unroll
+    for (int b = 0; b < FNB; ++b) Xb[b] = mma16(Xa[b], eye, zero4());
     // T = X Diag(beta) satisfies the same recurrence, T_ij = -X_ii sum A_im T_mj,
     // from T_jj = X_jj Diag(beta_j).  Row wavefront: for row block i, every
     // column block j < i at once (the T_mj it needs, m < i, are done), so
@@ -496,11 +599,10 @@ __device__ __forceinline__ void prep_t(char* smem, const char* st, const float* 
     }
 }
 
-// Prep P: the off-diagonal blocks of A (for the T wave) and P = (Q K^T)
-// masked and decayed, stored transposed.
+// Prep P: P = (Q K^T) masked and decayed, stored transposed (and, with the
+// prologue, the compute waves' per-token norm factors).
 template <int DK, int NW, bool NORM>
-__device__ __forceinline__ void prep_p(char* smem, const char* st, float* tab, char* tp, int n,
-                                       int lane) {
+__device__ __forceinline__ void prep_p(const char* st, float* tab, char* tp, int lane) {
     using L = FLayout<DK, NW>;
     constexpr int NKC = DK / 32;
     const int col = lane & 15, g4 = lane >> 4;
@@ -539,47 +641,6 @@ __device__ __forceinline__ void prep_p(char* smem, const char* st, float* tab, c
         tab[L::G_GMK * FC + lane] = gm * nk1;
         tab[L::G_GQ * FC + lane] = gm * nq1;
         tab[L::G_GHK * FC + lane] = tab[L::G_GH * FC + lane] * nk1;
-    }
-    // Off-diagonal blocks of A for the T wave, first: lane (col, g4) of block
-    // (rb, cb) holds A[16rb + col][16cb + 4g4 + e], computed as K_cb K_rb^T
-    // (the transpose of the needed block of the symmetric Gram matrix), with
-    // A[r][i] = beta_r e^{g_r - g_i} G[r][i] and the decay split at the block
-    // boundaries (see gate_table).
-    {
-        constexpr int NOFF = FNB * (FNB - 1) / 2;
-        f32x4 go[NOFF];
-#pragma unroll
-        for (int t = 0; t < NOFF; ++t) go[t] = zero4();
-#pragma unroll
-        for (int s = 0; s < NKC; ++s) {
-            int t = 0;
-#pragma unroll
-            for (int rb = 1; rb < FNB; ++rb)
-#pragma unroll
-                for (int cb = 0; cb < rb; ++cb, ++t) go[t] = Mma<__bf16>::mma(kf[cb][s], kf[rb][s], go[t]);
-        }
-        f16x4* ao = reinterpret_cast<f16x4*>(smem + L::AO);
-#pragma unroll
-        for (int rb = 1; rb < FNB; ++rb) {
-            const float f0 = tab[L::G_BE * FC + 16 * rb + col] * tab[L::G_EB * FC + 16 * rb + col];
-#pragma unroll
-            for (int cb = 0; cb < rb; ++cb) {
-                const float4 fr = *reinterpret_cast<const float4*>(tab + L::G_FB * FC + 16 * cb + 4 * g4);
-                const float f = f0 * cross_decay<DK, NW>(tab, cb, rb);
-                f32x4 acc = go[rb * (rb - 1) / 2 + cb];
-                acc[0] *= f * fr.x;
-                acc[1] *= f * fr.y;
-                acc[2] *= f * fr.z;
-                acc[3] *= f * fr.w;
-                if constexpr (NORM) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[e] *= nk[rb].c * nk[cb].r[e];
-                }
-                ao[(rb * (rb - 1) / 2 + cb) * 64 + lane] = to_f16(acc);
-            }
-        }
-        __hip_atomic_store(reinterpret_cast<int*>(smem + L::FLAG), n + 1, __ATOMIC_RELEASE,
-                           __HIP_MEMORY_SCOPE_WORKGROUP);
     }
     constexpr int NP = FNB * (FNB + 1) / 2;
     f32x4 pa[NP];
@@ -623,7 +684,7 @@ __device__ __forceinline__ void prep_p(char* smem, const char* st, float* tab, c
 }
 
 template <int DK, int NW, bool NORM>
-__global__ __launch_bounds__(64 * (NW + 4)) void fused_chunk(
+__global__ __launch_bounds__(64 * (NW + 5)) void fused_chunk(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta, const float* __restrict__ S0,
     __bf16* __restrict__ o, float* __restrict__ ST, int64_t T, int H, int NT, int DV, int sigb) {
@@ -835,7 +896,54 @@ __global__ __launch_bounds__(64 * (NW + 4)) void fused_chunk(
             }
         }
     } else if (wave == NW) {
-        // ---------------- prep T ----------------
+        // ---------------- prep P ----------------
+        for (int w = -2; w < NT; ++w) {
+            const int n = w + 1;
+            if (n >= 0 && n < NT) prep_p<DK, NW, NORM>(GDR_STAGE(n), GDR_GTAB(n), GDR_TPBUF(n), lane);
+            __syncthreads();
+        }
+    } else if (wave == NW + 1) {
+        // ---------------- solve: diagonal blocks of T, one chunk ahead ----------------
+        // Window w inverts the diagonal blocks of chunk c = w + 2 from K
+        // fragments and gate values loaded from global memory in the window
+        // before, and loads chunk c + 1's.
+        bf16x8 kc[FNB][NKC];
+        float la, bb;
+        solve_loads<DK>(k, log_alpha, beta, GDR_ROW0(0), GDR_LEN(0), H, lane, kc, la, bb);
+        // Nothing may enter the loop in flight: the compiler cannot count loads
+        // across the loop's back edge, and a load pending at its entry would
+        // make it wait for every load at the first use in each window, the new
+        // prefetch included.  The empty asm reads the values, which places the
+        // wait for them here.
+#pragma unroll
+        for (int rb = 0; rb < FNB; ++rb)
+#pragma unroll
+            for (int s = 0; s < NKC; ++s) asm volatile("" ::"v"(kc[rb][s]));
+        asm volatile("" ::"v"(la), "v"(bb));
+        for (int w = -2; w < NT; ++w) {
+            const int c = w + 2;
+            if (c < NT) {
+                bf16x8 kn[FNB][NKC];
+                float la1 = 0.f, bb1 = 0.f;
+                if (c + 1 < NT)
+                    solve_loads<DK>(k, log_alpha, beta, GDR_ROW0(c + 1), GDR_LEN(c + 1), H, lane, kn, la1, bb1);
+                solve_diag<DK, NW, NORM>(smem, kc, la, bb, GDR_LEN(c), sigb != 0,
+                                         smem + L::XH + (c & 1) * L::XHB, lane);
+                // The prefetch has landed by now (a window of work after it
+                // was issued); the copies wait for it here.
+                if (c + 1 < NT) {
+#pragma unroll
+                    for (int rb = 0; rb < FNB; ++rb)
+#pragma unroll
+                        for (int s = 0; s < NKC; ++s) kc[rb][s] = kn[rb][s];
+                    la = la1;
+                    bb = bb1;
+                }
+            }
+            __syncthreads();
+        }
+    } else if (wave == NW + 4) {
+        // ---------------- recurrence: off-diagonal blocks of T ----------------
         // The strictly upper tiles of T and P are zero in both buffers for good.
         for (int bf = 0; bf < 2; ++bf)
 #pragma unroll
@@ -847,15 +955,9 @@ __global__ __launch_bounds__(64 * (NW + 4)) void fused_chunk(
                 }
         for (int w = -2; w < NT; ++w) {
             const int n = w + 1;
-            if (n >= 0 && n < NT) prep_t<DK, NW, NORM>(smem, GDR_STAGE(n), GDR_GTAB(n), GDR_TPBUF(n), n, lane);
-            __syncthreads();
-        }
-    } else if (wave == NW + 1) {
-        // ---------------- prep P ----------------
-        if (lane == 0) *reinterpret_cast<int*>(smem + L::FLAG) = 0;
-        for (int w = -2; w < NT; ++w) {
-            const int n = w + 1;
-            if (n >= 0 && n < NT) prep_p<DK, NW, NORM>(smem, GDR_STAGE(n), GDR_GTAB(n), GDR_TPBUF(n), n, lane);
+            if (n >= 0 && n < NT)
+                recur_off<DK, NW, NORM>(GDR_STAGE(n), GDR_GTAB(n), smem + L::XH + (n & 1) * L::XHB,
+                                        GDR_TPBUF(n), lane);
             __syncthreads();
         }
     } else {
@@ -901,7 +1003,7 @@ template <int DK, int NW, bool NORM>
 hipError_t launch_fused(const ChunkArgs& a) {
     const int NT = (int)((a.T + FC - 1) / FC);
     const int64_t grid = a.B * a.H * (a.dv / (16 * NW));
-    hipLaunchKernelGGL((fused_chunk<DK, NW, NORM>), dim3((unsigned)grid), dim3(64 * (NW + 4)), 0, a.stream,
+    hipLaunchKernelGGL((fused_chunk<DK, NW, NORM>), dim3((unsigned)grid), dim3(64 * (NW + 5)), 0, a.stream,
                        (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, a.log_alpha, a.beta,
                        a.S0, (__bf16*)a.o, a.S_T, a.T, (int)a.H, NT, (int)a.dv,
                        (a.prologue & kPrologueBetaSigmoid) ? 1 : 0);
