@@ -97,14 +97,21 @@ struct FLayout {
     static constexpr int G_GHK = 9;       // e^{g_last - g_r} n_k(r)
     static constexpr int GSLOT = 10 * FC * 4;
     static constexpr int GT0 = XA + FNB * 272 * 4;
-    // Solve wave -> recurrence wave, a 2-deep ring (chunk c in slot c % 2): the
-    // inverted diagonal blocks X_bb (fp16, A-operand layout, 64 lanes x 4 per
-    // block), then the inverse key norms n_k (prologue).
+    // The rest depends on how T is built (see the kernel):
+    // - one T wave: the off-diagonal blocks of A (P wave -> T wave), fp16 per
+    //   lane, and the index + 1 of the chunk whose blocks are there;
+    static constexpr int AO = GT0 + 3 * GSLOT;
+    static constexpr int FLAG = AO + 6 * 64 * 8;
+    // - solve and recurrence waves: a 2-deep ring (chunk c in slot c % 2) of
+    //   the inverted diagonal blocks X_bb (fp16, A-operand layout, 64 lanes x 4
+    //   per block) and the inverse key norms n_k (prologue), then the solve
+    //   wave's own g (log2 units) and beta rows.
     static constexpr int XH = GT0 + 3 * GSLOT;
     static constexpr int XHB = FNB * 64 * 8 + FC * 4;
-    static constexpr int TG = XH + 2 * XHB;               // solve wave's own g (log2 units) and beta rows
-    static constexpr int TOTAL = TG + 2 * FC * 4;
-    static_assert(TOTAL <= 160 * 1024, "LDS budget");
+    static constexpr int TG = XH + 2 * XHB;
+    template <bool SPLIT>
+    static constexpr int total() { return SPLIT ? TG + 2 * FC * 4 : FLAG + 16; }
+    static_assert(total<true>() <= 160 * 1024 && total<false>() <= 160 * 1024, "LDS budget");
 };
 
 __device__ __forceinline__ bf16x8 lds_b128(const char* p) { return *reinterpret_cast<const bf16x8*>(p); }
@@ -337,6 +344,169 @@ __device__ __forceinline__ InvNorms inv_norms(const f32x4& G, int lane) {
     return n;
 }
 
+// Prep T: T = (I + A)^-1 Diag(beta) for one chunk, in one wave.
+//  - The diagonal Gram tiles K_b K_b^T on the matrix cores; the off-diagonal
+//    blocks of A come from the P wave (A-operand layout) through LDS.
+//  - Diagonal blocks: with A_bb = [[A11, 0], [A21, A22]] (8x8 blocks),
+//    D = blockdiag((I + A11)^-1, (I + A22)^-1) and N = [[0, 0], [A21, 0]],
+//        X_bb = (I + A_bb)^-1 = D - D N D.
+//    The 8x8 inverses come from forward substitution in fp32 (lane = column j
+//    of half h of block b; at most 7 dependent steps), the correction from fp16
+//    16x16x16 MFMAs, in both operand layouts.
+//  - Off-diagonal blocks of X = (I + A)^-1 by the block recurrence
+//        X_ij = -X_ii sum_{m=j}^{i-1} A_im X_mj
+//    (carried out for T = X Diag(beta) directly) on fp16 16x16x16 MFMAs with
+//    fp32 accumulation, row block by row block.
+//  Entries of A and X are bounded by small constants here (unit-norm keys,
+//  beta <= 1, decays <= 1), well inside fp16's range; T is rounded to bf16 after.
+template <int DK, int NW, bool NORM>
+__device__ __forceinline__ void prep_t(char* smem, const char* st, const float* tab, char* tp, int n,
+                                       int lane) {
+    using L = FLayout<DK, NW>;
+    constexpr int NKC = DK / 32;
+    float* xa = reinterpret_cast<float*>(smem + L::XA);
+    const int col = lane & 15, g4 = lane >> 4;
+
+    bf16x8 kf[FNB][NKC];
+#pragma unroll
+    for (int rb = 0; rb < FNB; ++rb)
+#pragma unroll
+        for (int s = 0; s < NKC; ++s) kf[rb][s] = qk_frag<DK>(st + L::S_K, rb, s, lane);
+    // Gram tiles of the diagonal blocks (symmetric): element (4g4 + e, col).
+    f32x4 Gd[FNB];
+#pragma unroll
+    for (int b = 0; b < FNB; ++b) Gd[b] = zero4();
+#pragma unroll
+    for (int s = 0; s < NKC; ++s)
+#pragma unroll
+        for (int b = 0; b < FNB; ++b) Gd[b] = Mma<__bf16>::mma(kf[b][s], kf[b][s], Gd[b]);
+    // A_bb in B layout (row 4g4 + e, column col), also stored transposed:
+    // xa[b][m][i] = A_bb[i][m].  Entries on or above the diagonal are not
+    // masked: nothing reads them (the substitution uses rows i > m only, and N
+    // lies strictly below).
+    f32x4 Ab[FNB];
+#pragma unroll
+    for (int b = 0; b < FNB; ++b) {
+        const float4 gr = *reinterpret_cast<const float4*>(tab + L::G_G2 * FC + 16 * b + 4 * g4);
+        const float4 br = *reinterpret_cast<const float4*>(tab + L::G_BE * FC + 16 * b + 4 * g4);
+        const float gc = tab[L::G_G2 * FC + 16 * b + col];
+        const float grv[4] = {gr.x, gr.y, gr.z, gr.w}, brv[4] = {br.x, br.y, br.z, br.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Ab[b][e] = Gd[b][e] * brv[e] * __builtin_amdgcn_exp2f(grv[e] - gc);
+        if constexpr (NORM) {   // prologue: A from the normalised keys
+            const InvNorms nk = inv_norms(Gd[b], lane);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Ab[b][e] *= nk.r[e] * nk.c;
+        }
+        *reinterpret_cast<float4*>(xa + b * 272 + col * 16 + 4 * g4) =
+            make_float4(Ab[b][0], Ab[b][1], Ab[b][2], Ab[b][3]);
+    }
+    // 8x8 forward substitution: lane (blk, h, j) builds column j of (I + A_hh)^-1.
+    {
+        const int blk = lane >> 4, h = (lane >> 3) & 1, j = lane & 7;
+        float* Ab8 = xa + blk * 272 + 8 * h * 16 + 8 * h;   // element (i, m) of A_hh at Ab8[m * 16 + i]
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = (i == j) ? 1.f : 0.f;
+#pragma unroll
+        for (int m = 0; m < 7; ++m) {
+            float am[8];
+#pragma unroll
+            for (int qv = (m + 1) / 4; qv < 2; ++qv) {
+                const float4 t = *reinterpret_cast<const float4*>(Ab8 + m * 16 + 4 * qv);
+                am[4 * qv] = t.x; am[4 * qv + 1] = t.y; am[4 * qv + 2] = t.z; am[4 * qv + 3] = t.w;
+            }
+#pragma unroll
+            for (int i = m + 1; i < 8; ++i) x[i] -= am[i] * x[m];
+        }
+        // D = blockdiag of the 8x8 inverses, staged row-major over the diagonal
+        // quadrants of the A tile: D[blk][r][c] at blk*272 + r*16 + c.  The
+        // upper-right quadrant (rows < 8, columns >= 8) keeps A transposed, i.e.
+        // the lower-left block N of A_bb: N[c][r] at blk*272 + r*16 + c.
+#pragma unroll
+        for (int i = 0; i < 8; ++i) Ab8[i * 16 + j] = x[i];
+    }
+    // Operands of X_bb = D - D N D for all four blocks (loads first, selects after).
+    const bool same = (g4 >> 1) == (col >> 3);   // rows 4g4.. and column col in one 8x8 half
+    f32x4 DbB[FNB], DbA[FNB], NA[FNB], NB[FNB];
+#pragma unroll
+    for (int b = 0; b < FNB; ++b) {
+        const float* Db = xa + b * 272;
+        // element (4g4 + e, col) of the staged tile: D there on the diagonal
+        // quadrants, N[col][4g4 + e] on the upper-right one
+        f32x4 tb;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tb[e] = Db[(4 * g4 + e) * 16 + col];
+        const float4 t = *reinterpret_cast<const float4*>(Db + col * 16 + 4 * g4);
+        const bool nb = g4 >= 2 && col < 8, na = col >= 8 && g4 < 2;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            DbB[b][e] = same ? tb[e] : 0.f;
+            NA[b][e] = na ? tb[e] : 0.f;
+            NB[b][e] = nb ? Ab[b][e] : 0.f;
+        }
+        DbA[b] = same ? f32x4{t.x, t.y, t.z, t.w} : zero4();
+    }
+    f32x4 Xb[FNB];   // X_bb, B layout: (4g4 + e, col)
+    f16x4 Xa[FNB];   // X_bb, A layout: (col, 4g4 + e)
+    {
+        f16x4 dB[FNB], dA[FNB];
+        f32x4 nd[FNB], ntdt[FNB];
+#pragma unroll
+        for (int b = 0; b < FNB; ++b) {
+            dB[b] = to_f16(DbB[b]);
+            dA[b] = to_f16(DbA[b]);
+            nd[b] = mma16(to_f16(NA[b]), dB[b], zero4());       // B layout of N D
+            ntdt[b] = mma16(to_f16(NB[b]), dA[b], zero4());     // B layout of N^T D^T
+        }
+#pragma unroll
+        for (int b = 0; b < FNB; ++b) {
+            Xb[b] = DbB[b] - mma16(dA[b], to_f16(nd[b]), zero4());            // D - (D N D), B layout
+            Xa[b] = to_f16(DbA[b] - mma16(dB[b], to_f16(ntdt[b]), zero4()));  // the same, A layout
+        }
+    }
+    // Off-diagonal blocks of A, from the P wave (A-operand layout).
+    while (__hip_atomic_load(reinterpret_cast<int*>(smem + L::FLAG), __ATOMIC_ACQUIRE,
+                             __HIP_MEMORY_SCOPE_WORKGROUP) != n + 1)
+        __builtin_amdgcn_s_sleep(1);
+    f16x4 Ao[FNB][FNB];
+    {
+        const f16x4* ao = reinterpret_cast<const f16x4*>(smem + L::AO);
+#pragma unroll
+        for (int rb = 1; rb < FNB; ++rb)
+#pragma unroll
+            for (int cb = 0; cb < rb; ++cb) Ao[rb][cb] = ao[(rb * (rb - 1) / 2 + cb) * 64 + lane];
+    }
+    // T = X Diag(beta) satisfies the same recurrence, T_ij = -X_ii sum A_im T_mj,
+    // from T_jj = X_jj Diag(beta_j).  Row wavefront: for row block i, every
+    // column block j < i at once (the T_mj it needs, m < i, are done), so
+    // independent chains interleave.
+    char* Tt = tp + L::T_T;
+    f16x4 xm[FNB][FNB];   // B layout of T_mj, fp16
+#pragma unroll
+    for (int j = 0; j < FNB; ++j) {
+        const f32x4 t = Xb[j] * tab[L::G_BE * FC + 16 * j + col];
+        tp_store(Tt, j, j, lane, t);
+        xm[j][j] = to_f16(t);
+    }
+#pragma unroll
+    for (int i = 1; i < FNB; ++i) {
+        f32x4 y[FNB];
+#pragma unroll
+        for (int j = 0; j < i; ++j) y[j] = zero4();
+#pragma unroll
+        for (int m = 0; m < i; ++m)
+#pragma unroll
+            for (int j = 0; j <= m; ++j) y[j] = mma16(Ao[i][m], xm[m][j], y[j]);
+#pragma unroll
+        for (int j = 0; j < i; ++j) {
+            const f32x4 z = -mma16(Xa[i], to_f16(y[j]), zero4());
+            xm[i][j] = to_f16(z);
+            tp_store(Tt, i, j, lane, z);
+        }
+    }
+}
+
 // Within one wave, LDS written by some lanes and read by others: the fences
 // keep the compiler from moving the reads above the writes (the hardware keeps
 // one wave's LDS accesses in order).
@@ -346,8 +516,9 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// T = (I + A)^-1 Diag(beta) is built by two waves, so that neither waits on
-// the other inside a window:
+// With the gate prologue (whose P wave carries the norm work), T = (I + A)^-1
+// Diag(beta) is built by two waves instead, so that neither waits on the other
+// inside a window:
 //  - the solve wave inverts the diagonal blocks of chunk c one window before
 //    the recurrence wave needs them, from K fragments and gate values it reads
 //    from global memory itself (prefetched one window earlier still; the LDS
@@ -599,10 +770,11 @@ __device__ __forceinline__ void recur_off(const char* st, const float* tab, cons
     }
 }
 
-// Prep P: P = (Q K^T) masked and decayed, stored transposed (and, with the
-// prologue, the compute waves' per-token norm factors).
-template <int DK, int NW, bool NORM>
-__device__ __forceinline__ void prep_p(const char* st, float* tab, char* tp, int lane) {
+// Prep P: with one T wave, first the off-diagonal blocks of A for it; then
+// P = (Q K^T) masked and decayed, stored transposed (and, with the prologue,
+// the compute waves' per-token norm factors).
+template <int DK, int NW, bool NORM, bool SPLIT>
+__device__ __forceinline__ void prep_p(char* smem, const char* st, float* tab, char* tp, int n, int lane) {
     using L = FLayout<DK, NW>;
     constexpr int NKC = DK / 32;
     const int col = lane & 15, g4 = lane >> 4;
@@ -641,6 +813,47 @@ __device__ __forceinline__ void prep_p(const char* st, float* tab, char* tp, int
         tab[L::G_GMK * FC + lane] = gm * nk1;
         tab[L::G_GQ * FC + lane] = gm * nq1;
         tab[L::G_GHK * FC + lane] = tab[L::G_GH * FC + lane] * nk1;
+    }
+    // Off-diagonal blocks of A for the T wave, first: lane (col, g4) of block
+    // (rb, cb) holds A[16rb + col][16cb + 4g4 + e], computed as K_cb K_rb^T
+    // (the transpose of the needed block of the symmetric Gram matrix), with
+    // A[r][i] = beta_r e^{g_r - g_i} G[r][i] and the decay split at the block
+    // boundaries (see gate_table).
+    if constexpr (!SPLIT) {
+        constexpr int NOFF = FNB * (FNB - 1) / 2;
+        f32x4 go[NOFF];
+#pragma unroll
+        for (int t = 0; t < NOFF; ++t) go[t] = zero4();
+#pragma unroll
+        for (int s = 0; s < NKC; ++s) {
+            int t = 0;
+#pragma unroll
+            for (int rb = 1; rb < FNB; ++rb)
+#pragma unroll
+                for (int cb = 0; cb < rb; ++cb, ++t) go[t] = Mma<__bf16>::mma(kf[cb][s], kf[rb][s], go[t]);
+        }
+        f16x4* ao = reinterpret_cast<f16x4*>(smem + L::AO);
+#pragma unroll
+        for (int rb = 1; rb < FNB; ++rb) {
+            const float f0 = tab[L::G_BE * FC + 16 * rb + col] * tab[L::G_EB * FC + 16 * rb + col];
+#pragma unroll
+            for (int cb = 0; cb < rb; ++cb) {
+                const float4 fr = *reinterpret_cast<const float4*>(tab + L::G_FB * FC + 16 * cb + 4 * g4);
+                const float f = f0 * cross_decay<DK, NW>(tab, cb, rb);
+                f32x4 acc = go[rb * (rb - 1) / 2 + cb];
+                acc[0] *= f * fr.x;
+                acc[1] *= f * fr.y;
+                acc[2] *= f * fr.z;
+                acc[3] *= f * fr.w;
+                if constexpr (NORM) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[e] *= nk[rb].c * nk[cb].r[e];
+                }
+                ao[(rb * (rb - 1) / 2 + cb) * 64 + lane] = to_f16(acc);
+            }
+        }
+        __hip_atomic_store(reinterpret_cast<int*>(smem + L::FLAG), n + 1, __ATOMIC_RELEASE,
+                           __HIP_MEMORY_SCOPE_WORKGROUP);
     }
     constexpr int NP = FNB * (FNB + 1) / 2;
     f32x4 pa[NP];
@@ -684,7 +897,7 @@ __device__ __forceinline__ void prep_p(const char* st, float* tab, char* tp, int
 }
 
 template <int DK, int NW, bool NORM>
-__global__ __launch_bounds__(64 * (NW + 5)) void fused_chunk(
+__global__ __launch_bounds__(64 * (NW + (NORM ? 5 : 4))) void fused_chunk(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta, const float* __restrict__ S0,
     __bf16* __restrict__ o, float* __restrict__ ST, int64_t T, int H, int NT, int DV, int sigb) {
@@ -694,7 +907,10 @@ __global__ __launch_bounds__(64 * (NW + 5)) void fused_chunk(
     constexpr int NKC = DK / 32;     // channel k-steps
     constexpr int NKT = FC / 32;     // token k-steps
     constexpr int CT = DK / 16;      // state tiles
-    __shared__ __attribute__((aligned(16))) char smem[L::TOTAL];
+    // With the gate prologue T is built by a solve and a recurrence wave (seven
+    // waves at NW = 2); without it by one T wave fed by the P wave (six).
+    constexpr bool SPLIT = NORM;
+    __shared__ __attribute__((aligned(16))) char smem[L::template total<SPLIT>()];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g4 = lane >> 4, col = lane & 15;
@@ -896,69 +1112,99 @@ __global__ __launch_bounds__(64 * (NW + 5)) void fused_chunk(
             }
         }
     } else if (wave == NW) {
-        // ---------------- prep P ----------------
-        for (int w = -2; w < NT; ++w) {
-            const int n = w + 1;
-            if (n >= 0 && n < NT) prep_p<DK, NW, NORM>(GDR_STAGE(n), GDR_GTAB(n), GDR_TPBUF(n), lane);
-            __syncthreads();
+        if constexpr (SPLIT) {
+            // ---------------- prep P ----------------
+            for (int w = -2; w < NT; ++w) {
+                const int n = w + 1;
+                if (n >= 0 && n < NT) prep_p<DK, NW, NORM, SPLIT>(smem, GDR_STAGE(n), GDR_GTAB(n), GDR_TPBUF(n), n, lane);
+                __syncthreads();
+            }
+        } else {
+            // ---------------- prep T ----------------
+            // The strictly upper tiles of T and P are zero in both buffers for good.
+            for (int bf = 0; bf < 2; ++bf)
+#pragma unroll
+                for (int rb = 0; rb < FNB; ++rb)
+#pragma unroll
+                    for (int cb = rb + 1; cb < FNB; ++cb) {
+                        tp_store(GDR_TPBUF(bf) + L::T_T, rb, cb, lane, zero4());
+                        tp_store(GDR_TPBUF(bf) + L::T_P, rb, cb, lane, zero4());
+                    }
+            for (int w = -2; w < NT; ++w) {
+                const int n = w + 1;
+                if (n >= 0 && n < NT) prep_t<DK, NW, NORM>(smem, GDR_STAGE(n), GDR_GTAB(n), GDR_TPBUF(n), n, lane);
+                __syncthreads();
+            }
         }
     } else if (wave == NW + 1) {
-        // ---------------- solve: diagonal blocks of T, one chunk ahead ----------------
-        // Window w inverts the diagonal blocks of chunk c = w + 2 from K
-        // fragments and gate values loaded from global memory in the window
-        // before, and loads chunk c + 1's.
-        bf16x8 kc[FNB][NKC];
-        float la, bb;
-        solve_loads<DK>(k, log_alpha, beta, GDR_ROW0(0), GDR_LEN(0), H, lane, kc, la, bb);
-        // Nothing may enter the loop in flight: the compiler cannot count loads
-        // across the loop's back edge, and a load pending at its entry would
-        // make it wait for every load at the first use in each window, the new
-        // prefetch included.  The empty asm reads the values, which places the
-        // wait for them here.
-#pragma unroll
-        for (int rb = 0; rb < FNB; ++rb)
-#pragma unroll
-            for (int s = 0; s < NKC; ++s) asm volatile("" ::"v"(kc[rb][s]));
-        asm volatile("" ::"v"(la), "v"(bb));
-        for (int w = -2; w < NT; ++w) {
-            const int c = w + 2;
-            if (c < NT) {
-                bf16x8 kn[FNB][NKC];
-                float la1 = 0.f, bb1 = 0.f;
-                if (c + 1 < NT)
-                    solve_loads<DK>(k, log_alpha, beta, GDR_ROW0(c + 1), GDR_LEN(c + 1), H, lane, kn, la1, bb1);
-                solve_diag<DK, NW, NORM>(smem, kc, la, bb, GDR_LEN(c), sigb != 0,
-                                         smem + L::XH + (c & 1) * L::XHB, lane);
-                // The prefetch has landed by now (a window of work after it
-                // was issued); the copies wait for it here.
-                if (c + 1 < NT) {
-#pragma unroll
-                    for (int rb = 0; rb < FNB; ++rb)
-#pragma unroll
-                        for (int s = 0; s < NKC; ++s) kc[rb][s] = kn[rb][s];
-                    la = la1;
-                    bb = bb1;
-                }
-            }
-            __syncthreads();
-        }
-    } else if (wave == NW + 4) {
-        // ---------------- recurrence: off-diagonal blocks of T ----------------
-        // The strictly upper tiles of T and P are zero in both buffers for good.
-        for (int bf = 0; bf < 2; ++bf)
-#pragma unroll
+        if constexpr (SPLIT) {
+            // ---------------- solve: diagonal blocks of T, one chunk ahead ----------------
+            // Window w inverts the diagonal blocks of chunk c = w + 2 from K
+            // fragments and gate values loaded from global memory in the window
+            // before, and loads chunk c + 1's.
+            bf16x8 kc[FNB][NKC];
+            float la, bb;
+            solve_loads<DK>(k, log_alpha, beta, GDR_ROW0(0), GDR_LEN(0), H, lane, kc, la, bb);
+            // Nothing may enter the loop in flight: the compiler cannot count loads
+            // across the loop's back edge, and a load pending at its entry would
+            // make it wait for every load at the first use in each window, the new
+            // prefetch included.  The empty asm reads the values, which places the
+            // wait for them here.
+    #pragma unroll
             for (int rb = 0; rb < FNB; ++rb)
-#pragma unroll
-                for (int cb = rb + 1; cb < FNB; ++cb) {
-                    tp_store(GDR_TPBUF(bf) + L::T_T, rb, cb, lane, zero4());
-                    tp_store(GDR_TPBUF(bf) + L::T_P, rb, cb, lane, zero4());
+    #pragma unroll
+                for (int s = 0; s < NKC; ++s) asm volatile("" ::"v"(kc[rb][s]));
+            asm volatile("" ::"v"(la), "v"(bb));
+            for (int w = -2; w < NT; ++w) {
+                const int c = w + 2;
+                if (c < NT) {
+                    bf16x8 kn[FNB][NKC];
+                    float la1 = 0.f, bb1 = 0.f;
+                    if (c + 1 < NT)
+                        solve_loads<DK>(k, log_alpha, beta, GDR_ROW0(c + 1), GDR_LEN(c + 1), H, lane, kn, la1, bb1);
+                    solve_diag<DK, NW, NORM>(smem, kc, la, bb, GDR_LEN(c), sigb != 0,
+                                             smem + L::XH + (c & 1) * L::XHB, lane);
+                    // The prefetch has landed by now (a window of work after it
+                    // was issued); the copies wait for it here.
+                    if (c + 1 < NT) {
+    #pragma unroll
+                        for (int rb = 0; rb < FNB; ++rb)
+    #pragma unroll
+                            for (int s = 0; s < NKC; ++s) kc[rb][s] = kn[rb][s];
+                        la = la1;
+                        bb = bb1;
+                    }
                 }
-        for (int w = -2; w < NT; ++w) {
-            const int n = w + 1;
-            if (n >= 0 && n < NT)
-                recur_off<DK, NW, NORM>(GDR_STAGE(n), GDR_GTAB(n), smem + L::XH + (n & 1) * L::XHB,
-                                        GDR_TPBUF(n), lane);
-            __syncthreads();
+                __syncthreads();
+            }
+        } else {
+            // ---------------- prep P ----------------
+            if (lane == 0) *reinterpret_cast<int*>(smem + L::FLAG) = 0;
+            for (int w = -2; w < NT; ++w) {
+                const int n = w + 1;
+                if (n >= 0 && n < NT) prep_p<DK, NW, NORM, SPLIT>(smem, GDR_STAGE(n), GDR_GTAB(n), GDR_TPBUF(n), n, lane);
+                __syncthreads();
+            }
+        }
+    } else if (SPLIT && wave == NW + 4) {
+        if constexpr (SPLIT) {
+            // ---------------- recurrence: off-diagonal blocks of T ----------------
+            // The strictly upper tiles of T and P are zero in both buffers for good.
+            for (int bf = 0; bf < 2; ++bf)
+    #pragma unroll
+                for (int rb = 0; rb < FNB; ++rb)
+    #pragma unroll
+                    for (int cb = rb + 1; cb < FNB; ++cb) {
+                        tp_store(GDR_TPBUF(bf) + L::T_T, rb, cb, lane, zero4());
+                        tp_store(GDR_TPBUF(bf) + L::T_P, rb, cb, lane, zero4());
+                    }
+            for (int w = -2; w < NT; ++w) {
+                const int n = w + 1;
+                if (n >= 0 && n < NT)
+                    recur_off<DK, NW, NORM>(GDR_STAGE(n), GDR_GTAB(n), smem + L::XH + (n & 1) * L::XHB,
+                                            GDR_TPBUF(n), lane);
+                __syncthreads();
+            }
         }
     } else {
         // ---------------- loaders ----------------
@@ -1003,7 +1249,7 @@ template <int DK, int NW, bool NORM>
 hipError_t launch_fused(const ChunkArgs& a) {
     const int NT = (int)((a.T + FC - 1) / FC);
     const int64_t grid = a.B * a.H * (a.dv / (16 * NW));
-    hipLaunchKernelGGL((fused_chunk<DK, NW, NORM>), dim3((unsigned)grid), dim3(64 * (NW + 5)), 0, a.stream,
+    hipLaunchKernelGGL((fused_chunk<DK, NW, NORM>), dim3((unsigned)grid), dim3(64 * (NW + (NORM ? 5 : 4))), 0, a.stream,
                        (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, a.log_alpha, a.beta,
                        a.S0, (__bf16*)a.o, a.S_T, a.T, (int)a.H, NT, (int)a.dv,
                        (a.prologue & kPrologueBetaSigmoid) ? 1 : 0);
