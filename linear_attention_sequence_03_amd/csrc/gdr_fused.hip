@@ -55,11 +55,18 @@ __device__ __forceinline__ f16x4 to_f16(f32x4 x) {
 }
 
 // Swizzles (piece index XOR), functions of the row's low 4 bits only, so rows
-// r and r + 16 share one.
+// r and r + 16 share one.  LDS has 32 banks of 4 bytes (128 bytes per cycle);
+// a 16-byte read serves 8 lanes per cycle, a 64-bit transposing read 16.
+// Q / K tiles: the 8 lanes of a row-fragment read (rows r..r+7, one piece
+// column) land on 8 distinct 16-byte bank groups; the K^T reads (4 rows x 4
+// pieces per 16 lanes, one 8-byte half of each piece) use every group twice,
+// the least possible for a fixed half.  The low three bits are r & 7 with bits
+// 1 and 2 swapped, flipped in bit 0 for rows 8..15.
 template <int DK>
 __device__ __forceinline__ int swz_qk(int r) {
-    if constexpr (DK == 128) return ((r & 7) << 1) | ((r >> 3) & 1);   // 16 pieces per row
-    else return (r >> 1) & 7;                                          // 8 pieces per row
+    const int lo = ((r & 1) | ((r & 2) << 1) | ((r & 4) >> 1)) ^ ((r >> 3) & 1);
+    if constexpr (DK == 128) return lo | (r & 8);   // 16 pieces per row
+    else return lo;                                 // 8 pieces per row
 }
 template <int VT>
 __device__ __forceinline__ int swz_v(int r) {
