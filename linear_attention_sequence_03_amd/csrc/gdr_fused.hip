@@ -75,6 +75,11 @@ __device__ __forceinline__ int swz_v(int r) {
 }
 __device__ __forceinline__ int swz_t(int i) { return (((i >> 1) & 3) << 1) | ((i >> 3) & 1); }
 
+// The T solve's fp32 scratch (four 16x16 tiles): rows of 20 floats, tiles of
+// 336, so that its float4 row accesses, its column reads and the substitution's
+// stores all spread over the 32 banks.
+constexpr int XROW = 20, XTILE = 16 * XROW + 16;
+
 template <int DK, int NW>
 struct FLayout {
     static constexpr int VT = 16 * NW;
@@ -88,7 +93,7 @@ struct FLayout {
     static constexpr int TP0 = NSTAGE * STAGE;
     static constexpr int XA = TP0 + 2 * TPB;              // solve wave's scratch: diagonal blocks of A
                                                           // (transposed), then blockdiag of their 8x8
-                                                          // inverses; fp32, tile stride 272, rows of 16
+                                                          // inverses; fp32, rows of XROW, tiles of XTILE
     // Gate tables, a 3-deep ring (chunk n in slot n % 3), 64 floats per field:
     static constexpr int G_G2 = 0;        // g_r * log2(e), g the in-chunk cumulative log decay
     static constexpr int G_BE = 1;        // beta_r
@@ -103,7 +108,7 @@ struct FLayout {
     static constexpr int G_GQ = 8;        // gamma_r n_q(r)
     static constexpr int G_GHK = 9;       // e^{g_last - g_r} n_k(r)
     static constexpr int GSLOT = 10 * FC * 4;
-    static constexpr int GT0 = XA + FNB * 272 * 4;
+    static constexpr int GT0 = XA + FNB * XTILE * 4;
     // The rest depends on how T is built (see the kernel):
     // - one T wave: the off-diagonal blocks of A (P wave -> T wave), fp16 per
     //   lane, and the index + 1 of the chunk whose blocks are there;
@@ -405,13 +410,13 @@ __device__ __forceinline__ void prep_t(char* smem, const char* st, const float* 
 #pragma unroll
             for (int e = 0; e < 4; ++e) Ab[b][e] *= nk.r[e] * nk.c;
         }
-        *reinterpret_cast<float4*>(xa + b * 272 + col * 16 + 4 * g4) =
+        *reinterpret_cast<float4*>(xa + b * XTILE + col * XROW + 4 * g4) =
             make_float4(Ab[b][0], Ab[b][1], Ab[b][2], Ab[b][3]);
     }
     // 8x8 forward substitution: lane (blk, h, j) builds column j of (I + A_hh)^-1.
     {
         const int blk = lane >> 4, h = (lane >> 3) & 1, j = lane & 7;
-        float* Ab8 = xa + blk * 272 + 8 * h * 16 + 8 * h;   // element (i, m) of A_hh at Ab8[m * 16 + i]
+        float* Ab8 = xa + blk * XTILE + 8 * h * XROW + 8 * h;   // element (i, m) of A_hh at Ab8[m * XROW + i]
         float x[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) x[i] = (i == j) ? 1.f : 0.f;
@@ -420,31 +425,31 @@ __device__ __forceinline__ void prep_t(char* smem, const char* st, const float* 
             float am[8];
 #pragma unroll
             for (int qv = (m + 1) / 4; qv < 2; ++qv) {
-                const float4 t = *reinterpret_cast<const float4*>(Ab8 + m * 16 + 4 * qv);
+                const float4 t = *reinterpret_cast<const float4*>(Ab8 + m * XROW + 4 * qv);
                 am[4 * qv] = t.x; am[4 * qv + 1] = t.y; am[4 * qv + 2] = t.z; am[4 * qv + 3] = t.w;
             }
 #pragma unroll
             for (int i = m + 1; i < 8; ++i) x[i] -= am[i] * x[m];
         }
         // D = blockdiag of the 8x8 inverses, staged row-major over the diagonal
-        // quadrants of the A tile: D[blk][r][c] at blk*272 + r*16 + c.  The
+        // quadrants of the A tile: D[blk][r][c] at blk*XTILE + r*XROW + c.  The
         // upper-right quadrant (rows < 8, columns >= 8) keeps A transposed, i.e.
-        // the lower-left block N of A_bb: N[c][r] at blk*272 + r*16 + c.
+        // the lower-left block N of A_bb: N[c][r] at blk*XTILE + r*XROW + c.
 #pragma unroll
-        for (int i = 0; i < 8; ++i) Ab8[i * 16 + j] = x[i];
+        for (int i = 0; i < 8; ++i) Ab8[i * XROW + j] = x[i];
     }
     // Operands of X_bb = D - D N D for all four blocks (loads first, selects after).
     const bool same = (g4 >> 1) == (col >> 3);   // rows 4g4.. and column col in one 8x8 half
     f32x4 DbB[FNB], DbA[FNB], NA[FNB], NB[FNB];
 #pragma unroll
     for (int b = 0; b < FNB; ++b) {
-        const float* Db = xa + b * 272;
+        const float* Db = xa + b * XTILE;
         // element (4g4 + e, col) of the staged tile: D there on the diagonal
         // quadrants, N[col][4g4 + e] on the upper-right one
         f32x4 tb;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) tb[e] = Db[(4 * g4 + e) * 16 + col];
-        const float4 t = *reinterpret_cast<const float4*>(Db + col * 16 + 4 * g4);
+        for (int e = 0; e < 4; ++e) tb[e] = Db[(4 * g4 + e) * XROW + col];
+        const float4 t = *reinterpret_cast<const float4*>(Db + col * XROW + 4 * g4);
         const bool nb = g4 >= 2 && col < 8, na = col >= 8 && g4 < 2;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -611,14 +616,14 @@ __device__ __forceinline__ void solve_diag(char* smem, const bf16x8 (&kf)[FNB][D
             for (int e = 0; e < 4; ++e) Ab[b][e] *= nk.r[e] * nk.c;
             nkl = g4 == b ? nk.c : nkl;
         }
-        *reinterpret_cast<float4*>(xa + b * 272 + col * 16 + 4 * g4) =
+        *reinterpret_cast<float4*>(xa + b * XTILE + col * XROW + 4 * g4) =
             make_float4(Ab[b][0], Ab[b][1], Ab[b][2], Ab[b][3]);
     }
     wave_lds_sync();
     // 8x8 forward substitution: lane (blk, h, j) builds column j of (I + A_hh)^-1.
     {
         const int blk = lane >> 4, h = (lane >> 3) & 1, j = lane & 7;
-        float* Ab8 = xa + blk * 272 + 8 * h * 16 + 8 * h;   // element (i, m) of A_hh at Ab8[m * 16 + i]
+        float* Ab8 = xa + blk * XTILE + 8 * h * XROW + 8 * h;   // element (i, m) of A_hh at Ab8[m * XROW + i]
         float x[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) x[i] = (i == j) ? 1.f : 0.f;
@@ -627,18 +632,18 @@ __device__ __forceinline__ void solve_diag(char* smem, const bf16x8 (&kf)[FNB][D
             float am[8];
 #pragma unroll
             for (int qv = (m + 1) / 4; qv < 2; ++qv) {
-                const float4 t = *reinterpret_cast<const float4*>(Ab8 + m * 16 + 4 * qv);
+                const float4 t = *reinterpret_cast<const float4*>(Ab8 + m * XROW + 4 * qv);
                 am[4 * qv] = t.x; am[4 * qv + 1] = t.y; am[4 * qv + 2] = t.z; am[4 * qv + 3] = t.w;
             }
 #pragma unroll
             for (int i = m + 1; i < 8; ++i) x[i] -= am[i] * x[m];
         }
         // D = blockdiag of the 8x8 inverses, staged row-major over the diagonal
-        // quadrants of the A tile: D[blk][r][c] at blk*272 + r*16 + c.  The
+        // quadrants of the A tile: D[blk][r][c] at blk*XTILE + r*XROW + c.  The
         // upper-right quadrant (rows < 8, columns >= 8) keeps A transposed, i.e.
-        // the lower-left block N of A_bb: N[c][r] at blk*272 + r*16 + c.
+        // the lower-left block N of A_bb: N[c][r] at blk*XTILE + r*XROW + c.
 #pragma unroll
-        for (int i = 0; i < 8; ++i) Ab8[i * 16 + j] = x[i];
+        for (int i = 0; i < 8; ++i) Ab8[i * XROW + j] = x[i];
     }
     wave_lds_sync();
     // Operands of X_bb = D - D N D for all four blocks (loads first, selects after).
@@ -646,13 +651,13 @@ __device__ __forceinline__ void solve_diag(char* smem, const bf16x8 (&kf)[FNB][D
     f32x4 DbB[FNB], DbA[FNB], NA[FNB], NB[FNB];
 #pragma unroll
     for (int b = 0; b < FNB; ++b) {
-        const float* Db = xa + b * 272;
+        const float* Db = xa + b * XTILE;
         // element (4g4 + e, col) of the staged tile: D there on the diagonal
         // quadrants, N[col][4g4 + e] on the upper-right one
         f32x4 tb;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) tb[e] = Db[(4 * g4 + e) * 16 + col];
-        const float4 t = *reinterpret_cast<const float4*>(Db + col * 16 + 4 * g4);
+        for (int e = 0; e < 4; ++e) tb[e] = Db[(4 * g4 + e) * XROW + col];
+        const float4 t = *reinterpret_cast<const float4*>(Db + col * XROW + 4 * g4);
         const bool nb = g4 >= 2 && col < 8, na = col >= 8 && g4 < 2;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
