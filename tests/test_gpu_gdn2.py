@@ -44,6 +44,20 @@ def test_gdn2_parity(io, d, gate, T):
     assert eo <= TOL[io] and es <= TOL[io], (eo, es)
 
 
+@pytest.mark.parametrize("T", [2, 5, 6, 7, 12])
+@pytest.mark.parametrize("io,d,gate", [("bf16", 64, "channel"), ("f32", 128, "scalar")])
+def test_gdn2_short_sequences(io, d, gate, T):
+    """Lengths around the kernel's ring of token-input buffers (shorter than
+    it, equal to it, one past it, two rounds): every token applied once, in
+    order."""
+    inp = _inputs(1, T, 2, d, gate, io, seed=240 + T + d)
+    o, st = _run(inp, io)
+    o_ref, st_ref = oracle.gdn2_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"],
+                                          inp["erase"], inp["write"], inp["S0"])
+    assert rel_err(host(o), o_ref) <= TOL[io]
+    assert rel_err(host(st), st_ref) <= TOL[io]
+
+
 def test_gdn2_tied_gates_match_kda_call():
     """b = w = beta (one number per token): the Gated DeltaNet-2 call equals the
     KDA call (two different GPU paths), fp32."""
