@@ -213,50 +213,51 @@ struct FragOffsets {
     }
 };
 
-// Loader wave lw (0 or 1): copies of chunk inputs into one stage, half of the
-// 1 KB copy instructions each.  The per-lane source offsets (bytes from the
-// chunk's first row) are fixed for full chunks and computed once; rows at or
-// past len repeat row len-1 (finite; the prep masks them out).
-template <int DK, int NW>
+// Loader wave lw (of NL): copies of chunk inputs into one stage, every NL-th
+// 1 KB copy instruction.  The per-lane source offsets (bytes from the chunk's
+// first row) are fixed for full chunks and computed once; rows at or past len
+// repeat row len-1 (finite; the prep masks them out).
+template <int DK, int NW, int NL>
 struct LoadOffsets {
-    static constexpr int NIQ = FLayout<DK, NW>::QB / 1024 / 2;   // Q (and K) instructions per loader
-    static constexpr int NIV = FLayout<DK, NW>::VB / 1024 / 2;   // V instructions per loader
+    static constexpr int NIQ = FLayout<DK, NW>::QB / 1024 / NL;   // Q (and K) instructions per loader
+    static constexpr int NIV = FLayout<DK, NW>::VB / 1024 / NL;   // V instructions per loader
+    static_assert(NIV * NL * 1024 == FLayout<DK, NW>::VB, "V tile split");
     int qk[NIQ];
     int v[NIV];
     __device__ __forceinline__ void set(int len, int H, int DV, int vt, int lw, int lane) {
         constexpr int VT = 16 * NW, RP = DK / 8, RPV = VT / 8;
 #pragma unroll
         for (int j = 0; j < NIQ; ++j) {
-            const int slot = 64 * (2 * j + lw) + lane;
+            const int slot = 64 * (NL * j + lw) + lane;
             const int r = slot / RP, pp = slot % RP;
             qk[j] = (r < len ? r : len - 1) * (H * DK * 2) + 16 * (pp ^ swz_qk<DK>(r));
         }
 #pragma unroll
         for (int j = 0; j < NIV; ++j) {
-            const int slot = 64 * (2 * j + lw) + lane;
+            const int slot = 64 * (NL * j + lw) + lane;
             const int r = slot / RPV, pp = slot % RPV;
             v[j] = (r < len ? r : len - 1) * (H * DV * 2) + vt * VT * 2 + 16 * (pp ^ swz_v<VT>(r));
         }
     }
 };
 
-template <int DK, int NW>
+template <int DK, int NW, int NL>
 __device__ __forceinline__ void load_chunk(char* stg, const __bf16* q, const __bf16* k, const __bf16* v,
-                                           int64_t row0, int DV, const LoadOffsets<DK, NW>& lo, int lw) {
+                                           int64_t row0, int DV, const LoadOffsets<DK, NW, NL>& lo, int lw) {
     using L = FLayout<DK, NW>;
-    using LO = LoadOffsets<DK, NW>;
+    using LO = LoadOffsets<DK, NW, NL>;
     const char* qb = reinterpret_cast<const char*>(q + row0 * DK);
     const char* kb = reinterpret_cast<const char*>(k + row0 * DK);
     const char* vb = reinterpret_cast<const char*>(v + row0 * DV);
 #pragma unroll
     for (int j = 0; j < LO::NIQ; ++j) {
-        const int ins = 2 * j + lw;
+        const int ins = NL * j + lw;
         __builtin_amdgcn_global_load_lds(qb + (uint32_t)lo.qk[j], (GDR_LDS void*)(stg + L::S_Q + 1024 * ins), 16, 0, 0);
         __builtin_amdgcn_global_load_lds(kb + (uint32_t)lo.qk[j], (GDR_LDS void*)(stg + L::S_K + 1024 * ins), 16, 0, 0);
     }
 #pragma unroll
     for (int j = 0; j < LO::NIV; ++j) {
-        const int ins = 2 * j + lw;
+        const int ins = NL * j + lw;
         __builtin_amdgcn_global_load_lds(vb + (uint32_t)lo.v[j], (GDR_LDS void*)(stg + L::S_V + 1024 * ins), 16, 0, 0);
     }
 }
@@ -908,8 +909,8 @@ __device__ __forceinline__ void prep_p(char* smem, const char* st, float* tab, c
     }
 }
 
-template <int DK, int NW, bool NORM>
-__global__ __launch_bounds__(64 * (NW + (NORM ? 5 : 4))) void fused_chunk(
+template <int DK, int NW, bool NORM, int NL>
+__global__ __launch_bounds__(64 * (NW + 2 + NL + (NORM ? 1 : 0))) void fused_chunk(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta, const float* __restrict__ S0,
     __bf16* __restrict__ o, float* __restrict__ ST, int64_t T, int H, int NT, int DV, int sigb) {
@@ -1198,7 +1199,7 @@ __global__ __launch_bounds__(64 * (NW + (NORM ? 5 : 4))) void fused_chunk(
                 __syncthreads();
             }
         }
-    } else if (SPLIT && wave == NW + 4) {
+    } else if (SPLIT && wave == NW + 2 + NL) {
         if constexpr (SPLIT) {
             // ---------------- recurrence: off-diagonal blocks of T ----------------
             // The strictly upper tiles of T and P are zero in both buffers for good.
@@ -1224,7 +1225,7 @@ __global__ __launch_bounds__(64 * (NW + (NORM ? 5 : 4))) void fused_chunk(
         // chunk c's gate table from gate values gathered one window earlier
         // (so nothing waits inside the window), and both gather chunk c + 1's.
         const int lw = wave - NW - 2;
-        LoadOffsets<DK, NW> lo;
+        LoadOffsets<DK, NW, NL> lo;
         lo.set(FC, H, DV, vt, lw, lane);
         float la, bb;
         {
@@ -1237,7 +1238,7 @@ __global__ __launch_bounds__(64 * (NW + (NORM ? 5 : 4))) void fused_chunk(
             if (n < NT) {
                 const int len = GDR_LEN(n);
                 if (len < FC) lo.set(len, H, DV, vt, lw, lane);   // ragged last chunk
-                load_chunk<DK, NW>(GDR_STAGE(n), q, k, v, GDR_ROW0(n), DV, lo, lw);
+                load_chunk<DK, NW, NL>(GDR_STAGE(n), q, k, v, GDR_ROW0(n), DV, lo, lw);
                 if (lw == 0) gate_table<DK, NW>(la, bb, len, lane, GDR_GTAB(n), sigb != 0);
                 if (n + 1 < NT) {
                     const int len1 = GDR_LEN(n + 1);
@@ -1257,11 +1258,18 @@ __global__ __launch_bounds__(64 * (NW + (NORM ? 5 : 4))) void fused_chunk(
 #undef GDR_GTAB
 }
 
+// Loader waves per workgroup.  One loader (every role alone on a SIMD at
+// NW = 1) measured 9 % slower on the 1x32x32768 shape and no faster at NW = 2.
+template <int NW, bool NORM>
+constexpr int kLoaders = 2;
+
 template <int DK, int NW, bool NORM>
 hipError_t launch_fused(const ChunkArgs& a) {
     const int NT = (int)((a.T + FC - 1) / FC);
     const int64_t grid = a.B * a.H * (a.dv / (16 * NW));
-    hipLaunchKernelGGL((fused_chunk<DK, NW, NORM>), dim3((unsigned)grid), dim3(64 * (NW + (NORM ? 5 : 4))), 0, a.stream,
+    constexpr int NL = kLoaders<NW, NORM>;
+    hipLaunchKernelGGL((fused_chunk<DK, NW, NORM, NL>), dim3((unsigned)grid), dim3(64 * (NW + 2 + NL + (NORM ? 1 : 0))), 0,
+                       a.stream,
                        (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, a.log_alpha, a.beta,
                        a.S0, (__bf16*)a.o, a.S_T, a.T, (int)a.H, NT, (int)a.dv,
                        (a.prologue & kPrologueBetaSigmoid) ? 1 : 0);
