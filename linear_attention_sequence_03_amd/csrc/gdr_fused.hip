@@ -121,8 +121,9 @@ struct FLayout {
     static constexpr int XH = GT0 + 3 * GSLOT;
     static constexpr int XHB = FNB * 64 * 8 + FC * 4;
     static constexpr int TG = XH + 2 * XHB;
+    static constexpr int WARM = FLAG + 16;   // L2-warming target of the loaders (never read)
     template <bool SPLIT>
-    static constexpr int total() { return SPLIT ? TG + 2 * FC * 4 : FLAG + 16; }
+    static constexpr int total() { return SPLIT ? TG + 2 * FC * 4 : WARM + 256; }
     static_assert(total<true>() <= 160 * 1024 && total<false>() <= 160 * 1024, "LDS budget");
 };
 
@@ -259,6 +260,27 @@ __device__ __forceinline__ void load_chunk(char* stg, const __bf16* q, const __b
     for (int j = 0; j < LO::NIV; ++j) {
         const int ins = NL * j + lw;
         __builtin_amdgcn_global_load_lds(vb + (uint32_t)lo.v[j], (GDR_LDS void*)(stg + L::S_V + 1024 * ins), 16, 0, 0);
+    }
+}
+
+// L2 warming of the chunk copied in the next window: one 4-byte LDS-DMA load
+// per 128-byte line of its Q rows (loader 0) and of its K rows and the
+// workgroup's V segment (loader 1), into a scratch word per lane that nothing
+// reads.  These loads stay in flight across the window barrier, and the next
+// window's copies then find the lines in L2.
+template <int DK, int NW>
+__device__ __forceinline__ void warm_chunk(char* scratch, const __bf16* q, const __bf16* k, const __bf16* v,
+                                           int64_t row0, int len, int H, int DV, int vt, int lw, int lane) {
+    const int64_t r = row0 + (int64_t)(lane < len ? lane : len - 1) * H;
+    if (lw == 0) {
+#pragma unroll
+        for (int j = 0; j < DK / 64; ++j)
+            __builtin_amdgcn_global_load_lds(q + r * DK + 64 * j, (GDR_LDS void*)scratch, 4, 0, 0);
+    } else {
+#pragma unroll
+        for (int j = 0; j < DK / 64; ++j)
+            __builtin_amdgcn_global_load_lds(k + r * DK + 64 * j, (GDR_LDS void*)scratch, 4, 0, 0);
+        __builtin_amdgcn_global_load_lds(v + r * DV + vt * 16 * NW, (GDR_LDS void*)scratch, 4, 0, 0);
     }
 }
 
@@ -923,6 +945,10 @@ __global__ __launch_bounds__(64 * (NW + 2 + NL + (NORM ? 1 : 0))) void fused_chu
     // With the gate prologue T is built by a solve and a recurrence wave (seven
     // waves at NW = 2); without it by one T wave fed by the P wave (six).
     constexpr bool SPLIT = NORM;
+    // L2 warming from the loaders where they set the window (one compute wave,
+    // eight workgroups per head: -7 % on the 1x32x32768 shape); with two
+    // compute waves the prep waves set it and the extra loads cost 1-2 %.
+    constexpr bool WARMING = !SPLIT && NW == 1;
     __shared__ __attribute__((aligned(16))) char smem[L::template total<SPLIT>()];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1233,6 +1259,10 @@ __global__ __launch_bounds__(64 * (NW + 2 + NL + (NORM ? 1 : 0))) void fused_chu
             la = log_alpha[go];
             bb = beta[go];
         }
+        // No load may be in flight at the loop entry (the compiler cannot count
+        // loads across the back edge and would then wait for all of them, the
+        // warming loads included, at each window's first use of la / bb).
+        asm volatile("" ::"v"(la), "v"(bb));
         for (int w = -2; w < NT; ++w) {
             const int n = w + 2;
             if (n < NT) {
@@ -1246,7 +1276,20 @@ __global__ __launch_bounds__(64 * (NW + 2 + NL + (NORM ? 1 : 0))) void fused_chu
                     la = log_alpha[go];
                     bb = beta[go];
                 }
-                __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): copies and gathers landed
+                if (WARMING && n + 1 < NT) {
+                    warm_chunk<DK, NW>(smem + L::WARM, q, k, v, GDR_ROW0(n + 1), GDR_LEN(n + 1), H, DV, vt, lw,
+                                       lane);
+                    // copies and gathers landed; the warming loads (issued last) stay in flight
+                    if (lw == 0) {
+                        if constexpr (DK == 128) __builtin_amdgcn_s_waitcnt(0x0F72);   // vmcnt(2)
+                        else __builtin_amdgcn_s_waitcnt(0x0F71);                       // vmcnt(1)
+                    } else {
+                        if constexpr (DK == 128) __builtin_amdgcn_s_waitcnt(0x0F73);   // vmcnt(3)
+                        else __builtin_amdgcn_s_waitcnt(0x0F72);                       // vmcnt(2)
+                    }
+                } else {
+                    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): copies and gathers landed
+                }
             }
             __syncthreads();
         }
