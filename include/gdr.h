@@ -244,6 +244,35 @@ gdr_status gdr_gdn2_fwd(const void *q, const void *k, const void *v,
                         int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                         gdr_dtype io, gdr_gate gate, hipStream_t stream);
 
+/*
+ * The same recurrence in chunkwise form (the organisation of the "FG2-GDN"
+ * page, section 3.6, carried over to the decoupled gates): per chunk of 64
+ * tokens, the reads of the chunk come from a unit-lower triangular solve
+ * against the erase directions, and everything that involves neither the
+ * state nor v is folded into per-chunk operands that a sequential pass over
+ * the chunks then applies on the matrix cores.  The result is the token
+ * recurrence above, reorganised with no approximation.
+ *
+ * Arguments as in gdr_gdn2_fwd, plus chunk and a caller-owned device
+ * workspace of gdr_gdn2_chunk_fwd_workspace_size bytes (72.5 KiB per
+ * 64-token chunk and head at dk = 128; no contents kept between calls).
+ * Supported: io = GDR_BF16, chunk = 64, dk = dv in {64, 128}; anything else
+ * returns GDR_ERR_UNSUPPORTED (gdr_gdn2_fwd takes those).  The preparation
+ * works in fp16 on matrix-core products whose entries stay small for keys of
+ * unit norm and gates in [0, 1]; keys of much larger norm should use
+ * gdr_gdn2_fwd.  Errors as in gdr_chunk_fwd.
+ */
+gdr_status gdr_gdn2_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H,
+                                             int64_t dk, int64_t dv, int64_t chunk,
+                                             gdr_dtype io, gdr_gate gate, size_t *bytes);
+
+gdr_status gdr_gdn2_chunk_fwd(const void *q, const void *k, const void *v,
+                              const float *log_alpha, const float *erase, const float *write,
+                              const float *S0, void *o, float *S_T,
+                              int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                              int64_t chunk, gdr_dtype io, gdr_gate gate,
+                              void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char *gdr_status_string(gdr_status s);
 

@@ -15,6 +15,8 @@ from .gdr import (  # noqa: F401
     gdr_fg2_chunk_fwd,
     gdr_fg2_chunk_fwd_workspace_size,
     gdr_fg2_decode_step,
+    gdr_gdn2_chunk_fwd,
+    gdr_gdn2_chunk_fwd_workspace_size,
     gdr_gdn2_fwd,
     gdr_status_string,
     load_library,

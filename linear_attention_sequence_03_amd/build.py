@@ -19,7 +19,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgdr.so")
-SOURCES = ["gdr_api.cpp", "gdr_decode.hip", "gdr_chunk.hip", "gdr_fused.hip", "gdr_fg2.hip", "gdr_gdn2.hip"]
+SOURCES = ["gdr_api.cpp", "gdr_decode.hip", "gdr_chunk.hip", "gdr_fused.hip", "gdr_fg2.hip", "gdr_gdn2.hip",
+           "gdr_gdn2_chunk.hip"]
 # plain device copy used only to calibrate hardware byte counters (bench.py --traffic)
 CALIB_LIB = os.path.join(PKG, "libgdr_calib.so")
 CALIB_SOURCES = ["gdr_calib.hip"]

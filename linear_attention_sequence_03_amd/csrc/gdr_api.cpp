@@ -309,6 +309,68 @@ gdr_status gdr_gdn2_fwd(const void* q, const void* k, const void* v, const float
     return GDR_OK;
 }
 
+gdr_status gdr_gdn2_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t dk,
+                                             int64_t dv, int64_t chunk, gdr_dtype io, gdr_gate gate,
+                                             size_t* bytes) {
+    g_last_error[0] = 0;
+    if (!bytes) return fail(GDR_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = 0;
+    gdr_status s = check_common(B, H, dk, dv, io, gate);
+    if (s != GDR_OK) return s;
+    if (T < 0) return fail(GDR_ERR_INVALID_ARG, "T must be >= 0 (T=%lld)", (long long)T);
+    if (chunk < 1) return fail(GDR_ERR_INVALID_ARG, "chunk must be positive");
+    if (!gdr::gdn2_chunk_supported(dk, dv, chunk, io == GDR_BF16))
+        return fail(GDR_ERR_UNSUPPORTED,
+                    "the chunkwise form takes bf16 io and chunk 64 (chunk=%lld); gdr_gdn2_fwd takes the rest",
+                    (long long)chunk);
+    const int64_t units = mul({B, H, (T + chunk - 1) / chunk});
+    if (units < 0 || units > INT32_MAX) return fail(GDR_ERR_UNSUPPORTED, "B*H*ceil(T/chunk) too large");
+    *bytes = gdr::gdn2_chunk_workspace_bytes(B, T, H, dk);
+    return GDR_OK;
+}
+
+gdr_status gdr_gdn2_chunk_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
+                              const float* erase, const float* write, const float* S0, void* o,
+                              float* S_T, int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                              int64_t chunk, gdr_dtype io, gdr_gate gate, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+    size_t need = 0;
+    gdr_status s = gdr_gdn2_chunk_fwd_workspace_size(B, T, H, dk, dv, chunk, io, gate, &need);
+    if (s != GDR_OK) return s;
+    const int64_t ntok = mul({B, T, H});
+    if (ntok < 0 || mul({ntok, dk}) < 0 || mul({B, H, dv, dk}) < 0 || mul({B, H, dv / 16}) > INT32_MAX)
+        return fail(GDR_ERR_UNSUPPORTED, "tensor sizes overflow");
+    if (mul({H, dv, 4, 64}) > INT32_MAX) return fail(GDR_ERR_UNSUPPORTED, "H too large");
+    if (T > 0 && (!q || !k || !v || !log_alpha || !erase || !write || !o))
+        return fail(GDR_ERR_INVALID_ARG, "q, k, v, log_alpha, erase, write and o must be non-NULL");
+    if (need > 0 && !workspace) return fail(GDR_ERR_INVALID_ARG, "workspace is NULL");
+    if (workspace_bytes < need)
+        return fail(GDR_ERR_INVALID_ARG, "workspace too small (%zu < %zu bytes)", workspace_bytes, need);
+    const int64_t la_elems = gate == GDR_GATE_CHANNEL ? ntok * dk : ntok;
+    const Range rs[] = {
+        rng("q", q, ntok * dk, 2),           rng("k", k, ntok * dk, 2),
+        rng("v", v, ntok * dv, 2),           rng("log_alpha", log_alpha, la_elems, 4),
+        rng("erase", erase, ntok * dk, 4),   rng("write", write, ntok * dv, 4),
+        rng("S0", S0, B * H * dv * dk, 4),   rng("o", o, ntok * dv, 2),
+        rng("S_T", S_T, B * H * dv * dk, 4), rng("workspace", workspace, (int64_t)need, 1),
+    };
+    s = check_ptrs(rs, 10, 7);
+    if (s != GDR_OK) return s;
+    if (T == 0) {   // no tokens: S_T = S0 (zeros when S0 is NULL)
+        if (!S_T) return GDR_OK;
+        gdr::ChunkArgs c{q, k, v, log_alpha, nullptr, S0, o, S_T, B, 0, H, dk, dv, 64,
+                         true, gate == GDR_GATE_CHANNEL, nullptr, stream};
+        const hipError_t err = gdr::chunk_fwd_launch(c);
+        if (err != hipSuccess) return fail(GDR_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(err));
+        return GDR_OK;
+    }
+    gdr::Gdn2Args a{q, k, v, log_alpha, erase, write, S0, o, S_T, B, T, H, dk, dv,
+                    true, gate == GDR_GATE_CHANNEL, stream};
+    const hipError_t err = gdr::gdn2_chunk_fwd_launch(a, workspace);
+    if (err != hipSuccess) return fail(GDR_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(err));
+    return GDR_OK;
+}
+
 gdr_status gdr_fg2_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t dk,
                                             int64_t dv, int64_t chunk, gdr_dtype io, gdr_gate gate,
                                             size_t* bytes) {

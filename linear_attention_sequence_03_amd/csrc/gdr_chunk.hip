@@ -627,13 +627,6 @@ __global__ __launch_bounds__(kThreads) void wy_prep_channel(
 //    zero above the diagonal blocks), Qg = Q.Gamma, Kg = K.Gamma,
 //    Kh = K.(gamma_C / Gamma) and gl = gamma_C.
 // ---------------------------------------------------------------------------
-template <int CTRL>
-__device__ __forceinline__ float dpp_shr(float x) {
-    // lanes without a source in their row of 16 get 0
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf,
-                                                                  0xf, false));
-}
-
 // LDS of one workgroup of wy_prep_channel_bf16.
 template <int DK, int C>
 struct ChanPrepSmem {
@@ -1049,46 +1042,6 @@ __global__ __launch_bounds__(64 * (C / 16), 4) void wy_prep_channel_bf16(
 // Kernel 2: sequential state pass.
 // ---------------------------------------------------------------------------
 
-// One tile of a chunk's inputs, copied global -> LDS by global_load_lds_dwordx4:
-// lane l of an instruction lands at LDS base + 16 l, so an instruction fills
-// 64 consecutive 16-byte slots and each lane fetches the global bytes of its
-// slot.  Rows are stored with a 16-byte pad, and the tile's LDS region is
-// rounded up to whole instructions; lanes whose slot is a pad or lies past the
-// tile fetch the tile's first 16 bytes again (in bounds, never read back), so
-// every lane of every instruction is active.  The per-lane source offsets are
-// fixed for the kernel and computed once.
-template <int ROWS, int ROWB, int NW>
-struct DmaTile {
-    static constexpr int RS = ROWB / 16 + 1;                 // slots per row, with the pad
-    static constexpr int NSLOT = ROWS * RS;
-    static constexpr int NINS = (NSLOT + 63) / 64;           // instructions per tile
-    static constexpr int BYTES = NINS * 1024;                // LDS region
-    static constexpr int PER_WAVE = (NINS + NW - 1) / NW;    // instructions per wave
-    // Offsets for row stride gstride; rows >= valid read row valid-1 instead
-    // (kept finite; their contributions are cancelled by zero rows of T).
-    static __device__ __forceinline__ void offsets(int* off, int64_t gstride, int valid, int wave,
-                                                   int lane) {
-#pragma unroll
-        for (int j = 0; j < PER_WAVE; ++j) {
-            const int slot = (wave + j * NW) * 64 + lane;
-            const int r = slot / RS, sg = slot - r * RS;
-            const int rr = r < valid ? r : valid - 1;
-            off[j] = (slot < NSLOT && sg < RS - 1) ? (int)(rr * gstride) + sg * 16 : 0;
-        }
-    }
-    static __device__ __forceinline__ void issue(char* lds, const char* src, const int* off, int wave) {
-#pragma unroll
-        for (int j = 0; j < PER_WAVE; ++j) {
-            const int ins = wave + j * NW;
-            if (j + 1 < PER_WAVE || ins < NINS)   // wave-uniform
-                __builtin_amdgcn_global_load_lds(src + off[j], (GDR_LDS void*)(lds + ins * 1024), 16,
-                                                 0, 0);
-        }
-    }
-};
-
-__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
 template <typename E, int DK, int C, int NW, bool CHANNEL>
 struct StageLayout {
     static constexpr int ES = sizeof(E);
@@ -1152,21 +1105,6 @@ __device__ __forceinline__ void issue_chunk(char* base, int n, const E* q, const
         for (int s = wave * 64 + lane; s < NVEC; s += SL::NL * 64)
             __builtin_amdgcn_global_load_lds(blk + L::VEC + 16 * s,
                                              (GDR_LDS void*)(base + SL::OVEC + 16 * (s - lane)), 16, 0, 0);
-    }
-}
-
-// One wave's staged [C][16] output tile -> o, 16 bytes per store (rows < len).
-template <typename E, int C, int LO>
-__device__ __forceinline__ void store_out(E* o, const E* ostg, int64_t row0, int H, int DV, int c0,
-                                          int len, int lane) {
-    constexpr int ES = sizeof(E);
-    constexpr int PPR = 16 * ES / 16;   // 16-byte pieces per row
-#pragma unroll
-    for (int p = lane; p < C * PPR; p += 64) {
-        const int r = p / PPR, pc = p % PPR;
-        if (r < len)
-            *reinterpret_cast<V16*>(o + (row0 + (int64_t)r * H) * DV + c0 + pc * (16 / ES)) =
-                *reinterpret_cast<const V16*>(ostg + r * LO + pc * (16 / ES));
     }
 }
 

@@ -82,4 +82,11 @@ struct Gdn2Args {
 };
 hipError_t gdn2_fwd_launch(const Gdn2Args& a);
 
+// Chunkwise form of the same recurrence (bf16 io, 64-token chunks, dk = dv in
+// {64, 128}): a per-chunk preparation into the workspace, then the sequential
+// pass.  T > 0.
+bool gdn2_chunk_supported(int64_t dk, int64_t dv, int64_t chunk, bool bf16);
+size_t gdn2_chunk_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk);
+hipError_t gdn2_chunk_fwd_launch(const Gdn2Args& a, void* ws);
+
 }  // namespace gdr

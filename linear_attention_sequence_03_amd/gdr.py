@@ -24,7 +24,7 @@ GDR_PROLOGUE_L2NORM_QK, GDR_PROLOGUE_BETA_SIGMOID = 1, 2
 EXPORTS = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_decode_step", "gdr_decode_multi",
            "gdr_chunk_fwd_prologue", "gdr_decode_step_prologue",
            "gdr_fg2_chunk_fwd_workspace_size", "gdr_fg2_chunk_fwd", "gdr_fg2_decode_step",
-           "gdr_gdn2_fwd",
+           "gdr_gdn2_fwd", "gdr_gdn2_chunk_fwd_workspace_size", "gdr_gdn2_chunk_fwd",
            "gdr_status_string", "gdr_last_error")
 
 _lib = None
@@ -71,6 +71,13 @@ def load_library(path: Optional[str] = None):
     lib.gdr_gdn2_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                  i64, i64, i64, i64, i64, f, f, vp]
     lib.gdr_gdn2_fwd.restype = f
+    lib.gdr_gdn2_chunk_fwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64, f, f,
+                                                      ctypes.POINTER(ctypes.c_size_t)]
+    lib.gdr_gdn2_chunk_fwd_workspace_size.restype = f
+    lib.gdr_gdn2_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                       i64, i64, i64, i64, i64, i64, f, f,
+                                       vp, ctypes.c_size_t, vp]
+    lib.gdr_gdn2_chunk_fwd.restype = f
     lib.gdr_decode_multi.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                      i64, i64, i64, i64, i64, f, f, vp]
     lib.gdr_decode_multi.restype = f
@@ -377,6 +384,53 @@ def gdr_gdn2_fwd(q, k, v, log_alpha, erase, write, S0=None, o=None, S_T=None,
     st = load_library().gdr_gdn2_fwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(erase), _ptr(write), _ptr(S0), _ptr(o),
         _ptr(S_T), B, T, H, dk, dv, io, gate, _stream(dev, stream))
+    if st != GDR_OK:
+        _raise(st)
+    return o, S_T
+
+
+def gdr_gdn2_chunk_fwd_workspace_size(B, T, H, dk, dv, chunk, io, gate) -> int:
+    out = ctypes.c_size_t(0)
+    st = load_library().gdr_gdn2_chunk_fwd_workspace_size(B, T, H, dk, dv, chunk, io, gate,
+                                                          ctypes.byref(out))
+    if st != GDR_OK:
+        _raise(st)
+    return int(out.value)
+
+
+def gdr_gdn2_chunk_fwd(q, k, v, log_alpha, erase, write, S0=None, chunk: int = 64, o=None,
+                       S_T=None, workspace=None, want_state: bool = True, stream=None) -> Tuple:
+    """Chunkwise form of :func:`gdr_gdn2_fwd` (bf16 io, chunk 64).  The
+    workspace is allocated here when not given.  Returns (o, S_T)."""
+    import torch
+    dev = q.device
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    io = _io_code(q.dtype)
+    gate = GDR_GATE_CHANNEL if log_alpha.dim() == 4 else GDR_GATE_SCALAR
+    _need("q", q, q.dtype, (B, T, H, dk), dev)
+    _need("k", k, q.dtype, (B, T, H, dk), dev)
+    _need("v", v, q.dtype, (B, T, H, dv), dev)
+    _need("log_alpha", log_alpha, torch.float32,
+          (B, T, H, dk) if gate == GDR_GATE_CHANNEL else (B, T, H), dev)
+    _need("erase", erase, torch.float32, (B, T, H, dk), dev)
+    _need("write", write, torch.float32, (B, T, H, dv), dev)
+    if S0 is not None:
+        _need("S0", S0, torch.float32, (B, H, dv, dk), dev)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
+    _need("o", o, q.dtype, (B, T, H, dv), dev)
+    if S_T is None and want_state:
+        S_T = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+    if S_T is not None:
+        _need("S_T", S_T, torch.float32, (B, H, dv, dk), dev)
+    nbytes = gdr_gdn2_chunk_fwd_workspace_size(B, T, H, dk, dv, chunk, io, gate)
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load_library().gdr_gdn2_chunk_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(erase), _ptr(write), _ptr(S0), _ptr(o),
+        _ptr(S_T), B, T, H, dk, dv, chunk, io, gate, _ptr(workspace), wbytes, _stream(dev, stream))
     if st != GDR_OK:
         _raise(st)
     return o, S_T

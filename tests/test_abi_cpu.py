@@ -243,3 +243,36 @@ def _gdn2(lib, q=0, k=1, v=2, la=3, eb=4, ww=5, s0=None, o=6, st=7, B=1, T=64, H
 def test_gdn2_rejects(lib, kw, code):
     assert _gdn2(lib, **kw) == code
     assert lib.gdr_last_error()
+
+
+def _gdn2c(lib, q=0, k=1, v=2, la=3, eb=4, ww=5, s0=None, o=6, st=7, ws=8, wsb=1 << 24, B=1, T=64,
+           H=2, dk=64, dv=64, chunk=64, io=1, gate=0):
+    p = lambda i: None if i is None else (_addr(i) if isinstance(i, int) else i)  # noqa: E731
+    return lib.gdr_gdn2_chunk_fwd(p(q), p(k), p(v), p(la), p(eb), p(ww), p(s0), p(o), p(st),
+                                  B, T, H, dk, dv, chunk, io, gate, p(ws), wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(eb=None), 1), (dict(ww=None), 1), (dict(o=None), 1), (dict(T=-1), 1),
+    (dict(io=0), 2), (dict(chunk=32), 2), (dict(chunk=0), 1), (dict(dk=64, dv=128), 2),
+    (dict(ws=None), 1), (dict(wsb=100), 1),
+    (dict(ww=ctypes.c_void_p(BASE + 5 * MB + 8)), 1),     # misaligned
+    (dict(o=ctypes.c_void_p(BASE + 4 * MB + 1024)), 1),   # o inside erase
+    (dict(ws=ctypes.c_void_p(BASE + 6 * MB)), 1),         # workspace over o
+])
+def test_gdn2_chunk_rejects(lib, kw, code):
+    assert _gdn2c(lib, **kw) == code
+    assert lib.gdr_last_error()
+
+
+def test_gdn2_chunk_workspace_size():
+    """One block per (b, h, 64-token chunk): four bf16 [64][d] tiles, one bf16
+    [64][64] tile and d fp32 decay factors, rounded up to 256 bytes."""
+    for d in (64, 128):
+        blk = -(-(4 * 64 * d * 2 + 64 * 64 * 2 + 4 * d) // 256) * 256
+        for B, T, H in [(1, 1, 1), (2, 130, 3), (2, 8192, 32)]:
+            want = B * H * (-(-T // 64)) * blk
+            assert gdr.gdr_gdn2_chunk_fwd_workspace_size(B, T, H, d, d, 64, 1, 1) == want
+    assert gdr.gdr_gdn2_chunk_fwd_workspace_size(1, 0, 1, 64, 64, 64, 1, 0) == 0
+    with pytest.raises(gdr.GdrError):
+        gdr.gdr_gdn2_chunk_fwd_workspace_size(1, 64, 1, 64, 64, 64, 0, 0)   # fp32 io

@@ -1,0 +1,147 @@
+"""GPU parity of gdr_gdn2_chunk_fwd (the chunkwise form of the decoupled erase /
+write gates) against the oracle, through the C ABI.  bf16 io, so the bar is the
+bf16 one, 2e-2 normwise, for outputs and end states alike.  Lengths cover one
+token, a partial chunk, exactly one chunk, one past it and several chunks with
+a ragged tail."""
+import numpy as np
+import pytest
+
+from linear_attention_sequence_03_amd import synth
+from gpu_helpers import dev, host, rel_err, torch_mod
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+def _inputs(B, T, H, d, gate, seed, s0_std=0.1, log_alpha_range=(-0.1, -0.001)):
+    inp = synth.chunk_inputs(B, T, H, d, d, gate, "bf16", seed=seed, s0_std=s0_std,
+                             log_alpha_range=log_alpha_range)
+    inp["erase"], inp["write"] = synth.gdn2_gates(B, T, H, d, d, seed=seed)
+    return inp
+
+
+def _run(inp, S0=True, **kw):
+    from linear_attention_sequence_03_amd import gdr_gdn2_chunk_fwd
+    torch = torch_mod()
+    bf = torch.bfloat16
+    o, st = gdr_gdn2_chunk_fwd(dev(inp["q"], bf), dev(inp["k"], bf), dev(inp["v"], bf),
+                               dev(inp["log_alpha"]), dev(inp["erase"]), dev(inp["write"]),
+                               dev(inp["S0"]) if (S0 and inp["S0"] is not None) else None, **kw)
+    torch.cuda.synchronize()
+    return o, st
+
+
+def _oracle(inp, S0=True):
+    return oracle.gdn2_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["erase"],
+                                 inp["write"], inp["S0"] if S0 else None)
+
+
+@pytest.mark.parametrize("T", [1, 37, 64, 65, 200])
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_gdn2_chunk_parity(d, gate, T):
+    inp = _inputs(2, T, 3, d, gate, seed=300 + T + d)
+    o, st = _run(inp)
+    o_ref, st_ref = _oracle(inp)
+    eo, es = rel_err(host(o), o_ref), rel_err(host(st), st_ref)
+    print("d=%d gate=%s T=%d err_o=%.3g err_S=%.3g" % (d, gate, T, eo, es), flush=True)
+    assert eo <= TOL and es <= TOL, (eo, es)
+
+
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+def test_gdn2_chunk_strong_decay(gate):
+    """Decays of up to 8 nats per token: a 16-token block spans more than the
+    factored diagonal Gram products allow, so the exact pair-by-pair diagonal
+    blocks run (and the cross-block factors underflow harmlessly)."""
+    inp = _inputs(1, 150, 2, 128, gate, seed=331, log_alpha_range=(-8.0, -0.001))
+    o, st = _run(inp)
+    o_ref, st_ref = _oracle(inp)
+    assert rel_err(host(o), o_ref) <= TOL
+    assert rel_err(host(st), st_ref) <= TOL
+
+
+def test_gdn2_chunk_no_decay():
+    """log alpha = 0 (no forgetting): the reads and erase terms carry the
+    whole history, the hardest case for the rounding of the folded operands."""
+    inp = _inputs(1, 256, 2, 128, "channel", seed=332)
+    inp["log_alpha"] = np.zeros_like(inp["log_alpha"])
+    o, st = _run(inp)
+    o_ref, st_ref = _oracle(inp)
+    assert rel_err(host(o), o_ref) <= TOL
+    assert rel_err(host(st), st_ref) <= TOL
+
+
+def test_gdn2_chunk_matches_scan():
+    """Chunkwise and token-sequential GPU paths on the same bf16 inputs."""
+    from linear_attention_sequence_03_amd import gdr_gdn2_fwd
+    torch = torch_mod()
+    bf = torch.bfloat16
+    inp = _inputs(2, 300, 4, 128, "channel", seed=333)
+    o1, s1 = _run(inp)
+    o2, s2 = gdr_gdn2_fwd(dev(inp["q"], bf), dev(inp["k"], bf), dev(inp["v"], bf),
+                          dev(inp["log_alpha"]), dev(inp["erase"]), dev(inp["write"]), dev(inp["S0"]))
+    torch.cuda.synchronize()
+    assert rel_err(host(o1), host(o2)) <= TOL
+    assert rel_err(host(s1), host(s2)) <= TOL
+
+
+def test_gdn2_chunk_tied_gates_match_kda_call():
+    """b = w = beta: the chunkwise Gated DeltaNet-2 call equals the KDA chunk call."""
+    from linear_attention_sequence_03_amd import gdr_chunk_fwd
+    torch = torch_mod()
+    bf = torch.bfloat16
+    inp = _inputs(2, 150, 2, 64, "channel", seed=334)
+    inp["erase"] = np.repeat(inp["beta"][..., None], 64, axis=-1).astype(np.float32)
+    inp["write"] = np.repeat(inp["beta"][..., None], 64, axis=-1).astype(np.float32)
+    o1, s1 = _run(inp)
+    o2, s2 = gdr_chunk_fwd(dev(inp["q"], bf), dev(inp["k"], bf), dev(inp["v"], bf),
+                           dev(inp["log_alpha"]), dev(inp["beta"]), dev(inp["S0"]))
+    torch.cuda.synchronize()
+    assert rel_err(host(o1), host(o2)) <= TOL
+    assert rel_err(host(s1), host(s2)) <= TOL
+
+
+def test_gdn2_chunk_no_start_state_empty_and_reuse():
+    from linear_attention_sequence_03_amd import gdr_gdn2_chunk_fwd, gdr_gdn2_chunk_fwd_workspace_size
+    torch = torch_mod()
+    bf = torch.bfloat16
+    inp = _inputs(1, 90, 2, 64, "scalar", seed=335, s0_std=None)
+    o, st = _run(inp, S0=False)
+    o_ref, st_ref = _oracle(inp, S0=False)
+    assert rel_err(host(o), o_ref) <= TOL
+    assert rel_err(host(st), st_ref) <= TOL
+    # T = 0: S_T = S0
+    e = _inputs(1, 0, 2, 64, "scalar", seed=336)
+    _, st0 = gdr_gdn2_chunk_fwd(dev(e["q"], bf), dev(e["k"], bf), dev(e["v"], bf), dev(e["log_alpha"]),
+                                dev(e["erase"]), dev(e["write"]), dev(e["S0"]))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(st0), e["S0"])
+    # one workspace for a long call, then a shorter one
+    big = _inputs(2, 260, 3, 128, "channel", seed=337)
+    small = _inputs(1, 70, 3, 128, "channel", seed=338)
+    nbytes = gdr_gdn2_chunk_fwd_workspace_size(2, 260, 3, 128, 128, 64, 1, 1)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    for x in (big, small):
+        o, st = _run(x, workspace=ws)
+        o_ref, st_ref = _oracle(x)
+        assert rel_err(host(o), o_ref) <= TOL
+        assert rel_err(host(st), st_ref) <= TOL
+
+
+def test_gdn2_chunk_full_size_sampled():
+    """The KDA workload's shape (B=2, H=32, T=8192, d=128, bf16, channel decay)
+    with both gates; sampled (b,h) pairs against the oracle."""
+    w = synth.WORKLOADS[2]
+    inp = synth.workload_inputs(w)
+    inp["erase"], inp["write"] = synth.gdn2_gates(w.B, w.T, w.H, w.d, w.d, seed=w.seed)
+    o, st = _run(inp)
+    o, st = host(o), host(st)
+    for b, h in [(0, 3), (1, 30)]:
+        sl = lambda a: None if a is None else a[b:b + 1, :, h:h + 1]  # noqa: E731
+        o_ref, st_ref = oracle.gdn2_chunk_fwd(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]),
+                                              sl(inp["log_alpha"]), sl(inp["erase"]),
+                                              sl(inp["write"]), None)
+        assert rel_err(o[b, :, h], o_ref[0, :, 0]) <= TOL
+        assert rel_err(st[b, h], st_ref[0, 0]) <= TOL
