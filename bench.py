@@ -12,7 +12,8 @@ call over the whole batch.  The same line also carries the decode step
     python bench.py --workload 2 --fg2   # channel-wise write rates (FG2-GDN+) on that
                                          # shape, with the overhead over the KDA call
     python bench.py --workload 2 --gdn2  # decoupled erase / write gates (Gated
-                                         # DeltaNet-2) on that shape
+                                         # DeltaNet-2, chunkwise) on that shape, with
+                                         # the token-sequential scan beside it
     python bench.py --prologue           # raw q, k and beta logits: the gate prologue
                                          # fused into the kernels, against torch
                                          # normalising first
@@ -202,7 +203,8 @@ def main():
     ap.add_argument("--fg2", action="store_true",
                     help="time gdr_fg2_chunk_fwd with key and value rates (FG2-GDN+) instead")
     ap.add_argument("--gdn2", action="store_true",
-                    help="time gdr_gdn2_fwd (decoupled erase / write gates) instead")
+                    help="time gdr_gdn2_chunk_fwd (decoupled erase / write gates) instead, "
+                         "with gdr_gdn2_fwd (the scan) beside it")
     ap.add_argument("--prologue", action="store_true",
                     help="raw q, k and beta logits: time the fused gate prologue instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -298,10 +300,17 @@ def main():
             kn = (rk.float() * torch.rsqrt((rk.float() ** 2).sum(-1, keepdim=True) + 1e-6)).to(bf)
             gdr_chunk_fwd(qn, kn, v, la, torch.sigmoid(rbe), S0, chunk=C, o=o, S_T=st, workspace=ws)
     elif args.gdn2:
+        from linear_attention_sequence_03_amd import (gdr_gdn2_chunk_fwd,
+                                                      gdr_gdn2_chunk_fwd_workspace_size)
         eb, ww = synth.gdn2_gates(B, T, H, d, d, seed=w.seed)
         eb, ww = torch.from_numpy(eb).to(devn), torch.from_numpy(ww).to(devn)
+        ws3 = torch.empty(gdr_gdn2_chunk_fwd_workspace_size(B, T, H, d, d, C, GDR_BF16, gate),
+                          dtype=torch.uint8, device=devn)
 
         def step():
+            gdr_gdn2_chunk_fwd(q, k, v, la, eb, ww, S0, chunk=C, o=o, S_T=st, workspace=ws3)
+
+        def scan_step():
             gdr_gdn2_fwd(q, k, v, la, eb, ww, S0, o=o, S_T=st)
 
     for _ in range(args.warmup):
@@ -377,6 +386,22 @@ def main():
                     "overhead": float(np.mean(warm)) / base_ms - 1.0,
                     "algorithmic_bytes": nbytes, "base_algorithmic_bytes": base_bytes,
                     "bytes_overhead": nbytes / base_bytes - 1.0}
+    gdn2_info = None
+    if args.gdn2:
+        # the token-sequential scan on the same inputs, for comparison
+        scan_step()
+        ev5 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(min(args.steps, 5))]
+        for a, b in ev5:
+            a.record(stream)
+            scan_step()
+            b.record(stream)
+        torch.cuda.synchronize()
+        sms = float(np.mean([a.elapsed_time(b) for a, b in ev5]))
+        gdn2_info = {"call": "gdr_gdn2_chunk_fwd (gdn2_prep + gdn2_state_pass)",
+                     "launch_ms_mean": float(np.mean(warm)),
+                     "scan_call": "gdr_gdn2_fwd (gdn2_scan, token-sequential)",
+                     "scan_launch_ms_mean": sms, "speedup": sms / float(np.mean(warm))}
     launch_ms = float(np.mean(warm))
     traffic = None
     if args.workload == 1 and os.path.exists(TRAFFIC_FILE):
@@ -460,13 +485,14 @@ def main():
                 "log_alpha U(-0.1,-0.001)%s)" % (", S0 N(0,0.02^2)" if S0 is not None else ""),
         "config": {"workload": w.name + ("_fg2plus" if args.fg2 else "_gdn2" if args.gdn2
                                          else "_raw_prologue" if args.prologue else ""),
-                   "call": ("gdr_fg2_chunk_fwd" if args.fg2 else "gdr_gdn2_fwd" if args.gdn2
+                   "call": ("gdr_fg2_chunk_fwd" if args.fg2 else "gdr_gdn2_chunk_fwd" if args.gdn2
                             else "gdr_chunk_fwd"),
                    "gate": "channel" if channel else "scalar",
                    "B": B, "T": T, "H": H, "d_k": d, "d_v": d, "chunk": C,
                    "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm",
-                     "kernel": ("gdr_gdn2_fwd (gdn2_scan, token-sequential)" if args.gdn2 else
+                     "kernel": ("gdr_gdn2_chunk_fwd (gdn2_prep<128, channel> + gdn2_state_pass<128, 2>)"
+                                if args.gdn2 else
                                 ("gdr_fg2_chunk_fwd (fg2_scale prologue + " if args.fg2 else "")
                                 + ROOFLINE_KERNEL[args.workload] + (")" if args.fg2 else "")),
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -492,6 +518,8 @@ def main():
         out["fg2"] = fg2_info
     if pro_info is not None:
         out["prologue"] = pro_info
+    if gdn2_info is not None:
+        out["gdn2"] = gdn2_info
     if not args.no_cpu_baseline and not (args.fg2 or args.gdn2 or args.prologue):
         import oracle.gdr_oracle as og
         threads = min(16, og.default_threads())
