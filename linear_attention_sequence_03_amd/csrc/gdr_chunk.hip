@@ -30,7 +30,9 @@
 //     Each product's accumulator tiles are the next product's B operand (the
 //     permuted k-map in gdr_device.hpp), so nothing round-trips through LDS.
 //     The shared per-chunk inputs are copied global->LDS with global_load_lds
-//     (no registers), one chunk ahead, into a double buffer.
+//     (no registers), one chunk ahead, into a double buffer.  For the bf16
+//     channel gate the loaders also warm L2 with the chunk after that (the
+//     head's workspace block split over its workgroups, and the V rows).
 #include "gdr_device.hpp"
 #include "gdr_launch.hpp"
 
@@ -1061,7 +1063,11 @@ struct StageLayout {
     static constexpr int OSTG = C * LO * ES;
     // Double-buffered (copy of chunk n+1 overlaps chunk n) when it fits.
     static constexpr int NSTAGE = 2 * BYTES + NW * OSTG <= 160 * 1024 ? 2 : 1;
-    static constexpr int TOTAL = NSTAGE * BYTES + NW * OSTG;
+    // bf16 channel-gate calls warm L2 one chunk further ahead; those loads
+    // land in a small scratch area.
+    static constexpr bool WARM = CHANNEL && sizeof(E) == 2 && NSTAGE == 2;
+    static constexpr int OWARM = NSTAGE * BYTES + NW * OSTG;
+    static constexpr int TOTAL = OWARM + (WARM ? 256 : 0);
 };
 
 // Copies of chunk n's inputs into one LDS stage (see DmaTile).  PARTS selects
@@ -1106,6 +1112,37 @@ __device__ __forceinline__ void issue_chunk(char* base, int n, const E* q, const
             __builtin_amdgcn_global_load_lds(blk + L::VEC + 16 * s,
                                              (GDR_LDS void*)(base + SL::OVEC + 16 * (s - lane)), 16, 0, 0);
     }
+}
+
+// L2 warming for chunk n of a bf16 channel-gate call: this workgroup's share
+// of the head's workspace block (the block split evenly over the head's value
+// tiles; one 4-byte load per 128-byte line, a fixed number of loads per wave,
+// lanes past the share repeating its last line), then loader 0's own V rows.
+// Then waits for every copy issued before it; the warming loads stay in
+// flight (loads complete in issue order).
+template <typename E, int DK, int C, int NW, bool CHANNEL>
+__device__ __forceinline__ void warm_chunk_l2(char* scratch, int n, const E* v, const uint8_t* wsb,
+                                              int64_t bh, int64_t b, int64_t h, int64_t T, int H, int DV,
+                                              int NT, int vt, int lw, int lane) {
+    using L = WsLayout<E, DK, C, CHANNEL>;
+    using SL = StageLayout<E, DK, C, NW, CHANNEL>;
+    constexpr int NLINES = (int)((L::BYTES + 127) / 128);
+    constexpr int NVT = DK / SL::VT;
+    constexpr int PER = (NLINES + NVT - 1) / NVT;
+    constexpr int ROUNDS = (PER + SL::NL * 64 - 1) / (SL::NL * 64);
+    static_assert(ROUNDS + 1 <= 15, "vmcnt field");
+    const char* blk = reinterpret_cast<const char*>(wsb + (size_t)(bh * NT + n) * L::BYTES);
+    const int lo = vt * PER, hi = lo + PER < NLINES ? lo + PER : NLINES;
+#pragma unroll
+    for (int j = 0; j < ROUNDS; ++j) {
+        const int i = lo + (SL::NL * j + lw) * 64 + lane;
+        __builtin_amdgcn_global_load_lds(blk + 128 * (i < hi ? i : hi - 1), (GDR_LDS void*)scratch, 4, 0, 0);
+    }
+    const int64_t t0 = (int64_t)n * C;
+    const int len = (int)((T - t0) < C ? (T - t0) : C);
+    const int64_t r = (b * T + t0 + (lane < len ? lane : len - 1)) * H + h;
+    __builtin_amdgcn_global_load_lds(v + r * DV + vt * SL::VT, (GDR_LDS void*)scratch, 4, 0, 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (ROUNDS + 1));
 }
 
 // S^T <- Diag(gamma_last) S^T + Kh^T Ds for the chunk held in one LDS stage.
@@ -1196,7 +1233,16 @@ __global__ __launch_bounds__(64 * (NW + 2)) __attribute__((amdgpu_waves_per_eu(1
                     issue_chunk<E, DK, C, NW, CHANNEL, 3>(smem + ((n + 1) & 1) * SL::BYTES, n + 1, q, k, v,
                                                           wsb, bh, b, h, T, H, DV, NT, vt, qk_stride, oq,
                                                           ot, ov, lw, lane);
-                    wait_dma();
+                    if constexpr (SL::WARM) {
+                        if (n + 2 < NT) {
+                            warm_chunk_l2<E, DK, C, NW, CHANNEL>(smem + SL::OWARM, n + 2, v, wsb, bh, b, h, T,
+                                                                 H, DV, NT, vt, lw, lane);
+                        } else {
+                            wait_dma();
+                        }
+                    } else {
+                        wait_dma();
+                    }
                 }
                 __syncthreads();                                           // B2
             } else if (n > 0) {

@@ -32,7 +32,8 @@
 //     and keeps its fp32 state slice in MFMA accumulators across the chunks.
 //     W, QP, PP, V and w are double-buffered in LDS; KHP, EHN and gamma_C are
 //     needed only by the state update at the end of a chunk and are copied
-//     while the chunk's other products run.
+//     while the chunk's other products run.  The loaders also warm L2 with the
+//     chunk after next (the head's workspace block split over its workgroups).
 #include "gdr_device.hpp"
 #include "gdr_launch.hpp"
 
@@ -197,15 +198,49 @@ __device__ __forceinline__ void gdn2_prep_wave(G2PrepSmem<DK>& sm, const __bf16*
     for (int cb = 0; cb < NB; ++cb) lk[cb] = le[cb] = pk[cb] = pe[cb] = zero4();
     f32x4 qgk[NCT], khk[NCT];   // Qg and Kh of row r, R layout per 16-channel tile
     bool unsafe = false;
+    // Raw loads of a channel step, issued one step ahead of their use.
+    struct RawStep {
+        bf16x4 k0, k1, q0, q1;
+        float4 l0, l1, e0, e1;
+    };
+    auto ld_raw = [&](int s) {
+        RawStep y;
+        const int64_t o0 = grow * DK + 32 * s + 4 * kg;
+        y.k0 = *reinterpret_cast<const bf16x4*>(k + o0);
+        y.k1 = *reinterpret_cast<const bf16x4*>(k + o0 + 16);
+        y.q0 = *reinterpret_cast<const bf16x4*>(q + o0);
+        y.q1 = *reinterpret_cast<const bf16x4*>(q + o0 + 16);
+        if constexpr (CH) {
+            y.l0 = *reinterpret_cast<const float4*>(log_alpha + o0);
+            y.l1 = *reinterpret_cast<const float4*>(log_alpha + o0 + 16);
+        } else {
+            const float a = log_alpha[grow];
+            y.l0 = make_float4(a, a, a, a);
+            y.l1 = y.l0;
+        }
+        y.e0 = *reinterpret_cast<const float4*>(erase + o0);
+        y.e1 = *reinterpret_cast<const float4*>(erase + o0 + 16);
+        return y;
+    };
+    RawStep nxt = ld_raw(0);
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
+        const RawStep cur = nxt;
+        if (s + 1 < NS) nxt = ld_raw(s + 1);
         float gs[8], kv[8], qv[8], ev[8];
-        ld_la(s, gs);
-        ld_bf(k, s, kv);
-        ld_bf(q, s, qv);
-        ld_f(erase, s, ev);
+        {
+            const float lr[8] = {cur.l0.x, cur.l0.y, cur.l0.z, cur.l0.w, cur.l1.x, cur.l1.y, cur.l1.z, cur.l1.w};
+            const float er[8] = {cur.e0.x, cur.e0.y, cur.e0.z, cur.e0.w, cur.e1.x, cur.e1.y, cur.e1.z, cur.e1.w};
 #pragma unroll
-        for (int j = 0; j < 8; ++j) ev[j] *= kv[j];   // e = b * k
+            for (int j = 0; j < 8; ++j) {
+                const __bf16 kr = j < 4 ? cur.k0[j & 3] : cur.k1[j & 3];
+                const __bf16 qr = j < 4 ? cur.q0[j & 3] : cur.q1[j & 3];
+                kv[j] = valid ? (float)kr : 0.f;
+                qv[j] = valid ? (float)qr : 0.f;
+                ev[j] = valid ? er[j] * kv[j] : 0.f;   // e = b * k
+                gs[j] = valid ? fmaxf(lr[j], kG2MinLogAlpha) * kG2Log2e : 0.f;
+            }
+        }
         scan(gs);
         if (x == 15) {
             *reinterpret_cast<float4*>(&sm.tot[b][32 * s + 4 * kg]) = make_float4(gs[0], gs[1], gs[2], gs[3]);
@@ -539,7 +574,8 @@ struct G2Stage {
     static constexpr int OKHP = 2 * ABYTES, OEHN = OKHP + QB, OVEC = OEHN + QB;
     static constexpr int LO = 16 + 8;      // output staging row (bf16)
     static constexpr int OSTG = (OVEC + DK * 4 + 15) / 16 * 16;
-    static constexpr int TOTAL = OSTG + NW * GC * LO * 2;
+    static constexpr int OWARM = (OSTG + NW * GC * LO * 2 + 15) / 16 * 16;   // L2-warming loads land here
+    static constexpr int TOTAL = OWARM + 256;
 };
 
 // S^T <- Diag(gamma_C) S^T + KHP^T Vt + EHN^T X for the chunk whose single part
@@ -628,7 +664,35 @@ __device__ __forceinline__ void gdn2_loader(char* smem, const __bf16* v, const f
             DVt::issue(base + SL::OV, reinterpret_cast<const char*>(v + row0 * DV + vt * VT), ov, lw);
             DWt::issue(base + SL::OWR, reinterpret_cast<const char*>(wr + row0 * DV + vt * VT), ow, lw);
         }
-        wait_dma();
+        // Warm L2 with chunk n + 2: this workgroup's share of the head's
+        // workspace block (one 4-byte load per 128-byte line, a fixed number
+        // of loads per wave, lanes past the share repeating its last line),
+        // then its own V (loader 0) or w (loader 1) rows.  The copies above
+        // are waited for; the warming loads stay in flight.
+        constexpr int NLINES = (int)((L::BYTES + 127) / 128);
+        constexpr int NVT = DK / VT;
+        constexpr int PER = (NLINES + NVT - 1) / NVT;
+        constexpr int ROUNDS = (PER + 2 * 64 - 1) / (2 * 64);
+        const int nw = n + 2;
+        if (nw >= 0 && nw < NT) {
+            const char* blk = reinterpret_cast<const char*>(ws + (size_t)(bh * NT + nw) * L::BYTES);
+            const int lo = vt * PER, hi = (lo + PER < NLINES ? lo + PER : NLINES);
+#pragma unroll
+            for (int j = 0; j < ROUNDS; ++j) {
+                const int i = lo + (2 * j + lw) * 64 + lane;
+                __builtin_amdgcn_global_load_lds(blk + 128 * (i < hi ? i : hi - 1), (GDR_LDS void*)(smem + SL::OWARM), 4, 0, 0);
+            }
+            const int len = g2_len(nw, T);
+            const int64_t r = g2_row0(b, h, nw, T, H) + (int64_t)(lane < len ? lane : len - 1) * H;
+            if (lw == 0)
+                __builtin_amdgcn_global_load_lds(v + r * DV + vt * VT, (GDR_LDS void*)(smem + SL::OWARM), 4, 0, 0);
+            else
+                __builtin_amdgcn_global_load_lds(wr + r * DV + vt * VT, (GDR_LDS void*)(smem + SL::OWARM), 4, 0, 0);
+            static_assert(ROUNDS + 1 <= 15, "vmcnt field");
+            __builtin_amdgcn_s_waitcnt(0x0F70 | (ROUNDS + 1));
+        } else {
+            wait_dma();
+        }
         __syncthreads();                                                   // B0 (n = -1) or B2
     }
 }
