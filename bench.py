@@ -18,6 +18,7 @@ call over the whole batch.  The same line also carries the decode step
                                          # fused into the kernels, against torch
                                          # normalising first
     python bench.py --traffic        # HBM bytes per call from rocprofv3 counters
+    python bench.py --sweep          # every chunkwise call over 2k x 16 ... 32k x 1 (H=32)
 
 Prints ONE JSON line.  Only one GPU is used; --gpus above 1 exits.
 
@@ -192,6 +193,97 @@ def measure_traffic(outdir):
     return res
 
 
+# The pages' prefill sweep ("FG2-GDN" page, section 4.5, Figure 3): one batch of
+# 32k tokens split as 2k x 16 ... 32k x 1, here at H = 32 heads, d = 128.
+SWEEP = ((16, 2048), (8, 4096), (4, 8192), (2, 16384), (1, 32768))
+
+
+def run_sweep(steps: int, warmup: int):
+    """Prefill tokens/s of every chunkwise call over the pages' B x T sweep.
+    One set of seeded inputs [1, 32768, 32, 128] serves every split (a view)."""
+    import torch
+    from linear_attention_sequence_03_amd import (gdr_chunk_fwd, gdr_fg2_chunk_fwd, gdr_gdn2_chunk_fwd,
+                                                  synth)
+    from linear_attention_sequence_03_amd.gdr import (GDR_BF16, GDR_GATE_CHANNEL, GDR_GATE_SCALAR,
+                                                      gdr_chunk_fwd_workspace_size,
+                                                      gdr_fg2_chunk_fwd_workspace_size,
+                                                      gdr_gdn2_chunk_fwd_workspace_size)
+    assert torch.cuda.is_available(), "no GPU visible"
+    dev = torch.device("cuda:0")
+    H, d, C, N = 32, 128, 64, 32768
+    seed = 1100
+    inp = synth.chunk_inputs(1, N, H, d, d, "channel", "bf16", seed=seed)
+    bk, bv = synth.write_rates((1, N, H, d), d, seed=seed)
+    eb, ww = synth.gdn2_gates(1, N, H, d, d, seed=seed)
+    bf = torch.bfloat16
+    t = lambda a, dt=None: (torch.from_numpy(a).to(dev) if dt is None  # noqa: E731
+                            else torch.from_numpy(a).to(dev).to(dt))
+    q, k, v = t(inp["q"], bf), t(inp["k"], bf), t(inp["v"], bf)
+    la_c = t(inp["log_alpha"])
+    la_s = la_c[..., 0].contiguous()
+    be, bk, bv, eb, ww = t(inp["beta"]), t(bk), t(bv), t(eb), t(ww)
+    del inp
+    o = torch.empty((1, N, H, d), dtype=bf, device=dev)
+    st = torch.empty((16, H, d, d), dtype=torch.float32, device=dev)
+    nws = max(gdr_chunk_fwd_workspace_size(B, T, H, d, d, C, GDR_BF16, g) for B, T in SWEEP
+              for g in (GDR_GATE_SCALAR, GDR_GATE_CHANNEL))
+    nws = max([nws] + [gdr_fg2_chunk_fwd_workspace_size(B, T, H, d, d, C, GDR_BF16, GDR_GATE_CHANNEL)
+                       for B, T in SWEEP]
+              + [gdr_gdn2_chunk_fwd_workspace_size(B, T, H, d, d, C, GDR_BF16, GDR_GATE_CHANNEL)
+                 for B, T in SWEEP])
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+
+    def shaped(x, B, T):
+        return x.view((B, T) + tuple(x.shape[2:]))
+
+    calls = {
+        "gdn": lambda B, T: gdr_chunk_fwd(
+            shaped(q, B, T), shaped(k, B, T), shaped(v, B, T), shaped(la_s, B, T), shaped(be, B, T),
+            None, chunk=C, o=shaped(o, B, T), S_T=st[:B], workspace=ws),
+        "kda": lambda B, T: gdr_chunk_fwd(
+            shaped(q, B, T), shaped(k, B, T), shaped(v, B, T), shaped(la_c, B, T), shaped(be, B, T),
+            None, chunk=C, o=shaped(o, B, T), S_T=st[:B], workspace=ws),
+        "fg2_gdn": lambda B, T: gdr_fg2_chunk_fwd(
+            shaped(q, B, T), shaped(k, B, T), shaped(v, B, T), shaped(la_c, B, T), shaped(bk, B, T),
+            None, None, chunk=C, o=shaped(o, B, T), S_T=st[:B], workspace=ws),
+        "fg2_gdn_plus": lambda B, T: gdr_fg2_chunk_fwd(
+            shaped(q, B, T), shaped(k, B, T), shaped(v, B, T), shaped(la_c, B, T), shaped(bk, B, T),
+            shaped(bv, B, T), None, chunk=C, o=shaped(o, B, T), S_T=st[:B], workspace=ws),
+        "gdn2": lambda B, T: gdr_gdn2_chunk_fwd(
+            shaped(q, B, T), shaped(k, B, T), shaped(v, B, T), shaped(la_c, B, T), shaped(eb, B, T),
+            shaped(ww, B, T), None, chunk=C, o=shaped(o, B, T), S_T=st[:B], workspace=ws),
+    }
+    stream = torch.cuda.current_stream(dev)
+    res = {}
+    for name, fn in calls.items():
+        res[name] = {}
+        for B, T in SWEEP:
+            for _ in range(warmup):
+                fn(B, T)
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(steps)]
+            for a, b in ev:
+                a.record(stream)
+                fn(B, T)
+                b.record(stream)
+            torch.cuda.synchronize()
+            ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+            res[name]["%dkx%d" % (T // 1024, B)] = {"ms": ms, "tokens_per_s": B * T / (ms * 1e-3)}
+        print("sweep %s done" % name, file=sys.stderr, flush=True)
+    first, last = "%dkx%d" % (SWEEP[0][1] // 1024, SWEEP[0][0]), "%dkx%d" % (SWEEP[-1][1] // 1024, SWEEP[-1][0])
+    out = {
+        "metric": "prefill tokens/s over the B x T sweep (32k tokens per call)",
+        "unit": "tokens/s", "higher_is_better": True, "dtype": "bf16", "data": "synthetic (seeded)",
+        "config": {"H": H, "d_k": d, "d_v": d, "chunk": C, "splits": [list(x) for x in SWEEP]},
+        "results": res,
+        "ratio_last_over_first": {n: res[n][last]["tokens_per_s"] / res[n][first]["tokens_per_s"]
+                                  for n in res},
+        "overhead_vs_kda": {n: {c: res[n][c]["ms"] / res["kda"][c]["ms"] - 1.0 for c in res[n]}
+                            for n in ("fg2_gdn", "fg2_gdn_plus", "gdn2")},
+    }
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -208,6 +300,9 @@ def main():
     ap.add_argument("--prologue", action="store_true",
                     help="raw q, k and beta logits: time the fused gate prologue instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="prefill tokens/s of every chunkwise call over the B x T sweep 2k x 16 ... "
+                         "32k x 1 (H=32, d=128), one JSON line of its own")
     ap.add_argument("--traffic", action="store_true",
                     help="measure HBM bytes per call with rocprofv3 and write a summary")
     ap.add_argument("--traffic-probe", action="store_true", help=argparse.SUPPRESS)
@@ -215,6 +310,9 @@ def main():
                     help="time a plain device copy (the practical HBM read+write ceiling)")
     ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out"))
     args = ap.parse_args()
+    if args.sweep:
+        run_sweep(args.steps, args.warmup)
+        return
     if args.traffic_probe:
         traffic_probe()
         return

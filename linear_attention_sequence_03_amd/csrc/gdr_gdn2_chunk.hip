@@ -24,9 +24,9 @@
 //     parallel.  Wave b owns rows 16b..16b+15.  The four Gram matrices are
 //     built on bf16 MFMAs with the decay split at block boundaries (the same
 //     scheme as the KDA prep).  The rest runs on fp16 16x16x16 MFMAs, one
-//     16-token block per k-step: the unit-lower inverse Ti (8x8-free
-//     substitution on the diagonal blocks, then a block row wavefront), Z, M
-//     and the five operands above.  Entries of L, P, Ti, Z and M stay small
+//     16-token block per k-step: the unit-lower inverse Ti (forward
+//     substitution on the 16x16 diagonal blocks, then a block row wavefront),
+//     Z, M and the five operands above.  Entries of L, P, Ti, Z and M stay small
 //     for unit-norm keys and gates in [0, 1], well inside fp16's range.
 //  2. gdn2_state_pass -- each compute wave owns 16 value columns of one (b, h)
 //     and keeps its fp32 state slice in MFMA accumulators across the chunks.
