@@ -18,6 +18,7 @@ call over the whole batch.  The same line also carries the decode step
                                          # fused into the kernels, against torch
                                          # normalising first
     python bench.py --traffic        # HBM bytes per call from rocprofv3 counters
+    python bench.py --mfma           # issued MFMA FLOPs and MFMA-busy % per call (rocprofv3)
     python bench.py --sweep          # every chunkwise call over 2k x 16 ... 32k x 1 (H=32)
 
 Prints ONE JSON line.  Only one GPU is used; --gpus above 1 exits.
@@ -76,6 +77,10 @@ def decode_algorithmic(B, H, d, io_bytes=4):
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gdr_chunk_fwd_gdn_B4_H16_T4096_d128.traffic.txt")
 COPY_BYTES = 256 << 20
 PREFILL_KERNELS = ("fused_chunk", "wy_prep", "state_pass")
+MFMA_FILE = os.path.join(ROOT, "profiles", "gdr_chunk_fwd_gdn_B4_H16_T4096_d128.mfma.txt")
+# rocprofv3 derived counters: issued MFMA FLOPs by operand type (MOPS x 512) and
+# the MFMA-busy share of the SIMDs over the dispatch
+MFMA_COUNTERS = ("MfmaFlopsBF16", "MfmaFlopsF16", "MfmaUtil")
 ROOFLINE_KERNEL = {
     1: "gdr_chunk_fwd (single kernel: fused_chunk<128, 2>)",
     2: "gdr_chunk_fwd (wy_prep_channel_bf16<128, 64> + state_pass<bf16, 128, 64, 2, channel>)",
@@ -193,6 +198,25 @@ def measure_traffic(outdir):
     return res
 
 
+def measure_mfma(outdir):
+    """One rocprofv3 --pmc pass (MFMA counters) over traffic_probe(); returns the
+    per-call mean of each counter over the prefill kernel's dispatches."""
+    d = tempfile.mkdtemp(prefix="pmc_", dir=outdir)
+    cmd = (["rocprofv3", "--pmc"] + list(MFMA_COUNTERS) +
+           ["--output-format", "csv", "-d", d, "-o", "run", "--",
+            sys.executable, os.path.abspath(__file__), "--traffic-probe"])
+    subprocess.run(cmd, check=True, stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL, timeout=240)
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        rows += list(csv.DictReader(open(f)))
+    per = {}
+    for r in rows:
+        if "fused_chunk" in r["Kernel_Name"]:
+            per.setdefault(r["Counter_Name"], {}).setdefault(r["Dispatch_Id"], 0.0)
+            per[r["Counter_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    return {c: float(np.mean(list(per[c].values()))) for c in MFMA_COUNTERS if c in per}
+
+
 # The pages' prefill sweep ("FG2-GDN" page, section 4.5, Figure 3): one batch of
 # 32k tokens split as 2k x 16 ... 32k x 1, here at H = 32 heads, d = 128.
 SWEEP = ((16, 2048), (8, 4096), (4, 8192), (2, 16384), (1, 32768))
@@ -306,6 +330,9 @@ def main():
     ap.add_argument("--traffic", action="store_true",
                     help="measure HBM bytes per call with rocprofv3 and write a summary")
     ap.add_argument("--traffic-probe", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--mfma", action="store_true",
+                    help="issued MFMA FLOPs and MFMA-busy share of one prefill call from rocprofv3 "
+                         "counters; writes a summary")
     ap.add_argument("--copy", action="store_true",
                     help="time a plain device copy (the practical HBM read+write ceiling)")
     ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out"))
@@ -336,6 +363,19 @@ def main():
                          % (ctr, r["kib_per_call"], ctr, r["copy_kib"], ctr, r["factor"]))
             fh.write("traffic_bytes_per_call=%.0f\n" % total)
         print(json.dumps({"traffic_bytes_per_call": total, "summary": path, **res}))
+        return
+    if args.mfma:
+        os.makedirs(args.out, exist_ok=True)
+        res = measure_mfma(args.out)
+        path = os.path.join(args.out, os.path.basename(MFMA_FILE))
+        with open(path, "w") as fh:
+            fh.write("# Issued MFMA work of one gdr_chunk_fwd call (B=4,T=4096,H=16,d=128,chunk=64, bf16)\n")
+            fh.write("# command: python bench.py --mfma   (rocprofv3 --pmc %s)\n" % " ".join(MFMA_COUNTERS))
+            fh.write("# kernel: fused_chunk; per-dispatch means over the probe's calls\n")
+            fh.write("source_hash=%s\n" % kernel_source_hash())
+            for c, v in res.items():
+                fh.write("%s=%.6g\n" % (c, v))
+        print(json.dumps({"summary": path, **res}))
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only (this path has no multi-GPU part); "
@@ -509,6 +549,16 @@ def main():
             traffic = float(kv["traffic_bytes_per_call"])
     achieved = nbytes / (launch_ms * 1e-3) / 1e9
     tflops = flops / (launch_ms * 1e-3) / 1e12
+    issued = {}
+    if args.workload == 1 and not (args.fg2 or args.gdn2 or args.prologue) and os.path.exists(MFMA_FILE):
+        kv = dict(l.strip().split("=", 1) for l in open(MFMA_FILE)
+                  if "=" in l and not l.startswith("#"))
+        if kv.get("source_hash") == kernel_source_hash():
+            iflops = float(kv.get("MfmaFlopsBF16", 0.0)) + float(kv.get("MfmaFlopsF16", 0.0))
+            issued = {"issued_flops_per_launch": iflops,
+                      "issued_tflops": iflops / (launch_ms * 1e-3) / 1e12,
+                      "issued_frac": iflops / (launch_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                      "mfma_busy_pct": float(kv["MfmaUtil"]) if "MfmaUtil" in kv else None}
 
     # Decode step, in place on a resident 512 MiB state.
     wd = synth.WORKLOADS[4]
@@ -599,7 +649,7 @@ def main():
                      "launch_ms_mean": launch_ms,
                      "launch_ms_cold_cache_mean": float(np.mean(cold))},
         "prefill_mfma": {"algorithmic_flops_per_launch": flops, "tflops": tflops,
-                         "peak_tflops": BF16_PEAK_TFLOPS, "frac": tflops / BF16_PEAK_TFLOPS},
+                         "peak_tflops": BF16_PEAK_TFLOPS, "frac": tflops / BF16_PEAK_TFLOPS, **issued},
         "decode": {"workload": wd.name, "call": "gdr_decode_step", "ms_per_step": dms,
                    "tokens_per_s": wd.B / (dms * 1e-3),
                    "algorithmic_bytes": dbytes, "achieved_GBs": dgbs,
