@@ -198,6 +198,16 @@ def measure_traffic(outdir):
     return res
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
 def measure_mfma(outdir):
     """One rocprofv3 --pmc pass (MFMA counters) over traffic_probe(); returns the
     per-call mean of each counter over the prefill kernel's dispatches."""
@@ -676,7 +686,9 @@ def main():
                                "kind": "oracle",
                                "sample": "the whole prefill workload (B=%d,T=%d,H=%d,d=%d) "
                                          "through the fp64 token-by-token oracle, %d times, "
-                                         "%.1f s" % (B, T, H, d, reps, secs)}
+                                         "%.1f s on %s; the GPU call is %.0fx its throughput"
+                                         % (B, T, H, d, reps, secs, cpu_model(),
+                                            out["value"] / (reps * B * T / secs))}
     print(json.dumps(out))
 
 
