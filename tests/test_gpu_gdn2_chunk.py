@@ -145,3 +145,25 @@ def test_gdn2_chunk_full_size_sampled():
                                               sl(inp["write"]), None)
         assert rel_err(o[b, :, h], o_ref[0, :, 0]) <= TOL
         assert rel_err(st[b, h], st_ref[0, 0]) <= TOL
+
+
+@pytest.mark.parametrize("B,T,H,d,gate", [(3, 129, 5, 64, "channel"), (1, 1000, 2, 128, "scalar"),
+                                          (4, 63, 3, 128, "channel"), (2, 192, 1, 64, "scalar")])
+def test_gdn2_chunk_odd_shapes(B, T, H, d, gate):
+    """Odd batch and head counts, lengths just under and over chunk multiples,
+    one head (a single value-tile group), and no S_T requested for one case."""
+    from linear_attention_sequence_03_amd import gdr_gdn2_chunk_fwd
+    torch = torch_mod()
+    bf = torch.bfloat16
+    inp = _inputs(B, T, H, d, gate, seed=400 + B * 7 + T + H)
+    want_state = T != 63
+    o, st = gdr_gdn2_chunk_fwd(dev(inp["q"], bf), dev(inp["k"], bf), dev(inp["v"], bf),
+                               dev(inp["log_alpha"]), dev(inp["erase"]), dev(inp["write"]),
+                               dev(inp["S0"]), want_state=want_state)
+    torch.cuda.synchronize()
+    o_ref, st_ref = _oracle(inp)
+    assert rel_err(host(o), o_ref) <= TOL
+    if want_state:
+        assert rel_err(host(st), st_ref) <= TOL
+    else:
+        assert st is None
