@@ -153,15 +153,6 @@ __device__ __forceinline__ bf16x8 kt_frag(const char* tile, int mc, int s, int l
     return join(lds_tr(p), lds_tr(p + 16 * DK * 2));
 }
 
-// Operand of a transposed-stored T or P tile: lane%16 selects r = 16mt + lane%16,
-// k-slots = tokens i = 32s + 4g + (0..3) and 32s + 16 + 4g + (0..3).
-__device__ __forceinline__ bf16x8 tp_frag(const char* tile, int mt, int s, int lane) {
-    const int g = lane >> 4, j = (lane >> 2) & 3, qd = lane & 3;
-    const int i = 32 * s + 4 * g + j;
-    const char* p = tile + i * 128 + 16 * ((2 * mt + (qd >> 1)) ^ swz_t(i)) + 8 * (qd & 1);
-    return join(lds_tr(p), lds_tr(p + 16 * 128));
-}
-
 // V in accumulator layout of tile mt: lane (col, g) gets V[16mt + 4g + e][16w + col].
 template <int VT>
 __device__ __forceinline__ bf16x4 v_frag(const char* tile, int mt, int w, int lane) {
@@ -205,6 +196,8 @@ struct FragOffsets {
         const char* p = tile + kt[mc >> 1] + 8 * (mc & 1) + s * 32 * DK * 2;
         return join(lds_tr(p), lds_tr(p + 16 * DK * 2));
     }
+    // Operand of a transposed-stored T or P tile: lane%16 selects r = 16mt + lane%16,
+    // k-slots = tokens i = 32s + 4g + (0..3) and 32s + 16 + 4g + (0..3).
     __device__ __forceinline__ bf16x8 tpf(const char* tile, int mt, int s) const {
         const char* p = tile + tp[mt] + s * 32 * 128;
         return join(lds_tr(p), lds_tr(p + 16 * 128));

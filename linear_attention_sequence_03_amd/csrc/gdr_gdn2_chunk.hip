@@ -705,12 +705,7 @@ __global__ __launch_bounds__(64 * (NW + 2)) __attribute__((amdgpu_waves_per_eu(1
     __bf16* __restrict__ o, float* __restrict__ ST, const uint8_t* __restrict__ ws, int64_t T, int H, int NT,
     int DV) {
     using SL = G2Stage<DK, NW>;
-    using L = G2Ws<DK>;
     using M = Mma<__bf16>;
-    using DQ = typename SL::DQ;
-    using DT = typename SL::DT;
-    using DVt = typename SL::DVt;
-    using DWt = typename SL::DWt;
     constexpr int VT = SL::VT;
     constexpr int NKC = DK / 32, NKT = GC / 32, MT = GC / 16, CT = DK / 16;
     static_assert(SL::TOTAL <= 160 * 1024, "LDS budget");
