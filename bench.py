@@ -1,14 +1,17 @@
 """Benchmark of the gated delta rule forward pass on one MI355X.
 
-Headline: chunkwise prefill (gdr_chunk_fwd) tokens/s on the Gated DeltaNet
-workload B=4, H=16, T=4096, d_k=d_v=128, chunk 64, bf16 q/k/v/o, fp32 gates and
-state, seeded synthetic inputs resident in HBM.  One step = one gdr_chunk_fwd
-call over the whole batch.  The same line also carries the decode step
-(gdr_decode_step, B=256, H=32, d=128, fp32 state) as achieved HBM GB/s.
+Headline: chunkwise prefill (gdr_chunk_fwd) tokens/s on the largest prefill
+workload that fits one GPU, the long-context Gated DeltaNet call B=1, H=32,
+T=32768, d_k=d_v=128, chunk 64, bf16 q/k/v/o, fp32 gates, an fp32 start state
+S0 and the final state S_T; seeded synthetic inputs resident in HBM.  One step
+= one gdr_chunk_fwd call over the whole batch.  The same line carries the
+other two prefill workloads (B=4,H=16,T=4096 scalar gate; B=2,H=32,T=8192
+channel gate), the decode step (gdr_decode_step, B=256, H=32, d=128, fp32
+state) as achieved HBM GB/s, and the CPU oracle's throughput.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
-    python bench.py --workload 2     # the same line for another prefill workload
-                                     # (2: KDA B=2,H=32,T=8192; 3: GDN B=1,H=32,T=32768 with S0)
+    python bench.py --workload 1     # another prefill workload as the headline
+                                     # (1: GDN B=4,H=16,T=4096; 2: KDA B=2,H=32,T=8192)
     python bench.py --workload 2 --fg2   # channel-wise write rates (FG2-GDN+) on that
                                          # shape, with the overhead over the KDA call
     python bench.py --workload 2 --gdn2  # decoupled erase / write gates (Gated
@@ -17,18 +20,22 @@ call over the whole batch.  The same line also carries the decode step
     python bench.py --prologue           # raw q, k and beta logits: the gate prologue
                                          # fused into the kernels, against torch
                                          # normalising first
-    python bench.py --traffic        # HBM bytes per call from rocprofv3 counters
-    python bench.py --mfma           # issued MFMA FLOPs and MFMA-busy % per call (rocprofv3)
+    python bench.py --traffic [--workload N]  # HBM bytes per call (rocprofv3 counters);
+                                              # N = 4 is the decode step
+    python bench.py --mfma [--workload N]     # issued MFMA FLOPs and MFMA-busy % per call
     python bench.py --sweep          # every chunkwise call over 2k x 16 ... 32k x 1 (H=32)
 
 Prints ONE JSON line.  Only one GPU is used; --gpus above 1 exits.
 
-`roofline.traffic` is the HBM bytes one prefill call moves, from two
-rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE) over the call's kernels,
-each scaled by what the same counter reads for a plain 256 MiB device copy
-(libgdr_calib.so: 16-byte loads and stores).
-`--traffic` measures it and writes a summary; the default run reports it only
-when that summary was taken from the current kernel sources (hash match).
+Timing: `value` is whole-job tokens/s over K back-to-back calls bracketed by
+synchronisation.  `roofline` uses the median duration of K launches timed
+with HIP events on the launch stream, each launch after a 512 MiB write that
+evicts the inputs from the caches (the warm median is reported beside it).
+`roofline.traffic` is the HBM bytes one call moves, from two rocprofv3 --pmc
+passes (FETCH_SIZE, then WRITE_SIZE) over the call's kernels, each scaled by
+what the same counter reads for a plain 256 MiB device copy (libgdr_calib.so:
+16-byte loads and stores); it is reported only while the summary in profiles/
+was taken from the current kernel sources (hash match), else null.
 """
 from __future__ import annotations
 
@@ -74,18 +81,39 @@ def decode_algorithmic(B, H, d, io_bytes=4):
     return bh * (2 * d * d * 4 + 4 * d * io_bytes + 8)
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gdr_chunk_fwd_gdn_B4_H16_T4096_d128.traffic.txt")
 COPY_BYTES = 256 << 20
 PREFILL_KERNELS = ("fused_chunk", "wy_prep", "state_pass")
-MFMA_FILE = os.path.join(ROOT, "profiles", "gdr_chunk_fwd_gdn_B4_H16_T4096_d128.mfma.txt")
+DECODE_KERNELS = ("decode_kernel",)
 # rocprofv3 derived counters: issued MFMA FLOPs by operand type (MOPS x 512) and
 # the MFMA-busy share of the SIMDs over the dispatch
 MFMA_COUNTERS = ("MfmaFlopsBF16", "MfmaFlopsF16", "MfmaUtil")
+HEADLINE = 3
 ROOFLINE_KERNEL = {
     1: "gdr_chunk_fwd (single kernel: fused_chunk<128, 2>)",
     2: "gdr_chunk_fwd (wy_prep_channel_bf16<128, 64> + state_pass<bf16, 128, 64, 2, channel>)",
     3: "gdr_chunk_fwd (single kernel: fused_chunk<128, 1>)",
 }
+PROFILE_STEM = {
+    1: "gdr_chunk_fwd_gdn_B4_H16_T4096_d128",
+    2: "gdr_chunk_fwd_kda_B2_H32_T8192_d128",
+    3: "gdr_chunk_fwd_gdn_s0_B1_H32_T32768_d128",
+    4: "gdr_decode_step_B256_H32_d128",
+}
+
+
+def profile_file(workload, kind):
+    """profiles/<call and workload>.<kind>.txt (kind: traffic or mfma)."""
+    return os.path.join(ROOT, "profiles", "%s.%s.txt" % (PROFILE_STEM[workload], kind))
+
+
+def read_summary(workload, kind):
+    """The key=value lines of a counter summary, or None when it is absent or
+    was taken from other kernel sources."""
+    path = profile_file(workload, kind)
+    if not os.path.exists(path):
+        return None
+    kv = dict(l.strip().split("=", 1) for l in open(path) if "=" in l and not l.startswith("#"))
+    return kv if kv.get("source_hash") == kernel_source_hash() else None
 
 
 def kernel_source_hash():
@@ -109,19 +137,37 @@ def cpu_baseline(inp, threads, min_seconds=10.0, max_reps=40, S0=None):
     return reps, time.perf_counter() - t0
 
 
-def traffic_probe():
-    """Program run under rocprofv3 --pmc: 3 prefill calls, then 3 plain copies."""
+def host_threads():
+    """Host threads for the CPU baseline: the cores this process may run on,
+    limited to the per-GPU share the host sets in OMP_NUM_THREADS when it does."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    share = os.environ.get("OMP_NUM_THREADS", "")
+    if share.isdigit() and int(share) > 0:
+        n = min(n, int(share))
+    return max(1, n)
+
+
+def traffic_probe(workload):
+    """Program run under rocprofv3 --pmc: 3 calls of the workload (a prefill
+    call, or for workload 4 a decode step), then 3 plain copies."""
+    import ctypes
     import torch
-    from linear_attention_sequence_03_amd import gdr_chunk_fwd, synth
-    w = synth.WORKLOADS[1]
+    from linear_attention_sequence_03_amd import gdr_chunk_fwd, gdr_decode_step, synth
+    w = synth.WORKLOADS[workload]
     inp = synth.workload_inputs(w)
     dev = torch.device("cuda:0")
-    t = {n: torch.from_numpy(inp[n]).to(dev) for n in ("q", "k", "v", "log_alpha", "beta")}
-    for n in ("q", "k", "v"):
-        t[n] = t[n].to(torch.bfloat16)
+    t = {n: torch.from_numpy(a).to(dev) for n, a in inp.items() if a is not None}
+    if w.io == "bf16":
+        for n in ("q", "k", "v"):
+            t[n] = t[n].to(torch.bfloat16)
     for _ in range(3):
-        gdr_chunk_fwd(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], None, chunk=w.chunk)
-    import ctypes
+        if w.call == "chunk":
+            gdr_chunk_fwd(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], t.get("S0"), chunk=w.chunk)
+        else:
+            gdr_decode_step(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], t["S"], inplace=True)
     calib = ctypes.CDLL(os.path.join(ROOT, "linear_attention_sequence_03_amd", "libgdr_calib.so"))
     calib.gdr_calib_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                      ctypes.c_void_p]
@@ -169,33 +215,57 @@ def copy_ceiling():
     print(json.dumps(res))
 
 
-def measure_traffic(outdir):
+def _pmc_rows(outdir, counters, workload):
+    d = tempfile.mkdtemp(prefix="pmc_", dir=outdir)
+    cmd = (["rocprofv3", "--pmc"] + list(counters) + ["--output-format", "csv", "-d", d, "-o", "run",
+                                                      "--", sys.executable, os.path.abspath(__file__),
+                                                      "--traffic-probe", "--workload", str(workload)])
+    subprocess.run(cmd, check=True, stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL, timeout=240)
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        rows += list(csv.DictReader(open(f)))
+    return rows
+
+
+def measure_traffic(outdir, workload):
     """Two rocprofv3 --pmc passes over traffic_probe(); returns bytes per call."""
+    kernels = DECODE_KERNELS if workload == 4 else PREFILL_KERNELS
     res = {}
     for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
-        d = tempfile.mkdtemp(prefix="pmc_", dir=outdir)
-        cmd = ["rocprofv3", "--pmc", ctr, "--output-format", "csv", "-d", d, "-o", "run", "--",
-               sys.executable, os.path.abspath(__file__), "--traffic-probe"]
-        subprocess.run(cmd, check=True, stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL,
-                       timeout=240)
-        rows = []
-        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
-            rows += list(csv.DictReader(open(f)))
         per = {}
-        for r in rows:
+        for r in _pmc_rows(outdir, [ctr], workload):
             name = r["Kernel_Name"]
-            key = next((k for k in PREFILL_KERNELS if k in name), None)
+            key = next((k for k in kernels if k in name), None)
             if key is None and "gdr_calib_copy_kernel" in name:
                 key = "copy"
             if key:
                 per.setdefault(key, []).append(float(r["Counter_Value"]))
         kib_copy = sum(per["copy"]) / len(per["copy"])
         factor = (COPY_BYTES / 1024.0) / kib_copy
-        kib_call = sum(sum(per[k]) / len(per[k]) for k in PREFILL_KERNELS if k in per)
-        res.setdefault("kernels", sorted(k for k in PREFILL_KERNELS if k in per))
+        kib_call = sum(sum(per[k]) / len(per[k]) for k in kernels if k in per)
+        res.setdefault("kernels", sorted(k for k in kernels if k in per))
         res[ctr] = dict(kib_per_call=kib_call, copy_kib=kib_copy, factor=factor,
                         bytes_per_call=kib_call * factor * 1024.0)
     return res
+
+
+def measure_mfma(outdir, workload):
+    """One rocprofv3 --pmc pass (MFMA counters) over traffic_probe(); returns the
+    per-call sum over the prefill kernels of each counter's per-dispatch mean
+    (MfmaUtil: the mean over every prefill dispatch)."""
+    per = {}
+    for r in _pmc_rows(outdir, MFMA_COUNTERS, workload):
+        key = next((k for k in PREFILL_KERNELS if k in r["Kernel_Name"]), None)
+        if key:
+            d = per.setdefault(r["Counter_Name"], {}).setdefault(key, {})
+            d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    out = {}
+    for c, by_kernel in per.items():
+        if c == "MfmaUtil":
+            out[c] = float(np.mean([v for d in by_kernel.values() for v in d.values()]))
+        else:
+            out[c] = float(sum(np.mean(list(d.values())) for d in by_kernel.values()))
+    return out
 
 
 def cpu_model() -> str:
@@ -318,14 +388,68 @@ def run_sweep(steps: int, warmup: int):
     print(json.dumps(out))
 
 
+def prefill_tensors(w, devn):
+    """A prefill workload's seeded inputs on the device, outputs and workspace."""
+    import torch
+    from linear_attention_sequence_03_amd import synth
+    from linear_attention_sequence_03_amd.gdr import (GDR_BF16, GDR_GATE_CHANNEL, GDR_GATE_SCALAR,
+                                                      gdr_chunk_fwd_workspace_size)
+    inp = synth.workload_inputs(w)
+    B, T, H, d, C = w.B, w.T, w.H, w.d, w.chunk
+    bf = torch.bfloat16
+    t = {n: torch.from_numpy(inp[n]).to(devn) for n in ("log_alpha", "beta")}
+    for n in ("q", "k", "v"):
+        t[n] = torch.from_numpy(inp[n]).to(devn).to(bf)
+    t["S0"] = torch.from_numpy(inp["S0"]).to(devn) if inp.get("S0") is not None else None
+    t["o"] = torch.empty((B, T, H, d), dtype=bf, device=devn)
+    t["S_T"] = torch.empty((B, H, d, d), dtype=torch.float32, device=devn)
+    channel = inp["log_alpha"].ndim == 4
+    gate = GDR_GATE_CHANNEL if channel else GDR_GATE_SCALAR
+    t["ws"] = torch.empty(gdr_chunk_fwd_workspace_size(B, T, H, d, d, C, GDR_BF16, gate),
+                          dtype=torch.uint8, device=devn)
+    return inp, t, channel, gate
+
+
+def event_times(step, n, stream, flush=None):
+    """Durations (ms) of n launches of step(), HIP events on the launch stream;
+    with ``flush``, a 512 MiB write (not timed) evicts the caches before each."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in ev:
+        if flush is not None:
+            flush.fill_(1)
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+def roofline_entry(nbytes, cold, warm, traffic, kernel):
+    med = float(np.median(cold))
+    achieved = nbytes / (med * 1e-3) / 1e9
+    return {"bound": "hbm", "kernel": kernel, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "algorithmic_bytes_per_launch": nbytes,
+            "launch_ms_cold_median": med, "launch_ms_cold_min": float(np.min(cold)),
+            "launch_ms_cold_mean": float(np.mean(cold)), "launch_ms_warm_median": float(np.median(warm)),
+            "timing": "median of %d launches, each after a 512 MiB cache-evicting write; HIP events "
+                      "on the launch stream" % len(cold)}
+
+
+def traffic_of(workload):
+    kv = read_summary(workload, "traffic")
+    return float(kv["traffic_bytes_per_call"]) if kv else None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-steps", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=1, choices=(1, 2, 3),
-                    help="prefill workload to time (1 is the headline)")
+    ap.add_argument("--workload", type=int, default=HEADLINE, choices=(1, 2, 3, 4),
+                    help="prefill workload of the line (3, the largest, is the headline); "
+                         "with --traffic / --mfma, 4 selects the decode step")
     ap.add_argument("--fg2", action="store_true",
                     help="time gdr_fg2_chunk_fwd with key and value rates (FG2-GDN+) instead")
     ap.add_argument("--gdn2", action="store_true",
@@ -334,6 +458,8 @@ def main():
     ap.add_argument("--prologue", action="store_true",
                     help="raw q, k and beta logits: time the fused gate prologue instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the other prefill workloads in the line")
     ap.add_argument("--sweep", action="store_true",
                     help="prefill tokens/s of every chunkwise call over the B x T sweep 2k x 16 ... "
                          "32k x 1 (H=32, d=128), one JSON line of its own")
@@ -351,21 +477,25 @@ def main():
         run_sweep(args.steps, args.warmup)
         return
     if args.traffic_probe:
-        traffic_probe()
+        traffic_probe(args.workload)
         return
     if args.copy:
         copy_ceiling()
         return
+    from linear_attention_sequence_03_amd import synth
+    wname = synth.WORKLOADS[args.workload].name
     if args.traffic:
         os.makedirs(args.out, exist_ok=True)
-        res = measure_traffic(args.out)
+        res = measure_traffic(args.out, args.workload)
         total = res["FETCH_SIZE"]["bytes_per_call"] + res["WRITE_SIZE"]["bytes_per_call"]
-        path = os.path.join(args.out, os.path.basename(TRAFFIC_FILE))
+        path = os.path.join(args.out, os.path.basename(profile_file(args.workload, "traffic")))
         with open(path, "w") as fh:
-            fh.write("# HBM traffic of one gdr_chunk_fwd call (B=4,T=4096,H=16,d=128,chunk=64, bf16)\n")
-            fh.write("# command: python bench.py --traffic   (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)\n")
-            fh.write("# kernels: %s; calibration: plain %d MiB device copy\n"
-                     % (", ".join(res.get("kernels", PREFILL_KERNELS)), COPY_BYTES >> 20))
+            fh.write("# HBM traffic of one %s call, workload %s\n"
+                     % ("gdr_decode_step" if args.workload == 4 else "gdr_chunk_fwd", wname))
+            fh.write("# command: python bench.py --traffic --workload %d   (rocprofv3 --pmc FETCH_SIZE, "
+                     "then WRITE_SIZE, over 3 calls and 3 plain copies)\n" % args.workload)
+            fh.write("# kernels: %s; calibration: plain %d MiB device copy (libgdr_calib.so)\n"
+                     % (", ".join(res.get("kernels", ())), COPY_BYTES >> 20))
             fh.write("source_hash=%s\n" % kernel_source_hash())
             for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
                 r = res[ctr]
@@ -376,12 +506,14 @@ def main():
         return
     if args.mfma:
         os.makedirs(args.out, exist_ok=True)
-        res = measure_mfma(args.out)
-        path = os.path.join(args.out, os.path.basename(MFMA_FILE))
+        res = measure_mfma(args.out, args.workload)
+        path = os.path.join(args.out, os.path.basename(profile_file(args.workload, "mfma")))
         with open(path, "w") as fh:
-            fh.write("# Issued MFMA work of one gdr_chunk_fwd call (B=4,T=4096,H=16,d=128,chunk=64, bf16)\n")
-            fh.write("# command: python bench.py --mfma   (rocprofv3 --pmc %s)\n" % " ".join(MFMA_COUNTERS))
-            fh.write("# kernel: fused_chunk; per-dispatch means over the probe's calls\n")
+            fh.write("# Issued MFMA work of one gdr_chunk_fwd call, workload %s\n" % wname)
+            fh.write("# command: python bench.py --mfma --workload %d   (rocprofv3 --pmc %s)\n"
+                     % (args.workload, " ".join(MFMA_COUNTERS)))
+            fh.write("# kernels: %s; per-dispatch means over the probe's calls, summed over the "
+                     "call's kernels (MfmaUtil: mean over its dispatches)\n" % ", ".join(PREFILL_KERNELS))
             fh.write("source_hash=%s\n" % kernel_source_hash())
             for c, v in res.items():
                 fh.write("%s=%.6g\n" % (c, v))
@@ -391,32 +523,25 @@ def main():
         print("bench.py measures one GPU only (this path has no multi-GPU part); "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.workload == 4:
+        print("--workload 4 (the decode step) is part of every line; pick a prefill workload",
+              file=sys.stderr)
+        sys.exit(2)
 
     import torch
     from linear_attention_sequence_03_amd import (gdr_chunk_fwd, gdr_decode_step, gdr_fg2_chunk_fwd,
-                                                  gdr_gdn2_fwd, synth)
-    from linear_attention_sequence_03_amd.gdr import (GDR_BF16, GDR_GATE_CHANNEL, GDR_GATE_SCALAR,
-                                                      gdr_chunk_fwd_workspace_size,
-                                                      gdr_fg2_chunk_fwd_workspace_size)
+                                                  gdr_gdn2_fwd)
+    from linear_attention_sequence_03_amd.gdr import GDR_BF16, gdr_fg2_chunk_fwd_workspace_size
 
     assert torch.cuda.is_available(), "no GPU visible"
     devn = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(devn)
     w = synth.WORKLOADS[args.workload]
-    inp = synth.workload_inputs(w)
     B, T, H, d, C = w.B, w.T, w.H, w.d, w.chunk
-    channel = inp["log_alpha"].ndim == 4
-    S0 = torch.from_numpy(inp["S0"]).to(devn) if inp.get("S0") is not None else None
+    inp, t, channel, gate = prefill_tensors(w, devn)
+    q, k, v, la, be, S0, o, st, ws = (t[n] for n in ("q", "k", "v", "log_alpha", "beta", "S0", "o",
+                                                      "S_T", "ws"))
     bf = torch.bfloat16
-    q = torch.from_numpy(inp["q"]).to(devn).to(bf)
-    k = torch.from_numpy(inp["k"]).to(devn).to(bf)
-    v = torch.from_numpy(inp["v"]).to(devn).to(bf)
-    la = torch.from_numpy(inp["log_alpha"]).to(devn)
-    be = torch.from_numpy(inp["beta"]).to(devn)
-    o = torch.empty((B, T, H, d), dtype=bf, device=devn)
-    st = torch.empty((B, H, d, d), dtype=torch.float32, device=devn)
-    gate = GDR_GATE_CHANNEL if channel else GDR_GATE_SCALAR
-    ws = torch.empty(gdr_chunk_fwd_workspace_size(B, T, H, d, d, C, GDR_BF16, gate),
-                     dtype=torch.uint8, device=devn)
 
     def plain_step():
         gdr_chunk_fwd(q, k, v, la, be, S0, chunk=C, o=o, S_T=st, workspace=ws)
@@ -471,104 +596,92 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
+    print("headline workload timed: %.4f ms per call" % ms_per_step, file=sys.stderr, flush=True)
 
-    # Per-launch duration with HIP events on the launch stream, inputs evicted
-    # from the caches between launches by a 512 MiB write (not timed).
-    stream = torch.cuda.current_stream(devn)
+    # Per-launch durations: cold (caches evicted before each launch) and warm.
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=devn)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    for a, b in ev:
-        flush.fill_(1)
-        a.record(stream)
-        step()
-        b.record(stream)
-    torch.cuda.synchronize()
-    cold = [a.elapsed_time(b) for a, b in ev]
-    ev2 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for a, b in ev2:
-        a.record(stream)
-        step()
-        b.record(stream)
-    torch.cuda.synchronize()
-    warm = [a.elapsed_time(b) for a, b in ev2]
-    del flush
+    cold = event_times(step, args.steps, stream, flush)
+    warm = event_times(step, args.steps, stream)
 
+    variant = args.fg2 or args.gdn2 or args.prologue
     nbytes, flops = prefill_algorithmic(B, T, H, d, C, s0=S0 is not None, channel=channel,
                                         fg2=args.fg2 or args.gdn2)
-    fg2_info = None
-    pro_info = None
+    launch_ms = float(np.median(cold))
+    has_s0 = S0 is not None
+    extra_info = {}
     if args.prologue:
         for _ in range(3):
             torch_then_plain()
-        ev4 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
-        for a, b in ev4:
-            a.record(stream)
-            torch_then_plain()
-            b.record(stream)
-        torch.cuda.synchronize()
-        tms = float(np.mean([a.elapsed_time(b) for a, b in ev4]))
-        pro_info = {"call": "gdr_chunk_fwd_prologue (L2 norm of q, k + sigmoid of beta, fused)",
-                    "launch_ms_mean": float(np.mean(warm)),
-                    "unfused_call": "torch normalisation + sigmoid, then gdr_chunk_fwd",
-                    "unfused_ms_mean": tms,
-                    "speedup": tms / float(np.mean(warm))}
+        tms = float(np.median(event_times(torch_then_plain, args.steps, stream, flush)))
+        extra_info["prologue"] = {
+            "call": "gdr_chunk_fwd_prologue (L2 norm of q, k + sigmoid of beta, fused)",
+            "launch_ms_cold_median": launch_ms,
+            "unfused_call": "torch normalisation + sigmoid, then gdr_chunk_fwd",
+            "unfused_ms_cold_median": tms, "speedup": tms / launch_ms}
     if args.fg2:
-        # the same call without rates, timed the same way, for the overhead
         for _ in range(3):
             plain_step()
-        ev3 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
-        for a, b in ev3:
-            a.record(stream)
-            plain_step()
-            b.record(stream)
-        torch.cuda.synchronize()
-        base_ms = float(np.mean([a.elapsed_time(b) for a, b in ev3]))
+        base_ms = float(np.median(event_times(plain_step, args.steps, stream, flush)))
         base_bytes, _ = prefill_algorithmic(B, T, H, d, C, s0=S0 is not None, channel=channel)
-        fg2_info = {"call": "gdr_fg2_chunk_fwd (key and value rates: FG2-GDN+)",
-                    "launch_ms_mean": float(np.mean(warm)),
-                    "base_call": "gdr_chunk_fwd (scalar rate)", "base_launch_ms_mean": base_ms,
-                    "overhead": float(np.mean(warm)) / base_ms - 1.0,
-                    "algorithmic_bytes": nbytes, "base_algorithmic_bytes": base_bytes,
-                    "bytes_overhead": nbytes / base_bytes - 1.0}
-    gdn2_info = None
+        extra_info["fg2"] = {
+            "call": "gdr_fg2_chunk_fwd (key and value rates: FG2-GDN+)",
+            "launch_ms_cold_median": launch_ms, "base_call": "gdr_chunk_fwd (scalar rate)",
+            "base_launch_ms_cold_median": base_ms, "overhead": launch_ms / base_ms - 1.0,
+            "algorithmic_bytes": nbytes, "base_algorithmic_bytes": base_bytes,
+            "bytes_overhead": nbytes / base_bytes - 1.0}
     if args.gdn2:
-        # the token-sequential scan on the same inputs, for comparison
         scan_step()
-        ev5 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(min(args.steps, 5))]
-        for a, b in ev5:
-            a.record(stream)
-            scan_step()
-            b.record(stream)
-        torch.cuda.synchronize()
-        sms = float(np.mean([a.elapsed_time(b) for a, b in ev5]))
-        gdn2_info = {"call": "gdr_gdn2_chunk_fwd (gdn2_prep + gdn2_state_pass)",
-                     "launch_ms_mean": float(np.mean(warm)),
-                     "scan_call": "gdr_gdn2_fwd (gdn2_scan, token-sequential)",
-                     "scan_launch_ms_mean": sms, "speedup": sms / float(np.mean(warm))}
-    launch_ms = float(np.mean(warm))
-    traffic = None
-    if args.workload == 1 and os.path.exists(TRAFFIC_FILE):
-        kv = dict(l.strip().split("=", 1) for l in open(TRAFFIC_FILE)
-                  if "=" in l and not l.startswith("#"))
-        if kv.get("source_hash") == kernel_source_hash():
-            traffic = float(kv["traffic_bytes_per_call"])
-    achieved = nbytes / (launch_ms * 1e-3) / 1e9
+        sms = float(np.median(event_times(scan_step, min(args.steps, 5), stream, flush)))
+        extra_info["gdn2"] = {"call": "gdr_gdn2_chunk_fwd (gdn2_prep + gdn2_state_pass)",
+                              "launch_ms_cold_median": launch_ms,
+                              "scan_call": "gdr_gdn2_fwd (gdn2_scan, token-sequential)",
+                              "scan_launch_ms_cold_median": sms, "speedup": sms / launch_ms}
+    traffic = None if variant else traffic_of(args.workload)
+    kernel = ("gdr_gdn2_chunk_fwd (gdn2_prep<128, channel> + gdn2_state_pass<128, 2>)" if args.gdn2 else
+              ("gdr_fg2_chunk_fwd (fg2_scale prologue + " if args.fg2 else "")
+              + ROOFLINE_KERNEL[args.workload] + (")" if args.fg2 else ""))
+    roofline = roofline_entry(nbytes, cold, warm, traffic, kernel)
     tflops = flops / (launch_ms * 1e-3) / 1e12
     issued = {}
-    if args.workload == 1 and not (args.fg2 or args.gdn2 or args.prologue) and os.path.exists(MFMA_FILE):
-        kv = dict(l.strip().split("=", 1) for l in open(MFMA_FILE)
-                  if "=" in l and not l.startswith("#"))
-        if kv.get("source_hash") == kernel_source_hash():
-            iflops = float(kv.get("MfmaFlopsBF16", 0.0)) + float(kv.get("MfmaFlopsF16", 0.0))
-            issued = {"issued_flops_per_launch": iflops,
-                      "issued_tflops": iflops / (launch_ms * 1e-3) / 1e12,
-                      "issued_frac": iflops / (launch_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-                      "mfma_busy_pct": float(kv["MfmaUtil"]) if "MfmaUtil" in kv else None}
+    kv = None if variant else read_summary(args.workload, "mfma")
+    if kv:
+        iflops = float(kv.get("MfmaFlopsBF16", 0.0)) + float(kv.get("MfmaFlopsF16", 0.0))
+        issued = {"issued_flops_per_launch": iflops,
+                  "issued_tflops": iflops / (launch_ms * 1e-3) / 1e12,
+                  "issued_frac": iflops / (launch_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                  "mfma_busy_pct": float(kv["MfmaUtil"]) if "MfmaUtil" in kv else None}
+
+    # The other prefill workloads, timed the same way (one entry each).
+    others = {}
+    if not (variant or args.no_extra):
+        del q, k, v, la, be, S0, o, st, ws, t
+        torch.cuda.empty_cache()
+        for wi in (1, 2, 3):
+            if wi == args.workload:
+                continue
+            w2 = synth.WORKLOADS[wi]
+            _, t2, ch2, _ = prefill_tensors(w2, devn)
+
+            def step2(t2=t2, w2=w2):
+                gdr_chunk_fwd(t2["q"], t2["k"], t2["v"], t2["log_alpha"], t2["beta"], t2["S0"],
+                              chunk=w2.chunk, o=t2["o"], S_T=t2["S_T"], workspace=t2["ws"])
+
+            for _ in range(args.warmup):
+                step2()
+            c2 = event_times(step2, args.steps, stream, flush)
+            w2t = event_times(step2, args.steps, stream)
+            nb2, fl2 = prefill_algorithmic(w2.B, w2.T, w2.H, w2.d, w2.chunk, s0=t2["S0"] is not None,
+                                           channel=ch2)
+            r2 = roofline_entry(nb2, c2, w2t, traffic_of(wi), ROOFLINE_KERNEL[wi])
+            m2 = r2["launch_ms_cold_median"]
+            others[w2.name] = {"tokens_per_s": w2.B * w2.T / (m2 * 1e-3), "roofline": r2,
+                               "algorithmic_tflops": fl2 / (m2 * 1e-3) / 1e12,
+                               "algorithmic_mfma_frac": fl2 / (m2 * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+            del t2
+            torch.cuda.empty_cache()
+            print("workload %d timed: %.4f ms per call" % (wi, m2), file=sys.stderr, flush=True)
+    del flush
+    torch.cuda.empty_cache()
 
     # Decode step, in place on a resident 512 MiB state.
     wd = synth.WORKLOADS[4]
@@ -577,17 +690,15 @@ def main():
                               for n in ("q", "k", "v", "log_alpha", "beta"))
     S = torch.from_numpy(dinp["S"]).to(devn)
     do = torch.empty((wd.B, wd.H, wd.d), dtype=torch.float32, device=devn)
+
+    def dstep():
+        gdr_decode_step(dq, dk_, dv_, dla, dbe, S, o=do, inplace=True)
+
     for _ in range(3):
-        gdr_decode_step(dq, dk_, dv_, dla, dbe, S, o=do, inplace=True)
+        dstep()
     torch.cuda.synchronize()
-    dev_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.decode_steps)]
-    for a, b in dev_ev:
-        a.record(stream)
-        gdr_decode_step(dq, dk_, dv_, dla, dbe, S, o=do, inplace=True)
-        b.record(stream)
-    torch.cuda.synchronize()
-    dms = float(np.mean([a.elapsed_time(b) for a, b in dev_ev]))
+    dtimes = event_times(dstep, args.decode_steps, stream)
+    dms = float(np.median(dtimes))
     dbytes = decode_algorithmic(wd.B, wd.H, wd.d)
     dgbs = dbytes / (dms * 1e-3) / 1e9
 
@@ -614,14 +725,7 @@ def main():
         for _ in range(3):
             fn()
         torch.cuda.synchronize()
-        mev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.decode_steps)]
-        for a, b in mev:
-            a.record(stream)
-            fn()
-            b.record(stream)
-        torch.cuda.synchronize()
-        mres[name] = float(np.mean([a.elapsed_time(b) for a, b in mev]))
+        mres[name] = float(np.median(event_times(fn, args.decode_steps, stream)))
     state_bytes = wd.B * wd.H * wd.d * wd.d * 4
     vec_bytes = wd.B * Td * wd.H * (4 * wd.d * 4 + 8)
     mv_bytes = state_bytes + vec_bytes                      # read the state once
@@ -640,7 +744,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded; q,k unit-norm N(0,1), v N(0,1), beta sigmoid(N(0,1)), "
-                "log_alpha U(-0.1,-0.001)%s)" % (", S0 N(0,0.02^2)" if S0 is not None else ""),
+                "log_alpha U(-0.1,-0.001)%s)" % (", S0 N(0,0.02^2)" if has_s0 else ""),
         "config": {"workload": w.name + ("_fg2plus" if args.fg2 else "_gdn2" if args.gdn2
                                          else "_raw_prologue" if args.prologue else ""),
                    "call": ("gdr_fg2_chunk_fwd" if args.fg2 else "gdr_gdn2_chunk_fwd" if args.gdn2
@@ -648,22 +752,14 @@ def main():
                    "gate": "channel" if channel else "scalar",
                    "B": B, "T": T, "H": H, "d_k": d, "d_v": d, "chunk": C,
                    "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm",
-                     "kernel": ("gdr_gdn2_chunk_fwd (gdn2_prep<128, channel> + gdn2_state_pass<128, 2>)"
-                                if args.gdn2 else
-                                ("gdr_fg2_chunk_fwd (fg2_scale prologue + " if args.fg2 else "")
-                                + ROOFLINE_KERNEL[args.workload] + (")" if args.fg2 else "")),
-                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "algorithmic_bytes_per_launch": nbytes,
-                     "launch_ms_mean": launch_ms,
-                     "launch_ms_cold_cache_mean": float(np.mean(cold))},
+        "roofline": roofline,
         "prefill_mfma": {"algorithmic_flops_per_launch": flops, "tflops": tflops,
                          "peak_tflops": BF16_PEAK_TFLOPS, "frac": tflops / BF16_PEAK_TFLOPS, **issued},
-        "decode": {"workload": wd.name, "call": "gdr_decode_step", "ms_per_step": dms,
+        "decode": {"workload": wd.name, "call": "gdr_decode_step", "ms_per_step_median": dms,
                    "tokens_per_s": wd.B / (dms * 1e-3),
                    "algorithmic_bytes": dbytes, "achieved_GBs": dgbs,
-                   "peak_GBs": HBM_PEAK_GBS, "frac": dgbs / HBM_PEAK_GBS},
+                   "peak_GBs": HBM_PEAK_GBS, "frac": dgbs / HBM_PEAK_GBS, "traffic": traffic_of(4),
+                   "timing": "median of %d in-place steps, HIP events" % len(dtimes)},
         "decode_multi": {"call": "gdr_decode_multi", "draft_tokens": Td,
                          "verify_ms": mres["verify"], "verify_bytes": mv_bytes,
                          "verify_GBs": mv_bytes / (mres["verify"] * 1e-3) / 1e9,
@@ -672,22 +768,22 @@ def main():
                          "note": "verify: state read once, o for all draft tokens; commit: "
                                  "state of the accepted prefix written in place"},
     }
-    if fg2_info is not None:
-        out["fg2"] = fg2_info
-    if pro_info is not None:
-        out["prologue"] = pro_info
-    if gdn2_info is not None:
-        out["gdn2"] = gdn2_info
-    if not args.no_cpu_baseline and not (args.fg2 or args.gdn2 or args.prologue):
-        import oracle.gdr_oracle as og
-        threads = min(16, og.default_threads())
+    if others:
+        out["other_prefill"] = others
+    out.update(extra_info)
+    if not args.no_cpu_baseline and not variant:
+        import oracle.gdr_oracle as og  # noqa: F401  (builds the oracle on first use)
+        threads = host_threads()
         reps, secs = cpu_baseline(inp, threads, S0=inp.get("S0"))
         out["cpu_baseline"] = {"value": reps * B * T / secs, "unit": "tokens/s", "cores": threads,
                                "kind": "oracle",
                                "sample": "the whole prefill workload (B=%d,T=%d,H=%d,d=%d) "
                                          "through the fp64 token-by-token oracle, %d times, "
-                                         "%.1f s on %s; the GPU call is %.0fx its throughput"
-                                         % (B, T, H, d, reps, secs, cpu_model(),
+                                         "%.1f s on %d threads of %s (the host cores this process "
+                                         "may use, within the per-GPU share OMP_NUM_THREADS=%s); "
+                                         "the GPU call is %.0fx its throughput"
+                                         % (B, T, H, d, reps, secs, threads, cpu_model(),
+                                            os.environ.get("OMP_NUM_THREADS", "unset"),
                                             out["value"] / (reps * B * T / secs))}
     print(json.dumps(out))
 

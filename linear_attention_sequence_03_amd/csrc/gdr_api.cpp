@@ -123,6 +123,11 @@ gdr_status chunk_fwd_impl(const void* q, const void* k, const void* v, const flo
     if (ntok < 0 || mul({ntok, dk}) < 0 || mul({B, H, dv, dk}) < 0)
         return fail(GDR_ERR_UNSUPPORTED, "tensor sizes overflow");
     if (mul({B, H, dv / 16}) > INT32_MAX) return fail(GDR_ERR_UNSUPPORTED, "B*H too large");
+    // The kernels address one chunk's rows with 32-bit byte offsets from the
+    // chunk's first row (row stride at most H*d*4 bytes: fp32 rows, or the
+    // per-channel decay).
+    if (mul({chunk, H, dk > dv ? dk : dv, 4}) > INT32_MAX)
+        return fail(GDR_ERR_UNSUPPORTED, "H too large (chunk*H*d*4 bytes must stay below 2^31)");
     if (T > 0 && (!q || !k || !v || !log_alpha || !beta || !o))
         return fail(GDR_ERR_INVALID_ARG, "q, k, v, log_alpha, beta and o must be non-NULL");
     if (need > 0 && !workspace) return fail(GDR_ERR_INVALID_ARG, "workspace is NULL");
@@ -395,6 +400,11 @@ gdr_status gdr_fg2_chunk_fwd(const void* q, const void* k, const void* v, const 
     if (ntok < 0 || mul({ntok, dk}) < 0 || mul({B, H, dv, dk}) < 0)
         return fail(GDR_ERR_UNSUPPORTED, "tensor sizes overflow");
     if (mul({B, H, dv / 16}) > INT32_MAX) return fail(GDR_ERR_UNSUPPORTED, "B*H too large");
+    // The kernels address one chunk's rows with 32-bit byte offsets from the
+    // chunk's first row (row stride at most H*d*4 bytes: fp32 rows, or the
+    // per-channel decay).
+    if (mul({chunk, H, dk > dv ? dk : dv, 4}) > INT32_MAX)
+        return fail(GDR_ERR_UNSUPPORTED, "H too large (chunk*H*d*4 bytes must stay below 2^31)");
     if (T > 0 && (!q || !k || !v || !log_alpha || !beta_k || !o))
         return fail(GDR_ERR_INVALID_ARG, "q, k, v, log_alpha, beta_k and o must be non-NULL");
     if (need > 0 && !workspace) return fail(GDR_ERR_INVALID_ARG, "workspace is NULL");

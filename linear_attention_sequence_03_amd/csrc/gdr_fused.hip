@@ -971,6 +971,12 @@ __global__ __launch_bounds__(64 * (NW + 2 + NL + (NORM ? 1 : 0))) void fused_chu
             if (S0) x = *reinterpret_cast<const float4*>(S0 + (bh * DV + vcol) * DK + c0);
             S[mc] = f32x4{x.x, x.y, x.z, x.w};
         }
+        // The start state must have landed before the loop: the compiler cannot
+        // count loads across the loop's back edge, and a load pending at its entry
+        // makes it wait for every memory operation at the first use of S in each
+        // window, the previous window's output stores included.
+#pragma unroll
+        for (int mc = 0; mc < CT; ++mc) asm volatile("" ::"v"(S[mc]));
         // K fragments (first half of the channel steps) of the chunk computed
         // next, read one window ahead (its stage is complete then and stays
         // untouched until after it is used).

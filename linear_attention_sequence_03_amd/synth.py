@@ -150,3 +150,51 @@ def raw_prologue_inputs(inp, io="bf16", seed=0):
         out[n] = _store(x * rng.uniform(1.0, 8.0, x.shape[:-1] + (1,)), io)
     out["beta"] = (rng.standard_normal(inp["beta"].shape) * 1.5).astype(np.float32)
     return out
+
+
+EDGE_KEYS = ("repeated", "antiparallel", "near_collinear", "plane", "cyclic3")
+
+
+def edge_key_inputs(kind, B, T, H, d, io="bf16", seed=0, key_norm=1.0, beta=1.0,
+                    log_alpha=0.0, s0_std=0.1):
+    """Valid but adversarial inputs for the chunk solve: keys of norm
+    ``key_norm`` with a degenerate Gram structure, a constant write rate
+    ``beta`` and a constant ``log_alpha`` (0 = no decay).  Key patterns, per
+    (b, h), from one random unit direction u (and a second one w):
+      repeated        every token has key u
+      antiparallel    keys alternate u, -u, u, ...
+      near_collinear  u plus N(0, 0.01^2) noise, renormalised
+      plane           random directions inside span{u, w}
+      cyclic3         keys cycle through three orthonormal directions
+    q, v and S0 are drawn as in chunk_inputs.  Own seeded stream."""
+    if kind not in EDGE_KEYS:
+        raise ValueError(kind)
+    rng = np.random.Generator(np.random.PCG64(seed + 11000))
+    q = _store(_unit_rows(rng, (B, T, H, d)), io)
+    v = _store(rng.standard_normal((B, T, H, d)), io)
+    u = _unit_rows(rng, (B, 1, H, d))
+    w = rng.standard_normal((B, 1, H, d))
+    w -= np.sum(w * u, axis=-1, keepdims=True) * u
+    w /= np.linalg.norm(w, axis=-1, keepdims=True)
+    t = np.arange(T).reshape(1, T, 1, 1)
+    if kind == "repeated":
+        k = np.broadcast_to(u, (B, T, H, d)).copy()
+    elif kind == "antiparallel":
+        k = np.where(t % 2 == 0, 1.0, -1.0) * u
+    elif kind == "near_collinear":
+        k = u + 0.01 * rng.standard_normal((B, T, H, d))
+        k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    elif kind == "plane":
+        th = rng.uniform(0.0, 2.0 * np.pi, (B, T, H, 1))
+        k = np.cos(th) * u + np.sin(th) * w
+    else:
+        x = w - np.sum(w * u, axis=-1, keepdims=True) * u
+        z = rng.standard_normal((B, 1, H, d))
+        z -= np.sum(z * u, axis=-1, keepdims=True) * u + np.sum(z * x, axis=-1, keepdims=True) * x
+        z /= np.linalg.norm(z, axis=-1, keepdims=True)
+        k = np.where(t % 3 == 0, u, np.where(t % 3 == 1, x, z))
+    k = _store(key_norm * k, io)
+    S0 = None if s0_std is None else (rng.standard_normal((B, H, d, d)) * s0_std).astype(np.float32)
+    return dict(q=q, k=k, v=v,
+                log_alpha=np.full((B, T, H), log_alpha, np.float32),
+                beta=np.full((B, T, H), beta, np.float32), S0=S0)

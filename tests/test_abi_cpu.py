@@ -77,6 +77,9 @@ def lib():
     (dict(o=ctypes.c_void_p(BASE + 4 * 1024)), 1),      # o inside q
     (dict(st=ctypes.c_void_p(BASE + 3 * MB + 64)), 1),  # S_T inside log_alpha
     (dict(ws=ctypes.c_void_p(BASE + 6 * MB + 256)), 1), # workspace inside o
+    # a chunk's row offsets would pass 2^31 bytes: refused before any launch
+    (dict(H=70000, dk=128, dv=128, io=1, T=64), 2),
+    (dict(H=140000, dk=64, dv=64, io=0, T=64, wsbytes=1 << 62), 2),
 ])
 def test_chunk_fwd_rejects(lib, kw, code):
     assert _chunk(lib, **kw) == code
@@ -172,6 +175,7 @@ def _fg2_decode(lib, q=0, k=1, v=2, la=3, bk=4, bv=None, si=5, so=6, o=7, B=2, H
     (dict(bk=ctypes.c_void_p(BASE + 4 * MB + 4)), 1),     # misaligned
     (dict(o=ctypes.c_void_p(BASE + 4 * MB + 4096)), 1),   # o inside beta_k
     (dict(bv=ctypes.c_void_p(BASE + 6 * MB)), 1),         # beta_v is o
+    (dict(H=70000, dk=128, dv=128, T=64, wsbytes=1 << 62), 2),   # row offsets past 2^31 bytes
 ])
 def test_fg2_chunk_fwd_rejects(lib, kw, code):
     assert _fg2_chunk(lib, **kw) == code

@@ -1,0 +1,109 @@
+"""GPU parity for every kernel variant the launchers can select.
+
+Wide shapes.  Each chunkwise launcher runs two compute waves per
+   workgroup (32 value columns) when B*H*d_v/32 >= 256, and one otherwise.
+   The small-shape tests elsewhere stay below that line, so here every call
+   runs at B=4, H=32 (B*H*d_v/32 = 256 at d = 64, 512 at d = 128) and a ragged
+   length, and every element is compared with the oracle:
+     - gdr_chunk_fwd: both gates, both io types, chunks 16 / 32 / 64, d 64 / 128
+       (the fused kernel, and state_pass after each prep kernel);
+     - gdr_chunk_fwd_prologue on every fused route (fused kernel, channel prep);
+     - gdr_fg2_chunk_fwd and gdr_gdn2_chunk_fwd.
+
+Metric: normwise max|gpu - oracle| / max|oracle| per (b, h) head, separately
+for o and S_T; tolerance 2e-2 (bf16 io) or 1e-4 (fp32 io).
+"""
+import numpy as np
+import pytest
+
+from linear_attention_sequence_03_amd import synth
+from gpu_helpers import dev, gpu_chunk, host, io_dtype, rel_err, torch_mod
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+B_WIDE, H_WIDE, T_WIDE = 4, 32, 130
+
+
+def per_head_errors(o, st, o_ref, st_ref):
+    """Largest per-head normwise error of o and of the state."""
+    B, _, H, _ = o_ref.shape
+    eo = max(rel_err(o[b, :, h], o_ref[b, :, h]) for b in range(B) for h in range(H))
+    es = max(rel_err(st[b, h], st_ref[b, h]) for b in range(B) for h in range(H))
+    return eo, es
+
+
+def check_all_heads(name, o, st, o_ref, st_ref, tol):
+    o, st = host(o), host(st)
+    assert np.isfinite(o).all() and np.isfinite(st).all()
+    eo, es = per_head_errors(o, st, o_ref, st_ref)
+    print("%s: worst head err_o=%.3g err_S=%.3g (tol %g)" % (name, eo, es, tol))
+    assert eo <= tol and es <= tol, (name, eo, es)
+
+
+# --------------------------------------------------------------------------
+# 1. Wide shapes: the two-compute-wave kernels.
+# --------------------------------------------------------------------------
+CHUNK_CASES = [(io, gate, c) for io in ("bf16", "f32") for gate in ("scalar", "channel")
+               for c in (16, 32, 64)]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("io,gate,chunk", CHUNK_CASES)
+def test_wide_chunk_fwd(io, gate, chunk, d):
+    assert B_WIDE * H_WIDE * d // 32 >= 256   # the launchers' two-wave condition
+    inp = synth.chunk_inputs(B_WIDE, T_WIDE, H_WIDE, d, d, gate, io,
+                             seed=300 + d + chunk + (7 if gate == "channel" else 0), s0_std=0.1)
+    o, st = gpu_chunk(inp, io, chunk=chunk)
+    o_ref, st_ref = oracle.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"],
+                                     inp["S0"])
+    check_all_heads("chunk_fwd %s %s C=%d d=%d" % (io, gate, chunk, d), o, st, o_ref, st_ref, TOL[io])
+
+
+PROLOGUE_CASES = [("scalar", 64), ("channel", 16), ("channel", 32), ("channel", 64)]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("gate,chunk", PROLOGUE_CASES)
+def test_wide_prologue(gate, chunk, d):
+    from linear_attention_sequence_03_amd.gdr import GDR_PROLOGUE_BETA_SIGMOID, GDR_PROLOGUE_L2NORM_QK
+    inp = synth.chunk_inputs(B_WIDE, T_WIDE, H_WIDE, d, d, gate, "bf16", seed=400 + d + chunk,
+                             s0_std=0.1)
+    raw = synth.raw_prologue_inputs(inp, "bf16", seed=401)
+    flags = GDR_PROLOGUE_L2NORM_QK | GDR_PROLOGUE_BETA_SIGMOID
+    o, st = gpu_chunk(raw, "bf16", chunk=chunk, prologue=flags)
+    o_ref, st_ref = oracle.chunk_fwd_prologue(raw["q"], raw["k"], raw["v"], raw["log_alpha"],
+                                              raw["beta"], raw["S0"], flags=flags)
+    check_all_heads("prologue %s C=%d d=%d" % (gate, chunk, d), o, st, o_ref, st_ref, TOL["bf16"])
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_wide_fg2(d):
+    torch = torch_mod()
+    from linear_attention_sequence_03_amd import gdr_fg2_chunk_fwd
+    inp = synth.chunk_inputs(B_WIDE, T_WIDE, H_WIDE, d, d, "channel", "bf16", seed=500 + d, s0_std=0.1)
+    bk, bv = synth.write_rates((B_WIDE, T_WIDE, H_WIDE, d), d, seed=501)
+    bf = io_dtype("bf16")
+    o, st = gdr_fg2_chunk_fwd(dev(inp["q"], bf), dev(inp["k"], bf), dev(inp["v"], bf),
+                              dev(inp["log_alpha"]), dev(bk), dev(bv), dev(inp["S0"]), chunk=64)
+    torch.cuda.synchronize()
+    o_ref, st_ref = oracle.fg2_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], bk, bv,
+                                         inp["S0"])
+    check_all_heads("fg2 d=%d" % d, o, st, o_ref, st_ref, TOL["bf16"])
+
+
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_wide_gdn2_chunk(gate, d):
+    torch = torch_mod()
+    from linear_attention_sequence_03_amd import gdr_gdn2_chunk_fwd
+    inp = synth.chunk_inputs(B_WIDE, T_WIDE, H_WIDE, d, d, gate, "bf16", seed=600 + d, s0_std=0.1)
+    eb, ww = synth.gdn2_gates(B_WIDE, T_WIDE, H_WIDE, d, d, seed=601)
+    bf = io_dtype("bf16")
+    o, st = gdr_gdn2_chunk_fwd(dev(inp["q"], bf), dev(inp["k"], bf), dev(inp["v"], bf),
+                               dev(inp["log_alpha"]), dev(eb), dev(ww), dev(inp["S0"]), chunk=64)
+    torch.cuda.synchronize()
+    o_ref, st_ref = oracle.gdn2_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], eb, ww,
+                                          inp["S0"])
+    check_all_heads("gdn2 %s d=%d" % (gate, d), o, st, o_ref, st_ref, TOL["bf16"])

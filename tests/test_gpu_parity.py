@@ -2,9 +2,10 @@
 
 Metric: normwise relative error max|gpu - oracle| / max|oracle|, separately for
 o and the state.  Tolerances: 1e-4 for fp32 inputs, 2e-2 for bf16 inputs.
-Full-size workloads are compared on sampled (b,h) pairs (each pair is an
-independent sequence the oracle computes alone) plus properties that hold at
-any size; small shapes (several chunks, ragged tails) are compared in full.
+Every workload is compared in full, head by head (each (b,h) pair is an
+independent sequence; the oracle runs them on all host threads), plus
+properties that hold at any size; small shapes (several chunks, ragged tails)
+are compared in full too.
 """
 import numpy as np
 import pytest
@@ -71,43 +72,50 @@ def test_workload_gdn_chunk_f32_small():
     _check_full(inp, w.io, w.chunk)
 
 
-def _sampled(w, pairs, extra=None):
+def _all_heads(w):
+    """The whole workload on the GPU against the oracle over every (b, h) head
+    (the oracle runs the heads on all host threads); each head is compared with
+    its own normwise error, the worst one printed."""
     inp = synth.workload_inputs(w)
     o, st = gpu_chunk(inp, w.io, chunk=w.chunk)
     o, st = host(o), host(st)
-    ref = oracle_pairs(inp, pairs)
-    for (b, h), (o_ref, st_ref) in ref.items():
-        eo, es = rel_err(o[b, :, h], o_ref), rel_err(st[b, h], st_ref)
-        print("%s b=%d h=%d err_o=%.3g err_S=%.3g" % (w.name, b, h, eo, es))
-        assert eo <= w.tol and es <= w.tol, (b, h, eo, es)
     assert np.isfinite(o).all() and np.isfinite(st).all()
-    return inp, o, st
+    o_ref, st_ref = oracle.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"],
+                                     inp.get("S0"))
+    worst = (0.0, 0.0, None)
+    for b in range(w.B):
+        for h in range(w.H):
+            eo, es = rel_err(o[b, :, h], o_ref[b, :, h]), rel_err(st[b, h], st_ref[b, h])
+            if max(eo, es) > max(worst[0], worst[1]):
+                worst = (eo, es, (b, h))
+            assert eo <= w.tol and es <= w.tol, (b, h, eo, es)
+    print("%s: %d heads, worst head %s err_o=%.3g err_S=%.3g" % (w.name, w.B * w.H, worst[2],
+                                                                 worst[0], worst[1]))
+    return inp
 
 
 def test_workload_gdn_prefill_bf16():
-    w = synth.WORKLOADS[1]
-    _sampled(w, [(0, 0), (1, 7), (3, 15)])
+    _all_heads(synth.WORKLOADS[1])
 
 
 def test_workload_kda_prefill_bf16():
-    w = synth.WORKLOADS[2]
-    _sampled(w, [(0, 0), (1, 31)])
+    _all_heads(synth.WORKLOADS[2])
 
 
 def test_workload_gdn_long_with_start_state():
     w = synth.WORKLOADS[3]
-    inp, o, st = _sampled(w, [(0, 0), (0, 21)])
+    inp = _all_heads(w)
     # The start state only reaches the first ~100 outputs at this decay; check
     # its contribution on its own (linearity in (V, S0)): zero values, S0 only.
     short = {k: (a[:, :256] if k != "S0" else a) for k, a in inp.items()}
     short["v"] = np.zeros_like(short["v"])
     o_s, _ = gpu_chunk(short, w.io, chunk=w.chunk)
     o_s = host(o_s)
-    ref = oracle_pairs(short, [(0, 0), (0, 9), (0, 31)])
+    ref = oracle_pairs(short, [(0, h) for h in range(w.H)])
     for (b, h), (o_ref, _) in ref.items():
         e = rel_err(o_s[b, :, h], o_ref)
-        print("S0 response b=%d h=%d err=%.3g (max %.3g)" % (b, h, e, np.abs(o_ref).max()))
-        assert e <= w.tol
+        assert e <= w.tol, (b, h, e)
+    print("S0 response: %d heads within %g" % (len(ref), w.tol))
 
 
 def test_workload_decode_f32():
