@@ -26,10 +26,12 @@
 // row-wise and the transposing reads are both free of bank conflicts):
 //  - Q, K stage tiles: [64 tokens][DK] bf16, piece p of row r at p ^ swz_qk(r).
 //  - V stage tile:     [64 tokens][16*NW] bf16, piece p at p ^ swz_v(r).
-//  - T, P tiles are stored transposed, Tt[i][r] = T[r][i] (64 x 64 bf16),
-//    piece p of row i at p ^ swz_t(i): the prep waves write accumulator tiles
-//    with one 8-byte store per lane and the compute waves read operand
-//    fragments with ds_read_b64_tr_b16.
+//  - T tiles (and T's rounding residual where a chunk needs it) are stored
+//    transposed, Tt[i][r] = T[r][i] (64 x 64 bf16), piece p of row i at
+//    p ^ swz_t(i): the prep waves write accumulator tiles with one 8-byte store
+//    per lane and the compute waves read operand fragments with
+//    ds_read_b64_tr_b16.  P tiles are stored in the compute waves' operand
+//    order, lane by lane (see frag_store).
 //  - The d_k axis of the register-resident state is permuted: accumulator
 //    position p = 32s + 16h + 4g + e holds channel 32s + 8g + 4h + e, so a
 //    state tile pair is the B operand whose k-slots are 8 consecutive
@@ -73,7 +75,6 @@ __device__ __forceinline__ int swz_v(int r) {
     if constexpr (VT == 32) return ((r >> 2) & 1) << 1;                // 4 pieces per row
     else return 0;                                                     // 2 pieces per row
 }
-__device__ __forceinline__ int swz_t(int i) { return (((i >> 1) & 3) << 1) | ((i >> 3) & 1); }
 
 // The T solve's fp32 scratch (four 16x16 tiles): rows of 20 floats, tiles of
 // 336, so that its float4 row accesses, its column reads and the substitution's
@@ -85,12 +86,18 @@ struct FLayout {
     static constexpr int VT = 16 * NW;
     static constexpr int QB = FC * DK * 2;
     static constexpr int VB = FC * VT * 2;
-    static constexpr int S_Q = 0, S_K = QB, S_V = 2 * QB;
+    // K and V stages, a 3-deep ring (chunk n in slot n % 3).
+    static constexpr int S_K = 0, S_V = QB;
     static constexpr int STAGE = S_V + VB;
     static constexpr int NSTAGE = 3;
-    static constexpr int T_T = 0, T_P = FC * FC * 2;
-    static constexpr int TPB = 2 * FC * FC * 2;
-    static constexpr int TP0 = NSTAGE * STAGE;
+    // Q tiles, a 2-deep ring (chunk n in slot n % 2): a chunk's Q is read in
+    // the window before its state chain (prep P and the output's Q S^T part).
+    static constexpr int QR0 = NSTAGE * STAGE;
+    // T (with its bf16 residual T_lo where needed) and P tiles, a 2-deep ring (chunk n in slot n % 2).
+    static constexpr int T_T = 0, T_L = FC * FC * 2, T_P = 2 * FC * FC * 2;
+    static constexpr int T_FLAG = 3 * FC * FC * 2;   // int: this chunk applies T as a bf16 pair
+    static constexpr int TPB = 3 * FC * FC * 2 + 16;
+    static constexpr int TP0 = QR0 + 2 * QB;
     static constexpr int XA = TP0 + 2 * TPB;              // solve wave's scratch: diagonal blocks of A
                                                           // (transposed), then blockdiag of their 8x8
                                                           // inverses; fp32, rows of XROW, tiles of XTILE
@@ -116,10 +123,10 @@ struct FLayout {
     static constexpr int FLAG = AO + 6 * 64 * 8;
     // - solve and recurrence waves: a 2-deep ring (chunk c in slot c % 2) of
     //   the inverted diagonal blocks X_bb (fp16, A-operand layout, 64 lanes x 4
-    //   per block) and the inverse key norms n_k (prologue), then the solve
-    //   wave's own g (log2 units) and beta rows.
+    //   per block), the inverse key norms n_k (prologue) and the diagonal
+    //   blocks' pair flag, then the solve wave's own g (log2 units) and beta rows.
     static constexpr int XH = GT0 + 3 * GSLOT;
-    static constexpr int XHB = FNB * 64 * 8 + FC * 4;
+    static constexpr int XHB = FNB * 64 * 8 + FC * 4 + 16;
     static constexpr int TG = XH + 2 * XHB;
     static constexpr int WARM = FLAG + 16;   // L2-warming target of the loaders (never read)
     template <bool SPLIT>
@@ -161,11 +168,48 @@ __device__ __forceinline__ bf16x4 v_frag(const char* tile, int mt, int w, int la
     return lds_tr(tile + r * (VT * 2) + 16 * ((2 * w + (qd >> 1)) ^ swz_v<VT>(r)) + 8 * (qd & 1));
 }
 
-// Accumulator tile (rows 16rb + 4g + e, cols 16cb + lane%16) into transposed storage.
+__device__ __forceinline__ int swz_t(int i) { return (((i >> 1) & 3) << 1) | ((i >> 3) & 1); }
+
+// T tiles: accumulator tile (rows 16rb + 4g + e, cols 16cb + lane%16) into
+// transposed storage, Tt[i][r] = T[r][i] (64 x 64 bf16), piece p of row i at
+// p ^ swz_t(i); the compute waves read operand fragments with
+// ds_read_b64_tr_b16.
 __device__ __forceinline__ void tp_store(char* tile, int rb, int cb, int lane, f32x4 x) {
     const int i = 16 * cb + (lane & 15), g = lane >> 4;
     const bf16x4 y = {(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
     *reinterpret_cast<bf16x4*>(tile + i * 128 + 16 * ((2 * rb + (g >> 1)) ^ swz_t(i)) + 8 * (g & 1)) = y;
+}
+
+// T's rounding residual x - bf16(x), stored the same way into a second tile.
+// Chunks whose keys repeat or nearly repeat (large entries of A) apply T as the
+// bf16 pair (D = T R + T_lo R): T's rows then hold entries of size ~1 whose
+// sums are small, and one bf16 rounding of T alone would lose those sums.
+__device__ __forceinline__ void tp_store_lo(char* lo, int rb, int cb, int lane, f32x4 x) {
+    f32x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = x[e] - (float)(__bf16)x[e];
+    tp_store(lo, rb, cb, lane, r);
+}
+// A chunk takes the pair when some strictly lower entry of A exceeds this in
+// size.  Unit keys in general position stay well below it
+// (|k_r . k_i| is about 1/sqrt(d_k)); it catches keys that repeat or nearly
+// repeat over a stretch of the chunk at beta near 1 and weak decay.
+constexpr float kPairThresh = 0.5f;
+
+// P tiles are kept in the compute waves' operand order, lane by lane: fragment
+// (rb, s) of the 64 x 64 tile is 64 lanes x 16 bytes, and lane (r, g) holds
+// row 16rb + r, columns 32s + 4g + (0..3) and 32s + 16 + 4g + (0..3) (the
+// token k-slots of the output product), so a compute wave reads an operand
+// with one 16-byte load of its own.  The P wave computes transposed 16 x 16
+// blocks: in a transposed accumulator block (block row rb, block column cb)
+// lane (col, g4) holds P[16rb + col][16cb + 4g4 + e], e < 4, which is exactly
+// half of what the same lane reads back.
+__device__ __forceinline__ void frag_store(char* tile, int rb, int cb, int lane, f32x4 x) {
+    const bf16x4 y = {(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
+    *reinterpret_cast<bf16x4*>(tile + ((rb * (FC / 32) + (cb >> 1)) * 64 + lane) * 16 + 8 * (cb & 1)) = y;
+}
+__device__ __forceinline__ bf16x8 frag_load(const char* tile, int rb, int s, int lane) {
+    return lds_b128(tile + ((rb * (FC / 32) + s) * 64 + lane) * 16);
 }
 
 // Per-lane LDS byte offsets of the compute waves' fragment reads, computed once:
@@ -175,7 +219,7 @@ template <int DK, int VT>
 struct FragOffsets {
     int qk[DK / 32];   // row-wise Q / K fragment, channel step s (row block 0)
     int kt[DK / 32];   // K^T fragment, state tile pair mc/2 (token step 0, tile mc even)
-    int tp[FNB];       // T / P fragment, row block mt (token step 0)
+    int tp[FNB];       // T fragment, row block mt (token step 0)
     int v;             // V fragment, tile 0
     __device__ __forceinline__ FragOffsets(int lane, int wave) {
         const int g = lane >> 4, j = (lane >> 2) & 3, qd = lane & 3, c = lane & 15;
@@ -196,7 +240,7 @@ struct FragOffsets {
         const char* p = tile + kt[mc >> 1] + 8 * (mc & 1) + s * 32 * DK * 2;
         return join(lds_tr(p), lds_tr(p + 16 * DK * 2));
     }
-    // Operand of a transposed-stored T or P tile: lane%16 selects r = 16mt + lane%16,
+    // Operand of a transposed-stored T tile: lane%16 selects r = 16mt + lane%16,
     // k-slots = tokens i = 32s + 4g + (0..3) and 32s + 16 + 4g + (0..3).
     __device__ __forceinline__ bf16x8 tpf(const char* tile, int mt, int s) const {
         const char* p = tile + tp[mt] + s * 32 * 128;
@@ -236,8 +280,9 @@ struct LoadOffsets {
 };
 
 template <int DK, int NW, int NL>
-__device__ __forceinline__ void load_chunk(char* stg, const __bf16* q, const __bf16* k, const __bf16* v,
-                                           int64_t row0, int DV, const LoadOffsets<DK, NW, NL>& lo, int lw) {
+__device__ __forceinline__ void load_chunk(char* stg, char* qtile, const __bf16* q, const __bf16* k,
+                                           const __bf16* v, int64_t row0, int DV, const LoadOffsets<DK, NW, NL>& lo,
+                                           int lw) {
     using L = FLayout<DK, NW>;
     using LO = LoadOffsets<DK, NW, NL>;
     const char* qb = reinterpret_cast<const char*>(q + row0 * DK);
@@ -246,7 +291,7 @@ __device__ __forceinline__ void load_chunk(char* stg, const __bf16* q, const __b
 #pragma unroll
     for (int j = 0; j < LO::NIQ; ++j) {
         const int ins = NL * j + lw;
-        __builtin_amdgcn_global_load_lds(qb + (uint32_t)lo.qk[j], (GDR_LDS void*)(stg + L::S_Q + 1024 * ins), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(qb + (uint32_t)lo.qk[j], (GDR_LDS void*)(qtile + 1024 * ins), 16, 0, 0);
         __builtin_amdgcn_global_load_lds(kb + (uint32_t)lo.qk[j], (GDR_LDS void*)(stg + L::S_K + 1024 * ins), 16, 0, 0);
     }
 #pragma unroll
@@ -372,6 +417,29 @@ __device__ __forceinline__ InvNorms inv_norms(const f32x4& G, int lane) {
     return n;
 }
 
+// Whether a chunk applies T as a bf16 pair: some entry of the off-diagonal
+// 16 x 16 blocks of A (scaled, fp32) exceeds kPairThresh in size (the diagonal
+// blocks are tested where they are formed, below).  Wave-uniform.
+template <int N>
+__device__ __forceinline__ bool pair_needed(const f32x4 (&a)[N]) {
+    float m = 0.f;
+#pragma unroll
+    for (int t = 0; t < N; ++t) m = fmaxf(m, fmaxf(fmaxf(fabsf(a[t][0]), fabsf(a[t][1])), fmaxf(fabsf(a[t][2]), fabsf(a[t][3]))));
+    return __builtin_amdgcn_ballot_w64(m > kPairThresh) != 0;
+}
+
+// The same test on the diagonal blocks: strictly lower entries of A_bb in B
+// layout (lane (col, g4) holds A_bb[4g4 + e][col]).
+__device__ __forceinline__ bool pair_needed_diag(const f32x4 (&Ab)[FNB], int lane) {
+    const int col = lane & 15, g4 = lane >> 4;
+    float m = 0.f;
+#pragma unroll
+    for (int b = 0; b < FNB; ++b)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) m = fmaxf(m, col < 4 * g4 + e ? fabsf(Ab[b][e]) : 0.f);
+    return __builtin_amdgcn_ballot_w64(m > kPairThresh) != 0;
+}
+
 // Prep T: T = (I + A)^-1 Diag(beta) for one chunk, in one wave.
 //  - The diagonal Gram tiles K_b K_b^T on the matrix cores; the off-diagonal
 //    blocks of A come from the P wave (A-operand layout) through LDS.
@@ -429,6 +497,7 @@ __device__ __forceinline__ void prep_t(char* smem, const char* st, const float* 
         *reinterpret_cast<float4*>(xa + b * XTILE + col * XROW + 4 * g4) =
             make_float4(Ab[b][0], Ab[b][1], Ab[b][2], Ab[b][3]);
     }
+    const bool pair_diag = pair_needed_diag(Ab, lane);
     // 8x8 forward substitution: lane (blk, h, j) builds column j of (I + A_hh)^-1.
     {
         const int blk = lane >> 4, h = (lane >> 3) & 1, j = lane & 7;
@@ -510,12 +579,16 @@ __device__ __forceinline__ void prep_t(char* smem, const char* st, const float* 
     // column block j < i at once (the T_mj it needs, m < i, are done), so
     // independent chains interleave.
     char* Tt = tp + L::T_T;
+    char* Tl = tp + L::T_L;
+    const bool pair = pair_diag ||
+                      __builtin_amdgcn_readfirstlane(*reinterpret_cast<const int*>(tp + L::T_FLAG)) != 0;
+    if (pair_diag && lane == 0) *reinterpret_cast<int*>(tp + L::T_FLAG) = 1;
     f16x4 xm[FNB][FNB];   // B layout of T_mj, fp16
+    f32x4 tb[FNB * (FNB + 1) / 2];   // the blocks of T, stored after the recurrence
 #pragma unroll
     for (int j = 0; j < FNB; ++j) {
-        const f32x4 t = Xb[j] * tab[L::G_BE * FC + 16 * j + col];
-        tp_store(Tt, j, j, lane, t);
-        xm[j][j] = to_f16(t);
+        tb[j * (j + 1) / 2 + j] = Xb[j] * tab[L::G_BE * FC + 16 * j + col];
+        xm[j][j] = to_f16(tb[j * (j + 1) / 2 + j]);
     }
 #pragma unroll
     for (int i = 1; i < FNB; ++i) {
@@ -528,10 +601,19 @@ __device__ __forceinline__ void prep_t(char* smem, const char* st, const float* 
             for (int j = 0; j <= m; ++j) y[j] = mma16(Ao[i][m], xm[m][j], y[j]);
 #pragma unroll
         for (int j = 0; j < i; ++j) {
-            const f32x4 z = -mma16(Xa[i], to_f16(y[j]), zero4());
-            xm[i][j] = to_f16(z);
-            tp_store(Tt, i, j, lane, z);
+            tb[i * (i + 1) / 2 + j] = -mma16(Xa[i], to_f16(y[j]), zero4());
+            xm[i][j] = to_f16(tb[i * (i + 1) / 2 + j]);
         }
+    }
+#pragma unroll
+    for (int i = 0; i < FNB; ++i)
+#pragma unroll
+        for (int j = 0; j <= i; ++j) tp_store(Tt, i, j, lane, tb[i * (i + 1) / 2 + j]);
+    if (pair) {
+#pragma unroll
+        for (int i = 0; i < FNB; ++i)
+#pragma unroll
+            for (int j = 0; j <= i; ++j) tp_store_lo(Tl, i, j, lane, tb[i * (i + 1) / 2 + j]);
     }
 }
 
@@ -636,6 +718,7 @@ __device__ __forceinline__ void solve_diag(char* smem, const bf16x8 (&kf)[FNB][D
             make_float4(Ab[b][0], Ab[b][1], Ab[b][2], Ab[b][3]);
     }
     wave_lds_sync();
+    const bool pair_diag = pair_needed_diag(Ab, lane);
     // 8x8 forward substitution: lane (blk, h, j) builds column j of (I + A_hh)^-1.
     {
         const int blk = lane >> 4, h = (lane >> 3) & 1, j = lane & 7;
@@ -702,6 +785,7 @@ __device__ __forceinline__ void solve_diag(char* smem, const bf16x8 (&kf)[FNB][D
 #pragma unroll
     for (int b = 0; b < FNB; ++b) xo[b * 64 + lane] = Xa[b];
     if constexpr (NORM) reinterpret_cast<float*>(xh + FNB * 64 * 8)[lane] = nkl;
+    if (lane == 0) *reinterpret_cast<int*>(xh + FNB * 64 * 8 + FC * 4) = pair_diag ? 1 : 0;
 }
 
 // Recurrence: the off-diagonal blocks of A (K_cb K_rb^T, scaled) in A-operand
@@ -758,6 +842,7 @@ __device__ __forceinline__ void recur_off(const char* st, const float* tab, cons
                 const float4 nc = *reinterpret_cast<const float4*>(nkv + 16 * cb + 4 * g4);
                 acc[0] *= nr * nc.x; acc[1] *= nr * nc.y; acc[2] *= nr * nc.z; acc[3] *= nr * nc.w;
             }
+            go[rb * (rb - 1) / 2 + cb] = acc;
             Ao[rb][cb] = to_f16(acc);
         }
     }
@@ -773,12 +858,16 @@ __device__ __forceinline__ void recur_off(const char* st, const float* tab, cons
     // column block j < i at once (the T_mj it needs, m < i, are done), so
     // independent chains interleave.
     char* Tt = tp + L::T_T;
+    char* Tl = tp + L::T_L;
+    const bool pair = pair_needed(go) ||
+                      __builtin_amdgcn_readfirstlane(*reinterpret_cast<const int*>(xh + FNB * 64 * 8 + FC * 4)) != 0;
+    if (lane == 0) *reinterpret_cast<int*>(tp + L::T_FLAG) = pair ? 1 : 0;
     f16x4 xm[FNB][FNB];   // B layout of T_mj, fp16
+    f32x4 tb[FNB * (FNB + 1) / 2];   // the blocks of T, stored after the recurrence
 #pragma unroll
     for (int j = 0; j < FNB; ++j) {
-        const f32x4 t = Xb[j] * tab[L::G_BE * FC + 16 * j + col];
-        tp_store(Tt, j, j, lane, t);
-        xm[j][j] = to_f16(t);
+        tb[j * (j + 1) / 2 + j] = Xb[j] * tab[L::G_BE * FC + 16 * j + col];
+        xm[j][j] = to_f16(tb[j * (j + 1) / 2 + j]);
     }
 #pragma unroll
     for (int i = 1; i < FNB; ++i) {
@@ -791,10 +880,19 @@ __device__ __forceinline__ void recur_off(const char* st, const float* tab, cons
             for (int j = 0; j <= m; ++j) y[j] = mma16(Ao[i][m], xm[m][j], y[j]);
 #pragma unroll
         for (int j = 0; j < i; ++j) {
-            const f32x4 z = -mma16(Xa[i], to_f16(y[j]), zero4());
-            xm[i][j] = to_f16(z);
-            tp_store(Tt, i, j, lane, z);
+            tb[i * (i + 1) / 2 + j] = -mma16(Xa[i], to_f16(y[j]), zero4());
+            xm[i][j] = to_f16(tb[i * (i + 1) / 2 + j]);
         }
+    }
+#pragma unroll
+    for (int i = 0; i < FNB; ++i)
+#pragma unroll
+        for (int j = 0; j <= i; ++j) tp_store(Tt, i, j, lane, tb[i * (i + 1) / 2 + j]);
+    if (pair) {
+#pragma unroll
+        for (int i = 0; i < FNB; ++i)
+#pragma unroll
+            for (int j = 0; j <= i; ++j) tp_store_lo(Tl, i, j, lane, tb[i * (i + 1) / 2 + j]);
     }
 }
 
@@ -802,7 +900,8 @@ __device__ __forceinline__ void recur_off(const char* st, const float* tab, cons
 // P = (Q K^T) masked and decayed, stored transposed (and, with the prologue,
 // the compute waves' per-token norm factors).
 template <int DK, int NW, bool NORM, bool SPLIT>
-__device__ __forceinline__ void prep_p(char* smem, const char* st, float* tab, char* tp, int n, int lane) {
+__device__ __forceinline__ void prep_p(char* smem, const char* st, const char* qt, float* tab, char* tp, int n,
+                                       int lane) {
     using L = FLayout<DK, NW>;
     constexpr int NKC = DK / 32;
     const int col = lane & 15, g4 = lane >> 4;
@@ -813,7 +912,7 @@ __device__ __forceinline__ void prep_p(char* smem, const char* st, float* tab, c
 #pragma unroll
         for (int s = 0; s < NKC; ++s) {
             kf[rb][s] = qk_frag<DK>(st + L::S_K, rb, s, lane);
-            qf[rb][s] = qk_frag<DK>(st + L::S_Q, rb, s, lane);
+            qf[rb][s] = qk_frag<DK>(qt, rb, s, lane);
         }
     InvNorms nk[FNB], nq[FNB];   // prologue: inverse row norms of k and q
     if constexpr (NORM) {
@@ -877,9 +976,13 @@ __device__ __forceinline__ void prep_p(char* smem, const char* st, float* tab, c
 #pragma unroll
                     for (int e = 0; e < 4; ++e) acc[e] *= nk[rb].c * nk[cb].r[e];
                 }
+                go[rb * (rb - 1) / 2 + cb] = acc;
                 ao[(rb * (rb - 1) / 2 + cb) * 64 + lane] = to_f16(acc);
             }
         }
+        // whether this chunk applies T as a bf16 pair (read by the T wave and the
+        // compute waves; published with the blocks below)
+        if (lane == 0) *reinterpret_cast<int*>(tp + L::T_FLAG) = pair_needed(go) ? 1 : 0;
         __hip_atomic_store(reinterpret_cast<int*>(smem + L::FLAG), n + 1, __ATOMIC_RELEASE,
                            __HIP_MEMORY_SCOPE_WORKGROUP);
     }
@@ -893,33 +996,36 @@ __device__ __forceinline__ void prep_p(char* smem, const char* st, float* tab, c
 #pragma unroll
         for (int rb = 0; rb < FNB; ++rb)
 #pragma unroll
-            for (int cb = 0; cb <= rb; ++cb, ++t) pa[t] = Mma<__bf16>::mma(qf[rb][s], kf[cb][s], pa[t]);
+            for (int cb = 0; cb <= rb; ++cb, ++t) pa[t] = Mma<__bf16>::mma(kf[cb][s], qf[rb][s], pa[t]);
     }
-    // rows 16rb + 4g4 + e, columns 16cb + col
+    // Transposed blocks: lane (col, g4) holds P[r][i], r = 16rb + col, i = 16cb + 4g4 + e.
     char* Pt = tp + L::T_P;
 #pragma unroll
     for (int rb = 0; rb < FNB; ++rb) {
-        const float4 gr = *reinterpret_cast<const float4*>(tab + L::G_G2 * FC + 16 * rb + 4 * g4);
-        const float4 er = *reinterpret_cast<const float4*>(tab + L::G_EB * FC + 16 * rb + 4 * g4);
-        const float grv[4] = {gr.x, gr.y, gr.z, gr.w}, erv[4] = {er.x, er.y, er.z, er.w};
+        const float gr = tab[L::G_G2 * FC + 16 * rb + col];
+        const float er = tab[L::G_EB * FC + 16 * rb + col];
 #pragma unroll
         for (int cb = 0; cb <= rb; ++cb) {
             f32x4 acc = pa[rb * (rb + 1) / 2 + cb];
             if (cb == rb) {
-                const float gc = tab[L::G_G2 * FC + 16 * cb + col];
+                const float4 gi = *reinterpret_cast<const float4*>(tab + L::G_G2 * FC + 16 * cb + 4 * g4);
+                const float giv[4] = {gi.x, gi.y, gi.z, gi.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    acc[e] = col <= 4 * g4 + e ? acc[e] * __builtin_amdgcn_exp2f(grv[e] - gc) : 0.f;
+                    acc[e] = 4 * g4 + e <= col ? acc[e] * __builtin_amdgcn_exp2f(gr - giv[e]) : 0.f;
             } else {
-                const float f = cross_decay<DK, NW>(tab, cb, rb) * tab[L::G_FB * FC + 16 * cb + col];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc[e] *= erv[e] * f;
+                const float f = cross_decay<DK, NW>(tab, cb, rb) * er;
+                const float4 fb = *reinterpret_cast<const float4*>(tab + L::G_FB * FC + 16 * cb + 4 * g4);
+                acc[0] *= f * fb.x;
+                acc[1] *= f * fb.y;
+                acc[2] *= f * fb.z;
+                acc[3] *= f * fb.w;
             }
             if constexpr (NORM) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[e] *= nq[rb].r[e] * nk[cb].c;
+                for (int e = 0; e < 4; ++e) acc[e] *= nq[rb].c * nk[cb].r[e];
             }
-            tp_store(Pt, rb, cb, lane, acc);
+            frag_store(Pt, rb, cb, lane, acc);
         }
     }
 }
@@ -953,6 +1059,7 @@ __global__ __launch_bounds__(64 * (NW + 2 + NL + (NORM ? 1 : 0))) void fused_chu
     const int64_t b = bh / H, h = bh % H;
 #define GDR_STAGE(n) (smem + ((n) % 3) * L::STAGE)
 #define GDR_TPBUF(n) (smem + L::TP0 + ((n) & 1) * L::TPB)
+#define GDR_QTILE(n) (smem + L::QR0 + ((n) & 1) * L::QB)
 #define GDR_GTAB(n) (reinterpret_cast<float*>(smem + L::GT0 + ((n) % 3) * L::GSLOT))
 #define GDR_LEN(n) ((int)((T - (int64_t)(n) * FC) < FC ? (T - (int64_t)(n) * FC) : FC))
 #define GDR_ROW0(n) ((b * T + (int64_t)(n) * FC) * H + h)
@@ -977,17 +1084,36 @@ __global__ __launch_bounds__(64 * (NW + 2 + NL + (NORM ? 1 : 0))) void fused_chu
         // window, the previous window's output stores included.
 #pragma unroll
         for (int mc = 0; mc < CT; ++mc) asm volatile("" ::"v"(S[mc]));
+        // The state as a bf16 B operand, converted once per window (at its end):
+        // it serves the next chunk's K S^T and Q S^T.
+        M::frag sb[NKC];
+#pragma unroll
+        for (int s = 0; s < NKC; ++s) sb[s] = bfrag_acc<__bf16>(S, s);
         // K fragments (first half of the channel steps) of the chunk computed
         // next, read one window ahead (its stage is complete then and stays
         // untouched until after it is used).
         constexpr int NKP = NKC / 2;
         M::frag kn[FNB][NKP];
+        // S Q^T of the chunk computed next (O^T tiles, rows = value columns),
+        // made in the window before, where its Q tile is read anyway.
+        f32x4 Oa[FNB];
         for (int w = -2; w < NT; ++w) {
             if (w == -1) {
 #pragma unroll
                 for (int mt = 0; mt < FNB; ++mt)
 #pragma unroll
                     for (int s = 0; s < NKP; ++s) kn[mt][s] = fo.qkf(GDR_STAGE(0) + L::S_K, mt, s);
+                M::frag qf[FNB][NKC];
+#pragma unroll
+                for (int mt = 0; mt < FNB; ++mt)
+#pragma unroll
+                    for (int s = 0; s < NKC; ++s) qf[mt][s] = fo.qkf(GDR_QTILE(0), mt, s);
+#pragma unroll
+                for (int mt = 0; mt < FNB; ++mt) Oa[mt] = zero4();
+#pragma unroll
+                for (int s = 0; s < NKC; ++s)
+#pragma unroll
+                    for (int mt = 0; mt < FNB; ++mt) Oa[mt] = M::mma(sb[s], qf[mt][s], Oa[mt]);
             }
             if (w >= 0) {
                 const int n = w;
@@ -999,17 +1125,12 @@ __global__ __launch_bounds__(64 * (NW + 2 + NL + (NORM ? 1 : 0))) void fused_chu
                 // The window's work in phases; each phase first issues the LDS
                 // reads of a later phase, so their latency is covered by MFMAs
                 // (sched_barrier keeps the compiler from sinking reads to uses).
-                // Phase 0: the other K fragments, T fragments, V, decay factors.
+                // Phase 0: the other K fragments, V, decay factors.
                 M::frag kr[FNB][NKC - NKP];
 #pragma unroll
                 for (int mt = 0; mt < FNB; ++mt)
 #pragma unroll
                     for (int s = NKP; s < NKC; ++s) kr[mt][s - NKP] = fo.qkf(st + L::S_K, mt, s);
-                M::frag tf[FNB][NKT];
-#pragma unroll
-                for (int mt = 0; mt < FNB; ++mt)
-#pragma unroll
-                    for (int s = 0; s < NKT; ++s) tf[mt][s] = fo.tpf(tp + L::T_T, mt, s);
                 bf16x4 vv[FNB];
                 float4 gm[FNB];
 #pragma unroll
@@ -1018,9 +1139,6 @@ __global__ __launch_bounds__(64 * (NW + 2 + NL + (NORM ? 1 : 0))) void fused_chu
                     gm[mt] = *reinterpret_cast<const float4*>(tab + (NORM ? L::G_GMK : L::G_GM) * FC + 16 * mt + 4 * g4);
                 }
                 // Phase 1: R = K S^T (rows = tokens) from the prefetched K fragments.
-                M::frag sb[NKC];
-#pragma unroll
-                for (int s = 0; s < NKC; ++s) sb[s] = bfrag_acc<__bf16>(S, s);
                 f32x4 R[FNB];
 #pragma unroll
                 for (int mt = 0; mt < FNB; ++mt) R[mt] = zero4();
@@ -1030,14 +1148,14 @@ __global__ __launch_bounds__(64 * (NW + 2 + NL + (NORM ? 1 : 0))) void fused_chu
                     for (int mt = 0; mt < FNB; ++mt)
                         R[mt] = M::mma(s < NKP ? kn[mt][s] : kr[mt][s - NKP], sb[s], R[mt]);
                 __builtin_amdgcn_sched_barrier(0);
-                // K^T fragments for the state update.
-                M::frag kh[CT][NKT];
+                // T, read while R is finished on the VALU.
+                M::frag tf[FNB][NKT];
 #pragma unroll
-                for (int mc = 0; mc < CT; ++mc)
+                for (int mt = 0; mt < FNB; ++mt)
 #pragma unroll
-                    for (int s = 0; s < NKT; ++s) kh[mc][s] = fo.ktf(st + L::S_K, mc, s);
+                    for (int s = 0; s < NKT; ++s) tf[mt][s] = fo.tpf(tp + L::T_T, mt, s);
                 __builtin_amdgcn_sched_barrier(0);
-                // Phase 2: R = V - Diag(gamma) R;  D = T R.
+                // Phase 2: R = V - Diag(gamma) R;  D = (T + T_lo) R.
 #pragma unroll
                 for (int mt = 0; mt < FNB; ++mt) {
                     R[mt][0] = (float)vv[mt][0] - gm[mt].x * R[mt][0];
@@ -1056,21 +1174,35 @@ __global__ __launch_bounds__(64 * (NW + 2 + NL + (NORM ? 1 : 0))) void fused_chu
 #pragma unroll
                     for (int mt = 0; mt < FNB; ++mt) D[mt] = M::mma(tf[mt][s], rb[s], D[mt]);
                 __builtin_amdgcn_sched_barrier(0);
-                // P fragments and the remaining decay factors.
-                M::frag pf[FNB][NKT];
-                float4 gh[FNB];
-                float gc[FNB];
+                // T's rounding residual, for chunks that take the pair (read once T's
+                // fragments are consumed).
+                const int pair = __builtin_amdgcn_readfirstlane(*reinterpret_cast<const int*>(tp + L::T_FLAG));
+                if (pair) {
+                    M::frag tl[FNB][NKT];
 #pragma unroll
-                for (int mt = 0; mt < FNB; ++mt) {
+                    for (int mt = 0; mt < FNB; ++mt)
 #pragma unroll
-                    for (int s = 0; s < NKT; ++s) pf[mt][s] = fo.tpf(tp + L::T_P, mt, s);
-                    gh[mt] = *reinterpret_cast<const float4*>(tab + (NORM ? L::G_GHK : L::G_GH) * FC + 16 * mt + 4 * g4);
-                    gc[mt] = tab[(NORM ? L::G_GQ : L::G_GM) * FC + 16 * mt + col];
+                        for (int s = 0; s < NKT; ++s) tl[mt][s] = fo.tpf(tp + L::T_L, mt, s);
+#pragma unroll
+                    for (int s = 0; s < NKT; ++s)
+#pragma unroll
+                        for (int mt = 0; mt < FNB; ++mt) D[mt] = M::mma(tl[mt][s], rb[s], D[mt]);
                 }
+                __builtin_amdgcn_sched_barrier(0);
+                // K^T fragments for the state update, the remaining decay factors.
+                M::frag kh[CT][NKT];
+#pragma unroll
+                for (int mc = 0; mc < CT; ++mc)
+#pragma unroll
+                    for (int s = 0; s < NKT; ++s) kh[mc][s] = fo.ktf(st + L::S_K, mc, s);
+                float4 gh[FNB];
+#pragma unroll
+                for (int mt = 0; mt < FNB; ++mt)
+                    gh[mt] = *reinterpret_cast<const float4*>(tab + (NORM ? L::G_GHK : L::G_GH) * FC + 16 * mt + 4 * g4);
                 const float gl = tab[L::G_GM * FC + FC - 1];
                 __builtin_amdgcn_sched_barrier(0);
                 // Phase 3: S^T <- gamma_last S^T + K^T (Diag(gamma_last / gamma) D).
-                M::frag db[NKT], dsb[NKT];
+                M::frag dsb[NKT];
                 {
                     f32x4 Dsc[FNB];
 #pragma unroll
@@ -1078,10 +1210,7 @@ __global__ __launch_bounds__(64 * (NW + 2 + NL + (NORM ? 1 : 0))) void fused_chu
                         Dsc[mt] = f32x4{D[mt][0] * gh[mt].x, D[mt][1] * gh[mt].y, D[mt][2] * gh[mt].z,
                                         D[mt][3] * gh[mt].w};
 #pragma unroll
-                    for (int s = 0; s < NKT; ++s) {
-                        db[s] = bfrag_acc<__bf16>(D, s);
-                        dsb[s] = bfrag_acc<__bf16>(Dsc, s);
-                    }
+                    for (int s = 0; s < NKT; ++s) dsb[s] = bfrag_acc<__bf16>(Dsc, s);
                 }
 #pragma unroll
                 for (int mc = 0; mc < CT; ++mc) S[mc] *= gl;
@@ -1090,36 +1219,43 @@ __global__ __launch_bounds__(64 * (NW + 2 + NL + (NORM ? 1 : 0))) void fused_chu
 #pragma unroll
                     for (int mc = 0; mc < CT; ++mc) S[mc] = M::mma(kh[mc][s], dsb[s], S[mc]);
                 __builtin_amdgcn_sched_barrier(0);
-                // Q fragments for the output.
-                M::frag qf[FNB][NKC];
+                // Phase 4: O^T = Diag-scaled S Q^T (made one window ahead) + D^T P^T,
+                // with D as a bf16 pair as well.
+                {
+                    M::frag pf[FNB][NKT];
+                    float gc[FNB];
 #pragma unroll
-                for (int mt = 0; mt < FNB; ++mt)
+                    for (int mt = 0; mt < FNB; ++mt) {
 #pragma unroll
-                    for (int s = 0; s < NKC; ++s) qf[mt][s] = fo.qkf(st + L::S_Q, mt, s);
-                __builtin_amdgcn_sched_barrier(0);
-                // Phase 4: O^T = Diag-scaled S Q^T + D^T P^T  (rows = value columns);
-                // the P part first, while the Q fragments arrive.
-                f32x4 Op[FNB], Oa[FNB];
-#pragma unroll
-                for (int mt = 0; mt < FNB; ++mt) { Op[mt] = zero4(); Oa[mt] = zero4(); }
-#pragma unroll
-                for (int s = 0; s < NKT; ++s)
-#pragma unroll
-                    for (int mt = 0; mt < FNB; ++mt) Op[mt] = M::mma(db[s], pf[mt][s], Op[mt]);
-#pragma unroll
-                for (int s = 0; s < NKC; ++s)
-#pragma unroll
-                    for (int mt = 0; mt < FNB; ++mt) Oa[mt] = M::mma(sb[s], qf[mt][s], Oa[mt]);
-#pragma unroll
-                for (int mt = 0; mt < FNB; ++mt) Oa[mt] = Oa[mt] * gc[mt] + Op[mt];
-                __builtin_amdgcn_sched_barrier(0);
-                // Phase 5: K fragments of the next chunk; output stores.
-                if (n + 1 < NT) {
+                        for (int s = 0; s < NKT; ++s) pf[mt][s] = frag_load(tp + L::T_P, mt, s, lane);
+                        gc[mt] = tab[(NORM ? L::G_GQ : L::G_GM) * FC + 16 * mt + col];
+                    }
+                    f32x4 Dl[FNB];
 #pragma unroll
                     for (int mt = 0; mt < FNB; ++mt)
 #pragma unroll
-                        for (int s = 0; s < NKP; ++s)
-                            kn[mt][s] = fo.qkf(GDR_STAGE(n + 1) + L::S_K, mt, s);
+                        for (int e = 0; e < 4; ++e) Dl[mt][e] = D[mt][e] - (float)(__bf16)D[mt][e];
+                    M::frag db[NKT], dl[NKT];
+#pragma unroll
+                    for (int s = 0; s < NKT; ++s) {
+                        db[s] = bfrag_acc<__bf16>(D, s);
+                        dl[s] = bfrag_acc<__bf16>(Dl, s);
+                    }
+                    f32x4 Op[FNB];
+#pragma unroll
+                    for (int mt = 0; mt < FNB; ++mt) Op[mt] = zero4();
+#pragma unroll
+                    for (int s = 0; s < NKT; ++s)
+#pragma unroll
+                        for (int mt = 0; mt < FNB; ++mt) Op[mt] = M::mma(db[s], pf[mt][s], Op[mt]);
+                    if (pair) {
+#pragma unroll
+                        for (int s = 0; s < NKT; ++s)
+#pragma unroll
+                            for (int mt = 0; mt < FNB; ++mt) Op[mt] = M::mma(dl[s], pf[mt][s], Op[mt]);
+                    }
+#pragma unroll
+                    for (int mt = 0; mt < FNB; ++mt) Oa[mt] = Oa[mt] * gc[mt] + Op[mt];
                 }
                 // Output rows: lane (col, g4) of tile mt holds o[16mt + col][vcol0 + 4g4 + e]
                 // (wave-uniform row base, per-lane 32-bit offset).
@@ -1138,6 +1274,34 @@ __global__ __launch_bounds__(64 * (NW + 2 + NL + (NORM ? 1 : 0))) void fused_chu
                         if (16 * mt + col < len) *reinterpret_cast<bf16x4*>(ob + mt * tstride + olane) = y;
                     }
                 }
+                __builtin_amdgcn_sched_barrier(0);
+                // Phase 5: the next chunk's B operand of the state, its S Q^T and K fragments.
+#pragma unroll
+                for (int s = 0; s < NKC; ++s) sb[s] = bfrag_acc<__bf16>(S, s);
+                if (n + 1 < NT) {
+                    // (two row tiles at a time, to bound the live Q fragments)
+#pragma unroll
+                    for (int half = 0; half < 2; ++half) {
+                        M::frag qf[2][NKC];
+#pragma unroll
+                        for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+                            for (int s = 0; s < NKC; ++s) qf[m2][s] = fo.qkf(GDR_QTILE(n + 1), 2 * half + m2, s);
+#pragma unroll
+                        for (int m2 = 0; m2 < 2; ++m2) Oa[2 * half + m2] = zero4();
+#pragma unroll
+                        for (int s = 0; s < NKC; ++s)
+#pragma unroll
+                            for (int m2 = 0; m2 < 2; ++m2)
+                                Oa[2 * half + m2] = M::mma(sb[s], qf[m2][s], Oa[2 * half + m2]);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+#pragma unroll
+                    for (int mt = 0; mt < FNB; ++mt)
+#pragma unroll
+                        for (int s = 0; s < NKP; ++s)
+                            kn[mt][s] = fo.qkf(GDR_STAGE(n + 1) + L::S_K, mt, s);
+                }
             }
             __syncthreads();
         }
@@ -1154,7 +1318,7 @@ __global__ __launch_bounds__(64 * (NW + 2 + NL + (NORM ? 1 : 0))) void fused_chu
             // ---------------- prep P ----------------
             for (int w = -2; w < NT; ++w) {
                 const int n = w + 1;
-                if (n >= 0 && n < NT) prep_p<DK, NW, NORM, SPLIT>(smem, GDR_STAGE(n), GDR_GTAB(n), GDR_TPBUF(n), n, lane);
+                if (n >= 0 && n < NT) prep_p<DK, NW, NORM, SPLIT>(smem, GDR_STAGE(n), GDR_QTILE(n), GDR_GTAB(n), GDR_TPBUF(n), n, lane);
                 __syncthreads();
             }
         } else {
@@ -1166,7 +1330,8 @@ __global__ __launch_bounds__(64 * (NW + 2 + NL + (NORM ? 1 : 0))) void fused_chu
 #pragma unroll
                     for (int cb = rb + 1; cb < FNB; ++cb) {
                         tp_store(GDR_TPBUF(bf) + L::T_T, rb, cb, lane, zero4());
-                        tp_store(GDR_TPBUF(bf) + L::T_P, rb, cb, lane, zero4());
+                        tp_store(GDR_TPBUF(bf) + L::T_L, rb, cb, lane, zero4());
+                        frag_store(GDR_TPBUF(bf) + L::T_P, rb, cb, lane, zero4());
                     }
             for (int w = -2; w < NT; ++w) {
                 const int n = w + 1;
@@ -1220,7 +1385,7 @@ __global__ __launch_bounds__(64 * (NW + 2 + NL + (NORM ? 1 : 0))) void fused_chu
             if (lane == 0) *reinterpret_cast<int*>(smem + L::FLAG) = 0;
             for (int w = -2; w < NT; ++w) {
                 const int n = w + 1;
-                if (n >= 0 && n < NT) prep_p<DK, NW, NORM, SPLIT>(smem, GDR_STAGE(n), GDR_GTAB(n), GDR_TPBUF(n), n, lane);
+                if (n >= 0 && n < NT) prep_p<DK, NW, NORM, SPLIT>(smem, GDR_STAGE(n), GDR_QTILE(n), GDR_GTAB(n), GDR_TPBUF(n), n, lane);
                 __syncthreads();
             }
         }
@@ -1234,7 +1399,8 @@ __global__ __launch_bounds__(64 * (NW + 2 + NL + (NORM ? 1 : 0))) void fused_chu
     #pragma unroll
                     for (int cb = rb + 1; cb < FNB; ++cb) {
                         tp_store(GDR_TPBUF(bf) + L::T_T, rb, cb, lane, zero4());
-                        tp_store(GDR_TPBUF(bf) + L::T_P, rb, cb, lane, zero4());
+                        tp_store(GDR_TPBUF(bf) + L::T_L, rb, cb, lane, zero4());
+                        frag_store(GDR_TPBUF(bf) + L::T_P, rb, cb, lane, zero4());
                     }
             for (int w = -2; w < NT; ++w) {
                 const int n = w + 1;
@@ -1267,7 +1433,7 @@ __global__ __launch_bounds__(64 * (NW + 2 + NL + (NORM ? 1 : 0))) void fused_chu
             if (n < NT) {
                 const int len = GDR_LEN(n);
                 if (len < FC) lo.set(len, H, DV, vt, lw, lane);   // ragged last chunk
-                load_chunk<DK, NW, NL>(GDR_STAGE(n), q, k, v, GDR_ROW0(n), DV, lo, lw);
+                load_chunk<DK, NW, NL>(GDR_STAGE(n), GDR_QTILE(n), q, k, v, GDR_ROW0(n), DV, lo, lw);
                 if (lw == 0) gate_table<DK, NW>(la, bb, len, lane, GDR_GTAB(n), sigb != 0);
                 if (n + 1 < NT) {
                     const int len1 = GDR_LEN(n + 1);
@@ -1295,6 +1461,7 @@ __global__ __launch_bounds__(64 * (NW + 2 + NL + (NORM ? 1 : 0))) void fused_chu
     }
 #undef GDR_STAGE
 #undef GDR_TPBUF
+#undef GDR_QTILE
 #undef GDR_LEN
 #undef GDR_ROW0
 #undef GDR_GTAB

@@ -107,3 +107,72 @@ def test_wide_gdn2_chunk(gate, d):
     o_ref, st_ref = oracle.gdn2_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], eb, ww,
                                           inp["S0"])
     check_all_heads("gdn2 %s d=%d" % (gate, d), o, st, o_ref, st_ref, TOL["bf16"])
+
+
+# --------------------------------------------------------------------------
+# Adversarial but valid keys: unit keys that repeat, alternate in sign, nearly
+# coincide, lie in a plane or cycle through three directions over the whole
+# sequence, with beta near 1 and no decay (plus keys of norm 2 at beta = 1/4
+# and of norm sqrt(2) at beta = 1/2, the same beta |k|^2 = 1).  For such
+# chunks the rows of T = (I + A)^-1 Diag(beta) hold entries of size ~1 whose
+# sums are small, and the chunkwise products cancel: a bf16 rounding of T, D
+# or P loses digits that the token recurrence keeps.
+#  - fp32 io (fp32 operands and solve): the fp32 bar, 1e-4.
+#  - bf16, scalar gate, chunk 64 (the fused kernel): chunks whose A has an
+#    entry above 1/2 apply T and D as bf16 pairs; the worst case measured is
+#    2.3e-2 (near-collinear keys, beta = 0.9, d = 64; a CPU emulation of the
+#    kernel's roundings gives 1.7e-2, single bf16 roundings 0.13).  Bound 3e-2.
+# --------------------------------------------------------------------------
+EDGE_TOL = 3e-2
+EDGE_BETAS = (1.0, 0.99, 0.9, 0.7)
+EDGE_CASES = ([(kind, 1.0, beta) for kind in synth.EDGE_KEYS for beta in EDGE_BETAS]
+              + [("repeated", 2.0, 0.25), ("plane", 2.0, 0.25), ("antiparallel", 2.0 ** 0.5, 0.5)])
+
+
+def _edge_inputs(kind, norm, beta, d, io, B=2, T=200, H=3, seed=None):
+    return synth.edge_key_inputs(kind, B, T, H, d, io, seed=d if seed is None else seed, key_norm=norm,
+                                 beta=beta, log_alpha=0.0)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("kind,norm,beta", EDGE_CASES)
+def test_edge_keys_fused(kind, norm, beta, d):
+    inp = _edge_inputs(kind, norm, beta, d, "bf16")
+    o, st = gpu_chunk(inp, "bf16", chunk=64)
+    o_ref, st_ref = oracle.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], inp["S0"])
+    check_all_heads("edge %s |k|=%.2f beta=%.2f d=%d C=64" % (kind, norm, beta, d), o, st, o_ref, st_ref,
+                    EDGE_TOL)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("gate", ["scalar", "channel"])
+@pytest.mark.parametrize("kind", synth.EDGE_KEYS)
+def test_edge_keys_fp32(kind, gate, d):
+    inp = _edge_inputs(kind, 1.0, 0.99, d, "f32")
+    if gate == "channel":
+        inp["log_alpha"] = np.ascontiguousarray(np.repeat(inp["log_alpha"][..., None], d, axis=-1))
+    o, st = gpu_chunk(inp, "f32", chunk=64)
+    o_ref, st_ref = oracle.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], inp["S0"])
+    check_all_heads("edge fp32 %s %s d=%d" % (kind, gate, d), o, st, o_ref, st_ref, TOL["f32"])
+
+
+@pytest.mark.parametrize("kind", ["repeated", "antiparallel", "near_collinear"])
+def test_edge_keys_fused_wide(kind):
+    """The same inputs through the two-compute-wave fused kernel."""
+    inp = _edge_inputs(kind, 1.0, 0.99, 128, "bf16", B=B_WIDE, T=T_WIDE, H=H_WIDE, seed=7)
+    o, st = gpu_chunk(inp, "bf16", chunk=64)
+    o_ref, st_ref = oracle.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], inp["S0"])
+    check_all_heads("edge wide %s" % kind, o, st, o_ref, st_ref, EDGE_TOL)
+
+
+def test_edge_keys_short_run_in_one_block():
+    """A run of 8 repeated keys at the end of a ragged sequence: the last chunk's
+    A has no off-diagonal block, the diagonal blocks alone must select the pair."""
+    inp = synth.chunk_inputs(2, 200, 3, 64, 64, "scalar", "bf16", seed=77, s0_std=0.1)
+    rep = _edge_inputs("repeated", 1.0, 1.0, 64, "bf16", T=200, seed=78)
+    inp["k"][:, 192:] = rep["k"][:, 192:]
+    inp["beta"][:, 192:] = 1.0
+    inp["log_alpha"][:, 192:] = 0.0
+    o, st = gpu_chunk(inp, "bf16", chunk=64)
+    o_ref, st_ref = oracle.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], inp["S0"])
+    check_all_heads("edge short run", o, st, o_ref, st_ref, TOL["bf16"])
