@@ -33,7 +33,8 @@
  *    values are not inspected: NaN and Inf propagate.
  *  - Supported shapes: d_k = d_v in {64, 128}; chunk in {16, 32, 64};
  *    B >= 1, H >= 1, T >= 0 (T = 0 copies S0 to S_T).
- *  - The functions keep no state between calls and are reentrant.
+ *  - The functions keep no state between calls and are reentrant
+ *    (gdr_chunk_fwd_noalloc aside: it shares one scratch array per GPU).
  */
 #ifndef GDR_H
 #define GDR_H
@@ -93,6 +94,34 @@ gdr_status gdr_chunk_fwd(const void *q, const void *k, const void *v,
                          int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                          int64_t chunk, gdr_dtype io, gdr_gate gate,
                          void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * gdr_chunk_fwd for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * arguments are gdr_chunk_fwd's without the workspace; the caller still owns
+ * every input and output.  In place of the workspace the call uses a fixed
+ * device array of GDR_NOALLOC_SCRATCH_BYTES that the library holds on each
+ * GPU it runs on, from the first call there until the process ends (its device
+ * address is looked up on that first call, which therefore should not be made
+ * inside a graph capture).  The call itself allocates and frees nothing.
+ *  - A request whose gdr_chunk_fwd_workspace_size exceeds
+ *    GDR_NOALLOC_SCRATCH_BYTES returns GDR_ERR_UNSUPPORTED before any launch.
+ *    Calls that need no workspace (bf16, scalar gate, chunk 64) take any size.
+ *  - Every call on one GPU shares that GPU's array: calls that overlap in time
+ *    on one GPU (different streams, or different threads with no ordering)
+ *    race and give undefined results.  Calls ordered on one stream are safe;
+ *    each call writes every scratch byte it reads before reading it, so nothing
+ *    carries over from the previous call.
+ *  - Errors as in gdr_chunk_fwd, plus GDR_ERR_HIP if the array's address on
+ *    the stream's device cannot be obtained.
+ */
+#define GDR_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+gdr_status gdr_chunk_fwd_noalloc(const void *q, const void *k, const void *v,
+                                 const float *log_alpha, const float *beta, const float *S0,
+                                 void *o, float *S_T,
+                                 int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                                 int64_t chunk, gdr_dtype io, gdr_gate gate, hipStream_t stream);
 
 /*
  * One recurrent decode step (one token per sequence), reading the fixed-size

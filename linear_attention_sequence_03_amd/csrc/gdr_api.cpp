@@ -115,7 +115,7 @@ gdr_status chunk_fwd_impl(const void* q, const void* k, const void* v, const flo
                                  const float* beta, const float* S0, void* o, float* S_T, int64_t B,
                                  int64_t T, int64_t H, int64_t dk, int64_t dv, int64_t chunk,
                                  gdr_dtype io, gdr_gate gate, void* workspace, size_t workspace_bytes,
-                                 hipStream_t stream, unsigned prologue) {
+                                 hipStream_t stream, unsigned prologue, bool noalloc = false) {
     size_t need = 0;
     gdr_status s = gdr_chunk_fwd_workspace_size(B, T, H, dk, dv, chunk, io, gate, &need);
     if (s != GDR_OK) return s;
@@ -130,9 +130,17 @@ gdr_status chunk_fwd_impl(const void* q, const void* k, const void* v, const flo
         return fail(GDR_ERR_UNSUPPORTED, "H too large (chunk*H*d*4 bytes must stay below 2^31)");
     if (T > 0 && (!q || !k || !v || !log_alpha || !beta || !o))
         return fail(GDR_ERR_INVALID_ARG, "q, k, v, log_alpha, beta and o must be non-NULL");
-    if (need > 0 && !workspace) return fail(GDR_ERR_INVALID_ARG, "workspace is NULL");
-    if (workspace_bytes < need)
-        return fail(GDR_ERR_INVALID_ARG, "workspace too small (%zu < %zu bytes)", workspace_bytes, need);
+    if (noalloc) {
+        if (need > GDR_NOALLOC_SCRATCH_BYTES)
+            return fail(GDR_ERR_UNSUPPORTED,
+                        "this call needs %zu bytes of workspace, above the %zu-byte fixed scratch",
+                        need, (size_t)GDR_NOALLOC_SCRATCH_BYTES);
+    } else {
+        if (need > 0 && !workspace) return fail(GDR_ERR_INVALID_ARG, "workspace is NULL");
+        if (workspace_bytes < need)
+            return fail(GDR_ERR_INVALID_ARG, "workspace too small (%zu < %zu bytes)", workspace_bytes,
+                        need);
+    }
     const size_t es = io == GDR_BF16 ? 2 : 4;
     const int64_t la_elems = gate == GDR_GATE_CHANNEL ? ntok * dk : ntok;
     const Range rs[] = {
@@ -148,6 +156,13 @@ gdr_status chunk_fwd_impl(const void* q, const void* k, const void* v, const flo
         return fail(GDR_ERR_UNSUPPORTED,
                     "the gate prologue is fused into the bf16 calls with chunk 64 (scalar gate) or the "
                     "channel gate only");
+    if (noalloc && need > 0) {
+        // the fixed scratch stands in for the workspace; every byte of it the
+        // state pass reads is written by this call's preparation kernel first
+        const hipError_t e = gdr::noalloc_scratch(stream, &workspace);
+        if (e != hipSuccess)
+            return fail(GDR_ERR_HIP, "no device scratch on this stream's device: %s", hipGetErrorString(e));
+    }
     gdr::ChunkArgs a{q, k, v, log_alpha, beta, S0, o, S_T, B, T, H, dk, dv, chunk,
                      io == GDR_BF16, gate == GDR_GATE_CHANNEL, workspace, stream, prologue};
     const hipError_t err = gdr::chunk_fwd_launch(a);
@@ -168,6 +183,14 @@ gdr_status gdr_chunk_fwd(const void* q, const void* k, const void* v, const floa
                          hipStream_t stream) {
     return chunk_fwd_impl(q, k, v, log_alpha, beta, S0, o, S_T, B, T, H, dk, dv, chunk, io, gate,
                           workspace, workspace_bytes, stream, 0);
+}
+
+gdr_status gdr_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const float* log_alpha,
+                                 const float* beta, const float* S0, void* o, float* S_T, int64_t B,
+                                 int64_t T, int64_t H, int64_t dk, int64_t dv, int64_t chunk,
+                                 gdr_dtype io, gdr_gate gate, hipStream_t stream) {
+    return chunk_fwd_impl(q, k, v, log_alpha, beta, S0, o, S_T, B, T, H, dk, dv, chunk, io, gate,
+                          nullptr, 0, stream, 0, true);
 }
 
 gdr_status gdr_chunk_fwd_prologue(const void* q, const void* k, const void* v,

@@ -57,6 +57,9 @@ size_t chunk_block_bytes(int64_t dk, int64_t chunk, bool bf16, bool channel);
 size_t chunk_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t chunk,
                              bool bf16, bool channel);
 hipError_t chunk_fwd_launch(const ChunkArgs& a);
+// Device address of the fixed scratch array (GDR_NOALLOC_SCRATCH_BYTES) on the
+// device of `stream`; looked up on the first call per device, then cached.
+hipError_t noalloc_scratch(hipStream_t stream, void** out);
 // Which chunk calls take the gate prologue (fused into their loads).
 bool prologue_supported(int64_t chunk, bool bf16, bool channel);
 

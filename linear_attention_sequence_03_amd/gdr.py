@@ -19,9 +19,11 @@ GDR_OK, GDR_ERR_INVALID_ARG, GDR_ERR_UNSUPPORTED, GDR_ERR_HIP = 0, 1, 2, 3
 GDR_F32, GDR_BF16 = 0, 1
 GDR_GATE_SCALAR, GDR_GATE_CHANNEL = 0, 1
 GDR_PROLOGUE_L2NORM_QK, GDR_PROLOGUE_BETA_SIGMOID = 1, 2
+GDR_NOALLOC_SCRATCH_BYTES = 64 << 20   # the fixed scratch of gdr_chunk_fwd_noalloc
 
 # Every symbol include/gdr.h declares.
-EXPORTS = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_decode_step", "gdr_decode_multi",
+EXPORTS = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_chunk_fwd_noalloc",
+           "gdr_decode_step", "gdr_decode_multi",
            "gdr_chunk_fwd_prologue", "gdr_decode_step_prologue",
            "gdr_fg2_chunk_fwd_workspace_size", "gdr_fg2_chunk_fwd", "gdr_fg2_decode_step",
            "gdr_gdn2_fwd", "gdr_gdn2_chunk_fwd_workspace_size", "gdr_gdn2_chunk_fwd",
@@ -58,6 +60,9 @@ def load_library(path: Optional[str] = None):
                                   i64, i64, i64, i64, i64, i64, f, f,
                                   vp, ctypes.c_size_t, vp]
     lib.gdr_chunk_fwd.restype = f
+    lib.gdr_chunk_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp,
+                                          i64, i64, i64, i64, i64, i64, f, f, vp]
+    lib.gdr_chunk_fwd_noalloc.restype = f
     lib.gdr_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp,
                                     i64, i64, i64, i64, f, f, vp]
     lib.gdr_decode_step.restype = f
@@ -145,19 +150,12 @@ def gdr_chunk_fwd_workspace_size(B, T, H, dk, dv, chunk, io, gate) -> int:
     return int(out.value)
 
 
-def gdr_chunk_fwd(q, k, v, log_alpha, beta, S0=None, chunk: int = 64, o=None, S_T=None,
-                  workspace=None, want_state: bool = True, stream=None, prologue: int = 0) -> Tuple:
-    """Whole-sequence forward.  q,k: [B,T,H,dk]; v: [B,T,H,dv] (fp32 or bf16);
-    log_alpha: [B,T,H] (scalar gate) or [B,T,H,dk] (channel gate), fp32;
-    beta: [B,T,H] fp32; S0: [B,H,dv,dk] fp32 or None.
-    Returns (o [B,T,H,dv] in the io dtype, S_T [B,H,dv,dk] fp32 or None).
-    ``prologue`` (GDR_PROLOGUE_* flags) normalises q, k and / or maps beta
-    logits through a sigmoid inside the kernels."""
+def _chunk_io(q, k, v, log_alpha, beta, S0, o, S_T, want_state):
+    """Check the prefill tensors; allocate o and S_T when not given."""
     import torch
     dev = q.device
     B, T, H, dk = q.shape
     dv = v.shape[-1]
-    io = _io_code(q.dtype)
     gate = GDR_GATE_CHANNEL if log_alpha.dim() == 4 else GDR_GATE_SCALAR
     _need("q", q, q.dtype, (B, T, H, dk), dev)
     _need("k", k, q.dtype, (B, T, H, dk), dev)
@@ -174,6 +172,20 @@ def gdr_chunk_fwd(q, k, v, log_alpha, beta, S0=None, chunk: int = 64, o=None, S_
         S_T = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
     if S_T is not None:
         _need("S_T", S_T, torch.float32, (B, H, dv, dk), dev)
+    return (B, T, H, dk, dv, _io_code(q.dtype), gate), o, S_T
+
+
+def gdr_chunk_fwd(q, k, v, log_alpha, beta, S0=None, chunk: int = 64, o=None, S_T=None,
+                  workspace=None, want_state: bool = True, stream=None, prologue: int = 0) -> Tuple:
+    """Whole-sequence forward.  q,k: [B,T,H,dk]; v: [B,T,H,dv] (fp32 or bf16);
+    log_alpha: [B,T,H] (scalar gate) or [B,T,H,dk] (channel gate), fp32;
+    beta: [B,T,H] fp32; S0: [B,H,dv,dk] fp32 or None.
+    Returns (o [B,T,H,dv] in the io dtype, S_T [B,H,dv,dk] fp32 or None).
+    ``prologue`` (GDR_PROLOGUE_* flags) normalises q, k and / or maps beta
+    logits through a sigmoid inside the kernels."""
+    import torch
+    (B, T, H, dk, dv, io, gate), o, S_T = _chunk_io(q, k, v, log_alpha, beta, S0, o, S_T, want_state)
+    dev = q.device
     nbytes = gdr_chunk_fwd_workspace_size(B, T, H, dk, dv, chunk, io, gate)
     if workspace is None and nbytes > 0:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
@@ -187,6 +199,21 @@ def gdr_chunk_fwd(q, k, v, log_alpha, beta, S0=None, chunk: int = 64, o=None, S_
         st = load_library().gdr_chunk_fwd(
             _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0), _ptr(o), _ptr(S_T),
             B, T, H, dk, dv, chunk, io, gate, _ptr(workspace), wbytes, _stream(dev, stream))
+    if st != GDR_OK:
+        _raise(st)
+    return o, S_T
+
+
+def gdr_chunk_fwd_noalloc(q, k, v, log_alpha, beta, S0=None, chunk: int = 64, o=None, S_T=None,
+                          want_state: bool = True, stream=None) -> Tuple:
+    """:func:`gdr_chunk_fwd` with the library's fixed device scratch in place of
+    a workspace (at most GDR_NOALLOC_SCRATCH_BYTES of it).  Pass ``o`` (and
+    ``S_T``) to keep this call free of allocations too; calls that overlap on
+    one GPU race on the shared scratch."""
+    (B, T, H, dk, dv, io, gate), o, S_T = _chunk_io(q, k, v, log_alpha, beta, S0, o, S_T, want_state)
+    st = load_library().gdr_chunk_fwd_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0), _ptr(o), _ptr(S_T),
+        B, T, H, dk, dv, chunk, io, gate, _stream(q.device, stream))
     if st != GDR_OK:
         _raise(st)
     return o, S_T

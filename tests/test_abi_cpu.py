@@ -55,6 +55,13 @@ def _chunk(lib, q=0, k=1, v=2, la=3, be=4, s0=None, o=6, st=7, ws=8, B=1, T=128,
                              B, T, H, dk, dv, chunk, io, gate, p(ws), wsbytes, None)
 
 
+def _chunk_noalloc(lib, q=0, k=1, v=2, la=3, be=4, o=6, st=7, B=1, T=128, H=2, dk=64, dv=64,
+                   chunk=64, io=0, gate=0):
+    p = lambda i: None if i is None else (_addr(i) if isinstance(i, int) else i)  # noqa: E731
+    return lib.gdr_chunk_fwd_noalloc(p(q), p(k), p(v), p(la), p(be), None, p(o), p(st),
+                                     B, T, H, dk, dv, chunk, io, gate, None)
+
+
 def _decode(lib, q=0, k=1, v=2, la=3, be=4, si=5, so=6, o=7, B=2, H=2, dk=64, dv=64, io=0,
             gate=0):
     p = lambda i: None if i is None else (_addr(i) if isinstance(i, int) else i)  # noqa: E731
@@ -84,6 +91,26 @@ def lib():
 def test_chunk_fwd_rejects(lib, kw, code):
     assert _chunk(lib, **kw) == code
     assert lib.gdr_last_error()  # a message was left
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(B=0), 1), (dict(chunk=48), 2), (dict(dk=96, dv=96), 2),
+    (dict(o=ctypes.c_void_p(BASE + 4 * 1024)), 1),      # o inside q
+    # workspace beyond the fixed scratch: KDA bf16 d = 128, 1024 chunk blocks of
+    # 66048 bytes (67.6 MB > 64 MiB); refused before the scratch is looked up
+    (dict(B=1, T=4096, H=16, dk=128, dv=128, io=1, gate=1), 2),
+    # fp32 scalar d = 64, chunk 64: 2048 blocks, far past the scratch
+    (dict(B=8, T=16384, H=16), 2),
+])
+def test_chunk_fwd_noalloc_rejects(lib, kw, code):
+    assert _chunk_noalloc(lib, **kw) == code
+    assert lib.gdr_last_error()
+
+
+def test_noalloc_scratch_limit_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define GDR_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == gdr.GDR_NOALLOC_SCRATCH_BYTES
 
 
 @pytest.mark.parametrize("kw,code", [

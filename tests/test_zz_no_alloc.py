@@ -1,0 +1,79 @@
+"""gdr_chunk_fwd_noalloc (the library's fixed device scratch in place of the
+workspace) against gdr_chunk_fwd with a caller-allocated workspace.
+
+Two calls in a row per path, the second smaller than the first, so the second
+runs on scratch that still holds the first call's contents.  Both entry points
+launch the same kernels on the same inputs, so the outputs must agree bit for
+bit; each is also checked against the oracle at the parity bar (2e-2 normwise
+for bf16 io, 1e-4 for fp32)."""
+import numpy as np
+import pytest
+
+from linear_attention_sequence_03_amd import synth
+from gpu_helpers import dev, host, io_dtype, rel_err, torch_mod
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+# (io, gate, chunk, d): the scratch-using two-kernel paths, and the single
+# kernel (bf16, scalar gate, chunk 64) that needs no scratch
+PATHS = [("bf16", "channel", 64, 128), ("bf16", "channel", 16, 64), ("bf16", "scalar", 16, 128),
+         ("bf16", "scalar", 32, 64), ("f32", "scalar", 64, 64), ("f32", "channel", 32, 128),
+         ("bf16", "scalar", 64, 128)]
+CALLS = [(2, 300, 4, 40), (1, 70, 3, 41)]   # (B, T, H, seed): the second call is smaller
+
+
+def _run_both(inp, io, chunk):
+    torch = torch_mod()
+    from linear_attention_sequence_03_amd import gdr_chunk_fwd, gdr_chunk_fwd_noalloc
+    dt = io_dtype(io)
+    args = [dev(inp["q"], dt), dev(inp["k"], dt), dev(inp["v"], dt), dev(inp["log_alpha"]),
+            dev(inp["beta"]), dev(inp["S0"])]
+    o_ref, st_ref = gdr_chunk_fwd(*args, chunk=chunk)
+    o = torch.full_like(o_ref, float("nan"))
+    st = torch.full_like(st_ref, float("nan"))
+    torch.cuda.synchronize()
+    before = torch.cuda.memory_allocated()
+    gdr_chunk_fwd_noalloc(*args, chunk=chunk, o=o, S_T=st)
+    torch.cuda.synchronize()
+    assert torch.cuda.memory_allocated() == before
+    return (o, st), (o_ref, st_ref)
+
+
+@pytest.mark.parametrize("io,gate,chunk,d", PATHS)
+def test_noalloc_matches_chunk_fwd(io, gate, chunk, d):
+    torch = torch_mod()
+    for B, T, H, seed in CALLS:
+        inp = synth.chunk_inputs(B, T, H, d, d, gate, io, seed=seed + d + chunk, s0_std=0.1)
+        (o, st), (o_ws, st_ws) = _run_both(inp, io, chunk)
+        print("noalloc %s %s C=%d d=%d B=%d T=%d H=%d" % (io, gate, chunk, d, B, T, H), flush=True)
+        assert torch.equal(o, o_ws) and torch.equal(st, st_ws), (B, T, H)
+        o_or, st_or = oracle.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"],
+                                       inp["S0"])
+        eo, es = rel_err(host(o), o_or), rel_err(host(st), st_or)
+        assert eo <= TOL[io] and es <= TOL[io], (B, T, H, eo, es)
+
+
+def test_noalloc_rejects_requests_beyond_the_scratch():
+    torch = torch_mod()
+    from linear_attention_sequence_03_amd import gdr
+    # KDA, bf16, d = 128, chunk 64: 66048 bytes per (b, h, chunk) block, so
+    # 1024 blocks pass the 64 MiB limit; nothing is launched
+    B, T, H, d = 1, 64 * 64, 16, 128
+    need = gdr.gdr_chunk_fwd_workspace_size(B, T, H, d, d, 64, gdr.GDR_BF16, gdr.GDR_GATE_CHANNEL)
+    assert need > gdr.GDR_NOALLOC_SCRATCH_BYTES
+    bf = torch.bfloat16
+    q = torch.zeros((B, T, H, d), dtype=bf, device="cuda")
+    la = torch.zeros((B, T, H, d), dtype=torch.float32, device="cuda")
+    be = torch.zeros((B, T, H), dtype=torch.float32, device="cuda")
+    with pytest.raises(gdr.GdrError) as e:
+        gdr.gdr_chunk_fwd_noalloc(q, q.clone(), q.clone(), la, be)
+    assert e.value.status == gdr.GDR_ERR_UNSUPPORTED
+    # the same sizes with the scalar gate need no scratch and run
+    x = synth.chunk_inputs(B, 130, H, d, d, "scalar", "bf16", seed=5, s0_std=0.0)
+    o, st = gdr.gdr_chunk_fwd_noalloc(dev(x["q"], bf), dev(x["k"], bf), dev(x["v"], bf),
+                                      dev(x["log_alpha"]), dev(x["beta"]))
+    torch.cuda.synchronize()
+    assert np.isfinite(host(o)).all() and np.isfinite(host(st)).all()
