@@ -15,4 +15,5 @@ two share no code.
 """
 from .gdr_oracle import (build, chunk_fwd, chunk_fwd_prologue, decode_multi,  # noqa: F401
                          decode_step, decode_step_prologue, fg2_chunk_fwd, fg2_decode_step,
-                         gdn2_chunk_fwd, library_path, load, prologue_inputs)
+                         gdn2_chunk_fwd, library_path, load, prologue_decay,
+                         prologue_inputs)

@@ -237,6 +237,7 @@ def gdn2_chunk_fwd(q, k, v, log_alpha, erase, write, S0=None, threads=None, lib=
 
 PROLOGUE_L2NORM_QK = 1
 PROLOGUE_BETA_SIGMOID = 2
+PROLOGUE_DECAY_SOFTPLUS = 4
 PROLOGUE_EPS = 1e-6
 
 
@@ -255,13 +256,29 @@ def prologue_inputs(q, k, beta, flags, eps=PROLOGUE_EPS):
     return q, k, be
 
 
+def prologue_decay(log_alpha, flags):
+    """The decay from its logit (flag 4): log alpha = -softplus(x) = -ln(1 + e^x),
+    so alpha = 1 / (1 + e^x) lies in (0, 1) for every finite x.  The "FG2-GDN"
+    page (section 3.5) feeds channel-wise projections to KDA's gated-decay
+    transform, which yields alpha in (0, 1), without printing it; the NVFP4
+    abstract on the "Daily Papers" DeltaNet search page (finding ii) names
+    softplus / exponential parameterisations for the decay gate.  This reading
+    takes the plainest such map: a softplus, negated, then the exponential that
+    every call already applies to log alpha.  In fp64 through logaddexp (no
+    overflow for large |x|)."""
+    x = _f64(log_alpha)
+    if flags & PROLOGUE_DECAY_SOFTPLUS:
+        return -np.logaddexp(0.0, x)
+    return x
+
+
 def chunk_fwd_prologue(q, k, v, log_alpha, beta, S0=None, flags=0, threads=None, lib=None):
-    """The whole-sequence forward on raw q, k and beta logits: the prologue
-    above, then the recurrence (a composition, no arithmetic of its own)."""
+    """The whole-sequence forward on raw q, k, beta and decay logits: the
+    prologue above, then the recurrence (a composition, no arithmetic of its own)."""
     q2, k2, be2 = prologue_inputs(q, k, beta, flags)
-    return chunk_fwd(q2, k2, v, log_alpha, be2, S0, threads=threads, lib=lib)
+    return chunk_fwd(q2, k2, v, prologue_decay(log_alpha, flags), be2, S0, threads=threads, lib=lib)
 
 
 def decode_step_prologue(q, k, v, log_alpha, beta, S, flags=0, lib=None):
     q2, k2, be2 = prologue_inputs(q, k, beta, flags)
-    return decode_step(q2, k2, v, log_alpha, be2, S, lib=lib)
+    return decode_step(q2, k2, v, prologue_decay(log_alpha, flags), be2, S, lib=lib)

@@ -87,3 +87,69 @@ def test_decode_prologue_is_one_token_of_chunk():
     od, sd = oracle.decode_step_prologue(q[:, 0], k[:, 0], v[:, 0], la[:, 0], x[:, 0], S0, flags=3)
     np.testing.assert_allclose(od, o[:, 0], rtol=0, atol=1e-14)
     np.testing.assert_allclose(sd, st, rtol=0, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# The decay from its logit (flag 4): log alpha = -softplus(x), alpha = 1/(1+e^x).
+# ---------------------------------------------------------------------------
+DECAY = oracle.gdr_oracle.PROLOGUE_DECAY_SOFTPLUS
+
+
+def test_decay_softplus_closed_forms():
+    from scipy.special import log_expit
+    x = np.array([-600.0, -60.0, -5.0, -1e-3, 0.0, 1e-3, 2.0, 40.0, 800.0])
+    la = oracle.prologue_decay(x, DECAY)
+    # -softplus(x) = log sigmoid(-x): scipy's log-logistic, a separate routine
+    np.testing.assert_allclose(la, log_expit(-x), rtol=1e-15, atol=0)
+    assert la[4] == -np.log(2.0)                       # x = 0: alpha = 1/2
+    np.testing.assert_allclose(la[0], -np.exp(-600.0), rtol=1e-14)   # alpha -> 1: -e^x
+    np.testing.assert_allclose(la[-1], -800.0, rtol=1e-15)   # alpha ~ e^-x
+    assert np.all(np.diff(la) < 0)                     # monotone decreasing in x
+    assert np.all(la < 0)                              # alpha in (0, 1)
+    # flag off: the log decay passes through unchanged
+    np.testing.assert_array_equal(oracle.prologue_decay(x, 3), x)
+
+
+@pytest.mark.parametrize("channel", [False, True])
+def test_decay_softplus_inverts_to_the_log_decay(channel):
+    """x = ln(e^{-log alpha} - 1) is the logit of a given decay; the prologue on x
+    must reproduce the plain recurrence on log alpha."""
+    q, k, v, la, _, S0 = _raw(7, channel=channel)
+    be = expit(_rng(70).standard_normal(la.shape[:3]))
+    x = np.log(np.expm1(-la))
+    o1, s1 = oracle.chunk_fwd_prologue(q, k, v, x, be, S0, flags=DECAY)
+    o2, s2 = oracle.chunk_fwd(q, k, v, la, be, S0)
+    np.testing.assert_allclose(o1, o2, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(s1, s2, rtol=1e-11, atol=1e-12)
+    od, sd = oracle.decode_step_prologue(q[:, 0], k[:, 0], v[:, 0], x[:, 0], be[:, 0], S0, flags=DECAY)
+    od2, sd2 = oracle.decode_step(q[:, 0], k[:, 0], v[:, 0], la[:, 0], be[:, 0], S0)
+    np.testing.assert_allclose(od, od2, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(sd, sd2, rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("channel", [False, True])
+def test_decay_softplus_exact_rational(channel):
+    """Logits x = ln m (m a positive integer) give alpha = 1/(1+m) exactly: the
+    prologue against the exact rational recurrence of oracle.exact."""
+    from fractions import Fraction
+    from oracle import exact
+    r = _rng(71)
+    T, dk, dv = 6, 3, 2
+    fr = lambda lo, hi, den: Fraction(int(r.integers(lo, hi)), den)  # noqa: E731
+    q = [[fr(-8, 9, 8) for _ in range(dk)] for _ in range(T)]
+    k = [[fr(-8, 9, 8) for _ in range(dk)] for _ in range(T)]
+    v = [[fr(-8, 9, 4) for _ in range(dv)] for _ in range(T)]
+    m = r.integers(1, 9, (T, dk if channel else 1))
+    alpha = [[Fraction(1, 1 + int(m[t, c if channel else 0])) for c in range(dk)] for t in range(T)]
+    beta = [fr(0, 9, 8) for _ in range(T)]
+    S0 = [[fr(-4, 5, 4) for _ in range(dk)] for _ in range(dv)]
+    o_ex, s_ex = exact.run(q, k, v, alpha, beta, S0)
+    f = lambda a: np.array([[float(x) for x in row] for row in a])  # noqa: E731
+    x = np.log(m.astype(np.float64))
+    x = x.reshape(1, T, 1, dk) if channel else x.reshape(1, T, 1)
+    o, st = oracle.chunk_fwd_prologue(f(q).reshape(1, T, 1, dk), f(k).reshape(1, T, 1, dk),
+                                      f(v).reshape(1, T, 1, dv), x,
+                                      np.array([float(b) for b in beta]).reshape(1, T, 1),
+                                      f(S0).reshape(1, 1, dv, dk), flags=DECAY)
+    np.testing.assert_allclose(o[0, :, 0], f(o_ex), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(st[0, 0], f(s_ex), rtol=0, atol=1e-13)
