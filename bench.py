@@ -113,14 +113,22 @@ def read_summary(workload, kind):
     if not os.path.exists(path):
         return None
     kv = dict(l.strip().split("=", 1) for l in open(path) if "=" in l and not l.startswith("#"))
-    return kv if kv.get("source_hash") == kernel_source_hash() else None
+    return kv if kv.get("source_hash") == kernel_source_hash(workload) else None
 
 
-def kernel_source_hash():
+# The sources that build the kernels each workload's summary measures (plus the
+# calibration copy): a summary counts only while these are unchanged.
+KERNEL_SOURCES = {
+    1: ("gdr_fused.hip",), 3: ("gdr_fused.hip",), 2: ("gdr_chunk.hip",), 4: ("gdr_decode.hip",),
+}
+
+
+def kernel_source_hash(workload):
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "linear_attention_sequence_03_amd", "csrc", "*"))):
-        with open(f, "rb") as fh:
-            h.update(os.path.basename(f).encode() + fh.read())
+    csrc = os.path.join(ROOT, "linear_attention_sequence_03_amd", "csrc")
+    for name in sorted(KERNEL_SOURCES[workload] + ("gdr_device.hpp", "gdr_launch.hpp", "gdr_calib.hip")):
+        with open(os.path.join(csrc, name), "rb") as fh:
+            h.update(name.encode() + fh.read())
     return h.hexdigest()[:16]
 
 
@@ -276,25 +284,6 @@ def cpu_model() -> str:
     except OSError:
         pass
     return "unknown CPU"
-
-
-def measure_mfma(outdir):
-    """One rocprofv3 --pmc pass (MFMA counters) over traffic_probe(); returns the
-    per-call mean of each counter over the prefill kernel's dispatches."""
-    d = tempfile.mkdtemp(prefix="pmc_", dir=outdir)
-    cmd = (["rocprofv3", "--pmc"] + list(MFMA_COUNTERS) +
-           ["--output-format", "csv", "-d", d, "-o", "run", "--",
-            sys.executable, os.path.abspath(__file__), "--traffic-probe"])
-    subprocess.run(cmd, check=True, stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL, timeout=240)
-    rows = []
-    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
-        rows += list(csv.DictReader(open(f)))
-    per = {}
-    for r in rows:
-        if "fused_chunk" in r["Kernel_Name"]:
-            per.setdefault(r["Counter_Name"], {}).setdefault(r["Dispatch_Id"], 0.0)
-            per[r["Counter_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
-    return {c: float(np.mean(list(per[c].values()))) for c in MFMA_COUNTERS if c in per}
 
 
 # The pages' prefill sweep ("FG2-GDN" page, section 4.5, Figure 3): one batch of
@@ -496,7 +485,7 @@ def main():
                      "then WRITE_SIZE, over 3 calls and 3 plain copies)\n" % args.workload)
             fh.write("# kernels: %s; calibration: plain %d MiB device copy (libgdr_calib.so)\n"
                      % (", ".join(res.get("kernels", ())), COPY_BYTES >> 20))
-            fh.write("source_hash=%s\n" % kernel_source_hash())
+            fh.write("source_hash=%s\n" % kernel_source_hash(args.workload))
             for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
                 r = res[ctr]
                 fh.write("%s_kib_per_call=%.1f\n%s_copy_kib=%.1f\n%s_factor=%.4f\n"
@@ -514,7 +503,7 @@ def main():
                      % (args.workload, " ".join(MFMA_COUNTERS)))
             fh.write("# kernels: %s; per-dispatch means over the probe's calls, summed over the "
                      "call's kernels (MfmaUtil: mean over its dispatches)\n" % ", ".join(PREFILL_KERNELS))
-            fh.write("source_hash=%s\n" % kernel_source_hash())
+            fh.write("source_hash=%s\n" % kernel_source_hash(args.workload))
             for c, v in res.items():
                 fh.write("%s=%.6g\n" % (c, v))
         print(json.dumps({"summary": path, **res}))
