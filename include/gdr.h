@@ -144,21 +144,39 @@ gdr_status gdr_decode_step(const void *q, const void *k, const void *v,
                            gdr_dtype io, gdr_gate gate, hipStream_t stream);
 
 /*
- * The gate prologue, fused into the kernels' loads ("FG2-GDN" page, section
- * 3.5: queries and keys are L2-normalised, and the write rate is the sigmoid of
- * its projection).  `flags` is a bitwise OR of:
- *   GDR_PROLOGUE_L2NORM_QK     q and k are normalised per token and head,
- *                              x / sqrt(sum x^2 + 1e-6), inside the kernel
- *   GDR_PROLOGUE_BETA_SIGMOID  beta holds logits; the kernel uses 1 / (1 + e^-beta)
- * The decay is taken as log_alpha, as in the other calls (the page names a
- * gated-decay transform without its formula).  Arguments are otherwise those of
- * gdr_chunk_fwd / gdr_decode_step, with q, k and beta holding the raw values.
- * The prefill prologue is fused into the bf16 paths: chunk 64 with the scalar
- * gate (the single-kernel path) and every chunk size with the channel gate;
- * other requests return GDR_ERR_UNSUPPORTED.  The decode step takes it for
- * every dtype and gate.  flags = 0 is exactly gdr_chunk_fwd / gdr_decode_step.
+ * The gate prologue, applied to raw projections inside the library ("FG2-GDN"
+ * page, section 3.5: queries and keys are L2-normalised, the write rate is the
+ * sigmoid of its projection, and the decay comes from KDA's gated-decay
+ * transform of channel-wise projections).  `flags` is a bitwise OR of:
+ *   GDR_PROLOGUE_L2NORM_QK       q and k are normalised per token and head,
+ *                                x / sqrt(sum x^2 + 1e-6)
+ *   GDR_PROLOGUE_BETA_SIGMOID    beta holds logits; the call uses 1 / (1 + e^-beta)
+ *   GDR_PROLOGUE_DECAY_SOFTPLUS  log_alpha holds decay logits x (per token and
+ *                                head, or per key channel); the call uses
+ *                                log alpha = -softplus(x) = -ln(1 + e^x), i.e.
+ *                                alpha = 1 / (1 + e^x) in (0, 1).  The page does
+ *                                not print the transform; the NVFP4 abstract on
+ *                                the "Daily Papers" DeltaNet search page (its
+ *                                finding ii) names softplus / exponential
+ *                                parameterisations of the decay gate, and this is
+ *                                the plainest map of that kind into (0, 1).
+ * Arguments are otherwise those of gdr_chunk_fwd / gdr_decode_step, with q, k,
+ * beta and log_alpha holding the raw values the flags name.  The bf16 prefill
+ * calls with chunk 64 and the scalar gate, and every bf16 call with the channel
+ * gate, fold the maps into their own loads.  The other prefill calls (fp32 io;
+ * bf16 with the scalar gate at chunks 16 and 32) first run an elementwise pass
+ * that writes the mapped q, k (io dtype), beta and log alpha into the workspace,
+ * whose size for any flags comes from gdr_chunk_fwd_prologue_workspace_size.
+ * The decode step maps inside its kernel for every dtype and gate.  flags = 0
+ * is exactly gdr_chunk_fwd / gdr_decode_step; unknown bits return
+ * GDR_ERR_INVALID_ARG.
  */
-enum { GDR_PROLOGUE_L2NORM_QK = 1, GDR_PROLOGUE_BETA_SIGMOID = 2 };
+enum { GDR_PROLOGUE_L2NORM_QK = 1, GDR_PROLOGUE_BETA_SIGMOID = 2, GDR_PROLOGUE_DECAY_SOFTPLUS = 4 };
+
+gdr_status gdr_chunk_fwd_prologue_workspace_size(int64_t B, int64_t T, int64_t H,
+                                                 int64_t dk, int64_t dv, int64_t chunk,
+                                                 gdr_dtype io, gdr_gate gate, unsigned flags,
+                                                 size_t *bytes);
 
 gdr_status gdr_chunk_fwd_prologue(const void *q, const void *k, const void *v,
                                   const float *log_alpha, const float *beta, const float *S0,

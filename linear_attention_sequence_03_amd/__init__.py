@@ -10,6 +10,7 @@ from .gdr import (  # noqa: F401
     GdrError,
     gdr_chunk_fwd,
     gdr_chunk_fwd_noalloc,
+    gdr_chunk_fwd_prologue_workspace_size,
     gdr_chunk_fwd_workspace_size,
     gdr_decode_multi,
     gdr_decode_step,

@@ -48,6 +48,9 @@ int64_t mul(std::initializer_list<int64_t> xs) {
     return r;
 }
 
+constexpr unsigned kPrologueAll = GDR_PROLOGUE_L2NORM_QK | GDR_PROLOGUE_BETA_SIGMOID |
+                                   GDR_PROLOGUE_DECAY_SOFTPLUS;
+
 gdr_status check_common(int64_t B, int64_t H, int64_t dk, int64_t dv, gdr_dtype io, gdr_gate gate) {
     if (B < 1 || H < 1 || dk < 1 || dv < 1)
         return fail(GDR_ERR_INVALID_ARG, "sizes must be positive (B=%lld H=%lld dk=%lld dv=%lld)",
@@ -107,6 +110,24 @@ gdr_status gdr_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t
     return GDR_OK;
 }
 
+gdr_status gdr_chunk_fwd_prologue_workspace_size(int64_t B, int64_t T, int64_t H, int64_t dk,
+                                                 int64_t dv, int64_t chunk, gdr_dtype io,
+                                                 gdr_gate gate, unsigned flags, size_t* bytes) {
+    gdr_status s = gdr_chunk_fwd_workspace_size(B, T, H, dk, dv, chunk, io, gate, bytes);
+    if (s != GDR_OK) return s;
+    if (flags & ~kPrologueAll) {
+        *bytes = 0;
+        return fail(GDR_ERR_INVALID_ARG, "unknown prologue flags 0x%x", flags);
+    }
+    if (mul({B, T, H, dk, 4}) < 0) {
+        *bytes = 0;
+        return fail(GDR_ERR_UNSUPPORTED, "tensor sizes overflow");
+    }
+    *bytes = gdr::chunk_prologue_workspace_bytes(B, T, H, dk, chunk, io == GDR_BF16,
+                                                 gate == GDR_GATE_CHANNEL, flags);
+    return GDR_OK;
+}
+
 }  // extern "C"
 
 namespace {
@@ -117,7 +138,7 @@ gdr_status chunk_fwd_impl(const void* q, const void* k, const void* v, const flo
                                  gdr_dtype io, gdr_gate gate, void* workspace, size_t workspace_bytes,
                                  hipStream_t stream, unsigned prologue, bool noalloc = false) {
     size_t need = 0;
-    gdr_status s = gdr_chunk_fwd_workspace_size(B, T, H, dk, dv, chunk, io, gate, &need);
+    gdr_status s = gdr_chunk_fwd_prologue_workspace_size(B, T, H, dk, dv, chunk, io, gate, prologue, &need);
     if (s != GDR_OK) return s;
     const int64_t ntok = mul({B, T, H});
     if (ntok < 0 || mul({ntok, dk}) < 0 || mul({B, H, dv, dk}) < 0)
@@ -152,10 +173,6 @@ gdr_status chunk_fwd_impl(const void* q, const void* k, const void* v, const flo
     };
     s = check_ptrs(rs, 9, 6);
     if (s != GDR_OK) return s;
-    if (prologue && !gdr::prologue_supported(chunk, io == GDR_BF16, gate == GDR_GATE_CHANNEL))
-        return fail(GDR_ERR_UNSUPPORTED,
-                    "the gate prologue is fused into the bf16 calls with chunk 64 (scalar gate) or the "
-                    "channel gate only");
     if (noalloc && need > 0) {
         // the fixed scratch stands in for the workspace; every byte of it the
         // state pass reads is written by this call's preparation kernel first
@@ -200,7 +217,7 @@ gdr_status gdr_chunk_fwd_prologue(const void* q, const void* k, const void* v,
                                   void* workspace, size_t workspace_bytes, unsigned flags,
                                   hipStream_t stream) {
     g_last_error[0] = 0;
-    if (flags & ~3u) return fail(GDR_ERR_INVALID_ARG, "unknown prologue flags 0x%x", flags);
+    if (flags & ~kPrologueAll) return fail(GDR_ERR_INVALID_ARG, "unknown prologue flags 0x%x", flags);
     return chunk_fwd_impl(q, k, v, log_alpha, beta, S0, o, S_T, B, T, H, dk, dv, chunk, io, gate,
                           workspace, workspace_bytes, stream, flags);
 }
@@ -246,7 +263,7 @@ gdr_status gdr_decode_step_prologue(const void* q, const void* k, const void* v,
     if (!aligned16(S_in)) return fail(GDR_ERR_INVALID_ARG, "S_in is not 16-byte aligned");
     s = check_ptrs(rs, 8, 6);
     if (s != GDR_OK) return s;
-    if (flags & ~3u) return fail(GDR_ERR_INVALID_ARG, "unknown prologue flags 0x%x", flags);
+    if (flags & ~kPrologueAll) return fail(GDR_ERR_INVALID_ARG, "unknown prologue flags 0x%x", flags);
     gdr::DecodeArgs a{q, k, v, log_alpha, beta, S_in, S_out, o, B, H, dk, dv,
                       io == GDR_BF16, gate == GDR_GATE_CHANNEL, stream, nullptr, nullptr, flags};
     const hipError_t err = gdr::decode_step_launch(a);

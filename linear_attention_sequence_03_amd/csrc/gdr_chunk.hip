@@ -652,7 +652,7 @@ __device__ __forceinline__ void chan_prep_wave(ChanPrepSmem<DK, C>& sm, const __
                                                const __bf16* __restrict__ k,
                                                const float* __restrict__ log_alpha,
                                                const float* __restrict__ beta, uint8_t* __restrict__ ws,
-                                               int64_t T, int H, int NT, bool sigb) {
+                                               int64_t T, int H, int NT, int gflags) {
     using L = WsLayout<__bf16, DK, C, true>;
     using M = Mma<__bf16>;
     using MF = Mma<float>;
@@ -687,7 +687,7 @@ __device__ __forceinline__ void chan_prep_wave(ChanPrepSmem<DK, C>& sm, const __
     const bool valid = r < len;   // rows past len read row len-1 and are zeroed
     const int64_t grow = row0 + (int64_t)(valid ? r : len - 1) * H;
     float be = beta[grow];
-    if (sigb) be = 1.f / (1.f + __expf(-be));   // beta from its logit (prologue)
+    if (gflags & kPrologueBetaSigmoid) be = sigmoid_of(be);   // prologue: beta from its logit
     be = valid ? be : 0.f;
     if (kg == 0) bsh[r] = be;
 
@@ -734,7 +734,10 @@ __device__ __forceinline__ void chan_prep_wave(ChanPrepSmem<DK, C>& sm, const __
         const float4 l1 = *reinterpret_cast<const float4*>(p + 4);
         const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
 #pragma unroll
-        for (int j = 0; j < 8; ++j) la[j] = valid ? fmaxf(lv[j], kMinLogAlpha) * kLog2e : 0.f;
+        for (int j = 0; j < 8; ++j) {
+            const float x = (gflags & kPrologueDecaySoftplus) ? neg_softplus(lv[j]) : lv[j];
+            la[j] = valid ? fmaxf(x, kMinLogAlpha) * kLog2e : 0.f;
+        }
     };
     // In-block inclusive scan over the 16 rows (one DPP row per channel group).
     auto scan = [&](float* v) {
@@ -1026,17 +1029,16 @@ __device__ __forceinline__ void chan_prep_wave(ChanPrepSmem<DK, C>& sm, const __
 template <int DK, int C, bool NORM>
 __global__ __launch_bounds__(64 * (C / 16), 4) void wy_prep_channel_bf16(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const float* __restrict__ log_alpha,
-    const float* __restrict__ beta, uint8_t* __restrict__ ws, int64_t T, int H, int NT, int sigb) {
+    const float* __restrict__ beta, uint8_t* __restrict__ ws, int64_t T, int H, int NT, int gflags) {
     __shared__ ChanPrepSmem<DK, C> sm;
     const int w = threadIdx.x >> 6;
     constexpr int NB = C / 16;
-    const bool sg = sigb != 0;
-    if (w == 0) chan_prep_wave<DK, C, 0, NORM>(sm, q, k, log_alpha, beta, ws, T, H, NT, sg);
+    if (w == 0) chan_prep_wave<DK, C, 0, NORM>(sm, q, k, log_alpha, beta, ws, T, H, NT, gflags);
     if constexpr (NB > 1)
-        if (w == 1) chan_prep_wave<DK, C, (NB > 1 ? 1 : 0), NORM>(sm, q, k, log_alpha, beta, ws, T, H, NT, sg);
+        if (w == 1) chan_prep_wave<DK, C, (NB > 1 ? 1 : 0), NORM>(sm, q, k, log_alpha, beta, ws, T, H, NT, gflags);
     if constexpr (NB > 2) {
-        if (w == 2) chan_prep_wave<DK, C, (NB > 2 ? 2 : 0), NORM>(sm, q, k, log_alpha, beta, ws, T, H, NT, sg);
-        if (w == 3) chan_prep_wave<DK, C, (NB > 3 ? 3 : 0), NORM>(sm, q, k, log_alpha, beta, ws, T, H, NT, sg);
+        if (w == 2) chan_prep_wave<DK, C, (NB > 2 ? 2 : 0), NORM>(sm, q, k, log_alpha, beta, ws, T, H, NT, gflags);
+        if (w == 3) chan_prep_wave<DK, C, (NB > 3 ? 3 : 0), NORM>(sm, q, k, log_alpha, beta, ws, T, H, NT, gflags);
     }
 }
 
@@ -1446,15 +1448,15 @@ static hipError_t launch_chunk(const ChunkArgs& a) {
     const int NT = (int)((a.T + C - 1) / C);
     const int64_t BH = a.B * a.H;
     if constexpr (CHANNEL && sizeof(E) == 2) {
-        const int sigb = (a.prologue & kPrologueBetaSigmoid) ? 1 : 0;
+        const int gflags = (int)(a.prologue & kPrologueGates);
         if (a.prologue & kPrologueL2NormQK)
             hipLaunchKernelGGL((wy_prep_channel_bf16<DK, C, true>), dim3((unsigned)(BH * NT)), dim3(64 * (C / 16)),
                                0, a.stream, (const __bf16*)a.q, (const __bf16*)a.k, a.log_alpha, a.beta,
-                               (uint8_t*)a.ws, a.T, (int)a.H, NT, sigb);
+                               (uint8_t*)a.ws, a.T, (int)a.H, NT, gflags);
         else
             hipLaunchKernelGGL((wy_prep_channel_bf16<DK, C, false>), dim3((unsigned)(BH * NT)), dim3(64 * (C / 16)),
                                0, a.stream, (const __bf16*)a.q, (const __bf16*)a.k, a.log_alpha, a.beta,
-                               (uint8_t*)a.ws, a.T, (int)a.H, NT, sigb);
+                               (uint8_t*)a.ws, a.T, (int)a.H, NT, gflags);
     } else if constexpr (CHANNEL) {
         hipLaunchKernelGGL((wy_prep_channel<E, DK, C>), dim3((unsigned)(BH * NT)), dim3(kThreads), 0,
                            a.stream, (const E*)a.q, (const E*)a.k, a.log_alpha, a.beta,
@@ -1509,20 +1511,133 @@ size_t chunk_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_
     return (size_t)(B * H * NT) * chunk_block_bytes(dk, chunk, bf16, channel);
 }
 
-bool prologue_supported(int64_t chunk, bool bf16, bool channel) {
+bool prologue_fused(int64_t chunk, bool bf16, bool channel) {
     // fused into the loads of the single-kernel path and of the bf16
     // channel-gate prep (the state pass reads only the prep's outputs then)
     return bf16 && (channel || chunk == 64);
 }
 
+namespace {
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// The gate prologue as an elementwise pass, for the calls whose kernels do not
+// fuse it: fp32 io, and the scalar gate at chunks 16 and 32 (whose state pass
+// reads q and k straight from the caller's tensors).  Writes what the flags
+// select into the staging part of the workspace:
+//   unit-norm q and k (io dtype, x / sqrt(sum x^2 + 1e-6) per row),
+//   beta from its logit, and the log decay from its logit (fp32).
+// A group of DK/4 lanes takes one (token, head) row, 4 channels per lane.
+template <typename E, int DK, bool CHANNEL>
+__global__ __launch_bounds__(256) void prologue_stage(const E* __restrict__ q, const E* __restrict__ k,
+                                                      const float* __restrict__ log_alpha,
+                                                      const float* __restrict__ beta, E* __restrict__ qs,
+                                                      E* __restrict__ ks, float* __restrict__ las,
+                                                      float* __restrict__ bes, int64_t rows, unsigned flags) {
+    constexpr int LPR = DK / 4;
+    constexpr int RPB = 256 / LPR;
+    const int gl = threadIdx.x % LPR;
+    const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+    if (row >= rows) return;   // whole lane groups leave together
+    const int64_t e0 = row * DK + 4 * gl;
+    if (flags & kPrologueL2NormQK) {
+        float4 qq = load4(q + e0), kk = load4(k + e0);
+        float sq = qq.x * qq.x + qq.y * qq.y + qq.z * qq.z + qq.w * qq.w;
+        float sk = kk.x * kk.x + kk.y * kk.y + kk.z * kk.z + kk.w * kk.w;
+#pragma unroll
+        for (int m = LPR / 2; m >= 1; m >>= 1) {
+            sq += __shfl_xor(sq, m);
+            sk += __shfl_xor(sk, m);
+        }
+        const float nq = 1.f / sqrtf(sq + 1e-6f), nk = 1.f / sqrtf(sk + 1e-6f);
+        store4(qs + e0, make_float4(qq.x * nq, qq.y * nq, qq.z * nq, qq.w * nq));
+        store4(ks + e0, make_float4(kk.x * nk, kk.y * nk, kk.z * nk, kk.w * nk));
+    }
+    if ((flags & kPrologueBetaSigmoid) && gl == 0) bes[row] = sigmoid_of(beta[row]);
+    if (flags & kPrologueDecaySoftplus) {
+        if constexpr (CHANNEL) {
+            const float4 x = *reinterpret_cast<const float4*>(log_alpha + e0);
+            *reinterpret_cast<float4*>(las + e0) =
+                make_float4(neg_softplus(x.x), neg_softplus(x.y), neg_softplus(x.z), neg_softplus(x.w));
+        } else if (gl == 0) {
+            las[row] = neg_softplus(log_alpha[row]);
+        }
+    }
+}
+
+template <typename E, int DK, bool CHANNEL>
+hipError_t launch_prologue_stage(const ChunkArgs& a, ChunkArgs& b) {
+    const int64_t rows = a.B * a.T * a.H;
+    const size_t es = sizeof(E);
+    char* st = static_cast<char*>(a.ws) +
+               align256(chunk_workspace_bytes(a.B, a.T, a.H, a.dk, a.chunk, a.bf16, a.channel));
+    E* qs = nullptr;
+    E* ks = nullptr;
+    float *las = nullptr, *bes = nullptr;
+    if (a.prologue & kPrologueL2NormQK) {
+        qs = reinterpret_cast<E*>(st);
+        st += align256(rows * DK * es);
+        ks = reinterpret_cast<E*>(st);
+        st += align256(rows * DK * es);
+        b.q = qs;
+        b.k = ks;
+    }
+    if (a.prologue & kPrologueBetaSigmoid) {
+        bes = reinterpret_cast<float*>(st);
+        st += align256(rows * 4);
+        b.beta = bes;
+    }
+    if (a.prologue & kPrologueDecaySoftplus) {
+        las = reinterpret_cast<float*>(st);
+        b.log_alpha = las;
+    }
+    b.prologue = 0;
+    constexpr int RPB = 256 / (DK / 4);
+    hipLaunchKernelGGL((prologue_stage<E, DK, CHANNEL>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256),
+                       0, a.stream, (const E*)a.q, (const E*)a.k, a.log_alpha, a.beta, qs, ks, las, bes, rows,
+                       a.prologue);
+    return hipGetLastError();
+}
+
+template <typename E>
+hipError_t prologue_stage_e(const ChunkArgs& a, ChunkArgs& b) {
+    if (a.dk == 64)
+        return a.channel ? launch_prologue_stage<E, 64, true>(a, b) : launch_prologue_stage<E, 64, false>(a, b);
+    return a.channel ? launch_prologue_stage<E, 128, true>(a, b) : launch_prologue_stage<E, 128, false>(a, b);
+}
+
+}  // namespace
+
+size_t prologue_stage_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, bool bf16, bool channel,
+                            unsigned flags) {
+    const size_t rows = (size_t)(B * T * H);
+    size_t n = 0;
+    if (flags & kPrologueL2NormQK) n += 2 * align256(rows * dk * (bf16 ? 2 : 4));
+    if (flags & kPrologueBetaSigmoid) n += align256(rows * 4);
+    if (flags & kPrologueDecaySoftplus) n += align256(rows * (channel ? dk : 1) * 4);
+    return n;
+}
+
+size_t chunk_prologue_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t chunk,
+                                      bool bf16, bool channel, unsigned flags) {
+    const size_t base = chunk_workspace_bytes(B, T, H, dk, chunk, bf16, channel);
+    if (T == 0 || flags == 0 || prologue_fused(chunk, bf16, channel)) return base;
+    return align256(base) + prologue_stage_bytes(B, T, H, dk, bf16, channel, flags);
+}
+
 hipError_t chunk_fwd_launch(const ChunkArgs& a) {
-    if (a.prologue && a.T > 0 && !prologue_supported(a.chunk, a.bf16, a.channel)) return hipErrorNotSupported;
     if (a.T == 0) {
         if (!a.S_T) return hipSuccess;
         const int64_t n4 = a.B * a.H * a.dv * a.dk / 4;
         hipLaunchKernelGGL(copy_state, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, a.stream,
                            a.S0, a.S_T, n4);
         return hipGetLastError();
+    }
+    if (a.prologue && !prologue_fused(a.chunk, a.bf16, a.channel)) {
+        ChunkArgs b = a;
+        const hipError_t err = a.bf16 ? prologue_stage_e<__bf16>(a, b) : prologue_stage_e<float>(a, b);
+        if (err != hipSuccess) return err;
+        return chunk_fwd_launch(b);
     }
     if (fused_chunk_supported(a.dk, a.chunk, a.bf16, a.channel)) return fused_chunk_launch(a);
     if (a.bf16)

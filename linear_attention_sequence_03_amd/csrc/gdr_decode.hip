@@ -18,8 +18,9 @@
 // S_in) is safe: each 16-byte slice is read and written by the same lane.
 //
 // The gate prologue ("FG2-GDN" page, section 3.5: unit-norm q and k, beta as
-// the sigmoid of its logit) runs in the kernel when asked for: each row's
-// lanes sum the squares of their key and query channels.
+// the sigmoid of its logit, the decay from its logit as alpha = 1 / (1 + e^x))
+// runs in the kernel when asked for: each row's lanes sum the squares of their
+// key and query channels; beta and log alpha are mapped as they are loaded.
 //
 // With channel-wise write rates (FG2, "FG2-GDN" page, sections 3.2 and 3.4)
 // the same step runs with unit rate on the scaled key sqrt(beta^k) * k and the
@@ -66,15 +67,18 @@ __global__ __launch_bounds__(256) void decode_kernel(
         qq = make_float4(qq.x * nq, qq.y * nq, qq.z * nq, qq.w * nq);
     }
     float4 aa;
+    const bool lsp = !FG2 && (prologue & kPrologueDecaySoftplus);   // decay from its logit
     if constexpr (CHANNEL) {
-        const float4 la = *reinterpret_cast<const float4*>(log_alpha + bh * DK + c0);
+        float4 la = *reinterpret_cast<const float4*>(log_alpha + bh * DK + c0);
+        if (lsp) la = make_float4(neg_softplus(la.x), neg_softplus(la.y), neg_softplus(la.z), neg_softplus(la.w));
         aa = make_float4(expf(la.x), expf(la.y), expf(la.z), expf(la.w));
     } else {
-        const float a = expf(log_alpha[bh]);
+        const float la = log_alpha[bh];
+        const float a = expf(lsp ? neg_softplus(la) : la);
         aa = make_float4(a, a, a, a);
     }
     float b = FG2 ? 1.f : beta[bh];
-    if (!FG2 && (prologue & kPrologueBetaSigmoid)) b = 1.f / (1.f + __expf(-b));
+    if (!FG2 && (prologue & kPrologueBetaSigmoid)) b = sigmoid_of(b);
     const float* vrate = FG2 ? (beta_v ? beta_v : beta_k) : nullptr;
 
     const int64_t base = bh * (int64_t)DV * DK;

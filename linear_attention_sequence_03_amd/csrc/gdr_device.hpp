@@ -100,6 +100,17 @@ __device__ __forceinline__ typename Mma<E>::frag frag_rk_f32(const float* p, int
     }
 }
 
+// Gate prologue maps of one raw value.
+//   beta from its logit:        1 / (1 + e^-x)
+//   log alpha from its logit:   -softplus(x) = -(max(x, 0) + ln(1 + e^-|x|)),
+//                               so alpha = 1 / (1 + e^x) lies in (0, 1); the
+//                               log1p keeps the relative accuracy of small
+//                               decays (x << 0, where -softplus(x) ~ -e^x).
+__device__ __forceinline__ float sigmoid_of(float x) { return 1.f / (1.f + __expf(-x)); }
+__device__ __forceinline__ float neg_softplus(float x) {
+    return -(fmaxf(x, 0.f) + log1pf(__expf(-fabsf(x))));
+}
+
 // 4 consecutive elements <-> float4 (8-byte bf16 or 16-byte fp32 access).
 template <typename E>
 __device__ __forceinline__ float4 load4(const E* p) {

@@ -353,10 +353,11 @@ __device__ __forceinline__ float lane_value(float x, int l) {
 //   e^{g_r - g_i} = EB[r] * CX(cb, rb) * FB[i],
 // a product of factors <= 1 (no overflow; an underflow bounds a negligible value).
 template <int DK, int NW>
-__device__ __forceinline__ void gate_table(float la, float bb, int len, int lane, float* tab, bool sigb) {
+__device__ __forceinline__ void gate_table(float la, float bb, int len, int lane, float* tab, int gflags) {
     using L = FLayout<DK, NW>;
+    if (gflags & kPrologueDecaySoftplus) la = neg_softplus(la);   // prologue: decay from its logit
+    if (gflags & kPrologueBetaSigmoid) bb = sigmoid_of(bb);       // prologue: beta from its logit
     la = lane < len ? fmaxf(la, kFMinLogAlpha) : 0.f;
-    if (sigb) bb = 1.f / (1.f + __expf(-bb));   // beta from its logit (prologue)
     bb = lane < len ? bb : 0.f;
     const float g2 = wave_scan(la * 1.4426950408889634f);
     const float e0 = lane_value(g2, 15), e1 = lane_value(g2, 31), e2 = lane_value(g2, 47),
@@ -670,7 +671,7 @@ __device__ __forceinline__ void solve_loads(const __bf16* k, const float* log_al
 //  the chunk's hand-off slot xh.
 template <int DK, int NW, bool NORM>
 __device__ __forceinline__ void solve_diag(char* smem, const bf16x8 (&kf)[FNB][DK / 32], float la, float bb,
-                                           int len, bool sigb, char* xh, int lane) {
+                                           int len, int gflags, char* xh, int lane) {
     using L = FLayout<DK, NW>;
     constexpr int NKC = DK / 32;
     float* xa = reinterpret_cast<float*>(smem + L::XA);
@@ -679,8 +680,9 @@ __device__ __forceinline__ void solve_diag(char* smem, const bf16x8 (&kf)[FNB][D
 
     // The chunk's g (log2 units) and beta rows, as the gate table has them.
     {
+        if (gflags & kPrologueDecaySoftplus) la = neg_softplus(la);
+        if (gflags & kPrologueBetaSigmoid) bb = sigmoid_of(bb);
         la = lane < len ? fmaxf(la, kFMinLogAlpha) : 0.f;
-        if (sigb) bb = 1.f / (1.f + __expf(-bb));
         bb = lane < len ? bb : 0.f;
         tg[lane] = wave_scan(la * 1.4426950408889634f);
         tg[FC + lane] = bb;
@@ -1034,7 +1036,7 @@ template <int DK, int NW, bool NORM, int NL>
 __global__ __launch_bounds__(64 * (NW + 2 + NL + (NORM ? 1 : 0))) void fused_chunk(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta, const float* __restrict__ S0,
-    __bf16* __restrict__ o, float* __restrict__ ST, int64_t T, int H, int NT, int DV, int sigb) {
+    __bf16* __restrict__ o, float* __restrict__ ST, int64_t T, int H, int NT, int DV, int gflags) {
     using L = FLayout<DK, NW>;
     using M = Mma<__bf16>;
     constexpr int VT = L::VT;
@@ -1365,7 +1367,7 @@ __global__ __launch_bounds__(64 * (NW + 2 + NL + (NORM ? 1 : 0))) void fused_chu
                     float la1 = 0.f, bb1 = 0.f;
                     if (c + 1 < NT)
                         solve_loads<DK>(k, log_alpha, beta, GDR_ROW0(c + 1), GDR_LEN(c + 1), H, lane, kn, la1, bb1);
-                    solve_diag<DK, NW, NORM>(smem, kc, la, bb, GDR_LEN(c), sigb != 0,
+                    solve_diag<DK, NW, NORM>(smem, kc, la, bb, GDR_LEN(c), gflags,
                                              smem + L::XH + (c & 1) * L::XHB, lane);
                     // The prefetch has landed by now (a window of work after it
                     // was issued); the copies wait for it here.
@@ -1434,7 +1436,7 @@ __global__ __launch_bounds__(64 * (NW + 2 + NL + (NORM ? 1 : 0))) void fused_chu
                 const int len = GDR_LEN(n);
                 if (len < FC) lo.set(len, H, DV, vt, lw, lane);   // ragged last chunk
                 load_chunk<DK, NW, NL>(GDR_STAGE(n), GDR_QTILE(n), q, k, v, GDR_ROW0(n), DV, lo, lw);
-                if (lw == 0) gate_table<DK, NW>(la, bb, len, lane, GDR_GTAB(n), sigb != 0);
+                if (lw == 0) gate_table<DK, NW>(la, bb, len, lane, GDR_GTAB(n), gflags);
                 if (n + 1 < NT) {
                     const int len1 = GDR_LEN(n + 1);
                     const int64_t go = GDR_ROW0(n + 1) + (int64_t)(lane < len1 ? lane : len1 - 1) * H;
@@ -1481,7 +1483,7 @@ hipError_t launch_fused(const ChunkArgs& a) {
                        a.stream,
                        (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, a.log_alpha, a.beta,
                        a.S0, (__bf16*)a.o, a.S_T, a.T, (int)a.H, NT, (int)a.dv,
-                       (a.prologue & kPrologueBetaSigmoid) ? 1 : 0);
+                       (int)(a.prologue & kPrologueGates));
     return hipGetLastError();
 }
 

@@ -34,8 +34,10 @@ struct DecodeMultiArgs {
     hipStream_t stream;
 };
 
-// Gate prologue flags (in-kernel L2 normalisation of q and k, beta from logits).
-constexpr unsigned kPrologueL2NormQK = 1u, kPrologueBetaSigmoid = 2u;
+// Gate prologue flags (in-kernel L2 normalisation of q and k, beta and the
+// log decay from their logits).
+constexpr unsigned kPrologueL2NormQK = 1u, kPrologueBetaSigmoid = 2u, kPrologueDecaySoftplus = 4u;
+constexpr unsigned kPrologueGates = kPrologueBetaSigmoid | kPrologueDecaySoftplus;
 
 struct ChunkArgs {
     const void *q, *k, *v;
@@ -46,7 +48,7 @@ struct ChunkArgs {
     bool bf16, channel;
     void* ws;
     hipStream_t stream;
-    unsigned prologue = 0;   // kPrologue* flags; only the bf16 paths with a fused prologue accept them
+    unsigned prologue = 0;   // kPrologue* flags (fused into the loads, or a staging pass first)
 };
 
 hipError_t decode_step_launch(const DecodeArgs& a);
@@ -60,8 +62,14 @@ hipError_t chunk_fwd_launch(const ChunkArgs& a);
 // Device address of the fixed scratch array (GDR_NOALLOC_SCRATCH_BYTES) on the
 // device of `stream`; looked up on the first call per device, then cached.
 hipError_t noalloc_scratch(hipStream_t stream, void** out);
-// Which chunk calls take the gate prologue (fused into their loads).
-bool prologue_supported(int64_t chunk, bool bf16, bool channel);
+// Which chunk calls fuse the gate prologue into their loads; the others run
+// it as a separate pass into the workspace, which grows by
+// prologue_stage_bytes then.
+bool prologue_fused(int64_t chunk, bool bf16, bool channel);
+size_t prologue_stage_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, bool bf16, bool channel,
+                            unsigned flags);
+size_t chunk_prologue_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t chunk,
+                                      bool bf16, bool channel, unsigned flags);
 
 // Single-kernel path (bf16, scalar gate, 64-token chunks): needs no workspace.
 bool fused_chunk_supported(int64_t dk, int64_t chunk, bool bf16, bool channel);

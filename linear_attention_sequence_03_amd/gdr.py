@@ -18,13 +18,13 @@ LIBRARY_PATH = os.path.join(_PKG, "libgdr.so")
 GDR_OK, GDR_ERR_INVALID_ARG, GDR_ERR_UNSUPPORTED, GDR_ERR_HIP = 0, 1, 2, 3
 GDR_F32, GDR_BF16 = 0, 1
 GDR_GATE_SCALAR, GDR_GATE_CHANNEL = 0, 1
-GDR_PROLOGUE_L2NORM_QK, GDR_PROLOGUE_BETA_SIGMOID = 1, 2
+GDR_PROLOGUE_L2NORM_QK, GDR_PROLOGUE_BETA_SIGMOID, GDR_PROLOGUE_DECAY_SOFTPLUS = 1, 2, 4
 GDR_NOALLOC_SCRATCH_BYTES = 64 << 20   # the fixed scratch of gdr_chunk_fwd_noalloc
 
 # Every symbol include/gdr.h declares.
 EXPORTS = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_chunk_fwd_noalloc",
            "gdr_decode_step", "gdr_decode_multi",
-           "gdr_chunk_fwd_prologue", "gdr_decode_step_prologue",
+           "gdr_chunk_fwd_prologue", "gdr_chunk_fwd_prologue_workspace_size", "gdr_decode_step_prologue",
            "gdr_fg2_chunk_fwd_workspace_size", "gdr_fg2_chunk_fwd", "gdr_fg2_decode_step",
            "gdr_gdn2_fwd", "gdr_gdn2_chunk_fwd_workspace_size", "gdr_gdn2_chunk_fwd",
            "gdr_status_string", "gdr_last_error")
@@ -70,6 +70,9 @@ def load_library(path: Optional[str] = None):
                                            i64, i64, i64, i64, i64, i64, f, f,
                                            vp, ctypes.c_size_t, ctypes.c_uint, vp]
     lib.gdr_chunk_fwd_prologue.restype = f
+    lib.gdr_chunk_fwd_prologue_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64, f, f,
+                                                          ctypes.c_uint, ctypes.POINTER(ctypes.c_size_t)]
+    lib.gdr_chunk_fwd_prologue_workspace_size.restype = f
     lib.gdr_decode_step_prologue.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp,
                                              i64, i64, i64, i64, f, f, ctypes.c_uint, vp]
     lib.gdr_decode_step_prologue.restype = f
@@ -150,6 +153,15 @@ def gdr_chunk_fwd_workspace_size(B, T, H, dk, dv, chunk, io, gate) -> int:
     return int(out.value)
 
 
+def gdr_chunk_fwd_prologue_workspace_size(B, T, H, dk, dv, chunk, io, gate, flags) -> int:
+    out = ctypes.c_size_t(0)
+    st = load_library().gdr_chunk_fwd_prologue_workspace_size(B, T, H, dk, dv, chunk, io, gate,
+                                                              int(flags), ctypes.byref(out))
+    if st != GDR_OK:
+        _raise(st)
+    return int(out.value)
+
+
 def _chunk_io(q, k, v, log_alpha, beta, S0, o, S_T, want_state):
     """Check the prefill tensors; allocate o and S_T when not given."""
     import torch
@@ -181,12 +193,12 @@ def gdr_chunk_fwd(q, k, v, log_alpha, beta, S0=None, chunk: int = 64, o=None, S_
     log_alpha: [B,T,H] (scalar gate) or [B,T,H,dk] (channel gate), fp32;
     beta: [B,T,H] fp32; S0: [B,H,dv,dk] fp32 or None.
     Returns (o [B,T,H,dv] in the io dtype, S_T [B,H,dv,dk] fp32 or None).
-    ``prologue`` (GDR_PROLOGUE_* flags) normalises q, k and / or maps beta
-    logits through a sigmoid inside the kernels."""
+    ``prologue`` (GDR_PROLOGUE_* flags) normalises q, k and / or maps beta and
+    decay logits inside the library."""
     import torch
     (B, T, H, dk, dv, io, gate), o, S_T = _chunk_io(q, k, v, log_alpha, beta, S0, o, S_T, want_state)
     dev = q.device
-    nbytes = gdr_chunk_fwd_workspace_size(B, T, H, dk, dv, chunk, io, gate)
+    nbytes = gdr_chunk_fwd_prologue_workspace_size(B, T, H, dk, dv, chunk, io, gate, prologue)
     if workspace is None and nbytes > 0:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

@@ -139,16 +139,21 @@ def gdn2_gates(B, T, H, dk, dv, seed=0):
     return b, w
 
 
-def raw_prologue_inputs(inp, io="bf16", seed=0):
+def raw_prologue_inputs(inp, io="bf16", seed=0, decay_logits=False):
     """Raw inputs for the gate prologue from a workload's inputs: q and k rows
     scaled by factors U(1, 8) per token and head (then stored in the io type),
-    beta replaced by logits N(0, 1.5^2).  Own seeded stream."""
+    beta replaced by logits N(0, 1.5^2).  With ``decay_logits`` log_alpha
+    (same shape) is replaced by decay logits U(-8, 2): alpha = 1 / (1 + e^x)
+    from 0.9997 (x = -8) down to 0.12 (x = 2), the workloads' range of weak
+    decays plus strong ones.  Own seeded stream."""
     rng = np.random.Generator(np.random.PCG64(seed + 9000))
     out = dict(inp)
     for n in ("q", "k"):
         x = inp[n].astype(np.float64)
         out[n] = _store(x * rng.uniform(1.0, 8.0, x.shape[:-1] + (1,)), io)
     out["beta"] = (rng.standard_normal(inp["beta"].shape) * 1.5).astype(np.float32)
+    if decay_logits:
+        out["log_alpha"] = rng.uniform(-8.0, 2.0, inp["log_alpha"].shape).astype(np.float32)
     return out
 
 

@@ -132,14 +132,39 @@ def _chunk_pro(lib, flags, q=0, k=1, v=2, la=3, be=4, o=6, st=7, ws=8, B=1, T=12
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(flags=4), 1), (dict(flags=1 << 31), 1),              # unknown flags
-    (dict(flags=1, io=0), 2),                                   # fp32 io: not fused
-    (dict(flags=3, chunk=32), 2), (dict(flags=2, chunk=16), 2),  # scalar gate, chunk != 64
+    (dict(flags=8), 1), (dict(flags=1 << 31), 1),              # unknown flags
+    # staged calls (fp32 io, scalar chunk 16 / 32) need the prologue workspace
+    (dict(flags=1, io=0, wsbytes=4096), 1), (dict(flags=7, chunk=32, wsbytes=4096), 1),
+    (dict(flags=4, chunk=16, ws=None), 1),
     (dict(flags=1, q=None), 1),                                 # the plain checks still run
 ])
 def test_chunk_fwd_prologue_rejects(lib, kw, code):
     assert _chunk_pro(lib, **kw) == code
     assert lib.gdr_last_error()
+
+
+def test_prologue_workspace_size():
+    F32, BF16, SC, CH = gdr.GDR_F32, gdr.GDR_BF16, gdr.GDR_GATE_SCALAR, gdr.GDR_GATE_CHANNEL
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    B, T, H, d = 2, 100, 3, 64
+    rows = B * T * H
+    # fused calls: the plain size whatever the flags
+    for io, gate, c in ((BF16, SC, 64), (BF16, CH, 16), (BF16, CH, 64)):
+        plain = gdr.gdr_chunk_fwd_workspace_size(B, T, H, d, d, c, io, gate)
+        for f in (0, 1, 2, 4, 7):
+            assert gdr.gdr_chunk_fwd_prologue_workspace_size(B, T, H, d, d, c, io, gate, f) == plain
+    # staged calls: plain + the mapped tensors, each 256-byte aligned
+    for io, gate, c, es in ((F32, SC, 64, 4), (F32, CH, 32, 4), (BF16, SC, 16, 2)):
+        plain = gdr.gdr_chunk_fwd_workspace_size(B, T, H, d, d, c, io, gate)
+        la = rows * (d if gate == CH else 1) * 4
+        want = {0: plain, 1: al(plain) + 2 * al(rows * d * es), 2: al(plain) + al(rows * 4),
+                4: al(plain) + al(la), 7: al(plain) + 2 * al(rows * d * es) + al(rows * 4) + al(la)}
+        for f, w in want.items():
+            assert gdr.gdr_chunk_fwd_prologue_workspace_size(B, T, H, d, d, c, io, gate, f) == w, (io, c, f)
+    with pytest.raises(gdr.GdrError):
+        gdr.gdr_chunk_fwd_prologue_workspace_size(B, T, H, d, d, 64, F32, SC, 8)
+    # T = 0 stages nothing
+    assert gdr.gdr_chunk_fwd_prologue_workspace_size(B, 0, H, d, d, 64, F32, SC, 7) == 0
 
 
 def test_decode_step_prologue_rejects(lib):

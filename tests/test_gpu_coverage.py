@@ -7,7 +7,8 @@ Wide shapes.  Each chunkwise launcher runs two compute waves per
    length, and every element is compared with the oracle:
      - gdr_chunk_fwd: both gates, both io types, chunks 16 / 32 / 64, d 64 / 128
        (the fused kernel, and state_pass after each prep kernel);
-     - gdr_chunk_fwd_prologue on every fused route (fused kernel, channel prep);
+     - gdr_chunk_fwd_prologue (all three maps) on every fused route (fused
+       kernel, channel prep) and on staged ones (fp32 io, scalar chunk 16);
      - gdr_fg2_chunk_fwd and gdr_gdn2_chunk_fwd.
 
 Metric: normwise max|gpu - oracle| / max|oracle| per (b, h) head, separately
@@ -61,21 +62,23 @@ def test_wide_chunk_fwd(io, gate, chunk, d):
     check_all_heads("chunk_fwd %s %s C=%d d=%d" % (io, gate, chunk, d), o, st, o_ref, st_ref, TOL[io])
 
 
-PROLOGUE_CASES = [("scalar", 64), ("channel", 16), ("channel", 32), ("channel", 64)]
+PROLOGUE_CASES = [("bf16", "scalar", 64), ("bf16", "channel", 16), ("bf16", "channel", 32),
+                  ("bf16", "channel", 64), ("bf16", "scalar", 16), ("f32", "scalar", 32),
+                  ("f32", "channel", 64)]
 
 
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("gate,chunk", PROLOGUE_CASES)
-def test_wide_prologue(gate, chunk, d):
-    from linear_attention_sequence_03_amd.gdr import GDR_PROLOGUE_BETA_SIGMOID, GDR_PROLOGUE_L2NORM_QK
-    inp = synth.chunk_inputs(B_WIDE, T_WIDE, H_WIDE, d, d, gate, "bf16", seed=400 + d + chunk,
-                             s0_std=0.1)
-    raw = synth.raw_prologue_inputs(inp, "bf16", seed=401)
-    flags = GDR_PROLOGUE_L2NORM_QK | GDR_PROLOGUE_BETA_SIGMOID
-    o, st = gpu_chunk(raw, "bf16", chunk=chunk, prologue=flags)
+@pytest.mark.parametrize("io,gate,chunk", PROLOGUE_CASES)
+def test_wide_prologue(io, gate, chunk, d):
+    from linear_attention_sequence_03_amd.gdr import (GDR_PROLOGUE_BETA_SIGMOID, GDR_PROLOGUE_DECAY_SOFTPLUS,
+                                                      GDR_PROLOGUE_L2NORM_QK)
+    inp = synth.chunk_inputs(B_WIDE, T_WIDE, H_WIDE, d, d, gate, io, seed=400 + d + chunk, s0_std=0.1)
+    raw = synth.raw_prologue_inputs(inp, io, seed=401, decay_logits=True)
+    flags = GDR_PROLOGUE_L2NORM_QK | GDR_PROLOGUE_BETA_SIGMOID | GDR_PROLOGUE_DECAY_SOFTPLUS
+    o, st = gpu_chunk(raw, io, chunk=chunk, prologue=flags)
     o_ref, st_ref = oracle.chunk_fwd_prologue(raw["q"], raw["k"], raw["v"], raw["log_alpha"],
                                               raw["beta"], raw["S0"], flags=flags)
-    check_all_heads("prologue %s C=%d d=%d" % (gate, chunk, d), o, st, o_ref, st_ref, TOL["bf16"])
+    check_all_heads("prologue %s %s C=%d d=%d" % (io, gate, chunk, d), o, st, o_ref, st_ref, TOL[io])
 
 
 @pytest.mark.parametrize("d", [64, 128])

@@ -1,6 +1,8 @@
-"""GPU parity of the gate prologue (L2-normalised q and k, beta from logits,
-fused into the kernels' loads) against the oracle's prologue, through the C
-ABI.  Inputs are raw: q and k rows of norm 1..8, beta as logits."""
+"""GPU parity of the gate prologue (L2-normalised q and k, beta and the log
+decay from their logits) against the oracle's prologue, through the C ABI.
+Inputs are raw: q and k rows of norm 1..8, beta as logits, decay logits
+U(-8, 2).  The bf16 calls with chunk 64 (scalar gate) or the channel gate fold
+the maps into their kernels' loads; the other calls run the staging pass."""
 import numpy as np
 import pytest
 
@@ -11,6 +13,7 @@ import oracle
 pytestmark = pytest.mark.gpu
 
 TOL = {"f32": 1e-4, "bf16": 2e-2}
+ALL = 7
 
 
 def _call(inp, io, chunk, flags):
@@ -29,23 +32,38 @@ def _ref(inp, flags):
                                      inp["S0"], flags=flags)
 
 
-@pytest.mark.parametrize("flags", [1, 2, 3])
-@pytest.mark.parametrize("gate,chunk,d,H", [("scalar", 64, 128, 3), ("scalar", 64, 64, 3),
-                                            ("scalar", 64, 128, 40),     # two compute waves
-                                            ("channel", 64, 128, 3), ("channel", 32, 64, 3),
-                                            ("channel", 16, 128, 2)])
-def test_prologue_chunk(gate, chunk, d, H, flags):
-    base = synth.chunk_inputs(2, 170, H, d, d, gate, "bf16", seed=300 + d + chunk + H, s0_std=0.1)
-    inp = synth.raw_prologue_inputs(base, "bf16", seed=300 + flags)
-    if not flags & 1:            # without the normalisation the keys must already be unit rows
+def _raw(base, io, seed, flags):
+    """Raw inputs for the mapped quantities only; the rest stay as the plain
+    call takes them (unit keys, beta in (0, 1), log decays)."""
+    inp = synth.raw_prologue_inputs(base, io, seed=seed, decay_logits=True)
+    if not flags & 1:
         inp["q"], inp["k"] = base["q"], base["k"]
     if not flags & 2:
         inp["beta"] = base["beta"]
-    o, st = _call(inp, "bf16", chunk, flags)
+    if not flags & 4:
+        inp["log_alpha"] = base["log_alpha"]
+    return inp
+
+
+FUSED = [("bf16", "scalar", 64, 128, 3), ("bf16", "scalar", 64, 64, 3),
+         ("bf16", "scalar", 64, 128, 40),     # two compute waves
+         ("bf16", "channel", 64, 128, 3), ("bf16", "channel", 32, 64, 3), ("bf16", "channel", 16, 128, 2)]
+STAGED = [("bf16", "scalar", 16, 128, 3), ("bf16", "scalar", 32, 64, 3),
+          ("f32", "scalar", 64, 128, 3), ("f32", "scalar", 16, 64, 2),
+          ("f32", "channel", 64, 64, 3), ("f32", "channel", 32, 128, 2)]
+
+
+@pytest.mark.parametrize("flags", [1, 2, 3, 4, 7])
+@pytest.mark.parametrize("io,gate,chunk,d,H", FUSED + STAGED)
+def test_prologue_chunk(io, gate, chunk, d, H, flags):
+    base = synth.chunk_inputs(2, 170, H, d, d, gate, io, seed=300 + d + chunk + H, s0_std=0.1)
+    inp = _raw(base, io, 300 + flags, flags)
+    o, st = _call(inp, io, chunk, flags)
     o_ref, st_ref = _ref(inp, flags)
     eo, es = rel_err(host(o), o_ref), rel_err(host(st), st_ref)
-    print("gate=%s chunk=%d d=%d H=%d flags=%d err_o=%.3g err_S=%.3g" % (gate, chunk, d, H, flags, eo, es))
-    assert eo <= TOL["bf16"] and es <= TOL["bf16"], (eo, es)
+    print("io=%s gate=%s chunk=%d d=%d H=%d flags=%d err_o=%.3g err_S=%.3g"
+          % (io, gate, chunk, d, H, flags, eo, es))
+    assert eo <= TOL[io] and es <= TOL[io], (eo, es)
 
 
 def test_prologue_zero_flags_is_the_plain_call():
@@ -61,11 +79,29 @@ def test_prologue_zero_flags_is_the_plain_call():
 
 
 @pytest.mark.parametrize("io,gate,chunk", [("f32", "scalar", 64), ("bf16", "scalar", 32)])
-def test_prologue_unfused_paths_are_refused(io, gate, chunk):
-    inp = synth.chunk_inputs(1, 40, 2, 64, 64, gate, io, seed=311)
+def test_prologue_staged_workspace(io, gate, chunk):
+    """The staging pass lives in the workspace: the plain size is refused, the
+    prologue size runs (and grows by the mapped tensors only)."""
+    from linear_attention_sequence_03_amd import gdr_chunk_fwd
+    B, T, H, d = 1, 40, 2, 64
+    iod = gdr.GDR_F32 if io == "f32" else gdr.GDR_BF16
+    plain = gdr.gdr_chunk_fwd_workspace_size(B, T, H, d, d, chunk, iod, gdr.GDR_GATE_SCALAR)
+    sizes = {f: gdr.gdr_chunk_fwd_prologue_workspace_size(B, T, H, d, d, chunk, iod, gdr.GDR_GATE_SCALAR, f)
+             for f in (0, 1, 2, 4, 7)}
+    assert sizes[0] == plain and sizes[1] > sizes[2] > plain and sizes[4] == sizes[2]
+    torch = torch_mod()
+    base = synth.chunk_inputs(B, T, H, d, d, gate, io, seed=311)
+    inp = _raw(base, io, 311, ALL)
+    dt = io_dtype(io)
+    args = [dev(inp["q"], dt), dev(inp["k"], dt), dev(inp["v"], dt), dev(inp["log_alpha"]), dev(inp["beta"])]
+    small = torch.empty(max(plain, 16), dtype=torch.uint8, device="cuda")
     with pytest.raises(gdr.GdrError) as e:
-        _call(inp, io, chunk, 1)
-    assert e.value.status == gdr.GDR_ERR_UNSUPPORTED
+        gdr_chunk_fwd(*args, chunk=chunk, workspace=small, prologue=ALL)
+    assert e.value.status == gdr.GDR_ERR_INVALID_ARG
+    o, st = gdr_chunk_fwd(*args, chunk=chunk, prologue=ALL)
+    torch.cuda.synchronize()
+    o_ref, st_ref = _ref(inp, ALL)
+    assert rel_err(host(o), o_ref) <= TOL[io] and rel_err(host(st), st_ref) <= TOL[io]
 
 
 @pytest.mark.parametrize("gate", ["scalar", "channel"])
@@ -73,28 +109,29 @@ def test_prologue_unfused_paths_are_refused(io, gate, chunk):
 def test_prologue_decode(io, d, gate):
     from linear_attention_sequence_03_amd import gdr_decode_step
     torch = torch_mod()
-    base = synth.decode_inputs(8, 4, d, d, gate, io, seed=320 + d)
-    inp = synth.raw_prologue_inputs(base, io, seed=320)
-    dt = io_dtype(io)
-    o, S1 = gdr_decode_step(dev(inp["q"], dt), dev(inp["k"], dt), dev(inp["v"], dt),
-                            dev(inp["log_alpha"]), dev(inp["beta"]), dev(inp["S"]), prologue=3)
-    torch.cuda.synchronize()
-    o_ref, S_ref = oracle.decode_step_prologue(inp["q"], inp["k"], inp["v"], inp["log_alpha"],
-                                               inp["beta"], inp["S"], flags=3)
-    assert rel_err(host(o), o_ref) <= (4e-3 if io == "bf16" else 1e-5)
-    assert rel_err(host(S1), S_ref) <= 1e-5
+    for flags in (3, 4, 7):
+        base = synth.decode_inputs(8, 4, d, d, gate, io, seed=320 + d)
+        inp = _raw(base, io, 320, flags)
+        dt = io_dtype(io)
+        o, S1 = gdr_decode_step(dev(inp["q"], dt), dev(inp["k"], dt), dev(inp["v"], dt),
+                                dev(inp["log_alpha"]), dev(inp["beta"]), dev(inp["S"]), prologue=flags)
+        torch.cuda.synchronize()
+        o_ref, S_ref = oracle.decode_step_prologue(inp["q"], inp["k"], inp["v"], inp["log_alpha"],
+                                                   inp["beta"], inp["S"], flags=flags)
+        assert rel_err(host(o), o_ref) <= (4e-3 if io == "bf16" else 1e-5), flags
+        assert rel_err(host(S1), S_ref) <= 1e-5, flags
 
 
 def test_prologue_full_size_headline_shape():
     """The Gated DeltaNet prefill workload's shape (B=4, H=16, T=4096, d=128,
     bf16) from raw inputs; sampled (b,h) pairs against the oracle."""
     w = synth.WORKLOADS[1]
-    inp = synth.raw_prologue_inputs(synth.workload_inputs(w), "bf16", seed=w.seed)
-    o, st = _call(inp, "bf16", 64, 3)
+    inp = synth.raw_prologue_inputs(synth.workload_inputs(w), "bf16", seed=w.seed, decay_logits=True)
+    o, st = _call(inp, "bf16", 64, ALL)
     o, st = host(o), host(st)
     for b, h in [(0, 0), (3, 15), (2, 9)]:
         sl = lambda a: None if a is None else a[b:b + 1, :, h:h + 1]  # noqa: E731
         o_ref, st_ref = oracle.chunk_fwd_prologue(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]),
-                                                  sl(inp["log_alpha"]), sl(inp["beta"]), None, flags=3)
+                                                  sl(inp["log_alpha"]), sl(inp["beta"]), None, flags=ALL)
         assert rel_err(o[b, :, h], o_ref[0, :, 0]) <= TOL["bf16"]
         assert rel_err(st[b, h], st_ref[0, 0]) <= TOL["bf16"]
