@@ -55,9 +55,31 @@ struct WsLayout {
     //   scalar gate : gam[C] = exp(g_r), gh[C] = exp(g_last - g_r)
     //   channel gate: gl[DK] = exp(g_last,c)
     static constexpr size_t VEC = CHANNEL ? KH + (size_t)C * DK * sizeof(E) : QG;
-    static constexpr size_t VEC_BYTES = CHANNEL ? DK * 4 : 2 * C * 4;
-    static constexpr size_t BYTES = (VEC + VEC_BYTES + 255) / 256 * 256;
+    static constexpr size_t VEC_DATA = CHANNEL ? DK * 4 : 2 * C * 4;
+    // bf16: T may travel as a hi/lo pair.  FLAG (int, after the decay vector,
+    // copied with it) says whether this chunk's TL = T - bf16(T) was written
+    // and is to be applied; TL is read from global memory only then.
+    static constexpr bool PAIR = sizeof(E) == 2;
+    static constexpr size_t FLAG = VEC + VEC_DATA;
+    static constexpr size_t VEC_BYTES = VEC_DATA + (PAIR ? 16 : 0);
+    static constexpr size_t TL = VEC + VEC_BYTES;                     // E [C][C] (bf16)
+    static constexpr size_t BYTES = ((PAIR ? TL + (size_t)C * C * sizeof(E) : VEC + VEC_BYTES) + 255) / 256 * 256;
+    static constexpr size_t WARM_BYTES = PAIR ? TL : BYTES;           // read by every state pass
 };
+
+// A chunk applies T as a bf16 pair when some entry of its strictly lower A
+// exceeds this in magnitude (keys nearly repeated or opposed with a write rate
+// near 1 and weak decay): T then holds entries of size ~1 whose row sums are
+// small, and a single bf16 rounding of T loses them.
+constexpr float kPairThresh = 0.5f;
+
+// Store x as E at hi[i]; with a residual buffer, also x - E(x) at lo[i].
+template <typename E>
+__device__ __forceinline__ void put_pair(E* hi, E* lo, int i, float x) {
+    const E h = from_f32<E>(x);
+    hi[i] = h;
+    if (lo) lo[i] = from_f32<E>(x - to_f32(h));
+}
 
 // Copy a [ROWS][COLS] tile of E from global (row stride gstride elements) into
 // LDS (row stride ls elements) through registers; rows >= valid are zero.
@@ -186,7 +208,7 @@ __device__ __forceinline__ void g2s_pair(E* d0, E* d1, int ls, const E* s0, cons
 // on fp32 16x16x4 MFMAs, each new tile feeding the next product as its B
 // operand, and stores T_ij = X_ij Diag(beta_j) straight from the accumulators.
 template <typename E, int C>
-__device__ __forceinline__ void solve_store_T(const float* Ablk, float* Xd, const float* bs, E* Tw,
+__device__ __forceinline__ void solve_store_T(const float* Ablk, float* Xd, const float* bs, E* Tw, E* Tl,
                                               int tid) {
     constexpr int NB = C / 16;
     using MF = Mma<float>;
@@ -216,13 +238,13 @@ __device__ __forceinline__ void solve_store_T(const float* Ablk, float* Xd, cons
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int r = 4 * g4 + e;
-        Tw[(16 * j + r) * C + 16 * j + col] = from_f32<E>(Xd[j * kTS + r * 17 + col] * bcol);
+        put_pair<E>(Tw, Tl, (16 * j + r) * C + 16 * j + col, Xd[j * kTS + r * 17 + col] * bcol);
     }
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
         if (i < j)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) Tw[(16 * i + 4 * g4 + e) * C + 16 * j + col] = from_f32<E>(0.f);
+            for (int e = 0; e < 4; ++e) put_pair<E>(Tw, Tl, (16 * i + 4 * g4 + e) * C + 16 * j + col, 0.f);
     }
     f32x4 X[NB];
 #pragma unroll
@@ -247,7 +269,7 @@ __device__ __forceinline__ void solve_store_T(const float* Ablk, float* Xd, cons
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             X[i][e] = -Z[e];
-            Tw[(16 * i + 4 * g4 + e) * C + 16 * j + col] = from_f32<E>(-Z[e] * bcol);
+            put_pair<E>(Tw, Tl, (16 * i + 4 * g4 + e) * C + 16 * j + col, -Z[e] * bcol);
         }
     }
 }
@@ -286,9 +308,11 @@ __global__ __launch_bounds__(kThreads) void wy_prep_scalar(
     __shared__ float Ablk[NB * (NB + 1) / 2 * kTS];
     __shared__ float Xd[NB * kTS];
     __shared__ float gs[C], bs[C];
+    __shared__ int pair_sh;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g4 = lane >> 4, col = lane & 15;
+    if (tid == 0) pair_sh = 0;
     const int64_t bid = blockIdx.x;
     const int n = (int)(bid % NT);
     const int64_t bh = bid / NT;
@@ -321,6 +345,7 @@ __global__ __launch_bounds__(kThreads) void wy_prep_scalar(
     // P = Q K^T (gated, lower incl. diagonal) straight to the workspace.
     const int pr = wave >> 1;
     const bool isP = wave & 1;
+    float amax = 0.f;   // largest |A| entry this wave computed
     if (pr < (NB + 1) / 2) {
         const E* Ap = isP ? Qs : Ks;
 #pragma unroll
@@ -348,22 +373,30 @@ __global__ __launch_bounds__(kThreads) void wy_prep_scalar(
                     const int r = 16 * rb + 4 * g4 + e;
                     const bool keep = isP ? (c <= r) : (c < r);
                     const float dec = keep ? fast_exp(gs[r] - gc) : 0.f;
-                    if (isP)
+                    if (isP) {
                         Pw[r * C + c] = from_f32<E>(acc[e] * dec);
-                    else
-                        Ablk[ablk(r, c)] = acc[e] * bs[r] * dec;
+                    } else {
+                        const float a = acc[e] * bs[r] * dec;
+                        Ablk[ablk(r, c)] = a;
+                        amax = fmaxf(amax, fabsf(a));
+                    }
                 }
             }
         }
     }
+    if constexpr (L::PAIR)
+        if (__ballot(amax > kPairThresh) != 0 && lane == 0) pair_sh = 1;
     __syncthreads();
 
-    solve_store_T<E, C>(Ablk, Xd, bs, Tw, tid);
+    const bool pair = L::PAIR && pair_sh != 0;
+    solve_store_T<E, C>(Ablk, Xd, bs, Tw, pair ? reinterpret_cast<E*>(blk + L::TL) : nullptr, tid);
     float* vec = reinterpret_cast<float*>(blk + L::VEC);
     if (tid < C) {
         vec[tid] = expf(gs[tid]);
         vec[C + tid] = expf(gs[C - 1] - gs[tid]);
     }
+    if constexpr (L::PAIR)
+        if (tid == 0) *reinterpret_cast<int*>(blk + L::FLAG) = pair ? 1 : 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -643,6 +676,7 @@ struct ChanPrepSmem {
     alignas(16) f32x4 tpub[NTP][64];                     // T tiles of rows < NB-1
     alignas(16) __bf16 stg[NB][16 * SR];                 // row-block staging of P, T
     alignas(16) float bsh[C];
+    int pair;                                            // T travels as a bf16 pair
 };
 
 // The work of wave BW (16-row block BW).  The block index is a compile-time
@@ -683,6 +717,7 @@ __device__ __forceinline__ void chan_prep_wave(ChanPrepSmem<DK, C>& sm, const __
     const int64_t row0 = (bi * T + t0) * H + h;
     uint8_t* blk = ws + (size_t)bid * L::BYTES;
 
+    if (b == 0 && lane == 0) sm.pair = 0;   // set below by any wave whose A needs the pair
     const int r = 16 * b + x;
     const bool valid = r < len;   // rows past len read row len-1 and are zeroed
     const int64_t grow = row0 + (int64_t)(valid ? r : len - 1) * H;
@@ -921,6 +956,14 @@ __device__ __forceinline__ void chan_prep_wave(ChanPrepSmem<DK, C>& sm, const __
             ga[cb][e] = (cb < b || (cb == b && y < x)) ? ga[cb][e] * be : 0.f;
             gp[cb][e] = (cb < b || (cb == b && y <= x)) ? gp[cb][e] : 0.f;
         }
+    {
+        float amax = 0.f;
+#pragma unroll
+        for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fabsf(ga[cb][e]));
+        if (__ballot(amax > kPairThresh) != 0 && lane == 0) sm.pair = 1;
+    }
 
     // ---- P: row block b through the staging tile to the workspace ----
     __bf16* sb = stg[b];
@@ -1009,21 +1052,33 @@ __device__ __forceinline__ void chan_prep_wave(ChanPrepSmem<DK, C>& sm, const __
         }
     }
 
-    // ---- T: row block b through the staging tile to the workspace ----
+    // ---- T (and, when any wave flagged the chunk, its bf16 residual TL):
+    //      row block b through the staging tile to the workspace ----
+    __syncthreads();   // every wave's flag is in
+    const bool pair = sm.pair != 0;
 #pragma unroll
-    for (int j = 0; j < NB; ++j)
+    for (int half = 0; half < 2; ++half) {
+        if (half == 1 && !pair) break;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sb[(4 * kg + e) * SR + 16 * j + x] = (__bf16)tt[j][e];
-    __builtin_amdgcn_wave_barrier();
-    uint8_t* Tw = blk + L::T + (size_t)(16 * b) * C * sizeof(__bf16);
+        for (int j = 0; j < NB; ++j)
 #pragma unroll
-    for (int i = 0; i < (NPC + 63) / 64; ++i) {
-        const int p = lane + 64 * i;
-        if (p < NPC) {
-            const int rr = p / (C / 8), pc = p % (C / 8);
-            *reinterpret_cast<V16*>(Tw + (size_t)p * 16) = *reinterpret_cast<const V16*>(sb + rr * SR + 8 * pc);
+            for (int e = 0; e < 4; ++e) {
+                const __bf16 hi = (__bf16)tt[j][e];
+                sb[(4 * kg + e) * SR + 16 * j + x] = half == 0 ? hi : (__bf16)(tt[j][e] - (float)hi);
+            }
+        __builtin_amdgcn_wave_barrier();
+        uint8_t* Tw = blk + (half == 0 ? L::T : L::TL) + (size_t)(16 * b) * C * sizeof(__bf16);
+#pragma unroll
+        for (int i = 0; i < (NPC + 63) / 64; ++i) {
+            const int p = lane + 64 * i;
+            if (p < NPC) {
+                const int rr = p / (C / 8), pc = p % (C / 8);
+                *reinterpret_cast<V16*>(Tw + (size_t)p * 16) = *reinterpret_cast<const V16*>(sb + rr * SR + 8 * pc);
+            }
         }
+        __builtin_amdgcn_wave_barrier();
     }
+    if (b == 0 && lane == 0) *reinterpret_cast<int*>(blk + L::FLAG) = pair ? 1 : 0;
 }
 
 template <int DK, int C, bool NORM>
@@ -1128,7 +1183,7 @@ __device__ __forceinline__ void warm_chunk_l2(char* scratch, int n, const E* v, 
                                               int NT, int vt, int lw, int lane) {
     using L = WsLayout<E, DK, C, CHANNEL>;
     using SL = StageLayout<E, DK, C, NW, CHANNEL>;
-    constexpr int NLINES = (int)((L::BYTES + 127) / 128);
+    constexpr int NLINES = (int)((L::WARM_BYTES + 127) / 128);
     constexpr int NVT = DK / SL::VT;
     constexpr int PER = (NLINES + NVT - 1) / NVT;
     constexpr int ROUNDS = (PER + SL::NL * 64 - 1) / (SL::NL * 64);
@@ -1190,6 +1245,7 @@ __global__ __launch_bounds__(64 * (NW + 2)) __attribute__((amdgpu_waves_per_eu(1
     const float* __restrict__ S0, E* __restrict__ o, float* __restrict__ ST,
     const uint8_t* __restrict__ ws, int64_t T, int H, int NT, int DV) {
     using SL = StageLayout<E, DK, C, NW, CHANNEL>;
+    using L = WsLayout<E, DK, C, CHANNEL>;
     using M = Mma<E>;
     using frag = typename M::frag;
     using DQ = DmaTile<C, DK * sizeof(E), SL::NL>;    // Q, K (and Kh) tiles
@@ -1363,6 +1419,24 @@ __global__ __launch_bounds__(64 * (NW + 2)) __attribute__((amdgpu_waves_per_eu(1
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) D[mt] = M::mma(tf[mt][s], rb[s], D[mt]);
         }
+        // Chunks the prep flagged: D += TL R, TL = T - bf16(T) read from the
+        // workspace (rare; the flag sits after the decay vector in the stage).
+        int pair = 0;
+        if constexpr (L::PAIR) {
+            pair = __builtin_amdgcn_readfirstlane(*reinterpret_cast<const int*>(st + SL::OVEC + L::VEC_DATA));
+            if (pair) {
+                const E* TLg = reinterpret_cast<const E*>(wsb + (size_t)(bh * NT + n) * L::BYTES + L::TL);
+                frag tl[MT][NKT];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int s = 0; s < NKT; ++s) tl[mt][s] = afrag_nat_tok<E, HALF>(TLg, C, 16 * mt, s, lane);
+#pragma unroll
+                for (int s = 0; s < NKT; ++s)
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) D[mt] = M::mma(tl[mt][s], rb[s], D[mt]);
+            }
+        }
 
         // Phase C: O = Oi + P D; the state update's operand Ds is kept for the
         // next iteration (scalar gate: rows scaled by gamma_last / gamma_r).
@@ -1398,6 +1472,30 @@ __global__ __launch_bounds__(64 * (NW + 2)) __attribute__((amdgpu_waves_per_eu(1
             for (int s = 0; s < NKT; ++s)
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) Oa[mt] = M::mma(pf[mt][s], db[s], Oa[mt]);
+            if constexpr (L::PAIR) {
+                if (pair) {   // O += P (D - bf16(D)): the output keeps D's low bits too
+                    f32x4 Dr[MT];
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) Dr[mt][i] = D[mt][i] - (float)(__bf16)D[mt][i];
+                    frag dl[NKT];
+#pragma unroll
+                    for (int s = 0; s < NKT; ++s) {
+                        if constexpr (HALF) {
+                            const __bf16 z = (__bf16)0.f;
+                            dl[s] = bf16x8{(__bf16)Dr[0][0], (__bf16)Dr[0][1], (__bf16)Dr[0][2], (__bf16)Dr[0][3],
+                                           z, z, z, z};
+                        } else {
+                            dl[s] = bfrag_acc<E>(Dr, s);
+                        }
+                    }
+#pragma unroll
+                    for (int s = 0; s < NKT; ++s)
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt) Oa[mt] = M::mma(pf[mt][s], dl[s], Oa[mt]);
+                }
+            }
         }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)

@@ -97,7 +97,7 @@ def test_chunk_fwd_rejects(lib, kw, code):
     (dict(q=None), 1), (dict(B=0), 1), (dict(chunk=48), 2), (dict(dk=96, dv=96), 2),
     (dict(o=ctypes.c_void_p(BASE + 4 * 1024)), 1),      # o inside q
     # workspace beyond the fixed scratch: KDA bf16 d = 128, 1024 chunk blocks of
-    # 66048 bytes (67.6 MB > 64 MiB); refused before the scratch is looked up
+    # 74496 bytes (76.3 MB > 64 MiB); refused before the scratch is looked up
     (dict(B=1, T=4096, H=16, dk=128, dv=128, io=1, gate=1), 2),
     # fp32 scalar d = 64, chunk 64: 2048 blocks, far past the scratch
     (dict(B=8, T=16384, H=16), 2),
@@ -181,11 +181,14 @@ def test_workspace_size():
         assert gdr.gdr_chunk_fwd_workspace_size(4, 4096, 16, d, d, 64, gdr.GDR_BF16,
                                                 gdr.GDR_GATE_SCALAR) == 0
     # two-kernel path, per (b,h,chunk): scalar gate = T + P (C*C each) + two
-    # decay vectors (2C floats), 256-aligned
+    # decay vectors (2C floats), 256-aligned; bf16 adds a 16-byte flag slot
+    # and the residual of T (C*C)
     n = gdr.gdr_chunk_fwd_workspace_size(4, 4096, 16, 128, 128, 32, gdr.GDR_BF16,
                                          gdr.GDR_GATE_SCALAR)
-    blk = (2 * 32 * 32 * 2 + 2 * 32 * 4 + 255) // 256 * 256
+    blk = (2 * 32 * 32 * 2 + 2 * 32 * 4 + 16 + 32 * 32 * 2 + 255) // 256 * 256
     assert n == 4 * 16 * 128 * blk
+    n = gdr.gdr_chunk_fwd_workspace_size(1, 64, 1, 128, 128, 64, gdr.GDR_BF16, gdr.GDR_GATE_CHANNEL)
+    assert n == (2 * 64 * 64 * 2 + 3 * 64 * 128 * 2 + 128 * 4 + 16 + 64 * 64 * 2 + 255) // 256 * 256
     # channel gate: three gate-scaled [C, dk] operands and dk floats instead
     n = gdr.gdr_chunk_fwd_workspace_size(1, 100, 1, 64, 64, 32, gdr.GDR_F32,
                                          gdr.GDR_GATE_CHANNEL)

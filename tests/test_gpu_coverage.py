@@ -125,6 +125,12 @@ def test_wide_gdn2_chunk(gate, d):
 #    entry above 1/2 apply T and D as bf16 pairs; the worst case measured is
 #    2.3e-2 (near-collinear keys, beta = 0.9, d = 64; a CPU emulation of the
 #    kernel's roundings gives 1.7e-2, single bf16 roundings 0.13).  Bound 3e-2.
+#  - bf16 through the prep kernels and the state pass (chunks 16 and 32, and
+#    the channel gate at every chunk): the prep flags the same chunks and
+#    writes T's bf16 residual, which the state pass applies to D and to the
+#    output.  Worst measured: 1.2e-2 (chunk 16), 1.25e-2 (chunk 32), 1.8e-2
+#    (channel gate, chunk 64); with single roundings they were 4.8e-2, 8.6e-2
+#    and 0.16.  Same bound.
 # --------------------------------------------------------------------------
 EDGE_TOL = 3e-2
 EDGE_BETAS = (1.0, 0.99, 0.9, 0.7)
@@ -147,13 +153,45 @@ def test_edge_keys_fused(kind, norm, beta, d):
                     EDGE_TOL)
 
 
+TWO_KERNEL = [("scalar", 16), ("scalar", 32), ("channel", 16), ("channel", 32), ("channel", 64)]
+
+
+def _channel(inp, d):
+    inp["log_alpha"] = np.ascontiguousarray(np.repeat(inp["log_alpha"][..., None], d, axis=-1))
+    return inp
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("gate,chunk", TWO_KERNEL)
+@pytest.mark.parametrize("kind,norm,beta", EDGE_CASES)
+def test_edge_keys_two_kernel(kind, norm, beta, gate, chunk, d):
+    inp = _edge_inputs(kind, norm, beta, d, "bf16")
+    if gate == "channel":
+        inp = _channel(inp, d)
+    o, st = gpu_chunk(inp, "bf16", chunk=chunk)
+    o_ref, st_ref = oracle.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], inp["S0"])
+    check_all_heads("edge %s |k|=%.2f beta=%.2f %s C=%d d=%d" % (kind, norm, beta, gate, chunk, d), o, st,
+                    o_ref, st_ref, EDGE_TOL)
+
+
+@pytest.mark.parametrize("gate,chunk", TWO_KERNEL)
+def test_edge_keys_two_kernel_wide(gate, chunk):
+    """Near-collinear keys through the two-compute-wave state pass."""
+    inp = _edge_inputs("near_collinear", 1.0, 0.99, 128, "bf16", B=B_WIDE, T=T_WIDE, H=H_WIDE, seed=8)
+    if gate == "channel":
+        inp = _channel(inp, 128)
+    o, st = gpu_chunk(inp, "bf16", chunk=chunk)
+    o_ref, st_ref = oracle.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], inp["S0"])
+    check_all_heads("edge wide %s C=%d" % (gate, chunk), o, st, o_ref, st_ref, EDGE_TOL)
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("gate", ["scalar", "channel"])
 @pytest.mark.parametrize("kind", synth.EDGE_KEYS)
 def test_edge_keys_fp32(kind, gate, d):
     inp = _edge_inputs(kind, 1.0, 0.99, d, "f32")
     if gate == "channel":
-        inp["log_alpha"] = np.ascontiguousarray(np.repeat(inp["log_alpha"][..., None], d, axis=-1))
+        inp = _channel(inp, d)
     o, st = gpu_chunk(inp, "f32", chunk=64)
     o_ref, st_ref = oracle.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], inp["S0"])
     check_all_heads("edge fp32 %s %s d=%d" % (kind, gate, d), o, st, o_ref, st_ref, TOL["f32"])

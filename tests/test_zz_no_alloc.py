@@ -59,7 +59,7 @@ def test_noalloc_matches_chunk_fwd(io, gate, chunk, d):
 def test_noalloc_rejects_requests_beyond_the_scratch():
     torch = torch_mod()
     from linear_attention_sequence_03_amd import gdr
-    # KDA, bf16, d = 128, chunk 64: 66048 bytes per (b, h, chunk) block, so
+    # KDA, bf16, d = 128, chunk 64: 74496 bytes per (b, h, chunk) block, so
     # 1024 blocks pass the 64 MiB limit; nothing is launched
     B, T, H, d = 1, 64 * 64, 16, 128
     need = gdr.gdr_chunk_fwd_workspace_size(B, T, H, d, d, 64, gdr.GDR_BF16, gdr.GDR_GATE_CHANNEL)
@@ -77,3 +77,23 @@ def test_noalloc_rejects_requests_beyond_the_scratch():
                                       dev(x["log_alpha"]), dev(x["beta"]))
     torch.cuda.synchronize()
     assert np.isfinite(host(o)).all() and np.isfinite(host(st)).all()
+
+
+@pytest.mark.parametrize("gate,chunk", [("channel", 64), ("scalar", 16)])
+def test_noalloc_after_flagged_chunks(gate, chunk):
+    """A call whose chunks apply T as a bf16 pair (repeated keys, beta = 1, no
+    decay) leaves the scratch holding pair flags and residuals; the next, smaller
+    call on ordinary keys must not pick them up."""
+    torch = torch_mod()
+    d = 128
+    rep = synth.edge_key_inputs("repeated", 2, 260, 3, d, "bf16", seed=42, beta=1.0, log_alpha=0.0)
+    plain = synth.chunk_inputs(1, 90, 2, d, d, gate, "bf16", seed=43, s0_std=0.1)
+    if gate == "channel":
+        rep["log_alpha"] = np.ascontiguousarray(np.repeat(rep["log_alpha"][..., None], d, axis=-1))
+    for inp in (rep, plain):
+        (o, st), (o_ws, st_ws) = _run_both(inp, "bf16", chunk)
+        assert torch.equal(o, o_ws) and torch.equal(st, st_ws)
+        o_or, st_or = oracle.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"],
+                                       inp["S0"])
+        tol = 3e-2 if inp is rep else TOL["bf16"]
+        assert rel_err(host(o), o_or) <= tol and rel_err(host(st), st_or) <= tol
