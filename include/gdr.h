@@ -87,6 +87,16 @@ gdr_status gdr_chunk_fwd_workspace_size(int64_t B, int64_t T, int64_t H,
  *              ignored and on return are unspecified; concurrent calls need
  *              separate workspaces.
  * The final chunk may be partial; tokens beyond T are never read or written.
+ *
+ * Precision.  fp32 io computes in fp32 throughout (fp32 matrix-core products
+ * and an fp32 triangular solve).  bf16 io multiplies bf16 operands on the
+ * matrix cores with fp32 accumulation and keeps the state in fp32; its
+ * triangular solve (bf16, scalar gate, chunk 64) runs partly in fp16, which
+ * assumes |beta_r k_r.k_i| <= 1 within a chunk, i.e. keys of norm at most 1 and
+ * beta in [0, 1] as the pages' models feed them (L2-normalised keys, sigmoid
+ * rates).  Keys of larger norm belong on fp32 io.  Chunks whose keys nearly
+ * repeat or cancel (an off-diagonal |beta_r k_r.k_i decay| above 1/2) apply the
+ * UT factor as a bf16 hi/lo pair automatically.
  */
 gdr_status gdr_chunk_fwd(const void *q, const void *k, const void *v,
                          const float *log_alpha, const float *beta, const float *S0,
