@@ -157,6 +157,33 @@ def raw_prologue_inputs(inp, io="bf16", seed=0, decay_logits=False):
     return out
 
 
+DRAFT_TREES = ("chain", "star", "binary", "random")
+
+
+def draft_tree(kind, B, Td, seed=0):
+    """Parent indices [B, Td] (int32) of a draft tree per sequence, nodes in
+    topological order: parent -1 hangs a node off the committed state, any
+    other parent is an earlier node.
+      chain   one linear draft (parent i - 1)
+      star    Td alternatives for the next token (all -1)
+      binary  a complete binary tree under node 0
+      random  each node's parent uniform over -1 .. i - 1 (own seeded stream)"""
+    if kind == "chain":
+        p = np.arange(Td) - 1
+        return np.ascontiguousarray(np.broadcast_to(p, (B, Td)), dtype=np.int32)
+    if kind == "star":
+        return np.full((B, Td), -1, dtype=np.int32)
+    if kind == "binary":
+        p = (np.arange(Td) - 1) // 2
+        p[0] = -1
+        return np.ascontiguousarray(np.broadcast_to(p, (B, Td)), dtype=np.int32)
+    if kind == "random":
+        rng = np.random.Generator(np.random.PCG64(seed + 13000))
+        p = np.stack([np.array([rng.integers(-1, i) if i > 0 else -1 for i in range(Td)]) for _ in range(B)])
+        return p.astype(np.int32)
+    raise ValueError(kind)
+
+
 EDGE_KEYS = ("repeated", "antiparallel", "near_collinear", "plane", "cyclic3")
 
 

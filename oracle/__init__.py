@@ -14,6 +14,6 @@ two share no code.
   shapes.
 """
 from .gdr_oracle import (build, chunk_fwd, chunk_fwd_prologue, decode_multi,  # noqa: F401
-                         decode_step, decode_step_prologue, fg2_chunk_fwd, fg2_decode_step,
+                         decode_step, decode_tree, decode_tree_commit, decode_step_prologue, fg2_chunk_fwd, fg2_decode_step,
                          gdn2_chunk_fwd, library_path, load, prologue_decay,
                          prologue_inputs)

@@ -209,6 +209,52 @@ def decode_multi(q, k, v, log_alpha, beta, S, accepted=None, lib=None):
     return o, s_out
 
 
+def decode_tree(q, k, v, log_alpha, beta, S, parent):
+    """A tree of draft tokens applied to the committed state S (speculative
+    decoding with branching drafts; the TreeWY note on the mindpattern "Gated
+    DeltaNet-2" page verifies every node of such a tree at once and keeps a
+    pseudo-value per node in place of per-node state snapshots).
+
+    Node i of sequence b follows parent[b][i] (a node with a smaller index) or,
+    for parent -1, the committed state itself.  Its state is the delta rule
+    applied along its root path, one token per node:
+        S_pre = S_parent Diag(alpha_i),  u_i = beta_i (v_i - S_pre k_i),
+        S_i = S_pre + u_i k_i^T,         o_i = S_i q_i.
+    Returns (o [B,Td,H,dv], u [B,Td,H,dv] (the written value of every node),
+    states {(b, i): [H,dv,dk]}).  Plain fp64 numpy, node by node in index
+    order (parents come first), every state kept; for test sizes."""
+    q, k, v, la, be, s = (_f64(a) for a in (q, k, v, log_alpha, beta, S))
+    B, Td, H, dk = q.shape
+    dv = v.shape[-1]
+    o = np.zeros((B, Td, H, dv))
+    u = np.zeros((B, Td, H, dv))
+    states = {}
+    for b in range(B):
+        for i in range(Td):
+            p = int(parent[b][i])
+            if not -1 <= p < i:
+                raise ValueError("parent[%d][%d] = %d is not -1 or an earlier node" % (b, i, p))
+            prev = s[b] if p < 0 else states[(b, p)]
+            a = np.exp(la[b, i]) if la.ndim == 4 else np.exp(la[b, i])[:, None]
+            pre = prev * a[:, None, :]                       # S Diag(alpha), per head
+            pred = np.einsum("hvc,hc->hv", pre, k[b, i])
+            u[b, i] = be[b, i][:, None] * (v[b, i] - pred)
+            st = pre + u[b, i][:, :, None] * k[b, i][:, None, :]
+            states[(b, i)] = st
+            o[b, i] = np.einsum("hvc,hc->hv", st, q[b, i])
+    return o, u, states
+
+
+def decode_tree_commit(S, states, accepted):
+    """The state after the accepted node of every sequence (accepted[b] = -1
+    keeps S[b]), from decode_tree's states."""
+    out = _f64(S).copy()
+    for b, a in enumerate(accepted):
+        if int(a) >= 0:
+            out[b] = states[(b, int(a))]
+    return out
+
+
 def gdn2_chunk_fwd(q, k, v, log_alpha, erase, write, S0=None, threads=None, lib=None):
     """Whole-sequence forward with decoupled erase and write gates (Gated
     DeltaNet-2 reading, see gdr_oracle.c).  q, k: [B,T,H,dk]; v: [B,T,H,dv];
