@@ -715,8 +715,34 @@ def main():
             fn()
         torch.cuda.synchronize()
         mres[name] = float(np.median(event_times(fn, args.decode_steps, stream)))
+    # A draft tree per sequence on the same state: 16 nodes (a random tree),
+    # every node verified in one pass, then the accepted node's state rebuilt
+    # in place from the written values.
+    from linear_attention_sequence_03_amd import gdr_decode_tree, gdr_decode_tree_commit
+    Tt = 16
+    ti = synth.chunk_inputs(wd.B, Tt, wd.H, wd.d, wd.d, "scalar", "f32", seed=wd.seed + 2)
+    tq, tk, tv, tla, tbe = (torch.from_numpy(ti[n]).to(devn) for n in ("q", "k", "v", "log_alpha", "beta"))
+    tpar = torch.from_numpy(synth.draft_tree("random", wd.B, Tt, seed=wd.seed)).to(devn)
+    tacc = torch.from_numpy(np.random.Generator(np.random.PCG64(wd.seed + 1)).integers(
+        -1, Tt, wd.B).astype(np.int32)).to(devn)
+    to_ = torch.empty((wd.B, Tt, wd.H, wd.d), dtype=torch.float32, device=devn)
+    tD = torch.empty_like(to_)
+
+    def tverify():
+        gdr_decode_tree(tq, tk, tv, tla, tbe, S, tpar, o=to_, D=tD)
+
+    def tcommit():
+        gdr_decode_tree_commit(tk, tla, tpar, tD, tacc, S, inplace=True)
+
+    for name, fn in (("tree_verify", tverify), ("tree_commit", tcommit)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        mres[name] = float(np.median(event_times(fn, args.decode_steps, stream)))
     state_bytes = wd.B * wd.H * wd.d * wd.d * 4
     vec_bytes = wd.B * Td * wd.H * (4 * wd.d * 4 + 8)
+    tv_bytes = state_bytes + wd.B * Tt * wd.H * (5 * wd.d * 4 + 8) + wd.B * Tt * 4
+    tc_bytes = 2 * state_bytes
     mv_bytes = state_bytes + vec_bytes                      # read the state once
     mc_bytes = 2 * state_bytes + vec_bytes - wd.B * Td * wd.H * wd.d * 4   # no o written
 
@@ -756,6 +782,15 @@ def main():
                          "commit_GBs": mc_bytes / (mres["commit"] * 1e-3) / 1e9,
                          "note": "verify: state read once, o for all draft tokens; commit: "
                                  "state of the accepted prefix written in place"},
+        "decode_tree": {"call": "gdr_decode_tree + gdr_decode_tree_commit", "nodes": Tt, "tree": "random",
+                        "verify_ms": mres["tree_verify"], "verify_bytes": tv_bytes,
+                        "verify_GBs": tv_bytes / (mres["tree_verify"] * 1e-3) / 1e9,
+                        "commit_ms": mres["tree_commit"], "commit_bytes": tc_bytes,
+                        "commit_GBs": tc_bytes / (mres["tree_commit"] * 1e-3) / 1e9,
+                        "note": "verify: every node's o and written value from one pass over the state "
+                                "(bytes: the state, q, k, v, o, written values, gates, parents); commit: "
+                                "the accepted node's state rebuilt in place (bytes: state read and "
+                                "written; its path's keys and values are a few KiB)"},
     }
     if others:
         out["other_prefill"] = others

@@ -237,6 +237,51 @@ gdr_status gdr_decode_multi(const void *q, const void *k, const void *v,
                             gdr_dtype io, gdr_gate gate, hipStream_t stream);
 
 /*
+ * Draft trees: verify every node of a tree of draft tokens in one pass over the
+ * committed state, then rebuild the state of the accepted node (the TreeWY
+ * note on the mindpattern "Gated DeltaNet-2" page: one tree-structured WY
+ * transform yields every node's output, and the accepted state is rebuilt on
+ * commit from a small matrix of pseudo-values, with no per-node state
+ * snapshots).  Node i of sequence b follows parent[b][i]: an earlier node, or
+ * -1 for a child of the committed state.  Its state is the delta rule applied
+ * along its root path, one token per node, and o_i = S_i q_i; a chain of
+ * parents i - 1 is exactly gdr_decode_multi.
+ *
+ * gdr_decode_tree:
+ *   q, k       [B, Td, H, dk]   io dtype, one token per node
+ *   v          [B, Td, H, dv]   io dtype
+ *   log_alpha  [B, Td, H] or [B, Td, H, dk]   fp32 (scalar / channel gate)
+ *   beta       [B, Td, H]       fp32
+ *   S_in       [B, H, dv, dk]   fp32 committed state, only read
+ *   parent     [B, Td]          int32 device array, 4-byte aligned; an entry
+ *                               that is neither -1 nor an earlier node is read
+ *                               as -1 (values are not otherwise inspected)
+ *   o          [B, Td, H, dv]   io dtype, every node's output; or NULL
+ *   D          [B, Td, H, dv]   fp32, every node's written value
+ *                               u_i = beta_i (v_i - S_parent Diag(alpha_i) k_i),
+ *                               the pseudo-values the commit needs; or NULL
+ * gdr_decode_tree_commit: S_out = the state after node accepted[b] (an int32
+ * device array [B], 4-byte aligned; -1 or any value outside [0, Td) keeps
+ * S_in), from S_in, the keys, decays and parents of the accepted node's path
+ * and D from gdr_decode_tree.  S_out may equal S_in (in place) but must not
+ * partially overlap it.
+ * 1 <= Td <= 64.  The verify pass reads the state once and costs about one
+ * decode step of HBM traffic plus O(Td^2 d) work per (b, h); the commit reads
+ * and writes the state once.  Errors as in gdr_decode_multi.
+ */
+gdr_status gdr_decode_tree(const void *q, const void *k, const void *v,
+                           const float *log_alpha, const float *beta, const float *S_in,
+                           const int32_t *parent, void *o, float *D,
+                           int64_t B, int64_t Td, int64_t H, int64_t dk, int64_t dv,
+                           gdr_dtype io, gdr_gate gate, hipStream_t stream);
+
+gdr_status gdr_decode_tree_commit(const void *k, const float *log_alpha, const int32_t *parent,
+                                  const float *D, const int32_t *accepted,
+                                  const float *S_in, float *S_out,
+                                  int64_t B, int64_t Td, int64_t H, int64_t dk, int64_t dv,
+                                  gdr_dtype io, gdr_gate gate, hipStream_t stream);
+
+/*
  * Channel-wise write rates: FG2-GDN and FG2-GDN+ ("FG2-GDN" page, sections 3.2,
  * 3.4-3.6).  The scalar beta_t becomes a vector beta^k_t in R^{d_k} that enters
  * through the scaled key k~ = sqrt(beta^k) * k (elementwise); the value is

@@ -14,6 +14,8 @@ from .gdr import (  # noqa: F401
     gdr_chunk_fwd_workspace_size,
     gdr_decode_multi,
     gdr_decode_step,
+    gdr_decode_tree,
+    gdr_decode_tree_commit,
     gdr_fg2_chunk_fwd,
     gdr_fg2_chunk_fwd_workspace_size,
     gdr_fg2_decode_step,

@@ -315,6 +315,86 @@ gdr_status gdr_decode_multi(const void* q, const void* k, const void* v, const f
     return GDR_OK;
 }
 
+namespace {
+
+gdr_status tree_common(int64_t B, int64_t Td, int64_t H, int64_t dk, int64_t dv, gdr_dtype io, gdr_gate gate) {
+    gdr_status s = check_common(B, H, dk, dv, io, gate);
+    if (s != GDR_OK) return s;
+    if (Td < 1 || Td > 64)
+        return fail(GDR_ERR_UNSUPPORTED, "Td must be in [1, 64] (Td=%lld)", (long long)Td);
+    if (mul({B, H, dv, dk}) < 0 || mul({B, Td, H, dk > dv ? dk : dv}) < 0 || mul({B, H, dv / 64}) > INT32_MAX)
+        return fail(GDR_ERR_UNSUPPORTED, "tensors too large");
+    return GDR_OK;
+}
+
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+}  // namespace
+
+gdr_status gdr_decode_tree(const void* q, const void* k, const void* v, const float* log_alpha,
+                           const float* beta, const float* S_in, const int32_t* parent, void* o, float* D,
+                           int64_t B, int64_t Td, int64_t H, int64_t dk, int64_t dv, gdr_dtype io,
+                           gdr_gate gate, hipStream_t stream) {
+    g_last_error[0] = 0;
+    gdr_status s = tree_common(B, Td, H, dk, dv, io, gate);
+    if (s != GDR_OK) return s;
+    if (!q || !k || !v || !log_alpha || !beta || !S_in || !parent)
+        return fail(GDR_ERR_INVALID_ARG, "q, k, v, log_alpha, beta, S_in and parent must be non-NULL");
+    if (!aligned4(parent)) return fail(GDR_ERR_INVALID_ARG, "parent is not 4-byte aligned");
+    if (!o && !D) return GDR_OK;   // nothing requested
+    const size_t es = io == GDR_BF16 ? 2 : 4;
+    const int64_t ntok = B * Td * H;
+    const Range par = rng("parent", parent, B * Td, 4);
+    const Range rs[] = {
+        rng("q", q, ntok * dk, es), rng("k", k, ntok * dk, es), rng("v", v, ntok * dv, es),
+        rng("log_alpha", log_alpha, gate == GDR_GATE_CHANNEL ? ntok * dk : ntok, 4),
+        rng("beta", beta, ntok, 4), rng("S_in", S_in, B * H * dv * dk, 4),
+        rng("o", o, ntok * dv, es), rng("D", D, ntok * dv, 4),
+    };
+    s = check_ptrs(rs, 8, 6);
+    if (s != GDR_OK) return s;
+    for (int i = 6; i < 8; ++i)
+        if (overlap(rs[i], par)) return fail(GDR_ERR_INVALID_ARG, "%s overlaps parent", rs[i].name);
+    gdr::TreeArgs a{q, k, v, log_alpha, beta, S_in, parent, o, D, nullptr, nullptr, B, Td, H, dk, dv,
+                    io == GDR_BF16, gate == GDR_GATE_CHANNEL, stream};
+    const hipError_t err = gdr::decode_tree_launch(a);
+    if (err != hipSuccess) return fail(GDR_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(err));
+    return GDR_OK;
+}
+
+gdr_status gdr_decode_tree_commit(const void* k, const float* log_alpha, const int32_t* parent,
+                                  const float* D, const int32_t* accepted, const float* S_in, float* S_out,
+                                  int64_t B, int64_t Td, int64_t H, int64_t dk, int64_t dv, gdr_dtype io,
+                                  gdr_gate gate, hipStream_t stream) {
+    g_last_error[0] = 0;
+    gdr_status s = tree_common(B, Td, H, dk, dv, io, gate);
+    if (s != GDR_OK) return s;
+    if (!k || !log_alpha || !parent || !D || !accepted || !S_in || !S_out)
+        return fail(GDR_ERR_INVALID_ARG, "k, log_alpha, parent, D, accepted, S_in and S_out must be non-NULL");
+    if (!aligned4(parent) || !aligned4(accepted))
+        return fail(GDR_ERR_INVALID_ARG, "parent and accepted must be 4-byte aligned");
+    const size_t es = io == GDR_BF16 ? 2 : 4;
+    const int64_t ntok = B * Td * H, nst = B * H * dv * dk;
+    const Range in_state = rng("S_in", S_in, nst, 4), out_state = rng("S_out", S_out, nst, 4);
+    if (S_in != S_out && overlap(in_state, out_state))
+        return fail(GDR_ERR_INVALID_ARG, "S_out partially overlaps S_in");
+    const Range rs[] = {
+        rng("k", k, ntok * dk, es), rng("log_alpha", log_alpha, gate == GDR_GATE_CHANNEL ? ntok * dk : ntok, 4),
+        rng("D", D, ntok * dv, 4), S_in == S_out ? Range{"S_in", 0, 0} : in_state, out_state,
+    };
+    s = check_ptrs(rs, 5, 4);
+    if (s != GDR_OK) return s;
+    const Range small[] = {rng("parent", parent, B * Td, 4), rng("accepted", accepted, B, 4)};
+    for (const Range& r : small)
+        if (overlap(out_state, r)) return fail(GDR_ERR_INVALID_ARG, "S_out overlaps %s", r.name);
+    if (!aligned16(S_in)) return fail(GDR_ERR_INVALID_ARG, "S_in is not 16-byte aligned");
+    gdr::TreeArgs a{nullptr, k, nullptr, log_alpha, nullptr, S_in, parent, nullptr, const_cast<float*>(D),
+                    accepted, S_out, B, Td, H, dk, dv, io == GDR_BF16, gate == GDR_GATE_CHANNEL, stream};
+    const hipError_t err = gdr::decode_tree_commit_launch(a);
+    if (err != hipSuccess) return fail(GDR_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(err));
+    return GDR_OK;
+}
+
 gdr_status gdr_gdn2_fwd(const void* q, const void* k, const void* v, const float* log_alpha,
                         const float* erase, const float* write, const float* S0, void* o, float* S_T,
                         int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv, gdr_dtype io,

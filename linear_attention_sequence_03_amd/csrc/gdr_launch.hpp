@@ -54,6 +54,23 @@ struct ChunkArgs {
 hipError_t decode_step_launch(const DecodeArgs& a);
 hipError_t decode_multi_launch(const DecodeMultiArgs& a);
 
+// Draft trees (verify every node; rebuild the accepted node's state).
+struct TreeArgs {
+    const void *q, *k, *v;
+    const float *log_alpha, *beta, *S_in;
+    const int32_t* parent;      // [B, Td]
+    void* o;                    // verify: outputs, or NULL
+    float* D;                   // verify: written values (out); commit: in
+    const int32_t* accepted;    // commit: [B]
+    float* S_out;               // commit
+    int64_t B, Td, H, dk, dv;
+    bool bf16, channel;
+    hipStream_t stream;
+};
+hipError_t decode_tree_launch(const TreeArgs& a);
+hipError_t decode_tree_commit_launch(const TreeArgs& a);
+size_t tree_verify_lds_bytes(int64_t Td, int64_t dk);
+
 // Workspace bytes of one (b, h, chunk) block and of the whole call.
 size_t chunk_block_bytes(int64_t dk, int64_t chunk, bool bf16, bool channel);
 size_t chunk_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t chunk,

@@ -23,7 +23,7 @@ GDR_NOALLOC_SCRATCH_BYTES = 64 << 20   # the fixed scratch of gdr_chunk_fwd_noal
 
 # Every symbol include/gdr.h declares.
 EXPORTS = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_chunk_fwd_noalloc",
-           "gdr_decode_step", "gdr_decode_multi",
+           "gdr_decode_step", "gdr_decode_multi", "gdr_decode_tree", "gdr_decode_tree_commit",
            "gdr_chunk_fwd_prologue", "gdr_chunk_fwd_prologue_workspace_size", "gdr_decode_step_prologue",
            "gdr_fg2_chunk_fwd_workspace_size", "gdr_fg2_chunk_fwd", "gdr_fg2_decode_step",
            "gdr_gdn2_fwd", "gdr_gdn2_chunk_fwd_workspace_size", "gdr_gdn2_chunk_fwd",
@@ -89,6 +89,12 @@ def load_library(path: Optional[str] = None):
     lib.gdr_decode_multi.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                      i64, i64, i64, i64, i64, f, f, vp]
     lib.gdr_decode_multi.restype = f
+    lib.gdr_decode_tree.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                    i64, i64, i64, i64, i64, f, f, vp]
+    lib.gdr_decode_tree.restype = f
+    lib.gdr_decode_tree_commit.argtypes = [vp, vp, vp, vp, vp, vp, vp,
+                                           i64, i64, i64, i64, i64, f, f, vp]
+    lib.gdr_decode_tree_commit.restype = f
     lib.gdr_fg2_chunk_fwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64, f, f,
                                                      ctypes.POINTER(ctypes.c_size_t)]
     lib.gdr_fg2_chunk_fwd_workspace_size.restype = f
@@ -473,3 +479,70 @@ def gdr_gdn2_chunk_fwd(q, k, v, log_alpha, erase, write, S0=None, chunk: int = 6
     if st != GDR_OK:
         _raise(st)
     return o, S_T
+
+
+def gdr_decode_tree(q, k, v, log_alpha, beta, S, parent, o=None, D=None, want_o: bool = True,
+                    want_D: bool = True, stream=None) -> Tuple:
+    """Verify a tree of draft tokens: q,k: [B,Td,H,dk]; v: [B,Td,H,dv];
+    log_alpha: [B,Td,H] or [B,Td,H,dk]; beta: [B,Td,H]; S: [B,H,dv,dk] fp32
+    (read only); parent: [B,Td] int32 (-1 or an earlier node).  Returns
+    (o [B,Td,H,dv] io dtype, D [B,Td,H,dv] fp32 written values), either None
+    when not wanted."""
+    import torch
+    dev = q.device
+    B, Td, H, dk = q.shape
+    dv = v.shape[-1]
+    io = _io_code(q.dtype)
+    gate = GDR_GATE_CHANNEL if log_alpha.dim() == 4 else GDR_GATE_SCALAR
+    _need("q", q, q.dtype, (B, Td, H, dk), dev)
+    _need("k", k, q.dtype, (B, Td, H, dk), dev)
+    _need("v", v, q.dtype, (B, Td, H, dv), dev)
+    _need("log_alpha", log_alpha, torch.float32,
+          (B, Td, H, dk) if gate == GDR_GATE_CHANNEL else (B, Td, H), dev)
+    _need("beta", beta, torch.float32, (B, Td, H), dev)
+    _need("S", S, torch.float32, (B, H, dv, dk), dev)
+    _need("parent", parent, torch.int32, (B, Td), dev)
+    if o is None and want_o:
+        o = torch.empty((B, Td, H, dv), dtype=q.dtype, device=dev)
+    if o is not None:
+        _need("o", o, q.dtype, (B, Td, H, dv), dev)
+    if D is None and want_D:
+        D = torch.empty((B, Td, H, dv), dtype=torch.float32, device=dev)
+    if D is not None:
+        _need("D", D, torch.float32, (B, Td, H, dv), dev)
+    st = load_library().gdr_decode_tree(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S), _ptr(parent), _ptr(o), _ptr(D),
+        B, Td, H, dk, dv, io, gate, _stream(dev, stream))
+    if st != GDR_OK:
+        _raise(st)
+    return o, D
+
+
+def gdr_decode_tree_commit(k, log_alpha, parent, D, accepted, S, S_out=None, inplace: bool = False,
+                           stream=None):
+    """The state after the accepted node of every sequence (accepted: [B]
+    int32; -1 keeps S), from gdr_decode_tree's written values D.
+    ``inplace=True`` writes it into S.  Returns S_out."""
+    import torch
+    dev = k.device
+    B, Td, H, dk = k.shape
+    dv = D.shape[-1]
+    io = _io_code(k.dtype)
+    gate = GDR_GATE_CHANNEL if log_alpha.dim() == 4 else GDR_GATE_SCALAR
+    _need("log_alpha", log_alpha, torch.float32,
+          (B, Td, H, dk) if gate == GDR_GATE_CHANNEL else (B, Td, H), dev)
+    _need("parent", parent, torch.int32, (B, Td), dev)
+    _need("D", D, torch.float32, (B, Td, H, dv), dev)
+    _need("accepted", accepted, torch.int32, (B,), dev)
+    _need("S", S, torch.float32, (B, H, dv, dk), dev)
+    if inplace:
+        S_out = S
+    elif S_out is None:
+        S_out = torch.empty_like(S)
+    _need("S_out", S_out, torch.float32, (B, H, dv, dk), dev)
+    st = load_library().gdr_decode_tree_commit(
+        _ptr(k), _ptr(log_alpha), _ptr(parent), _ptr(D), _ptr(accepted), _ptr(S), _ptr(S_out),
+        B, Td, H, dk, dv, io, gate, _stream(dev, stream))
+    if st != GDR_OK:
+        _raise(st)
+    return S_out

@@ -335,3 +335,44 @@ def test_gdn2_chunk_workspace_size():
     assert gdr.gdr_gdn2_chunk_fwd_workspace_size(1, 0, 1, 64, 64, 64, 1, 0) == 0
     with pytest.raises(gdr.GdrError):
         gdr.gdr_gdn2_chunk_fwd_workspace_size(1, 64, 1, 64, 64, 64, 0, 0)   # fp32 io
+
+
+def _tree(lib, q=0, k=1, v=2, la=3, be=4, si=5, par=6, o=7, D=8, B=2, Td=5, H=2, dk=64, dv=64, io=0, gate=0):
+    p = lambda i: None if i is None else (_addr(i) if isinstance(i, int) else i)  # noqa: E731
+    return lib.gdr_decode_tree(p(q), p(k), p(v), p(la), p(be), p(si), p(par), p(o), p(D),
+                               B, Td, H, dk, dv, io, gate, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Td=0), 2), (dict(Td=65), 2), (dict(q=None), 1), (dict(par=None), 1), (dict(si=None), 1),
+    (dict(dk=96, dv=96), 2), (dict(io=3), 1),
+    (dict(par=ctypes.c_void_p(BASE + 6 * MB + 2)), 1),     # parent not 4-byte aligned
+    (dict(o=ctypes.c_void_p(BASE + 1024)), 1),              # o inside q
+    (dict(D=ctypes.c_void_p(BASE + 6 * MB + 16)), 1),       # D overlaps parent
+    (dict(o=ctypes.c_void_p(BASE + 7 * MB + 8)), 1),        # o misaligned
+])
+def test_decode_tree_rejects(lib, kw, code):
+    assert _tree(lib, **kw) == code
+    assert lib.gdr_last_error()
+
+
+def test_decode_tree_nothing_requested_is_ok(lib):
+    assert _tree(lib, o=None, D=None) == 0
+
+
+def _tree_commit(lib, k=1, la=3, par=6, D=8, acc=9, si=5, so=10, B=2, Td=5, H=2, dk=64, dv=64, io=0,
+                 gate=0):
+    p = lambda i: None if i is None else (_addr(i) if isinstance(i, int) else i)  # noqa: E731
+    return lib.gdr_decode_tree_commit(p(k), p(la), p(par), p(D), p(acc), p(si), p(so),
+                                      B, Td, H, dk, dv, io, gate, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Td=65), 2), (dict(acc=None), 1), (dict(D=None), 1), (dict(so=None), 1),
+    (dict(so=ctypes.c_void_p(BASE + 5 * MB + 4096)), 1),    # S_out partially overlaps S_in
+    (dict(so=ctypes.c_void_p(BASE + 8 * MB)), 1),           # S_out is D
+    (dict(acc=ctypes.c_void_p(BASE + 9 * MB + 1)), 1),      # accepted misaligned
+])
+def test_decode_tree_commit_rejects(lib, kw, code):
+    assert _tree_commit(lib, **kw) == code
+    assert lib.gdr_last_error()
