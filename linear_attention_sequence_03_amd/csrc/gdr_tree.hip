@@ -20,8 +20,8 @@
 //   S_a = S Diag(e^{g_a}) + sum_{j on the path of a} D_j (k_j * e^{g_a - g_j})^T.
 // Every exponent is <= 0 (decays are at most 1), so nothing overflows.
 //
-// gdr_decode_tree: one workgroup per (b, h, 64 state rows).  The workgroup
-// builds g, Kg, Qg, T and M = P T for its (b, h) in LDS (fp32), then each
+// gdr_decode_tree: one workgroup per (b, h).  The workgroup builds the path
+// decays, A, T and M = P T of its tree in LDS (fp32), then each
 // group of LPR = DK/16 lanes takes a state row (16 channels per lane, as in the
 // multi-token decode), reduces R_i and (Qg S^T)_i for every node with DPP row
 // sums, and the row's lanes split the nodes for D_i = T R and o_i = O0_i + M R.
@@ -53,26 +53,29 @@ __device__ __forceinline__ int tree_parent(const int32_t* parent, int i) {
     return (p >= 0 && p < i) ? p : -1;
 }
 
-// LDS carve-up of the verify kernel for Td nodes (in floats).  The per-wave
-// staging of v, R and Qg S^T (phase 3) reuses the path log-decays' space when
-// it fits (it does at DK = 128, where the total would pass 160 KiB otherwise).
+// LDS carve-up of the verify kernel for Td nodes (in floats): the nodes' raw
+// keys and queries (fp32), their path log-decays (then the decays e^g), A
+// (then M = P T), T and P, the per-wave staging of R and Qg S^T (in P's place
+// once P is spent, when it fits), beta and the ancestor masks.
 struct TreeLds {
     int td, dk;
     __host__ __device__ size_t rpp() const { return 1024 / dk; }                 // rows per wave pass
-    __host__ __device__ size_t stg_n() const { return 4 * rpp() * td * 3; }
-    __host__ __device__ bool stg_in_g() const { return stg_n() <= (size_t)td * dk; }
-    __host__ __device__ size_t g() const { return 0; }                           // [Td][dk] path log-decay
-    __host__ __device__ size_t kg() const { return g() + (size_t)td * dk; }     // [Td][dk]
-    __host__ __device__ size_t qg() const { return kg() + (size_t)td * dk; }    // [Td][dk]
-    __host__ __device__ size_t am() const { return qg() + (size_t)td * dk; }    // [Td][Td] A, then M = P T
+    __host__ __device__ size_t stg_n() const { return 4 * rpp() * td * 2; }
+    __host__ __device__ bool stg_in_p() const { return stg_n() <= (size_t)td * td; }
+    __host__ __device__ size_t kr() const { return 0; }                          // [Td][dk]
+    __host__ __device__ size_t qr() const { return kr() + (size_t)td * dk; }    // [Td][dk]
+    __host__ __device__ size_t ge() const { return qr() + (size_t)td * dk; }    // [Td][dk] g, then e^g
+    __host__ __device__ size_t am() const { return ge() + (size_t)td * dk; }    // [Td][Td] A, then M = P T
     __host__ __device__ size_t tm() const { return am() + (size_t)td * td; }    // [Td][Td] T
     __host__ __device__ size_t pm() const { return tm() + (size_t)td * td; }    // [Td][Td] P
-    __host__ __device__ size_t stg() const { return stg_in_g() ? g() : pm() + (size_t)td * td; }
-    __host__ __device__ size_t bet() const { return pm() + (size_t)td * td + (stg_in_g() ? 0 : stg_n()); }
+    __host__ __device__ size_t stg() const { return stg_in_p() ? pm() : pm() + (size_t)td * td; }
+    __host__ __device__ size_t bet() const { return pm() + (size_t)td * td + (stg_in_p() ? 0 : stg_n()); }
     __host__ __device__ size_t anc() const { return (bet() + td + 1) / 2 * 2; }  // [Td] uint64
-    __host__ __device__ size_t floats() const { return anc() + 2 * (size_t)td; }
+    __host__ __device__ size_t off() const { return anc() + 2 * (size_t)td; }   // [Td + 1] int: pair offsets
+    __host__ __device__ size_t floats() const { return off() + td + 1; }
 };
 
+// One workgroup per (b, h): the whole head's rows, in passes of 4 * RPP.
 template <typename E, bool CHANNEL, int DK>
 __global__ __launch_bounds__(256) void tree_verify_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
@@ -80,95 +83,106 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
     const int32_t* __restrict__ parent, E* __restrict__ o, float* __restrict__ D, int H, int Td, int DV) {
     constexpr int LPR = DK / 16;         // lanes per state row
     constexpr int RPP = kWave / LPR;     // rows per wave pass
+    constexpr int CPL = DK / kWave;      // channels per lane in the pair sums
     extern __shared__ __attribute__((aligned(16))) float tl[];
     const TreeLds L{Td, DK};
-    float* g = tl + L.g();
-    float* kg = tl + L.kg();
-    float* qg = tl + L.qg();
+    float* kr = tl + L.kr();
+    float* qr = tl + L.qr();
+    float* ge = tl + L.ge();
     float* am = tl + L.am();
     float* tm = tl + L.tm();
     float* pm = tl + L.pm();
     float* bet = tl + L.bet();
     uint64_t* anc = reinterpret_cast<uint64_t*>(tl + L.anc());
+    int* off = reinterpret_cast<int*>(tl + L.off());
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int nrb = DV / kTreeRows;
-    const int64_t bh = blockIdx.x / nrb;
-    const int rb = (int)(blockIdx.x % nrb);
+    const int64_t bh = blockIdx.x;
     const int64_t b = bh / H, h = bh % H;
     const int32_t* par = parent + b * Td;
     auto node_row = [&](int i) { return (b * Td + i) * H + h; };   // row of [B, Td, H, *]
 
-    // ---- ancestor masks and beta ----
+    // ---- inputs of every node into LDS; ancestor masks, and the offsets of
+    //      each node's (ancestor-or-self) pairs in one list ----
     if (tid == 0) {
+        int n = 0;
         for (int i = 0; i < Td; ++i) {
             const int p = tree_parent(par, i);
-            anc[i] = p < 0 ? 0ull : (anc[p] | (1ull << p));
+            const uint64_t a = p < 0 ? 0ull : (anc[p] | (1ull << p));
+            anc[i] = a;
+            off[i] = n;
+            n += __builtin_popcountll(a) + 1;
         }
+        off[Td] = n;
     }
     if (tid < Td) bet[tid] = beta[node_row(tid)];
-    // ---- path log-decays: the nodes' log-decays loaded together, then thread
-    //      c follows channel c down the tree ----
-    for (int e = tid; e < Td * (CHANNEL ? DK : 1); e += 256) {
-        const int i = CHANNEL ? e / DK : e, c = CHANNEL ? e % DK : 0;
-        g[i * DK + c] = CHANNEL ? log_alpha[node_row(i) * DK + c] : log_alpha[node_row(i)];
+    for (int e = tid; e < Td * DK; e += 256) {
+        const int i = e / DK, c = e % DK;
+        kr[e] = to_f32(k[node_row(i) * DK + c]);
+        qr[e] = to_f32(q[node_row(i) * DK + c]);
+        if (CHANNEL || c == 0) ge[e] = CHANNEL ? log_alpha[node_row(i) * DK + c] : log_alpha[node_row(i)];
     }
     __syncthreads();
+    // ---- path log-decays: thread c follows channel c down the tree ----
     if (tid < (CHANNEL ? DK : 1)) {
         for (int i = 0; i < Td; ++i) {
             const int p = tree_parent(par, i);
-            if (p >= 0) g[i * DK + tid] += g[p * DK + tid];
+            if (p >= 0) ge[i * DK + tid] += ge[p * DK + tid];
         }
     }
     __syncthreads();
-    // ---- decay-scaled keys and queries ----
-    for (int e = tid; e < Td * DK; e += 256) {
-        const int i = e / DK, c = e % DK;
-        const float gi = g[i * DK + (CHANNEL ? c : 0)];
-        const float w = __expf(gi);
-        kg[e] = to_f32(k[node_row(i) * DK + c]) * w;
-        qg[e] = to_f32(q[node_row(i) * DK + c]) * w;
+    // ---- A and P over the (ancestor-or-self) pairs: the pairs of the list
+    //      one per thread, each a sum over the channels from LDS ----
+    for (int e = tid; e < Td * Td; e += 256) {
+        am[e] = 0.f;
+        pm[e] = 0.f;
     }
-    // ---- A and P over ancestor pairs: one wave per pair, the channels over
-    //      its lanes, then a wave sum ----
-    constexpr int CPL = DK / kWave;   // channels per lane
-    for (int e = wave; e < Td * Td; e += 4) {
-        const int i = e / Td, j = e % Td;
-        const bool up = ((anc[i] >> j) & 1ull) != 0;   // j a strict ancestor of i (wave-uniform)
-        if (!up && j != i) {
-            if (lane == 0) { am[e] = 0.f; pm[e] = 0.f; }
-            continue;
+    __syncthreads();
+    const int npairs = off[Td];
+    for (int t = tid; t < npairs; t += 256) {
+        int lo = 0, hi = Td - 1;   // the node i with off[i] <= t < off[i + 1]
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (off[mid] <= t) lo = mid;
+            else hi = mid - 1;
         }
-        const E* ki = k + node_row(i) * DK;
-        const E* kj = k + node_row(j) * DK;
-        const E* qi = q + node_row(i) * DK;
+        const int i = lo;
+        uint64_t m = anc[i] | (1ull << i);
+        for (int r = t - off[i]; r > 0; --r) m &= m - 1ull;
+        const int j = __builtin_ctzll(m);
+        const float* ki = kr + i * DK;
+        const float* kj = kr + j * DK;
+        const float* qi = qr + i * DK;
         float a = 0.f, pp = 0.f;
-#pragma unroll
-        for (int u = 0; u < CPL; ++u) {
-            const int c = lane + kWave * u;
-            const float w = CHANNEL ? __expf(g[i * DK + c] - g[j * DK + c]) : 1.f;
-            const float kjw = to_f32(kj[c]) * w;
-            a += to_f32(ki[c]) * kjw;
-            pp += to_f32(qi[c]) * kjw;
-        }
-#pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) {
-            a += __shfl_xor(a, m);
-            pp += __shfl_xor(pp, m);
+#pragma unroll 4
+        for (int c = 0; c < DK; c += 4) {
+            const float4 x = *reinterpret_cast<const float4*>(ki + c);
+            float4 y = *reinterpret_cast<const float4*>(kj + c);
+            const float4 z = *reinterpret_cast<const float4*>(qi + c);
+            if constexpr (CHANNEL) {
+                const float4 gi = *reinterpret_cast<const float4*>(ge + i * DK + c);
+                const float4 gj = *reinterpret_cast<const float4*>(ge + j * DK + c);
+                y = make_float4(y.x * __expf(gi.x - gj.x), y.y * __expf(gi.y - gj.y), y.z * __expf(gi.z - gj.z),
+                                y.w * __expf(gi.w - gj.w));
+            }
+            a += x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
+            pp += z.x * y.x + z.y * y.y + z.z * y.z + z.w * y.w;
         }
         if constexpr (!CHANNEL) {
-            const float w = __expf(g[i * DK] - g[j * DK]);
+            const float w = __expf(ge[i * DK] - ge[j * DK]);
             a *= w;
             pp *= w;
         }
-        if (lane == 0) {
-            am[e] = up ? a * bet[i] : 0.f;
-            pm[e] = pp;
-        }
+        if (j != i) am[i * Td + j] = a * bet[i];
+        pm[i * Td + j] = pp;
     }
     __syncthreads();
-    // ---- T = (I + A)^-1 Diag(beta): thread j builds column j by forward
-    //      substitution over the nodes below j (only ancestors contribute) ----
+    // ---- decays e^g (g is spent); T = (I + A)^-1 Diag(beta): thread j builds
+    //      column j by forward substitution (only ancestors contribute) ----
+    for (int e = tid; e < Td * (CHANNEL ? DK : 1); e += 256) {
+        const int i = CHANNEL ? e / DK : e, c = CHANNEL ? e % DK : 0;
+        ge[i * DK + c] = __expf(ge[i * DK + c]);
+    }
     if (tid < Td) {
         const int j = tid;
         for (int i = 0; i < Td; ++i) {
@@ -204,47 +218,58 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
         }
         am[e] = x;   // A is no longer read
     }
-    __syncthreads();
+    __syncthreads();   // P is spent: the staging may take its place
 
     // ---- the state rows ----
-    const int cl = lane % LPR;
-    float* stg = tl + L.stg() + (size_t)wave * RPP * Td * 3;
-    for (int p0 = 0; p0 < kTreeRows; p0 += 4 * RPP) {
-        const int rw = lane / LPR;                                    // row within the wave pass
-        const int row = rb * kTreeRows + p0 + wave * RPP + rw;
+    const int cl = lane % LPR, rw = lane / LPR;
+    float* stg = tl + L.stg() + (size_t)wave * RPP * Td * 2;
+    for (int p0 = 0; p0 < DV; p0 += 4 * RPP) {
+        const int row = p0 + wave * RPP + rw;
         const int64_t sbase = (bh * DV + row) * (int64_t)DK;
         f32x4 s[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             s[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S_in + sbase + 4 * (cl + LPR * j)));
-        for (int i = cl; i < Td; i += LPR) stg[(rw * Td + i) * 3 + 2] = to_f32(v[node_row(i) * DV + row]);
+        // v of every node for this row, loaded together (the R slots take it)
+        for (int i = cl; i < Td; i += LPR) stg[(rw * Td + i) * 2] = to_f32(v[node_row(i) * DV + row]);
         __syncthreads();
+#pragma unroll 2
         for (int i = 0; i < Td; ++i) {
             float pd = 0.f, od = 0.f;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int c = 4 * (cl + LPR * j);
-                const float4 kv = *reinterpret_cast<const float4*>(kg + i * DK + c);
-                const float4 qv = *reinterpret_cast<const float4*>(qg + i * DK + c);
+                float4 kv = *reinterpret_cast<const float4*>(kr + i * DK + c);
+                float4 qv = *reinterpret_cast<const float4*>(qr + i * DK + c);
+                if constexpr (CHANNEL) {
+                    const float4 ev = *reinterpret_cast<const float4*>(ge + i * DK + c);
+                    kv = make_float4(kv.x * ev.x, kv.y * ev.y, kv.z * ev.z, kv.w * ev.w);
+                    qv = make_float4(qv.x * ev.x, qv.y * ev.y, qv.z * ev.z, qv.w * ev.w);
+                }
                 pd += s[j][0] * kv.x + s[j][1] * kv.y + s[j][2] * kv.z + s[j][3] * kv.w;
                 od += s[j][0] * qv.x + s[j][1] * qv.y + s[j][2] * qv.z + s[j][3] * qv.w;
             }
             pd = tree_row_sum<LPR>(pd);
             od = tree_row_sum<LPR>(od);
+            if constexpr (!CHANNEL) {
+                const float ei = ge[i * DK];
+                pd *= ei;
+                od *= ei;
+            }
             if (cl == 0) {
-                stg[(rw * Td + i) * 3] = stg[(rw * Td + i) * 3 + 2] - pd;   // R_i = v_i - (Kg S^T)_i
-                stg[(rw * Td + i) * 3 + 1] = od;                           // (Qg S^T)_i
+                stg[(rw * Td + i) * 2] -= pd;         // R_i = v_i - (Kg S^T)_i
+                stg[(rw * Td + i) * 2 + 1] = od;      // (Qg S^T)_i
             }
         }
         __syncthreads();
         // the row's lanes split the nodes: D_i = T R, o_i = O0_i + M R
         for (int i = cl; i < Td; i += LPR) {
-            float d = 0.f, y = stg[(rw * Td + i) * 3 + 1];
+            float d = 0.f, y = stg[(rw * Td + i) * 2 + 1];
             uint64_t m = anc[i] | (1ull << i);
             while (m) {
                 const int j = __builtin_ctzll(m);
                 m &= m - 1ull;
-                const float r = stg[(rw * Td + j) * 3];
+                const float r = stg[(rw * Td + j) * 2];
                 d += tm[i * Td + j] * r;
                 y += am[i * Td + j] * r;
             }
@@ -325,7 +350,7 @@ __global__ __launch_bounds__(256) void tree_commit_kernel(
 
 template <typename E, bool CHANNEL, int DK>
 hipError_t launch_tree(const TreeArgs& a) {
-    const int64_t grid = a.B * a.H * (a.dv / kTreeRows);
+    const int64_t grid = a.B * a.H;
     if (a.o || a.D) {
         const size_t lds = TreeLds{(int)a.Td, DK}.floats() * sizeof(float);
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&tree_verify_kernel<E, CHANNEL, DK>),
