@@ -217,3 +217,38 @@ def test_edge_keys_short_run_in_one_block():
     o, st = gpu_chunk(inp, "bf16", chunk=64)
     o_ref, st_ref = oracle.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], inp["S0"])
     check_all_heads("edge short run", o, st, o_ref, st_ref, TOL["bf16"])
+
+
+@pytest.mark.parametrize("io,gate,chunk", [("bf16", "scalar", 64), ("bf16", "channel", 64), ("bf16", "channel", 16),
+                                           ("bf16", "scalar", 32), ("f32", "scalar", 64)])
+@pytest.mark.parametrize("kind", ["repeated", "near_collinear", "antiparallel"])
+def test_edge_keys_through_the_prologue(kind, io, gate, chunk):
+    """Degenerate keys given raw (rows scaled by 1..8, beta as a logit of 0.99,
+    the decay as a logit of 1 - 1e-4): the prologue's normalisation and maps
+    feed the same near-degenerate chunks to every route (the fused kernel's
+    solve / recurrence waves, the channel prep, the staging pass)."""
+    from linear_attention_sequence_03_amd.gdr import GDR_PROLOGUE_BETA_SIGMOID, GDR_PROLOGUE_DECAY_SOFTPLUS, \
+        GDR_PROLOGUE_L2NORM_QK
+    d = 128
+    inp = _edge_inputs(kind, 1.0, 0.99, d, io)
+    rng = np.random.Generator(np.random.PCG64(91))
+    raw = dict(inp)
+    for n in ("q", "k"):
+        x = inp[n].astype(np.float64) * rng.uniform(1.0, 8.0, inp[n].shape[:-1] + (1,))
+        raw[n] = synth.round_bf16(x) if io == "bf16" else x.astype(np.float32)
+    raw["beta"] = np.full_like(inp["beta"], np.log(0.99 / 0.01))
+    la = np.full(inp["log_alpha"].shape, np.log(np.expm1(1e-4)), dtype=np.float32)   # alpha = 1 - ~1e-4
+    raw["log_alpha"] = np.ascontiguousarray(np.repeat(la[..., None], d, axis=-1)) if gate == "channel" else la
+    flags = GDR_PROLOGUE_L2NORM_QK | GDR_PROLOGUE_BETA_SIGMOID | GDR_PROLOGUE_DECAY_SOFTPLUS
+    o, st = gpu_chunk(raw, io, chunk=chunk, prologue=flags)
+    o_ref, st_ref = oracle.chunk_fwd_prologue(raw["q"], raw["k"], raw["v"], raw["log_alpha"], raw["beta"],
+                                              raw["S0"], flags=flags)
+    # Only the fused kernel (bf16, scalar gate, chunk 64) applies the norms as
+    # scalars after its products.  The channel-gate prep and the staging pass
+    # hand the products normalised keys rounded to bf16: one more rounding of
+    # the key (2^-9 relative) than a plain call's bf16 unit keys, which these
+    # degenerate chunks turn into up to 3.6e-2 in the state (measured); bound
+    # 4e-2 on those routes.
+    fused = io == "bf16" and gate == "scalar" and chunk == 64
+    tol = TOL["f32"] if io == "f32" else (EDGE_TOL if fused else 4e-2)
+    check_all_heads("edge prologue %s %s %s C=%d" % (kind, io, gate, chunk), o, st, o_ref, st_ref, tol)
