@@ -21,10 +21,10 @@
 // Every exponent is <= 0 (decays are at most 1), so nothing overflows.
 //
 // gdr_decode_tree: one workgroup per (b, h).  The workgroup builds the path
-// decays, A, T and M = P T of its tree in LDS (fp32), then each
-// group of LPR = DK/16 lanes takes a state row (16 channels per lane, as in the
-// multi-token decode), reduces R_i and (Qg S^T)_i for every node with DPP row
-// sums, and the row's lanes split the nodes for D_i = T R and o_i = O0_i + M R.
+// decays, A, T and M = P T of its tree in LDS (fp32), scales the keys and
+// queries by their path decays, then each wave takes 16-column tiles of the
+// values and forms R, Qg S^T, D = T R and o = Qg S^T + M R with fp32 MFMA
+// (every product is a small dense contraction; tiles past Td are zeros).
 // gdr_decode_tree_commit: one workgroup per (b, h, 64 rows); the path of the
 // accepted node and its key weights in LDS, then S_a row by row.
 #include "gdr_device.hpp"
@@ -36,16 +36,6 @@ namespace {
 constexpr int kTreeMax = 64;      // nodes per tree
 constexpr int kTreeRows = 64;     // state rows per workgroup
 
-// Sum over the LPR (4 or 8) consecutive lanes of a state row, left in each.
-template <int LPR>
-__device__ __forceinline__ float tree_row_sum(float x) {
-    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xf, 0xf, false));
-    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xf, 0xf, false));
-    if constexpr (LPR == 8)
-        x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x141, 0xf, 0xf, false));
-    return x;
-}
-
 // Parent of node i as the kernels read it: anything but -1 or an earlier node
 // is read as -1 (keeps every index in range; the header documents it).
 __device__ __forceinline__ int tree_parent(const int32_t* parent, int i) {
@@ -53,39 +43,43 @@ __device__ __forceinline__ int tree_parent(const int32_t* parent, int i) {
     return (p >= 0 && p < i) ? p : -1;
 }
 
-// LDS carve-up of the verify kernel for Td nodes (in floats): the nodes' raw
-// keys and queries (fp32), their path log-decays (then the decays e^g), A
-// (then M = P T), T and P, the per-wave staging of R and Qg S^T (in P's place
-// once P is spent, when it fits), beta and the ancestor masks.
+// LDS carve-up of the verify kernel for Td nodes (in floats): the nodes' keys
+// and queries (fp32; raw for A and P, then scaled by their path decays) and
+// their path log-decays, rows padded to DK + 4 floats so that the pair sums
+// (one node pair per thread, every thread at the same channel) spread over the
+// banks; A (then M = P T), T and P; beta, the ancestor masks, the offsets of
+// each node's pairs in the pair list and the parents as the kernel reads them.
 struct TreeLds {
     int td, dk;
-    __host__ __device__ size_t rpp() const { return 1024 / dk; }                 // rows per wave pass
-    __host__ __device__ size_t stg_n() const { return 4 * rpp() * td * 2; }
-    __host__ __device__ bool stg_in_p() const { return stg_n() <= (size_t)td * td; }
-    __host__ __device__ size_t kr() const { return 0; }                          // [Td][dk]
-    __host__ __device__ size_t qr() const { return kr() + (size_t)td * dk; }    // [Td][dk]
-    __host__ __device__ size_t ge() const { return qr() + (size_t)td * dk; }    // [Td][dk] g, then e^g
-    __host__ __device__ size_t am() const { return ge() + (size_t)td * dk; }    // [Td][Td] A, then M = P T
+    __host__ __device__ int ks() const { return dk + 4; }                       // key row stride
+    __host__ __device__ size_t kr() const { return 0; }                          // [Td][ks]
+    __host__ __device__ size_t qr() const { return kr() + (size_t)td * ks(); }  // [Td][ks]
+    __host__ __device__ size_t ge() const { return qr() + (size_t)td * ks(); }  // [Td][ks] path log-decay
+    __host__ __device__ size_t am() const { return ge() + (size_t)td * ks(); }  // [Td][Td] A, then M = P T
     __host__ __device__ size_t tm() const { return am() + (size_t)td * td; }    // [Td][Td] T
     __host__ __device__ size_t pm() const { return tm() + (size_t)td * td; }    // [Td][Td] P
-    __host__ __device__ size_t stg() const { return stg_in_p() ? pm() : pm() + (size_t)td * td; }
-    __host__ __device__ size_t bet() const { return pm() + (size_t)td * td + (stg_in_p() ? 0 : stg_n()); }
+    __host__ __device__ size_t bet() const { return pm() + (size_t)td * td; }   // [Td]
     __host__ __device__ size_t anc() const { return (bet() + td + 1) / 2 * 2; }  // [Td] uint64
-    __host__ __device__ size_t off() const { return anc() + 2 * (size_t)td; }   // [Td + 1] int: pair offsets
-    __host__ __device__ size_t floats() const { return off() + td + 1; }
+    __host__ __device__ size_t off() const { return anc() + 2 * (size_t)td; }   // [Td + 1] int
+    __host__ __device__ size_t pa() const { return off() + td + 1; }            // [Td] int parents
+    __host__ __device__ size_t floats() const { return pa() + td; }
 };
 
-// One workgroup per (b, h): the whole head's rows, in passes of 4 * RPP.
-template <typename E, bool CHANNEL, int DK>
+// One workgroup per (b, h); NT = ceil(Td / 16) node tiles.  Wave w owns the
+// value columns of tiles w, w + 4, ... (DK / 64 tiles of 16 columns); its
+// slice of the state and of the values is loaded first, so that the loads are
+// in flight while the workgroup builds A, T and M.
+template <typename E, bool CHANNEL, int DK, int NT>
 __global__ __launch_bounds__(256) void tree_verify_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta, const float* __restrict__ S_in,
     const int32_t* __restrict__ parent, E* __restrict__ o, float* __restrict__ D, int H, int Td, int DV) {
-    constexpr int LPR = DK / 16;         // lanes per state row
-    constexpr int RPP = kWave / LPR;     // rows per wave pass
-    constexpr int CPL = DK / kWave;      // channels per lane in the pair sums
+    using MF = Mma<float>;
+    constexpr int TPW = DK / 64;          // value tiles per wave
+    constexpr int KT = DK / 16;           // channel groups of the contraction
     extern __shared__ __attribute__((aligned(16))) float tl[];
     const TreeLds L{Td, DK};
+    const int KS = L.ks();
     float* kr = tl + L.kr();
     float* qr = tl + L.qr();
     float* ge = tl + L.ge();
@@ -95,19 +89,65 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
     float* bet = tl + L.bet();
     uint64_t* anc = reinterpret_cast<uint64_t*>(tl + L.anc());
     int* off = reinterpret_cast<int*>(tl + L.off());
+    int* pa = reinterpret_cast<int*>(tl + L.pa());
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 15, g4 = lane >> 4;
     const int64_t bh = blockIdx.x;
     const int64_t b = bh / H, h = bh % H;
     const int32_t* par = parent + b * Td;
     auto node_row = [&](int i) { return (b * Td + i) * H + h; };   // row of [B, Td, H, *]
 
-    // ---- inputs of every node into LDS; ancestor masks, and the offsets of
-    //      each node's (ancestor-or-self) pairs in one list ----
-    if (tid == 0) {
+    // ---- this wave's state columns and values (lane (col, g4) holds value
+    //      column 16 nt + col: the state row's channels 16 t + 4 g4 .. + 3 and
+    //      the values of nodes 16 mt + 4 g4 + e) ----
+    f32x4 sb[TPW][KT];
+    float vv[TPW][NT][4];
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+        const int vcol = 16 * (wave + 4 * u) + col;
+#pragma unroll
+        for (int t = 0; t < KT; ++t)
+            sb[u][t] = __builtin_nontemporal_load(
+                reinterpret_cast<const f32x4*>(S_in + (bh * DV + vcol) * (int64_t)DK + 16 * t + 4 * g4));
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int nd = 16 * mt + 4 * g4 + e;
+                vv[u][mt][e] = nd < Td ? to_f32(v[node_row(nd) * DV + vcol]) : 0.f;
+            }
+    }
+
+    // ---- inputs of every node into LDS; A and P start at zero ----
+    for (int e = tid; e < Td * Td; e += 256) {
+        am[e] = 0.f;
+        pm[e] = 0.f;
+    }
+    if (tid < Td) {
+        bet[tid] = beta[node_row(tid)];
+        pa[tid] = tree_parent(par, tid);
+    }
+    for (int e = tid; e < Td * DK; e += 256) {
+        const int i = e / DK, c = e % DK;
+        kr[i * KS + c] = to_f32(k[node_row(i) * DK + c]);
+        qr[i * KS + c] = to_f32(q[node_row(i) * DK + c]);
+        if (CHANNEL || c == 0) ge[i * KS + c] = CHANNEL ? log_alpha[node_row(i) * DK + c] : log_alpha[node_row(i)];
+    }
+    __syncthreads();
+    // ---- path log-decays (thread c follows channel c down the tree); on the
+    //      last wave, the ancestor masks and the offsets of each node's
+    //      (ancestor-or-self) pairs in one list ----
+    if (tid < (CHANNEL ? DK : 1)) {
+        for (int i = 0; i < Td; ++i) {
+            const int p = pa[i];
+            if (p >= 0) ge[i * KS + tid] += ge[p * KS + tid];
+        }
+    }
+    if (tid == 192) {
         int n = 0;
         for (int i = 0; i < Td; ++i) {
-            const int p = tree_parent(par, i);
+            const int p = pa[i];
             const uint64_t a = p < 0 ? 0ull : (anc[p] | (1ull << p));
             anc[i] = a;
             off[i] = n;
@@ -115,29 +155,9 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
         }
         off[Td] = n;
     }
-    if (tid < Td) bet[tid] = beta[node_row(tid)];
-    for (int e = tid; e < Td * DK; e += 256) {
-        const int i = e / DK, c = e % DK;
-        kr[e] = to_f32(k[node_row(i) * DK + c]);
-        qr[e] = to_f32(q[node_row(i) * DK + c]);
-        if (CHANNEL || c == 0) ge[e] = CHANNEL ? log_alpha[node_row(i) * DK + c] : log_alpha[node_row(i)];
-    }
-    __syncthreads();
-    // ---- path log-decays: thread c follows channel c down the tree ----
-    if (tid < (CHANNEL ? DK : 1)) {
-        for (int i = 0; i < Td; ++i) {
-            const int p = tree_parent(par, i);
-            if (p >= 0) ge[i * DK + tid] += ge[p * DK + tid];
-        }
-    }
     __syncthreads();
     // ---- A and P over the (ancestor-or-self) pairs: the pairs of the list
     //      one per thread, each a sum over the channels from LDS ----
-    for (int e = tid; e < Td * Td; e += 256) {
-        am[e] = 0.f;
-        pm[e] = 0.f;
-    }
-    __syncthreads();
     const int npairs = off[Td];
     for (int t = tid; t < npairs; t += 256) {
         int lo = 0, hi = Td - 1;   // the node i with off[i] <= t < off[i + 1]
@@ -150,9 +170,9 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
         uint64_t m = anc[i] | (1ull << i);
         for (int r = t - off[i]; r > 0; --r) m &= m - 1ull;
         const int j = __builtin_ctzll(m);
-        const float* ki = kr + i * DK;
-        const float* kj = kr + j * DK;
-        const float* qi = qr + i * DK;
+        const float* ki = kr + i * KS;
+        const float* kj = kr + j * KS;
+        const float* qi = qr + i * KS;
         float a = 0.f, pp = 0.f;
 #pragma unroll 4
         for (int c = 0; c < DK; c += 4) {
@@ -160,8 +180,8 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
             float4 y = *reinterpret_cast<const float4*>(kj + c);
             const float4 z = *reinterpret_cast<const float4*>(qi + c);
             if constexpr (CHANNEL) {
-                const float4 gi = *reinterpret_cast<const float4*>(ge + i * DK + c);
-                const float4 gj = *reinterpret_cast<const float4*>(ge + j * DK + c);
+                const float4 gi = *reinterpret_cast<const float4*>(ge + i * KS + c);
+                const float4 gj = *reinterpret_cast<const float4*>(ge + j * KS + c);
                 y = make_float4(y.x * __expf(gi.x - gj.x), y.y * __expf(gi.y - gj.y), y.z * __expf(gi.z - gj.z),
                                 y.w * __expf(gi.w - gj.w));
             }
@@ -169,7 +189,7 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
             pp += z.x * y.x + z.y * y.y + z.z * y.z + z.w * y.w;
         }
         if constexpr (!CHANNEL) {
-            const float w = __expf(ge[i * DK] - ge[j * DK]);
+            const float w = __expf(ge[i * KS] - ge[j * KS]);
             a *= w;
             pp *= w;
         }
@@ -177,11 +197,15 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
         pm[i * Td + j] = pp;
     }
     __syncthreads();
-    // ---- decays e^g (g is spent); T = (I + A)^-1 Diag(beta): thread j builds
-    //      column j by forward substitution (only ancestors contribute) ----
-    for (int e = tid; e < Td * (CHANNEL ? DK : 1); e += 256) {
-        const int i = CHANNEL ? e / DK : e, c = CHANNEL ? e % DK : 0;
-        ge[i * DK + c] = __expf(ge[i * DK + c]);
+    // ---- keys and queries scaled by their path decays, Kg = k e^g and
+    //      Qg = q e^g (the raw ones are spent); T = (I + A)^-1 Diag(beta):
+    //      thread j builds column j by forward substitution (only ancestors
+    //      contribute) ----
+    for (int e = tid; e < Td * DK; e += 256) {
+        const int i = e / DK, c = e % DK;
+        const float w = __expf(ge[i * KS + (CHANNEL ? c : 0)]);
+        kr[i * KS + c] *= w;
+        qr[i * KS + c] *= w;
     }
     if (tid < Td) {
         const int j = tid;
@@ -218,65 +242,68 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
         }
         am[e] = x;   // A is no longer read
     }
-    __syncthreads();   // P is spent: the staging may take its place
+    __syncthreads();
 
-    // ---- the state rows ----
-    const int cl = lane % LPR, rw = lane / LPR;
-    float* stg = tl + L.stg() + (size_t)wave * RPP * Td * 2;
-    for (int p0 = 0; p0 < DV; p0 += 4 * RPP) {
-        const int row = p0 + wave * RPP + rw;
-        const int64_t sbase = (bh * DV + row) * (int64_t)DK;
-        f32x4 s[4];
+    // ---- the outputs on the matrix cores (fp32 16x16x4), per value tile:
+    //      R = V - Kg S^T and Qg S^T for every node tile, then D = T R and
+    //      o = Qg S^T + M R.  The contractions over channels and over nodes
+    //      use the permuted k-map: k-step s of lane group g is channel (or
+    //      node) 16(s/4) + 4g + s%4, so an accumulator tile is directly the B
+    //      operand of the next product and each lane's state slice is one
+    //      16-byte load per four steps. ----
+    auto lds_or0 = [&](const float* base, int rowi, int coli) {
+        return (rowi < Td && coli < Td) ? base[rowi * Td + coli] : 0.f;
+    };
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            s[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S_in + sbase + 4 * (cl + LPR * j)));
-        // v of every node for this row, loaded together (the R slots take it)
-        for (int i = cl; i < Td; i += LPR) stg[(rw * Td + i) * 2] = to_f32(v[node_row(i) * DV + row]);
-        __syncthreads();
-#pragma unroll 2
-        for (int i = 0; i < Td; ++i) {
-            float pd = 0.f, od = 0.f;
+    for (int u = 0; u < TPW; ++u) {
+        const int vcol = 16 * (wave + 4 * u) + col;
+        f32x4 R[NT], O[NT];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int c = 4 * (cl + LPR * j);
-                float4 kv = *reinterpret_cast<const float4*>(kr + i * DK + c);
-                float4 qv = *reinterpret_cast<const float4*>(qr + i * DK + c);
-                if constexpr (CHANNEL) {
-                    const float4 ev = *reinterpret_cast<const float4*>(ge + i * DK + c);
-                    kv = make_float4(kv.x * ev.x, kv.y * ev.y, kv.z * ev.z, kv.w * ev.w);
-                    qv = make_float4(qv.x * ev.x, qv.y * ev.y, qv.z * ev.z, qv.w * ev.w);
+        for (int mt = 0; mt < NT; ++mt) {
+            R[mt] = zero4();
+            O[mt] = zero4();
+            const int node = 16 * mt + col;
+#pragma unroll
+            for (int t = 0; t < KT; ++t) {
+                float4 ka = make_float4(0.f, 0.f, 0.f, 0.f), qa = ka;
+                if (node < Td) {
+                    ka = *reinterpret_cast<const float4*>(kr + node * KS + 16 * t + 4 * g4);
+                    qa = *reinterpret_cast<const float4*>(qr + node * KS + 16 * t + 4 * g4);
                 }
-                pd += s[j][0] * kv.x + s[j][1] * kv.y + s[j][2] * kv.z + s[j][3] * kv.w;
-                od += s[j][0] * qv.x + s[j][1] * qv.y + s[j][2] * qv.z + s[j][3] * qv.w;
+                R[mt] = MF::mma(ka.x, sb[u][t][0], R[mt]);
+                O[mt] = MF::mma(qa.x, sb[u][t][0], O[mt]);
+                R[mt] = MF::mma(ka.y, sb[u][t][1], R[mt]);
+                O[mt] = MF::mma(qa.y, sb[u][t][1], O[mt]);
+                R[mt] = MF::mma(ka.z, sb[u][t][2], R[mt]);
+                O[mt] = MF::mma(qa.z, sb[u][t][2], O[mt]);
+                R[mt] = MF::mma(ka.w, sb[u][t][3], R[mt]);
+                O[mt] = MF::mma(qa.w, sb[u][t][3], O[mt]);
             }
-            pd = tree_row_sum<LPR>(pd);
-            od = tree_row_sum<LPR>(od);
-            if constexpr (!CHANNEL) {
-                const float ei = ge[i * DK];
-                pd *= ei;
-                od *= ei;
-            }
-            if (cl == 0) {
-                stg[(rw * Td + i) * 2] -= pd;         // R_i = v_i - (Kg S^T)_i
-                stg[(rw * Td + i) * 2 + 1] = od;      // (Qg S^T)_i
+#pragma unroll
+            for (int e = 0; e < 4; ++e) R[mt][e] = vv[u][mt][e] - R[mt][e];
+        }
+        // D = T R and o = O + M R (T and M are lower triangular in node order)
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt) {
+            f32x4 Dt = zero4(), Ot = O[mt];
+            const int i = 16 * mt + col;
+#pragma unroll
+            for (int jt = 0; jt <= mt; ++jt)
+#pragma unroll
+                for (int s2 = 0; s2 < 4; ++s2) {
+                    const int j = 16 * jt + 4 * g4 + s2;
+                    Dt = MF::mma(lds_or0(tm, i, j), R[jt][s2], Dt);
+                    Ot = MF::mma(lds_or0(am, i, j), R[jt][s2], Ot);
+                }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int nd = 16 * mt + 4 * g4 + e;
+                if (nd < Td) {
+                    if (D) D[node_row(nd) * DV + vcol] = Dt[e];
+                    if (o) o[node_row(nd) * DV + vcol] = from_f32<E>(Ot[e]);
+                }
             }
         }
-        __syncthreads();
-        // the row's lanes split the nodes: D_i = T R, o_i = O0_i + M R
-        for (int i = cl; i < Td; i += LPR) {
-            float d = 0.f, y = stg[(rw * Td + i) * 2 + 1];
-            uint64_t m = anc[i] | (1ull << i);
-            while (m) {
-                const int j = __builtin_ctzll(m);
-                m &= m - 1ull;
-                const float r = stg[(rw * Td + j) * 2];
-                d += tm[i * Td + j] * r;
-                y += am[i * Td + j] * r;
-            }
-            if (D) D[node_row(i) * DV + row] = d;
-            if (o) o[node_row(i) * DV + row] = from_f32<E>(y);
-        }
-        __syncthreads();
     }
 }
 
@@ -348,19 +375,29 @@ __global__ __launch_bounds__(256) void tree_commit_kernel(
     }
 }
 
+template <typename E, bool CHANNEL, int DK, int NT>
+hipError_t launch_tree_nt(const TreeArgs& a) {
+    const int64_t grid = a.B * a.H;
+    const size_t lds = TreeLds{(int)a.Td, DK}.floats() * sizeof(float);
+    const auto fn = &tree_verify_kernel<E, CHANNEL, DK, NT>;
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(256), lds, a.stream, (const E*)a.q, (const E*)a.k,
+                       (const E*)a.v, a.log_alpha, a.beta, a.S_in, a.parent, (E*)a.o, a.D, (int)a.H, (int)a.Td,
+                       (int)a.dv);
+    return hipGetLastError();
+}
+
 template <typename E, bool CHANNEL, int DK>
 hipError_t launch_tree(const TreeArgs& a) {
-    const int64_t grid = a.B * a.H;
-    if (a.o || a.D) {
-        const size_t lds = TreeLds{(int)a.Td, DK}.floats() * sizeof(float);
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&tree_verify_kernel<E, CHANNEL, DK>),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((tree_verify_kernel<E, CHANNEL, DK>), dim3((unsigned)grid), dim3(256), lds, a.stream,
-                           (const E*)a.q, (const E*)a.k, (const E*)a.v, a.log_alpha, a.beta, a.S_in, a.parent,
-                           (E*)a.o, a.D, (int)a.H, (int)a.Td, (int)a.dv);
+    if (!a.o && !a.D) return hipSuccess;
+    switch ((a.Td + 15) / 16) {   // node tiles; Td is in [1, 64]
+        case 1: return launch_tree_nt<E, CHANNEL, DK, 1>(a);
+        case 2: return launch_tree_nt<E, CHANNEL, DK, 2>(a);
+        case 3: return launch_tree_nt<E, CHANNEL, DK, 3>(a);
+        default: return launch_tree_nt<E, CHANNEL, DK, 4>(a);
     }
-    return hipGetLastError();
 }
 
 template <typename E, bool CHANNEL, int DK>
