@@ -6,6 +6,8 @@ runs on scratch that still holds the first call's contents.  Both entry points
 launch the same kernels on the same inputs, so the outputs must agree bit for
 bit; each is also checked against the oracle at the parity bar (2e-2 normwise
 for bf16 io, 1e-4 for fp32)."""
+import gc
+
 import numpy as np
 import pytest
 
@@ -34,11 +36,14 @@ def _run_both(inp, io, chunk):
     o_ref, st_ref = gdr_chunk_fwd(*args, chunk=chunk)
     o = torch.full_like(o_ref, float("nan"))
     st = torch.full_like(st_ref, float("nan"))
+    gc.collect()
     torch.cuda.synchronize()
-    before = torch.cuda.memory_allocated()
+    # the allocator's running count of allocation requests: frees of earlier
+    # tests' tensors during the call leave it unchanged
+    before = torch.cuda.memory_stats()["allocation.all.allocated"]
     gdr_chunk_fwd_noalloc(*args, chunk=chunk, o=o, S_T=st)
     torch.cuda.synchronize()
-    assert torch.cuda.memory_allocated() == before
+    assert torch.cuda.memory_stats()["allocation.all.allocated"] == before
     return (o, st), (o_ref, st_ref)
 
 
