@@ -750,11 +750,23 @@ __device__ __forceinline__ void chan_prep_wave(ChanPrepSmem<DK, C>& sm, const __
     }
 
     // Loads of channel step s: k or q (bf16x8, normalised by the prologue),
-    // log alpha (in log2 units).
-    auto ld_qk = [&](const __bf16* p, int s) {
-        const bf16x8 t = *reinterpret_cast<const bf16x8*>(p + grow * DK + 32 * s + 8 * kg);
+    // log alpha (in log2 units); the raw loads and their mapping are split so
+    // that the main loop can issue a step's loads one step ahead.
+    struct Raw {
+        bf16x8 k, q;
+        float4 l0, l1;
+    };
+    auto ld_raw = [&](int s) {
+        Raw w;
+        w.k = *reinterpret_cast<const bf16x8*>(k + grow * DK + 32 * s + 8 * kg);
+        w.q = *reinterpret_cast<const bf16x8*>(q + grow * DK + 32 * s + 8 * kg);
+        const float* p = log_alpha + grow * DK + 32 * s + 8 * kg;
+        w.l0 = *reinterpret_cast<const float4*>(p);
+        w.l1 = *reinterpret_cast<const float4*>(p + 4);
+        return w;
+    };
+    auto map_qk = [&](bf16x8 t, float sc) {
         if constexpr (NORM) {
-            const float sc = p == k ? nk : nq;
             bf16x8 u;
 #pragma unroll
             for (int j = 0; j < 8; ++j) u[j] = (__bf16)((float)t[j] * sc);
@@ -763,10 +775,7 @@ __device__ __forceinline__ void chan_prep_wave(ChanPrepSmem<DK, C>& sm, const __
             return valid ? t : bf16x8{};
         }
     };
-    auto ld_la = [&](int s, float* la) {
-        const float* p = log_alpha + grow * DK + 32 * s + 8 * kg;
-        const float4 l0 = *reinterpret_cast<const float4*>(p);
-        const float4 l1 = *reinterpret_cast<const float4*>(p + 4);
+    auto map_la = [&](float4 l0, float4 l1, float* la) {
         const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -800,11 +809,23 @@ __device__ __forceinline__ void chan_prep_wave(ChanPrepSmem<DK, C>& sm, const __
     bool unsafe_lane = false;
     // ---- per channel step s: g, the scaled operands, this block's B side,
     //      then the Gram tiles (b, cb <= b) ----
+    // (64-token chunks without the prologue: elsewhere the extra registers
+    // spill or lower the occupancy)
+    constexpr bool PREFETCH = !NORM && C == 64;
+    Raw nxt{};
+    if constexpr (PREFETCH) nxt = ld_raw(0);
 #pragma unroll 1
     for (int s = 0; s < NKS; ++s) {
+        Raw cur;
+        if constexpr (!PREFETCH) {
+            cur = ld_raw(s);
+        } else {
+            cur = nxt;
+            if (s + 1 < NKS) nxt = ld_raw(s + 1);
+        }
         float gs[8];
-        ld_la(s, gs);
-        const bf16x8 kv = ld_qk(k, s), qv = ld_qk(q, s);
+        map_la(cur.l0, cur.l1, gs);
+        const bf16x8 kv = map_qk(cur.k, nk), qv = map_qk(cur.q, nq);
         scan(gs);
         if (x == 15) {
             float* tp = &tot[b][32 * s + 8 * kg];
@@ -916,8 +937,9 @@ __device__ __forceinline__ void chan_prep_wave(ChanPrepSmem<DK, C>& sm, const __
 #pragma unroll 1
             for (int s = 0; s < NKS; ++s) {
                 float gs[8];
-                ld_la(s, gs);
-                const bf16x8 kv = ld_qk(k, s), qv = ld_qk(q, s);
+                const Raw raw = ld_raw(s);
+                map_la(raw.l0, raw.l1, gs);
+                const bf16x8 kv = map_qk(raw.k, nk), qv = map_qk(raw.q, nq);
                 scan(gs);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
