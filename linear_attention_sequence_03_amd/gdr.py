@@ -529,6 +529,7 @@ def gdr_decode_tree_commit(k, log_alpha, parent, D, accepted, S, S_out=None, inp
     dv = D.shape[-1]
     io = _io_code(k.dtype)
     gate = GDR_GATE_CHANNEL if log_alpha.dim() == 4 else GDR_GATE_SCALAR
+    _need("k", k, k.dtype, (B, Td, H, dk), dev)
     _need("log_alpha", log_alpha, torch.float32,
           (B, Td, H, dk) if gate == GDR_GATE_CHANNEL else (B, Td, H), dev)
     _need("parent", parent, torch.int32, (B, Td), dev)

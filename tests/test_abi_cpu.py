@@ -207,6 +207,12 @@ def test_binding_type_checks_before_calling():
         gdr.gdr_chunk_fwd(q.double(), q, q, torch.zeros(1, 4, 1), torch.zeros(1, 4, 1))
     with pytest.raises(ValueError):
         gdr.gdr_chunk_fwd(q, q, q, torch.zeros(1, 4, 2), torch.zeros(1, 4, 1))
+    # the tree commit takes its sizes from k, which must be contiguous like every other tensor
+    kt = torch.zeros(1, 4, 1, 128)[..., ::2]
+    with pytest.raises(ValueError, match="k must be contiguous"):
+        gdr.gdr_decode_tree_commit(kt, torch.zeros(1, 4, 1), torch.zeros(1, 4, dtype=torch.int32),
+                                   torch.zeros(1, 4, 1, 64), torch.zeros(1, dtype=torch.int32),
+                                   torch.zeros(1, 1, 64, 64))
 
 
 # ----- channel-wise write rates (FG2) ----------------------------------------
