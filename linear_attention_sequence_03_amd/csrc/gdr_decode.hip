@@ -136,23 +136,44 @@ __device__ __forceinline__ float row_sum(float x) {
 // state after the first n tokens is stored, n = accepted[b] clamped to
 // [0, Td] (Td when accepted is NULL; nothing stored when S_out is NULL).
 // S_out may equal S_in: a lane writes only the slices it read, after reading.
+//
+// Every wave of a workgroup works on the same (b, h), so the draft tokens'
+// inputs (k, q, the decay, beta, and the values of the workgroup's rows) are
+// staged in LDS once per workgroup, kMultiGroup tokens at a time, with the
+// loads of the first group in flight together with the state loads; the token
+// loop then reads them from LDS instead of waiting on global memory per token.
+constexpr int kMultiGroup = 16;
+
+template <int DK>
+struct MultiShape {
+    static constexpr int LPR = DK / 16;           // lanes per state row
+    static constexpr int RPP = kWave / LPR;       // rows per pass of one wave
+    static constexpr int NPASS = 2;
+    static constexpr int RPW = RPP * NPASS;       // rows per wave
+    static constexpr int WPH = DK / RPW;          // waves per (b, h) (d_v = d_k)
+    static constexpr int WPB = WPH < 4 ? WPH : 4; // waves per workgroup
+    static constexpr int ROWS = WPB * RPW;        // state rows per workgroup
+};
+
 template <typename E, bool CHANNEL, int DK>
-__global__ __launch_bounds__(256) void decode_multi_kernel(
+__global__ __launch_bounds__(64 * MultiShape<DK>::WPB) void decode_multi_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta, const float* S_in,
-    float* S_out, const int32_t* __restrict__ accepted, E* __restrict__ o, int64_t BH, int H,
-    int Td, int DV) {
-    constexpr int LPR = DK / 16;     // lanes per state row
-    constexpr int RPP = kWave / LPR; // rows per pass of one wave
-    constexpr int NPASS = 2;
-    constexpr int RPW = RPP * NPASS; // rows per wave
-    const int lane = threadIdx.x & 63;
-    const int64_t gw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int wpb = DV / RPW;
-    const int64_t bh = gw / wpb;
-    if (bh >= BH) return;
+    float* S_out, const int32_t* __restrict__ accepted, E* __restrict__ o, int H, int Td, int DV) {
+    using MS = MultiShape<DK>;
+    constexpr int LPR = MS::LPR, RPP = MS::RPP, NPASS = MS::NPASS, RPW = MS::RPW, ROWS = MS::ROWS;
+    constexpr int NTH = 64 * MS::WPB;
+    constexpr int G = kMultiGroup;
+    constexpr int LA = CHANNEL ? DK : 1;          // decay values per token
+    __shared__ __attribute__((aligned(16))) float sk[G][DK], sq[G][DK], sla[G][LA], sbt[G], sv[G][ROWS];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    // workgroups tile the (b, h) rows exactly: every wave of one is on the same (b, h)
+    const int nblk = DV / ROWS;
+    const int64_t bh = blockIdx.x / nblk;
+    const int rbase = (int)(blockIdx.x % nblk) * ROWS;   // first row of the workgroup
     const int64_t b = bh / H, h = bh % H;
-    const int row0 = (int)(gw % wpb) * RPW + lane / LPR;
+    const int row0 = rbase + (tid >> 6) * RPW + lane / LPR;
     const int cl = lane % LPR;
     int nacc = Td;
     if (accepted) nacc = min(max(accepted[b], 0), Td);
@@ -173,63 +194,86 @@ __global__ __launch_bounds__(256) void decode_multi_kernel(
                 __builtin_nontemporal_store(s[p][j], reinterpret_cast<f32x4*>(S_out + sp(p, j)));
     };
     if (S_out && nacc == 0) store_state();
-    for (int t = 0; t < Td; ++t) {
-        const int64_t bth = (b * Td + t) * H + h;   // token row of [B, Td, H, *]
-        float4 kk[4], qq[4], aa[4];
-        float a1 = 1.f;
-        if constexpr (!CHANNEL) a1 = expf(log_alpha[bth]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int c = 4 * (cl + LPR * j);
-            kk[j] = load4(k + bth * DK + c);
-            qq[j] = load4(q + bth * DK + c);
-            if constexpr (CHANNEL) {
-                const float4 la = *reinterpret_cast<const float4*>(log_alpha + bth * DK + c);
-                aa[j] = make_float4(expf(la.x), expf(la.y), expf(la.z), expf(la.w));
-            } else {
-                aa[j] = make_float4(a1, a1, a1, a1);
-            }
+    for (int t0 = 0; t0 < Td; t0 += G) {
+        const int ng = Td - t0 < G ? Td - t0 : G;
+        if (t0 > 0) __syncthreads();   // every wave is done with the previous group
+        // ---- stage tokens t0 .. t0 + ng - 1 (as fp32) ----
+        for (int e = tid; e < ng * (DK / 4); e += NTH) {
+            const int i = e / (DK / 4), c = 4 * (e % (DK / 4));
+            const int64_t bth = (b * Td + t0 + i) * H + h;
+            *reinterpret_cast<float4*>(&sk[i][c]) = load4(k + bth * DK + c);
+            *reinterpret_cast<float4*>(&sq[i][c]) = load4(q + bth * DK + c);
+            if constexpr (CHANNEL)
+                *reinterpret_cast<float4*>(&sla[i][c]) = *reinterpret_cast<const float4*>(log_alpha + bth * DK + c);
         }
-        const float bt = beta[bth];
-#pragma unroll
-        for (int p = 0; p < NPASS; ++p) {
-            const int row = row0 + p * RPP;
-            float pd = 0.f;
+        for (int e = tid; e < ng * ROWS; e += NTH) {
+            const int i = e / ROWS, r = e % ROWS;
+            const int64_t bth = (b * Td + t0 + i) * H + h;
+            sv[i][r] = to_f32(v[bth * DV + rbase + r]);
+        }
+        if (tid < ng) {
+            const int64_t bth = (b * Td + t0 + tid) * H + h;
+            sbt[tid] = beta[bth];
+            if constexpr (!CHANNEL) sla[tid][0] = log_alpha[bth];
+        }
+        __syncthreads();
+        for (int i = 0; i < ng; ++i) {
+            const int t = t0 + i;
+            const int64_t bth = (b * Td + t) * H + h;   // token row of [B, Td, H, *]
+            float4 kk[4], qq[4], aa[4];
+            float a1 = 1.f;
+            if constexpr (!CHANNEL) a1 = expf(sla[i][0]);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                s[p][j][0] *= aa[j].x; s[p][j][1] *= aa[j].y;
-                s[p][j][2] *= aa[j].z; s[p][j][3] *= aa[j].w;
-                pd += s[p][j][0] * kk[j].x + s[p][j][1] * kk[j].y + s[p][j][2] * kk[j].z +
-                      s[p][j][3] * kk[j].w;
+                const int c = 4 * (cl + LPR * j);
+                kk[j] = *reinterpret_cast<const float4*>(&sk[i][c]);
+                qq[j] = *reinterpret_cast<const float4*>(&sq[i][c]);
+                if constexpr (CHANNEL) {
+                    const float4 la = *reinterpret_cast<const float4*>(&sla[i][c]);
+                    aa[j] = make_float4(expf(la.x), expf(la.y), expf(la.z), expf(la.w));
+                } else {
+                    aa[j] = make_float4(a1, a1, a1, a1);
+                }
             }
-            pd = row_sum<LPR>(pd);
-            const float u = bt * (to_f32(v[bth * DV + row]) - pd);
-            float od = 0.f;
+            const float bt = sbt[i];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                s[p][j][0] += u * kk[j].x; s[p][j][1] += u * kk[j].y;
-                s[p][j][2] += u * kk[j].z; s[p][j][3] += u * kk[j].w;
-                od += s[p][j][0] * qq[j].x + s[p][j][1] * qq[j].y + s[p][j][2] * qq[j].z +
-                      s[p][j][3] * qq[j].w;
+            for (int p = 0; p < NPASS; ++p) {
+                const int row = row0 + p * RPP;
+                float pd = 0.f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    s[p][j][0] *= aa[j].x; s[p][j][1] *= aa[j].y;
+                    s[p][j][2] *= aa[j].z; s[p][j][3] *= aa[j].w;
+                    pd += s[p][j][0] * kk[j].x + s[p][j][1] * kk[j].y + s[p][j][2] * kk[j].z +
+                          s[p][j][3] * kk[j].w;
+                }
+                pd = row_sum<LPR>(pd);
+                const float u = bt * (sv[i][row - rbase] - pd);
+                float od = 0.f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    s[p][j][0] += u * kk[j].x; s[p][j][1] += u * kk[j].y;
+                    s[p][j][2] += u * kk[j].z; s[p][j][3] += u * kk[j].w;
+                    od += s[p][j][0] * qq[j].x + s[p][j][1] * qq[j].y + s[p][j][2] * qq[j].z +
+                          s[p][j][3] * qq[j].w;
+                }
+                if (o) {
+                    od = row_sum<LPR>(od);
+                    if (cl == 0) o[bth * DV + row] = from_f32<E>(od);
+                }
             }
-            if (o) {
-                od = row_sum<LPR>(od);
-                if (cl == 0) o[bth * DV + row] = from_f32<E>(od);
-            }
+            if (S_out && t + 1 == nacc) store_state();
         }
-        if (S_out && t + 1 == nacc) store_state();
     }
 }
 
 template <typename E, bool CHANNEL, int DK>
 static hipError_t launch_decode_multi(const DecodeMultiArgs& a) {
-    constexpr int RPW = (kWave / (DK / 16)) * 2;
-    const int64_t waves = a.B * a.H * (a.dv / RPW);
-    const int64_t blocks = (waves + 3) / 4;
-    hipLaunchKernelGGL((decode_multi_kernel<E, CHANNEL, DK>), dim3((unsigned)blocks), dim3(256), 0,
+    using MS = MultiShape<DK>;
+    const int64_t blocks = a.B * a.H * (a.dv / MS::ROWS);
+    hipLaunchKernelGGL((decode_multi_kernel<E, CHANNEL, DK>), dim3((unsigned)blocks), dim3(64 * MS::WPB), 0,
                        a.stream, (const E*)a.q, (const E*)a.k, (const E*)a.v, a.log_alpha, a.beta,
-                       a.S_in, a.S_out, a.accepted, (E*)a.o, a.B * a.H, (int)a.H, (int)a.Td,
-                       (int)a.dv);
+                       a.S_in, a.S_out, a.accepted, (E*)a.o, (int)a.H, (int)a.Td, (int)a.dv);
     return hipGetLastError();
 }
 

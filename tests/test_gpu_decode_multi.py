@@ -35,9 +35,10 @@ def _call(inp, io, accepted=None, S_out="new", want_o=True):
 OTOL = {"f32": 1e-5, "bf16": 4e-3}
 
 
-@pytest.mark.parametrize("Td", [1, 4, 16])
+# 17 and 40 draft tokens cross the kernel's 16-token staging groups (the last ragged)
+@pytest.mark.parametrize("Td", [1, 4, 16, 17, 40])
 @pytest.mark.parametrize("gate", ["scalar", "channel"])
-@pytest.mark.parametrize("io,d", [("f32", 128), ("f32", 64), ("bf16", 128)])
+@pytest.mark.parametrize("io,d", [("f32", 128), ("f32", 64), ("bf16", 128), ("bf16", 64)])
 def test_decode_multi_parity(io, d, gate, Td):
     B, H = 6, 4
     inp = _inputs(B, Td, H, d, gate, io, seed=100 + Td + d)
