@@ -21,12 +21,16 @@
 // Every exponent is <= 0 (decays are at most 1), so nothing overflows.
 //
 // gdr_decode_tree: one workgroup per (b, h).  The workgroup builds the path
-// decays, A, T and M = P T of its tree in LDS (fp32), scales the keys and
-// queries by their path decays, then each wave takes 16-column tiles of the
-// values and forms R, Qg S^T, D = T R and o = Qg S^T + M R with fp32 MFMA
-// (every product is a small dense contraction; tiles past Td are zeros).
+// decays, A and P of its tree in LDS (fp32) and T as a blocked dense inverse
+// (forward substitution on the 16 x 16 diagonal blocks, then the blocks below
+// on fp32 MFMA; T keeps A's zeros exactly), scales the keys and queries by
+// their path decays, then each wave takes 16-column tiles of the values and
+// forms R, Qg S^T, D = T R and o = Qg S^T + P D with fp32 MFMA (every product
+// is a small dense contraction; node slots past Td are zeros).
 // gdr_decode_tree_commit: one workgroup per (b, h, 64 rows); the path of the
 // accepted node and its key weights in LDS, then S_a row by row.
+#include <type_traits>
+
 #include "gdr_device.hpp"
 #include "gdr_launch.hpp"
 
@@ -36,6 +40,13 @@ namespace {
 constexpr int kTreeMax = 64;      // nodes per tree
 constexpr int kTreeRows = 64;     // state rows per workgroup
 
+// Sum over the four lanes of a quad, left in each (DPP quad permutations).
+__device__ __forceinline__ float quad_sum(float x) {
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xf, 0xf, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xf, 0xf, false));
+    return x;
+}
+
 // Parent of node i as the kernels read it: anything but -1 or an earlier node
 // is read as -1 (keeps every index in range; the header documents it).
 __device__ __forceinline__ int tree_parent(const int32_t* parent, int i) {
@@ -43,32 +54,46 @@ __device__ __forceinline__ int tree_parent(const int32_t* parent, int i) {
     return (p >= 0 && p < i) ? p : -1;
 }
 
-// LDS carve-up of the verify kernel for Td nodes (in floats): the nodes' keys
-// and queries (fp32; raw for A and P, then scaled by their path decays) and
-// their path log-decays, rows padded to DK + 4 floats so that the pair sums
-// (one node pair per thread, every thread at the same channel) spread over the
-// banks; A (then M = P T), T and P; beta, the ancestor masks, the offsets of
-// each node's pairs in the pair list and the parents as the kernel reads them.
+// LDS carve-up of the verify kernel for Td nodes in NP = 16 ceil(Td / 16) node
+// slots (in floats): the nodes' keys and queries (fp32; raw for A and P, then
+// scaled by their path decays) and their path log-decays, rows padded to
+// DK + 4 floats so that the pair sums (one node pair per thread, every thread
+// at the same channel) spread over the banks; A, T and P as NP x NP tiles (rows
+// of NP + 4 floats, zero outside the nodes), the inverted diagonal blocks of
+// I + A, beta (zero past Td), the root paths (ancestor-or-self masks), the
+// offsets of each node's pairs in the pair list and the parents as the kernel
+// reads them (then the pointer-jumping targets).
 struct TreeLds {
-    int td, dk;
+    int td, dk, np;
     __host__ __device__ int ks() const { return dk + 4; }                       // key row stride
+    __host__ __device__ int ns() const { return np + 4; }                       // A / T / P row stride
     __host__ __device__ size_t kr() const { return 0; }                          // [Td][ks]
     __host__ __device__ size_t qr() const { return kr() + (size_t)td * ks(); }  // [Td][ks]
     __host__ __device__ size_t ge() const { return qr() + (size_t)td * ks(); }  // [Td][ks] path log-decay
-    __host__ __device__ size_t am() const { return ge() + (size_t)td * ks(); }  // [Td][Td] A, then M = P T
-    __host__ __device__ size_t tm() const { return am() + (size_t)td * td; }    // [Td][Td] T
-    __host__ __device__ size_t pm() const { return tm() + (size_t)td * td; }    // [Td][Td] P
-    __host__ __device__ size_t bet() const { return pm() + (size_t)td * td; }   // [Td]
-    __host__ __device__ size_t anc() const { return (bet() + td + 1) / 2 * 2; }  // [Td] uint64
+    __host__ __device__ size_t am() const { return ge() + (size_t)td * ks(); }  // [NP][ns] A
+    __host__ __device__ size_t tm() const { return am() + (size_t)np * ns(); }  // [NP][ns] T
+    __host__ __device__ size_t pm() const { return tm() + (size_t)np * ns(); }  // [NP][ns] P
+    __host__ __device__ size_t xd() const { return pm() + (size_t)np * ns(); }  // [NP/16][16][16] (I + A_bb)^-1
+    __host__ __device__ size_t bet() const { return xd() + (size_t)np * 16; }   // [NP]
+    __host__ __device__ size_t anc() const { return (bet() + np + 1) / 2 * 2; }  // [Td] uint64
     __host__ __device__ size_t off() const { return anc() + 2 * (size_t)td; }   // [Td + 1] int
     __host__ __device__ size_t pa() const { return off() + td + 1; }            // [Td] int parents
     __host__ __device__ size_t floats() const { return pa() + td; }
 };
 
+template <typename E>
+using Raw4 = typename std::conditional<sizeof(E) == 4, float4, bf16x4>::type;
+
+template <typename E>
+__device__ __forceinline__ float4 widen4(const Raw4<E>& x) {
+    if constexpr (sizeof(E) == 4) return x;
+    else return make_float4((float)x[0], (float)x[1], (float)x[2], (float)x[3]);
+}
+
 // One workgroup per (b, h); NT = ceil(Td / 16) node tiles.  Wave w owns the
 // value columns of tiles w, w + 4, ... (DK / 64 tiles of 16 columns); its
-// slice of the state and of the values is loaded first, so that the loads are
-// in flight while the workgroup builds A, T and M.
+// slice of the state and of the values, and the nodes' inputs, are loaded
+// first, so that the loads are in flight together.
 template <typename E, bool CHANNEL, int DK, int NT>
 __global__ __launch_bounds__(256) void tree_verify_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
@@ -77,8 +102,12 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
     using MF = Mma<float>;
     constexpr int TPW = DK / 64;          // value tiles per wave
     constexpr int KT = DK / 16;           // channel groups of the contraction
+    constexpr int NP = 16 * NT;           // node slots
+    constexpr int NS = NP + 4;            // A / T / P row stride
+    constexpr int V4 = DK / 4;            // 16-byte units of a key row
+    constexpr int NU = (NP * V4 + 255) / 256;   // node-input units per thread
     extern __shared__ __attribute__((aligned(16))) float tl[];
-    const TreeLds L{Td, DK};
+    const TreeLds L{Td, DK, NP};
     const int KS = L.ks();
     float* kr = tl + L.kr();
     float* qr = tl + L.qr();
@@ -86,6 +115,7 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
     float* am = tl + L.am();
     float* tm = tl + L.tm();
     float* pm = tl + L.pm();
+    float* xd = tl + L.xd();
     float* bet = tl + L.bet();
     uint64_t* anc = reinterpret_cast<uint64_t*>(tl + L.anc());
     int* off = reinterpret_cast<int*>(tl + L.off());
@@ -100,7 +130,8 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
 
     // ---- this wave's state columns and values (lane (col, g4) holds value
     //      column 16 nt + col: the state row's channels 16 t + 4 g4 .. + 3 and
-    //      the values of nodes 16 mt + 4 g4 + e) ----
+    //      the values of nodes 16 mt + 4 g4 + e), and the nodes' keys, queries
+    //      and decays, all loads issued before any is used ----
     f32x4 sb[TPW][KT];
     float vv[TPW][NT][4];
 #pragma unroll
@@ -118,142 +149,212 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
                 vv[u][mt][e] = nd < Td ? to_f32(v[node_row(nd) * DV + vcol]) : 0.f;
             }
     }
+    Raw4<E> kb[NU], qb[NU];
+    float4 lb[CHANNEL ? NU : 1];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+        const int e = tid + 256 * u;
+        if (e < Td * V4) {
+            const int64_t src = node_row(e / V4) * DK + 4 * (e % V4);
+            kb[u] = *reinterpret_cast<const Raw4<E>*>(k + src);
+            qb[u] = *reinterpret_cast<const Raw4<E>*>(q + src);
+            if constexpr (CHANNEL) lb[u] = *reinterpret_cast<const float4*>(log_alpha + src);
+        }
+    }
 
-    // ---- inputs of every node into LDS; A and P start at zero ----
-    for (int e = tid; e < Td * Td; e += 256) {
-        am[e] = 0.f;
-        pm[e] = 0.f;
-    }
+    // ---- A, T and P start at zero; beta (zero past Td), parents, and the
+    //      node inputs into LDS ----
+    for (int e = tid; e < 3 * NP * NS; e += 256) am[e] = 0.f;   // am, tm, pm are contiguous
+    if (tid < NP) bet[tid] = tid < Td ? beta[node_row(tid)] : 0.f;
     if (tid < Td) {
-        bet[tid] = beta[node_row(tid)];
         pa[tid] = tree_parent(par, tid);
+        anc[tid] = 1ull << tid;
+        if constexpr (!CHANNEL) ge[tid * KS] = log_alpha[node_row(tid)];
     }
-    for (int e = tid; e < Td * DK; e += 256) {
-        const int i = e / DK, c = e % DK;
-        kr[i * KS + c] = to_f32(k[node_row(i) * DK + c]);
-        qr[i * KS + c] = to_f32(q[node_row(i) * DK + c]);
-        if (CHANNEL || c == 0) ge[i * KS + c] = CHANNEL ? log_alpha[node_row(i) * DK + c] : log_alpha[node_row(i)];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+        const int e = tid + 256 * u;
+        if (e < Td * V4) {
+            const int i = e / V4, c = 4 * (e % V4);
+            *reinterpret_cast<float4*>(kr + i * KS + c) = widen4<E>(kb[u]);
+            *reinterpret_cast<float4*>(qr + i * KS + c) = widen4<E>(qb[u]);
+            if constexpr (CHANNEL) *reinterpret_cast<float4*>(ge + i * KS + c) = lb[u];
+        }
     }
     __syncthreads();
-    // ---- path log-decays (thread c follows channel c down the tree); on the
-    //      last wave, the ancestor masks and the offsets of each node's
-    //      (ancestor-or-self) pairs in one list ----
-    if (tid < (CHANNEL ? DK : 1)) {
-        for (int i = 0; i < Td; ++i) {
-            const int p = pa[i];
-            if (p >= 0) ge[i * KS + tid] += ge[p * KS + tid];
+    // ---- root paths by pointer jumping: anc[i] holds the nodes from i up to,
+    //      not including, pa[i]; each round joins the segment of pa[i] and
+    //      jumps twice as far, so ceil(log2 Td) rounds reach the root ----
+    for (int r = Td > 1 ? 32 - __builtin_clz(Td - 1) : 0; r > 0; --r) {
+        uint64_t nm = 0;
+        int nj = -1;
+        if (tid < Td) {
+            const int j = pa[tid];
+            nm = anc[tid] | (j >= 0 ? anc[j] : 0ull);
+            nj = j >= 0 ? pa[j] : -1;
+        }
+        __syncthreads();
+        if (tid < Td) {
+            anc[tid] = nm;
+            pa[tid] = nj;
+        }
+        __syncthreads();
+    }
+    // ---- path log-decays g_i = sum of log alpha over the root path of i,
+    //      summed root first (per key channel for KDA); on the last wave, the
+    //      offsets of each node's (ancestor-or-self) pairs in one list ----
+    constexpr int GN = (NP * (CHANNEL ? DK : 1) + 255) / 256;
+    float gsum[GN];
+#pragma unroll
+    for (int u = 0; u < GN; ++u) {
+        const int e = tid + 256 * u;
+        gsum[u] = 0.f;
+        if (e < Td * (CHANNEL ? DK : 1)) {
+            const int i = CHANNEL ? e / DK : e, c = CHANNEL ? e % DK : 0;
+            for (uint64_t m = anc[i]; m; m &= m - 1ull) gsum[u] += ge[__builtin_ctzll(m) * KS + c];
         }
     }
     if (tid == 192) {
         int n = 0;
         for (int i = 0; i < Td; ++i) {
-            const int p = pa[i];
-            const uint64_t a = p < 0 ? 0ull : (anc[p] | (1ull << p));
-            anc[i] = a;
             off[i] = n;
-            n += __builtin_popcountll(a) + 1;
+            n += __builtin_popcountll(anc[i]);
         }
         off[Td] = n;
     }
     __syncthreads();
+#pragma unroll
+    for (int u = 0; u < GN; ++u) {
+        const int e = tid + 256 * u;
+        if (e < Td * (CHANNEL ? DK : 1)) {
+            const int i = CHANNEL ? e / DK : e, c = CHANNEL ? e % DK : 0;
+            ge[i * KS + c] = gsum[u];
+        }
+    }
+    __syncthreads();
     // ---- A and P over the (ancestor-or-self) pairs: the pairs of the list
-    //      one per thread, each a sum over the channels from LDS ----
+    //      four lanes each (a quad; lane s of it sums channels 16 cc + 4 s ..
+    //      + 3), the partial sums joined by two DPP steps ----
     const int npairs = off[Td];
-    for (int t = tid; t < npairs; t += 256) {
-        int lo = 0, hi = Td - 1;   // the node i with off[i] <= t < off[i + 1]
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (off[mid] <= t) lo = mid;
-            else hi = mid - 1;
-        }
-        const int i = lo;
-        uint64_t m = anc[i] | (1ull << i);
-        for (int r = t - off[i]; r > 0; --r) m &= m - 1ull;
-        const int j = __builtin_ctzll(m);
-        const float* ki = kr + i * KS;
-        const float* kj = kr + j * KS;
-        const float* qi = qr + i * KS;
+    const int sub = tid & 3;
+    for (int t = tid >> 2; t < (npairs + 63) / 64 * 64; t += 64) {   // quad-uniform trip count
         float a = 0.f, pp = 0.f;
-#pragma unroll 4
-        for (int c = 0; c < DK; c += 4) {
-            const float4 x = *reinterpret_cast<const float4*>(ki + c);
-            float4 y = *reinterpret_cast<const float4*>(kj + c);
-            const float4 z = *reinterpret_cast<const float4*>(qi + c);
-            if constexpr (CHANNEL) {
-                const float4 gi = *reinterpret_cast<const float4*>(ge + i * KS + c);
-                const float4 gj = *reinterpret_cast<const float4*>(ge + j * KS + c);
-                y = make_float4(y.x * __expf(gi.x - gj.x), y.y * __expf(gi.y - gj.y), y.z * __expf(gi.z - gj.z),
-                                y.w * __expf(gi.w - gj.w));
+        int i = 0, j = 0;
+        if (t < npairs) {
+            int lo = 0, hi = Td - 1;   // the node i with off[i] <= t < off[i + 1]
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (off[mid] <= t) lo = mid;
+                else hi = mid - 1;
             }
-            a += x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
-            pp += z.x * y.x + z.y * y.y + z.z * y.z + z.w * y.w;
+            i = lo;
+            uint64_t m = anc[i];   // ancestors and i itself
+            for (int r = t - off[i]; r > 0; --r) m &= m - 1ull;
+            j = __builtin_ctzll(m);
+            const float* ki = kr + i * KS;
+            const float* kj = kr + j * KS;
+            const float* qi = qr + i * KS;
+#pragma unroll 4
+            for (int c = 4 * sub; c < DK; c += 16) {
+                const float4 x = *reinterpret_cast<const float4*>(ki + c);
+                float4 y = *reinterpret_cast<const float4*>(kj + c);
+                const float4 z = *reinterpret_cast<const float4*>(qi + c);
+                if constexpr (CHANNEL) {
+                    const float4 gi = *reinterpret_cast<const float4*>(ge + i * KS + c);
+                    const float4 gj = *reinterpret_cast<const float4*>(ge + j * KS + c);
+                    y = make_float4(y.x * __expf(gi.x - gj.x), y.y * __expf(gi.y - gj.y),
+                                    y.z * __expf(gi.z - gj.z), y.w * __expf(gi.w - gj.w));
+                }
+                a += x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
+                pp += z.x * y.x + z.y * y.y + z.z * y.z + z.w * y.w;
+            }
         }
-        if constexpr (!CHANNEL) {
-            const float w = __expf(ge[i * KS] - ge[j * KS]);
-            a *= w;
-            pp *= w;
+        a = quad_sum(a);
+        pp = quad_sum(pp);
+        if (t < npairs && sub == 0) {
+            if constexpr (!CHANNEL) {
+                const float w = __expf(ge[i * KS] - ge[j * KS]);
+                a *= w;
+                pp *= w;
+            }
+            if (j != i) am[i * NS + j] = a * bet[i];
+            pm[i * NS + j] = pp;
         }
-        if (j != i) am[i * Td + j] = a * bet[i];
-        pm[i * Td + j] = pp;
     }
     __syncthreads();
     // ---- keys and queries scaled by their path decays, Kg = k e^g and
-    //      Qg = q e^g (the raw ones are spent); T = (I + A)^-1 Diag(beta):
-    //      thread j builds column j by forward substitution (only ancestors
-    //      contribute) ----
+    //      Qg = q e^g (the raw ones are spent); the diagonal blocks of
+    //      T = (I + A)^-1 Diag(beta) on wave 0: lane (bb, jc) builds column jc
+    //      of X_bb = (I + A_bb)^-1 by forward substitution in registers (dense:
+    //      the tree's zeros of A stay exact zeros of T), keeps X_bb and writes
+    //      T_bb = X_bb Diag(beta_bb) ----
     for (int e = tid; e < Td * DK; e += 256) {
         const int i = e / DK, c = e % DK;
         const float w = __expf(ge[i * KS + (CHANNEL ? c : 0)]);
         kr[i * KS + c] *= w;
         qr[i * KS + c] *= w;
     }
-    if (tid < Td) {
-        const int j = tid;
-        for (int i = 0; i < Td; ++i) {
-            float x = 0.f;
-            if (i == j) {
-                x = 1.f;
-            } else if (i > j && ((anc[i] >> j) & 1ull)) {
-                uint64_t m = anc[i] & ~((1ull << j) - 1ull);   // ancestors m >= j
-                while (m) {
-                    const int mi = __builtin_ctzll(m);
-                    m &= m - 1ull;
-                    x -= am[i * Td + mi] * tm[mi * Td + j];
+    if (wave == 0 && g4 < NT) {
+        const int bb = g4, jc = col;
+        const float* Ab = am + 16 * bb * NS + 16 * bb;
+        float x[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float arow[16];
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd)
+                if (4 * qd < i) {
+                    const float4 t = *reinterpret_cast<const float4*>(Ab + i * NS + 4 * qd);
+                    arow[4 * qd] = t.x; arow[4 * qd + 1] = t.y; arow[4 * qd + 2] = t.z; arow[4 * qd + 3] = t.w;
                 }
+            float acc = i == jc ? 1.f : 0.f;
+#pragma unroll
+            for (int m = 0; m < i; ++m) acc -= arow[m] * x[m];
+            x[i] = acc;
+        }
+        const float bj = bet[16 * bb + jc];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            xd[bb * 256 + i * 16 + jc] = x[i];
+            tm[(16 * bb + i) * NS + 16 * bb + jc] = x[i] * bj;
+        }
+    }
+    // ---- the tiles below the diagonal, one block row at a time (wave jt
+    //      builds T_{it, jt}): T_ij = -X_ii sum_{m = j}^{i - 1} A_im T_mj ----
+#pragma unroll
+    for (int it = 1; it < NT; ++it) {
+        __syncthreads();
+        if (wave < it) {
+            const int jt = wave;
+            f32x4 y = zero4();
+#pragma unroll
+            for (int mt = 0; mt < it; ++mt) {
+                if (mt < jt) continue;
+                const float4 a = *reinterpret_cast<const float4*>(am + (16 * it + col) * NS + 16 * mt + 4 * g4);
+                const float av[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+                for (int s2 = 0; s2 < 4; ++s2)
+                    y = MF::mma(av[s2], tm[(16 * mt + 4 * g4 + s2) * NS + 16 * jt + col], y);
             }
-            tm[i * Td + j] = x;
+            const float4 xa = *reinterpret_cast<const float4*>(xd + it * 256 + col * 16 + 4 * g4);
+            f32x4 z = zero4();
+            z = MF::mma(xa.x, y[0], z);
+            z = MF::mma(xa.y, y[1], z);
+            z = MF::mma(xa.z, y[2], z);
+            z = MF::mma(xa.w, y[3], z);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) tm[(16 * it + 4 * g4 + e) * NS + 16 * jt + col] = -z[e];
         }
-    }
-    __syncthreads();
-    if (tid < Td) {
-        const float bj = bet[tid];
-        for (int i = 0; i < Td; ++i) tm[i * Td + tid] *= bj;
-    }
-    __syncthreads();
-    // ---- M = P T (in A's place) ----
-    for (int e = tid; e < Td * Td; e += 256) {
-        const int i = e / Td, j = e % Td;
-        float x = 0.f;
-        uint64_t m = (anc[i] | (1ull << i)) & ~((1ull << j) - 1ull);
-        while (m) {
-            const int mi = __builtin_ctzll(m);
-            m &= m - 1ull;
-            x += pm[i * Td + mi] * tm[mi * Td + j];
-        }
-        am[e] = x;   // A is no longer read
     }
     __syncthreads();
 
     // ---- the outputs on the matrix cores (fp32 16x16x4), per value tile:
-    //      R = V - Kg S^T and Qg S^T for every node tile, then D = T R and
-    //      o = Qg S^T + M R.  The contractions over channels and over nodes
+    //      R = V - Kg S^T and Qg S^T for every node tile, D = T R, then
+    //      o = Qg S^T + P D.  The contractions over channels and over nodes
     //      use the permuted k-map: k-step s of lane group g is channel (or
     //      node) 16(s/4) + 4g + s%4, so an accumulator tile is directly the B
     //      operand of the next product and each lane's state slice is one
     //      16-byte load per four steps. ----
-    auto lds_or0 = [&](const float* base, int rowi, int coli) {
-        return (rowi < Td && coli < Td) ? base[rowi * Td + coli] : 0.f;
-    };
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
         const int vcol = 16 * (wave + 4 * u) + col;
@@ -282,24 +383,36 @@ __global__ __launch_bounds__(256) void tree_verify_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) R[mt][e] = vv[u][mt][e] - R[mt][e];
         }
-        // D = T R and o = O + M R (T and M are lower triangular in node order)
+        // D = T R, then o = O + P D (T and P are lower triangular in node order)
+        f32x4 Dt[NT];
 #pragma unroll
         for (int mt = 0; mt < NT; ++mt) {
-            f32x4 Dt = zero4(), Ot = O[mt];
-            const int i = 16 * mt + col;
+            Dt[mt] = zero4();
 #pragma unroll
-            for (int jt = 0; jt <= mt; ++jt)
+            for (int jt = 0; jt <= mt; ++jt) {
+                const float4 ta = *reinterpret_cast<const float4*>(tm + (16 * mt + col) * NS + 16 * jt + 4 * g4);
+                Dt[mt] = MF::mma(ta.x, R[jt][0], Dt[mt]);
+                Dt[mt] = MF::mma(ta.y, R[jt][1], Dt[mt]);
+                Dt[mt] = MF::mma(ta.z, R[jt][2], Dt[mt]);
+                Dt[mt] = MF::mma(ta.w, R[jt][3], Dt[mt]);
+            }
+        }
 #pragma unroll
-                for (int s2 = 0; s2 < 4; ++s2) {
-                    const int j = 16 * jt + 4 * g4 + s2;
-                    Dt = MF::mma(lds_or0(tm, i, j), R[jt][s2], Dt);
-                    Ot = MF::mma(lds_or0(am, i, j), R[jt][s2], Ot);
-                }
+        for (int mt = 0; mt < NT; ++mt) {
+            f32x4 Ot = O[mt];
+#pragma unroll
+            for (int jt = 0; jt <= mt; ++jt) {
+                const float4 pa4 = *reinterpret_cast<const float4*>(pm + (16 * mt + col) * NS + 16 * jt + 4 * g4);
+                Ot = MF::mma(pa4.x, Dt[jt][0], Ot);
+                Ot = MF::mma(pa4.y, Dt[jt][1], Ot);
+                Ot = MF::mma(pa4.z, Dt[jt][2], Ot);
+                Ot = MF::mma(pa4.w, Dt[jt][3], Ot);
+            }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int nd = 16 * mt + 4 * g4 + e;
                 if (nd < Td) {
-                    if (D) D[node_row(nd) * DV + vcol] = Dt[e];
+                    if (D) D[node_row(nd) * DV + vcol] = Dt[mt][e];
                     if (o) o[node_row(nd) * DV + vcol] = from_f32<E>(Ot[e]);
                 }
             }
@@ -378,7 +491,7 @@ __global__ __launch_bounds__(256) void tree_commit_kernel(
 template <typename E, bool CHANNEL, int DK, int NT>
 hipError_t launch_tree_nt(const TreeArgs& a) {
     const int64_t grid = a.B * a.H;
-    const size_t lds = TreeLds{(int)a.Td, DK}.floats() * sizeof(float);
+    const size_t lds = TreeLds{(int)a.Td, DK, 16 * NT}.floats() * sizeof(float);
     const auto fn = &tree_verify_kernel<E, CHANNEL, DK, NT>;
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -423,7 +536,9 @@ hipError_t tree_dispatch(const TreeArgs& a) {
 
 }  // namespace
 
-size_t tree_verify_lds_bytes(int64_t Td, int64_t dk) { return TreeLds{(int)Td, (int)dk}.floats() * sizeof(float); }
+size_t tree_verify_lds_bytes(int64_t Td, int64_t dk) {
+    return TreeLds{(int)Td, (int)dk, (int)(16 * ((Td + 15) / 16))}.floats() * sizeof(float);
+}
 
 hipError_t decode_tree_launch(const TreeArgs& a) { return tree_dispatch<false>(a); }
 hipError_t decode_tree_commit_launch(const TreeArgs& a) { return tree_dispatch<true>(a); }
