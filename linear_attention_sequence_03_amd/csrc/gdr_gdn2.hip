@@ -12,9 +12,12 @@
 // its output written after it; the next token's inputs are loaded while the
 // current one is applied (and only waited for at the top of the next step).
 // The state is read and written once; the time goes into the per-token
-// arithmetic and row reductions (three or four DPP steps); the scan is bound by
-// VALU issue.  Two rows per lane share each token's decay factors and widened
-// q, k, and the update is two FMAs per element.
+// arithmetic, the row reductions (three or four DPP steps) and the latency of
+// the token loads that the ring does not cover.  Two rows per lane share each
+// token's decay factors and widened q, k, and the update is two FMAs per
+// element.  No load or store sits under a branch inside the ring's whole
+// rounds: with a load that may or may not have been issued the compiler
+// cannot count the loads in flight and waits for all of them.
 #include <type_traits>
 
 #include "gdr_device.hpp"
@@ -164,9 +167,11 @@ __global__ __launch_bounds__(256) void gdn2_scan(
         const int64_t bth = (b * T + t) * H + h;    // token row of [B, T, H, *]
         landed(cur);
         __builtin_amdgcn_sched_barrier(0);
-        if (t + RING - 1 < T)
-            load_token<E, CHANNEL, DK, LPR>(nxt, q, k, v, log_alpha, erase, write, bth + (RING - 1) * H, DV,
+        {   // past the end, the last token again: every step issues the same loads
+            const int64_t tn = t + RING - 1 < T ? t + RING - 1 : T - 1;
+            load_token<E, CHANNEL, DK, LPR>(nxt, q, k, v, log_alpha, erase, write, (b * T + tn) * H + h, DV,
                                             row0, cl);
+        }
         float4 kk[kGdn2NJ], qq[kGdn2NJ], a[kGdn2NJ];
         const float a1 = CHANNEL ? 1.f : __expf(cur.la[0].x);
 #pragma unroll
@@ -206,24 +211,33 @@ __global__ __launch_bounds__(256) void gdn2_scan(
         }
 #pragma unroll
         for (int r = 0; r < RL; ++r) od[r] = row_sum<LPR>(od[r]);
-        if (cl == 0) {
-            o[bth * DV + row0] = from_f32<E>(od[0]);
-            o[bth * DV + row0 + 1] = from_f32<E>(od[1]);
-        }
+        // every lane of a row holds its sum: all store it (no branch around the store)
+        o[bth * DV + row0] = from_f32<E>(od[0]);
+        o[bth * DV + row0 + 1] = from_f32<E>(od[1]);
     };
     TokenIn<E, CHANNEL> buf[RING];
+    if (T > 0) {
 #pragma unroll
-    for (int i = 0; i + 1 < RING; ++i)
-        if (i < T) {
-            load_token<E, CHANNEL, DK, LPR>(buf[i], q, k, v, log_alpha, erase, write, (b * T + i) * H + h, DV,
-                                            row0, cl);
-            landed(buf[i]);   // nothing enters the loop in flight
-        }
-    for (int64_t t = 0; t < T; t += RING) {
+        for (int i = 0; i + 1 < RING; ++i)
+            load_token<E, CHANNEL, DK, LPR>(buf[i], q, k, v, log_alpha, erase, write,
+                                            (b * T + (i < T ? i : T - 1)) * H + h, DV, row0, cl);
 #pragma unroll
-        for (int i = 0; i < RING; ++i)
-            if (t + i < T) step(buf[i], buf[(i + RING - 1) % RING], t + i);
+        for (int i = 0; i + 1 < RING; ++i) landed(buf[i]);   // nothing enters the loop in flight
+#pragma unroll
+        for (int r = 0; r < RL; ++r)
+#pragma unroll
+            for (int j = 0; j < kGdn2NJ; ++j) asm volatile("" ::"v"(s[r][j]));
     }
+    // Whole rounds of RING tokens with no condition around any step (so the
+    // compiler can count the loads in flight), then the tail.
+    int64_t t = 0;
+    for (; t + RING <= T; t += RING) {
+#pragma unroll
+        for (int i = 0; i < RING; ++i) step(buf[i], buf[(i + RING - 1) % RING], t + i);
+    }
+#pragma unroll
+    for (int i = 0; i < RING; ++i)
+        if (t + i < T) step(buf[i], buf[(i + RING - 1) % RING], t + i);
     if (ST) {
 #pragma unroll
         for (int r = 0; r < RL; ++r)
