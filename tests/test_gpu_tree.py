@@ -47,8 +47,11 @@ def _commit(k, la, par, D, acc, S, io, inplace=False):
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("gate", ["scalar", "channel"])
 @pytest.mark.parametrize("d", [64, 128])
+# 17 and 40 nodes: two and three node tiles of 16 with a ragged last tile (the
+# verify kernel is specialised on the tile count; 64 nodes is four)
 @pytest.mark.parametrize("kind,Td", [("chain", 7), ("star", 5), ("binary", 16), ("random", 16),
-                                     ("random", 64), ("chain", 64), ("random", 1)])
+                                     ("random", 17), ("binary", 40), ("random", 64), ("chain", 64),
+                                     ("random", 1)])
 def test_tree_verify_and_commit(kind, Td, d, gate, io):
     B, H = 2, 3
     q, k, v, la, be, S = _inputs(B, Td, H, d, gate, io, seed=40 + Td + d)
