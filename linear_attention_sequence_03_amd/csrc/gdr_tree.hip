@@ -491,7 +491,7 @@ __global__ __launch_bounds__(256) void tree_commit_kernel(
 template <typename E, bool CHANNEL, int DK, int NT>
 hipError_t launch_tree_nt(const TreeArgs& a) {
     const int64_t grid = a.B * a.H;
-    const size_t lds = TreeLds{(int)a.Td, DK, 16 * NT}.floats() * sizeof(float);
+    const size_t lds = tree_verify_lds_bytes(a.Td, DK);   // NT = ceil(Td / 16) node tiles
     const auto fn = &tree_verify_kernel<E, CHANNEL, DK, NT>;
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
