@@ -33,7 +33,7 @@ def _inputs(B, T, H, d, gate, io, seed, s0_std=0.1):
 
 @pytest.mark.parametrize("T", [1, 37, 200])
 @pytest.mark.parametrize("gate", ["scalar", "channel"])
-@pytest.mark.parametrize("io,d", [("f32", 64), ("f32", 128), ("bf16", 128)])
+@pytest.mark.parametrize("io,d", [("f32", 64), ("f32", 128), ("bf16", 64), ("bf16", 128)])
 def test_gdn2_parity(io, d, gate, T):
     inp = _inputs(2, T, 3, d, gate, io, seed=200 + T + d)
     o, st = _run(inp, io)
