@@ -144,11 +144,14 @@ __device__ __forceinline__ float row_sum(float x) {
 // loop then reads them from LDS instead of waiting on global memory per token.
 constexpr int kMultiGroup = 16;
 
-template <int DK>
+// Rows per lane: the channel gate's per-token decay factors (an exp per key
+// channel) are shared by four rows of a lane, the scalar gate's by two (more
+// rows cost registers and occupancy that the scalar gate does not win back).
+template <int DK, bool CHANNEL>
 struct MultiShape {
     static constexpr int LPR = DK / 16;           // lanes per state row
     static constexpr int RPP = kWave / LPR;       // rows per pass of one wave
-    static constexpr int NPASS = 2;
+    static constexpr int NPASS = CHANNEL ? 4 : 2;
     static constexpr int RPW = RPP * NPASS;       // rows per wave
     static constexpr int WPH = DK / RPW;          // waves per (b, h) (d_v = d_k)
     static constexpr int WPB = WPH < 4 ? WPH : 4; // waves per workgroup
@@ -156,11 +159,11 @@ struct MultiShape {
 };
 
 template <typename E, bool CHANNEL, int DK>
-__global__ __launch_bounds__(64 * MultiShape<DK>::WPB) void decode_multi_kernel(
+__global__ __launch_bounds__(64 * MultiShape<DK, CHANNEL>::WPB) void decode_multi_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ log_alpha, const float* __restrict__ beta, const float* S_in,
     float* S_out, const int32_t* __restrict__ accepted, E* __restrict__ o, int H, int Td, int DV) {
-    using MS = MultiShape<DK>;
+    using MS = MultiShape<DK, CHANNEL>;
     constexpr int LPR = MS::LPR, RPP = MS::RPP, NPASS = MS::NPASS, RPW = MS::RPW, ROWS = MS::ROWS;
     constexpr int NTH = 64 * MS::WPB;
     constexpr int G = kMultiGroup;
@@ -269,7 +272,7 @@ __global__ __launch_bounds__(64 * MultiShape<DK>::WPB) void decode_multi_kernel(
 
 template <typename E, bool CHANNEL, int DK>
 static hipError_t launch_decode_multi(const DecodeMultiArgs& a) {
-    using MS = MultiShape<DK>;
+    using MS = MultiShape<DK, CHANNEL>;
     const int64_t blocks = a.B * a.H * (a.dv / MS::ROWS);
     hipLaunchKernelGGL((decode_multi_kernel<E, CHANNEL, DK>), dim3((unsigned)blocks), dim3(64 * MS::WPB), 0,
                        a.stream, (const E*)a.q, (const E*)a.k, (const E*)a.v, a.log_alpha, a.beta,
